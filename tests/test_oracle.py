@@ -1,0 +1,353 @@
+"""Pins for the fp64 CPU oracle: checks against things other than itself.
+
+Each test fixes part of the oracle with a value the pages print, a closed form,
+an invariant, a brute-force evaluation or an independent library routine.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import gpt_inputs as gi
+from oracle import gpt_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _page(key):
+    with open(os.path.join(GOLDEN, "page_values.json")) as f:
+        return json.load(f)[key]
+
+
+def small_shape(**kw):
+    base = dict(name="fd", depth=2, d_model=16, n_head=2, head_dim=8,
+                mlp_hidden=64, vocab=50, seq_len=12, batch=2, window=4,
+                window_pattern="SL", precision="fp32", init_std=0.3)
+    base.update(kw)
+    return gi.GPTShape(**base)
+
+
+def load(s, zero_lm_head=False):
+    W = gi.weights_f64(s, gi.make_weights(s, zero_lm_head=zero_lm_head))
+    X, Y = gi.make_tokens(s)
+    return W, X, Y
+
+
+# ---------------------------------------------------------------- page values
+
+def test_param_count_matches_d20_log():
+    pv = _page("d20_param_count")
+    s = gi.preset("d20")
+    assert O.param_count(s) == pv["value"]
+
+
+def test_param_shapes_are_the_logged_muon_groups():
+    # d20 log: 80 matrices [1280,1280], 20 of [1280,5120], 20 of [5120,1280]
+    s = gi.preset("d20")
+    shapes = [shp for n, shp in gi.param_shapes(s) if n not in ("E", "U")]
+    assert shapes.count((1280, 1280)) == 80
+    assert shapes.count((1280, 5120)) == 20
+    assert shapes.count((5120, 1280)) == 20
+
+
+@pytest.mark.parametrize("key", ["d20_step0_loss", "d24_step1_loss"])
+def test_zero_lm_head_loss_is_ln_vocab(key):
+    pv = _page(key)
+    # the closed form and the printed value agree
+    assert abs(math.log(pv["vocab"]) - pv["value"]) <= pv["abs_tol"]
+    # and the oracle reproduces it at that vocabulary on a small body
+    s = small_shape(vocab=pv["vocab"], seq_len=8, batch=1, depth=1,
+                    window_pattern="L", init_std=0.02)
+    W, X, Y = load(s, zero_lm_head=True)
+    loss = O.loss_only(s, W, X, Y)
+    assert abs(loss - pv["value"]) <= pv["abs_tol"]
+    assert abs(loss - math.log(pv["vocab"])) < 1e-12
+
+
+def test_zero_lm_head_gradients_closed_form():
+    s = small_shape(init_std=0.5)
+    W, X, Y = load(s, zero_lm_head=True)
+    loss, G = O.forward_backward(s, W, X, Y)
+    assert abs(loss - math.log(s.vocab)) < 1e-13
+    h, _, _ = O.forward(s, W, X)
+    n, _ = O.rmsnorm(h, s.norm_eps)
+    onehot = np.zeros((s.bt, s.vocab))
+    onehot[np.arange(s.bt), Y.reshape(-1)] = 1.0
+    dU = (1.0 / s.vocab - onehot).T @ n / s.bt
+    np.testing.assert_allclose(G["U"], dU, rtol=1e-12, atol=1e-15)
+    for k, g in G.items():
+        if k != "U":
+            assert np.all(g == 0.0), k
+
+
+# ---------------------------------------------------------------- special cases
+
+def test_identity_blocks_reduce_to_embedding_softmax():
+    """With Wo = W2 = 0 every block adds nothing to the residual, so the loss
+    is plain softmax cross-entropy of N(E[X]) U^T (scipy's log_softmax)."""
+    s = small_shape(init_std=0.5)
+    W, X, Y = load(s)
+    for l in range(s.depth):
+        W[f"L{l}.Wo"][...] = 0.0
+        W[f"L{l}.W2"][...] = 0.0
+    h0 = W["E"][X.reshape(-1)]
+    n = h0 / np.sqrt(np.mean(h0 ** 2, axis=1, keepdims=True) + s.norm_eps)
+    z = n @ W["U"].T
+    ref = -np.mean(scipy.special.log_softmax(z, axis=1)[np.arange(s.bt), Y.reshape(-1)])
+    assert abs(O.loss_only(s, W, X, Y) - ref) < 1e-12
+
+
+def test_zero_value_projection_leaves_only_mlp():
+    """Wv = 0 makes every attention output 0, so the block is h + MLP(h)."""
+    s = small_shape(init_std=0.5, depth=1, window_pattern="L")
+    W, X, Y = load(s)
+    W["L0.Wv"][...] = 0.0
+    h = W["E"][X.reshape(-1)]
+    m = h / np.sqrt(np.mean(h ** 2, axis=1, keepdims=True) + s.norm_eps)
+    h = h + (np.maximum(m @ W["L0.W1"].T, 0) ** 2) @ W["L0.W2"].T
+    n = h / np.sqrt(np.mean(h ** 2, axis=1, keepdims=True) + s.norm_eps)
+    z = n @ W["U"].T
+    ref = -np.mean(scipy.special.log_softmax(z, axis=1)[np.arange(s.bt), Y.reshape(-1)])
+    assert abs(O.loss_only(s, W, X, Y) - ref) < 1e-12
+
+
+def test_cross_entropy_matches_scipy_and_dz_rows_sum_to_zero():
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal((7, 33)) * 3
+    assert np.allclose(O.logsumexp_rows(z), scipy.special.logsumexp(z, axis=1), rtol=0, atol=1e-13)
+    p = np.exp(z - O.logsumexp_rows(z)[:, None])
+    y = rng.integers(0, 33, 7)
+    dz = p.copy()
+    dz[np.arange(7), y] -= 1
+    assert np.all(p >= 0)
+    assert np.allclose(dz.sum(axis=1), 0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- attention
+
+def brute_attention(q, k, v, window):
+    """Per-(i, j) loops with an explicit predicate; no matrix form."""
+    H, T, Dh = q.shape
+    o = np.zeros_like(q)
+    for h in range(H):
+        for i in range(T):
+            js = [j for j in range(T) if 0 <= i - j <= window - 1]
+            sc = [sum(q[h, i, c] * k[h, j, c] for c in range(Dh)) / math.sqrt(Dh) for j in js]
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            tot = sum(w)
+            for jj, j in enumerate(js):
+                o[h, i] += (w[jj] / tot) * v[h, j]
+    return o
+
+
+@pytest.mark.parametrize("window", [1, 3, 5, 16])
+def test_attention_matches_brute_force(window):
+    rng = np.random.default_rng(window)
+    q, k, v = (rng.standard_normal((2, 9, 4)) for _ in range(3))
+    np.testing.assert_allclose(O.attention_fwd(q, k, v, window),
+                               brute_attention(q, k, v, window), rtol=0, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(0)
+    T = 10
+    q, k, v = (rng.standard_normal((3, T, 8)) for _ in range(3))
+    # window >= T is plain causal attention
+    np.testing.assert_array_equal(O.attention_fwd(q, k, v, T), O.attention_fwd(q, k, v, 10 * T))
+    # row 0 sees only itself
+    np.testing.assert_allclose(O.attention_fwd(q, k, v, 4)[:, 0], v[:, 0], rtol=0, atol=1e-15)
+    # q = 0 gives the mean of the visible values
+    o = O.attention_fwd(np.zeros_like(q), k, v, 4)
+    for i in range(T):
+        lo = max(0, i - 3)
+        np.testing.assert_allclose(o[:, i], v[:, lo:i + 1].mean(axis=1), rtol=0, atol=1e-14)
+
+
+def test_attention_backward_finite_differences():
+    rng = np.random.default_rng(3)
+    q, k, v, do = (rng.standard_normal((2, 7, 4)) for _ in range(4))
+    dq, dk, dv = O.attention_bwd(do, q, k, v, 3)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [(0, 0, 0), (1, 3, 2), (0, 6, 3), (1, 5, 1)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = dict(q=q, k=k, v=v)
+            args_m = dict(q=q, k=k, v=v)
+            args_p[name], args_m[name] = xp, xm
+            fp = np.sum(O.attention_fwd(args_p["q"], args_p["k"], args_p["v"], 3) * do)
+            fm = np.sum(O.attention_fwd(args_m["q"], args_m["k"], args_m["v"], 3) * do)
+            assert abs((fp - fm) / (2 * eps) - g[idx]) < 1e-8, (name, idx)
+
+
+# ---------------------------------------------------------------- rope / norm
+
+def test_rope_invariants():
+    rng = np.random.default_rng(1)
+    T, H, Dh = 12, 2, 16
+    cos, sin = O.rope_tables(T, Dh, 10000.0)
+    x = rng.standard_normal((1, T, H, Dh))
+    y = O.rope(x, cos, sin)
+    # rotation keeps the norm of every head vector
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14)
+    # position 0 is the identity
+    np.testing.assert_array_equal(y[:, 0], x[:, 0])
+    # scores depend only on the relative position: shift both by s
+    q, k = rng.standard_normal(Dh), rng.standard_normal(Dh)
+    def rot(vec, t):
+        a = np.zeros((1, T, 1, Dh))
+        a[0, t, 0] = vec
+        return O.rope(a, cos, sin)[0, t, 0]
+    base = rot(q, 5) @ rot(k, 2)
+    for s_ in (1, 3, 6):
+        assert abs(rot(q, 5 + s_) @ rot(k, 2 + s_) - base) < 1e-12
+    # first frequency pair rotates by exactly t radians (theta_0 = 1)
+    e = np.zeros(Dh)
+    e[0] = 1.0
+    r = rot(e, 7)
+    assert abs(r[0] - math.cos(7)) < 1e-15 and abs(r[Dh // 2] - math.sin(7)) < 1e-15
+    # the adjoint is the inverse rotation
+    np.testing.assert_allclose(O.rope_bwd(y, cos, sin), x, rtol=0, atol=1e-14)
+
+
+def test_rmsnorm_commutes_with_rope_and_has_rms_one():
+    rng = np.random.default_rng(2)
+    T, H, Dh, eps = 6, 3, 8, 1e-6
+    cos, sin = O.rope_tables(T, Dh, 10000.0)
+    x = rng.standard_normal((2, T, H, Dh)) * 3
+    a = O.rmsnorm(O.rope(x, cos, sin), eps)[0]
+    b = O.rope(O.rmsnorm(x, eps)[0], cos, sin)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+    y, _ = O.rmsnorm(x, eps)
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), np.sqrt(ms / (ms + eps)), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- causality
+
+def test_causality_bit_identical():
+    s = gi.preset("tiny").replace(precision="fp32")
+    W, X, Y = load(s)
+    z = O.logits(s, W, X)
+    for i in (0, 17, 64, 126):
+        X2 = X.copy()
+        X2[:, i + 1:] = (X2[:, i + 1:] * 7 + 3) % s.vocab
+        z2 = O.logits(s, W, X2)
+        assert np.array_equal(z[:, :i + 1], z2[:, :i + 1]), i
+        if i + 1 < s.seq_len:
+            assert not np.array_equal(z[:, i + 1:], z2[:, i + 1:])
+
+
+def test_sliding_window_locality():
+    """With one 'S' layer of window W and no later attention, logits at i do
+    not depend on tokens older than i - W + 1 ... through attention.  The
+    embedding path still feeds position i itself, so perturb only j < i-W+1."""
+    s = small_shape(depth=2, window=3, window_pattern="SS", seq_len=12)
+    # last layer is forced full: use depth 1 pattern S via a 2-layer model
+    # whose full layer sees everything; so test the single S layer alone.
+    s = s.replace(depth=1)
+    s1 = gi.GPTShape(**{**s.__dict__, "window_pattern": "S"})
+    # depth 1 forces the only layer to 'L'; check that forcing happens
+    assert gi.layer_windows(s1) == [s1.seq_len]
+    s2 = small_shape(depth=3, window=3, window_pattern="S", seq_len=12)
+    assert gi.layer_windows(s2) == [3, 3, 12]
+    d24 = gi.preset("d24")
+    w = gi.layer_windows(d24)
+    assert [l for l in range(24) if w[l] == 2048] == [3, 7, 11, 15, 19, 23]
+    assert w.count(1024) == 18
+
+
+def test_window_layer_ignores_old_tokens():
+    """Single-layer check of the window: attention output at i is unchanged
+    when keys/values older than i-W+1 change."""
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((2, 11, 4)) for _ in range(3))
+    W_ = 4
+    o = O.attention_fwd(q, k, v, W_)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :3] += 5.0
+    v2[:, :3] -= 2.0
+    o2 = O.attention_fwd(q, k2, v2, W_)
+    # rows i >= 3 + W - 1 = 6 see only keys >= 3
+    assert np.array_equal(o[:, 6:], o2[:, 6:])
+    assert not np.allclose(o[:, 5], o2[:, 5])
+
+
+# ---------------------------------------------------------------- whole-step FD
+
+def _fd_check(s, n_coords, seed, rtol=1e-6, atol=1e-9):
+    W, X, Y = load(s)
+    loss, G = O.forward_backward(s, W, X, Y)
+    rng = np.random.default_rng(seed)
+    h = 1e-5
+    worst = 0.0
+    for name, (r, c) in gi.param_shapes(s):
+        flat = W[name].reshape(-1)
+        g = G[name].reshape(-1)
+        if name == "E":   # rows that appear in X carry gradient
+            rows = np.unique(X)
+            cand = (rows[:, None] * c + np.arange(c)[None]).reshape(-1)
+            idx = rng.choice(cand, size=min(n_coords, cand.size), replace=False)
+        else:
+            idx = rng.choice(r * c, size=min(n_coords, r * c), replace=False)
+        for i in idx:
+            old = flat[i]
+            flat[i] = old + h
+            lp = O.loss_only(s, W, X, Y)
+            flat[i] = old - h
+            lm = O.loss_only(s, W, X, Y)
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            err = abs(fd - g[i])
+            worst = max(worst, err / (atol + rtol * abs(g[i])))
+            assert err <= atol + rtol * abs(g[i]), (name, i, fd, g[i])
+    return worst
+
+
+def test_finite_differences_small_windowed_model():
+    _fd_check(small_shape(), n_coords=12, seed=0)
+
+
+def test_finite_differences_tiny_config():
+    s = gi.preset("tiny").replace(init_std=0.3)
+    _fd_check(s, n_coords=6, seed=1)
+
+
+def test_unseen_embedding_rows_have_zero_gradient():
+    s = small_shape(vocab=200)
+    W, X, Y = load(s)
+    _, G = O.forward_backward(s, W, X, Y)
+    seen = np.zeros(s.vocab, bool)
+    seen[np.unique(X)] = True
+    assert np.all(G["E"][~seen] == 0)
+    assert np.all(np.any(G["E"][seen] != 0, axis=1))
+
+
+# ---------------------------------------------------------------- inputs
+
+def test_zipf_head_probability():
+    # p(id 0) for Zipf(1.1) over V ranks
+    assert abs(gi.zipf_probabilities(32768, 1.1)[0] - 0.142) < 1e-3
+    assert abs(gi.zipf_probabilities(65536, 1.1)[0] - 0.137) < 1e-3
+    s = gi.preset("d24")
+    X, Y = gi.make_tokens(s)
+    assert X.shape == (8, 2048) and X.dtype == np.int32
+    assert np.array_equal(X[:, 1:], Y[:, :-1])
+    assert 0.13 < np.mean(X == 0) < 0.155
+    assert X.min() >= 0 and X.max() < s.vocab
+
+
+def test_bf16_rounding_is_rne():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 0.0, 3.0e38], np.float32)
+    b = gi.bf16_bits_from_f32(x)
+    back = gi.bf16_bits_to_f64(b)
+    # 1+2^-8 is a tie between 1 and 1+2^-7: even mantissa is 1.0
+    assert back[1] == 1.0
+    # 1+3*2^-8 ties between 1+2^-7 and 1+2^-6: even is 1+2^-6
+    assert back[2] == 1.0 + 2 ** -6
+    assert back[3] == -2.5 and back[0] == 1.0 and back[4] == 0.0
