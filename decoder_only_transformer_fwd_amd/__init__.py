@@ -1,0 +1,271 @@
+"""Python binding of the gfx950 GPT training-step library (``libgpt_mi355x.so``).
+
+The functions here only marshal arguments to the C ABI declared in
+``include/gpt.h``; every step of the computation runs in the library's HIP
+kernels.  PyTorch is used by ``Session`` for device memory and the stream.
+Importing this package without the built library raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgpt_mi355x.so")
+
+GPT_OK, GPT_EINVAL, GPT_ENULL, GPT_ETOKEN, GPT_EHIP, GPT_ENONFINITE, GPT_ESPACE, GPT_EALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
+
+EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_destroy",
+            "gpt_debug_tensor", "gpt_gemm", "gpt_strerror", "gpt_last_error"]
+
+
+class gpt_config(ctypes.Structure):
+    _fields_ = [
+        ("depth", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_head", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("mlp_hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32), ("batch", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("window_pattern", ctypes.c_char * 8), ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float),
+        ("precision", ctypes.c_int32), ("weights", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
+    ]
+
+
+class gpt_tensor_desc(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 24), ("offset", ctypes.c_int64),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: run decoder_only_transformer_fwd_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.gpt_param_layout.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(gpt_tensor_desc), I,
+                                     ctypes.POINTER(I), ctypes.POINTER(I64)]
+    lib.gpt_workspace_bytes.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(ctypes.c_size_t)]
+    lib.gpt_create.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(P)]
+    lib.gpt_step.argtypes = [P, P, P, P, ctypes.POINTER(F)]
+    lib.gpt_destroy.argtypes = [P]
+    lib.gpt_destroy.restype = None
+    lib.gpt_debug_tensor.argtypes = [P, I, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                     ctypes.POINTER(I)]
+    lib.gpt_gemm.argtypes = [I, I, I, I, I, P, P, P, P, I, I, P]
+    lib.gpt_strerror.argtypes = [I]
+    lib.gpt_strerror.restype = ctypes.c_char_p
+    lib.gpt_last_error.argtypes = []
+    lib.gpt_last_error.restype = ctypes.c_char_p
+    for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step",
+                 "gpt_debug_tensor", "gpt_gemm"):
+        getattr(lib, name).restype = I
+    return lib
+
+
+_lib = _load()
+
+
+class GPTError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.gpt_strerror(code).decode()
+        detail = _lib.gpt_last_error().decode()
+        super().__init__(f"{where}: {msg} ({code}): {detail}")
+
+
+def _check(code: int, where: str) -> None:
+    if code != GPT_OK:
+        raise GPTError(code, where)
+
+
+_PREC = {"fp32": GPT_FP32, "bf16": GPT_BF16, "fp8": GPT_FP8}
+
+
+def make_config(shape, weights: int = 0, workspace: int = 0, workspace_bytes: int = 0,
+                stream: int = 0) -> gpt_config:
+    """gpt_config from a workload description (any object with the fields of
+    ``gpt_inputs.GPTShape``) plus raw device pointers."""
+    c = gpt_config()
+    c.depth, c.d_model, c.n_head, c.head_dim = shape.depth, shape.d_model, shape.n_head, shape.head_dim
+    c.mlp_hidden, c.vocab, c.seq_len, c.batch = shape.mlp_hidden, shape.vocab, shape.seq_len, shape.batch
+    c.window = shape.window
+    c.window_pattern = shape.window_pattern.encode()
+    c.rope_base, c.norm_eps = shape.rope_base, shape.norm_eps
+    c.precision = _PREC[shape.precision]
+    c.weights, c.workspace, c.workspace_bytes, c.stream = weights or None, workspace or None, workspace_bytes, stream or None
+    return c
+
+
+def gpt_param_layout(cfg: gpt_config) -> Tuple[List[Tuple[str, int, int, int]], int]:
+    """[(name, element offset, rows, cols)], total elements."""
+    n = ctypes.c_int()
+    tot = ctypes.c_int64()
+    _check(_lib.gpt_param_layout(ctypes.byref(cfg), None, 0, ctypes.byref(n), ctypes.byref(tot)), "gpt_param_layout")
+    arr = (gpt_tensor_desc * n.value)()
+    _check(_lib.gpt_param_layout(ctypes.byref(cfg), arr, n.value, ctypes.byref(n), ctypes.byref(tot)),
+           "gpt_param_layout")
+    return [(a.name.decode(), a.offset, a.rows, a.cols) for a in arr], tot.value
+
+
+def gpt_workspace_bytes(cfg: gpt_config) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.gpt_workspace_bytes(ctypes.byref(cfg), ctypes.byref(b)), "gpt_workspace_bytes")
+    return b.value
+
+
+def gpt_create(cfg: gpt_config) -> int:
+    h = ctypes.c_void_p()
+    _check(_lib.gpt_create(ctypes.byref(cfg), ctypes.byref(h)), "gpt_create")
+    return h.value
+
+
+def gpt_step(model: int, tokens: int, targets: int, grads: int) -> float:
+    loss = ctypes.c_float()
+    _check(_lib.gpt_step(model, tokens, targets, grads, ctypes.byref(loss)), "gpt_step")
+    return loss.value
+
+
+def gpt_step_rc(model: int, tokens: int, targets: int, grads: int) -> Tuple[int, float]:
+    """Like gpt_step but returns (code, loss) instead of raising."""
+    loss = ctypes.c_float()
+    rc = _lib.gpt_step(model, tokens, targets, grads, ctypes.byref(loss))
+    return rc, loss.value
+
+
+def gpt_destroy(model: int) -> None:
+    _lib.gpt_destroy(model)
+
+
+def gpt_debug_tensor(model: int, which: int, layer: int = 0) -> Tuple[int, int, int, int]:
+    p = ctypes.c_void_p()
+    r, c, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int()
+    _check(_lib.gpt_debug_tensor(model, which, layer, ctypes.byref(p), ctypes.byref(r), ctypes.byref(c),
+                                 ctypes.byref(e)), "gpt_debug_tensor")
+    return p.value, r.value, c.value, e.value
+
+
+def gpt_gemm(dtype: int, layout: int, M: int, N: int, K: int, A: int, B: int, C: int,
+             workspace: int = 0, splits: int = 1, tile: int = -1, stream: int = 0) -> None:
+    _check(_lib.gpt_gemm(dtype, layout, M, N, K, A, B, C, workspace or None, splits, tile, stream or None),
+           "gpt_gemm")
+
+
+def gpt_strerror(code: int) -> str:
+    return _lib.gpt_strerror(code).decode()
+
+
+def gpt_create_rc(cfg: gpt_config) -> int:
+    """Return code of gpt_create (the handle, if any, is destroyed)."""
+    h = ctypes.c_void_p()
+    rc = _lib.gpt_create(ctypes.byref(cfg), ctypes.byref(h))
+    if rc == GPT_OK:
+        _lib.gpt_destroy(h)
+    return rc
+
+
+# ---------------------------------------------------------------------------
+# Session: device buffers owned by torch, one handle, one stream.
+# ---------------------------------------------------------------------------
+
+class Session:
+    """Holds the weights, workspace, gradients and token buffers of one
+    workload on a torch device and a library handle bound to them."""
+
+    def __init__(self, shape, weights: Dict[str, np.ndarray], device: str = "cuda:0", stream=None):
+        import torch
+        self.torch = torch
+        self.shape = shape
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        cfg = make_config(shape)
+        self.layout, self.total = gpt_param_layout(cfg)
+        pdt = torch.float32 if shape.precision == "fp32" else torch.bfloat16
+        host = np.zeros(self.total, dtype=np.float32 if pdt == torch.float32 else np.uint16)
+        for name, off, r, c in self.layout:
+            w = weights[name]
+            assert w.shape == (r, c), (name, w.shape, (r, c))
+            host[off:off + r * c] = w.reshape(-1).view(host.dtype)
+        ht = torch.from_numpy(host)
+        if pdt == torch.bfloat16:
+            ht = ht.view(torch.bfloat16)
+        # allocations are 256-byte aligned by torch's caching allocator
+        self.weights = ht.to(self.device)
+        self.grads = torch.empty(self.total, dtype=torch.float32, device=self.device)
+        cfg = make_config(shape, weights=self.weights.data_ptr())
+        self.ws_bytes = gpt_workspace_bytes(cfg)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        cfg = make_config(shape, self.weights.data_ptr(), self.workspace.data_ptr(), self.ws_bytes,
+                          self.stream.cuda_stream)
+        self.cfg = cfg
+        self.handle = gpt_create(cfg)
+        self.tokens = None
+        self.targets = None
+
+    def set_tokens(self, X: np.ndarray, Y: np.ndarray) -> None:
+        t = self.torch
+        self.tokens = t.from_numpy(np.ascontiguousarray(X, dtype=np.int32)).to(self.device)
+        self.targets = t.from_numpy(np.ascontiguousarray(Y, dtype=np.int32)).to(self.device)
+
+    def step(self) -> float:
+        return gpt_step(self.handle, self.tokens.data_ptr(), self.targets.data_ptr(), self.grads.data_ptr())
+
+    def step_rc(self) -> Tuple[int, float]:
+        return gpt_step_rc(self.handle, self.tokens.data_ptr(), self.targets.data_ptr(), self.grads.data_ptr())
+
+    def grads_numpy(self) -> Dict[str, np.ndarray]:
+        g = self.grads.cpu().numpy()
+        return {name: g[off:off + r * c].reshape(r, c).copy() for name, off, r, c in self.layout}
+
+    def grad_samples(self, indices: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+        """Gradient values at flat per-tensor indices, gathered on the device."""
+        t = self.torch
+        out = {}
+        offs = {name: off for name, off, _, _ in self.layout}
+        for name, idx in indices.items():
+            gi = t.from_numpy(idx + offs[name]).to(self.device)
+            out[name] = self.grads[gi].cpu().numpy().astype(np.float64)
+        return out
+
+    def grad_norms(self) -> Dict[str, float]:
+        return {name: float(self.grads[off:off + r * c].double().norm().item()) for name, off, r, c in self.layout}
+
+    def debug_tensor(self, which: int, layer: int = 0) -> np.ndarray:
+        t = self.torch
+        ptr, rows, cols, eb = gpt_debug_tensor(self.handle, which, layer)
+        n = rows * cols
+        dt = t.float32 if eb == 4 else t.bfloat16
+        # copy through a torch buffer on the same stream
+        buf = t.empty(n, dtype=dt, device=self.device)
+        import ctypes as _c
+        hip = _hip()
+        self.stream.synchronize()
+        rc = hip.hipMemcpy(_c.c_void_p(buf.data_ptr()), _c.c_void_p(ptr), _c.c_size_t(n * eb), 3)
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpy failed: {rc}")
+        return buf.float().cpu().numpy().reshape(rows, cols)
+
+    def close(self) -> None:
+        if self.handle:
+            gpt_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_hip_lib = None
+
+
+def _hip():
+    global _hip_lib
+    if _hip_lib is None:
+        _hip_lib = ctypes.CDLL("libamdhip64.so")
+        _hip_lib.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _hip_lib.hipMemcpy.restype = ctypes.c_int
+    return _hip_lib

@@ -1,0 +1,551 @@
+// Host runtime of the GPT step: configuration checks, parameter layout,
+// workspace carve-up, and the launch sequence of one forward+backward pass on
+// one HIP stream.  No device memory is allocated here: the caller passes the
+// weights, gradients, tokens and one workspace buffer.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt.h"
+#include "kernels.h"
+
+using namespace gk;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      return fail(GPT_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_));    \
+  } while (0)
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
+
+struct Shape {
+  int L, d, H, Dh, F, V, T, B, BT, Tp, dtype, es;
+  float eps, base;
+  std::vector<int> win;   // keys visible per layer
+};
+
+int check_config(const gpt_config* c, Shape& s) {
+  if (!c) return fail(GPT_ENULL, "cfg is NULL");
+  if (c->precision == GPT_FP8) return fail(GPT_EINVAL, "GPT_FP8 is not supported by this build");
+  if (c->precision != GPT_FP32 && c->precision != GPT_BF16) return fail(GPT_EINVAL, "unknown precision");
+  s.dtype = c->precision == GPT_FP32 ? DT_F32 : DT_BF16;
+  s.es = s.dtype == DT_F32 ? 4 : 2;
+  s.L = c->depth; s.d = c->d_model; s.H = c->n_head; s.Dh = c->head_dim; s.F = c->mlp_hidden;
+  s.V = c->vocab; s.T = c->seq_len; s.B = c->batch;
+  s.eps = c->norm_eps; s.base = c->rope_base;
+  if (s.L < 1 || s.d < 1 || s.H < 1 || s.F < 1 || s.V < 1 || s.T < 1 || s.B < 1)
+    return fail(GPT_EINVAL, "all sizes must be positive");
+  if ((long)s.H * s.Dh != s.d) return fail(GPT_EINVAL, "d_model must equal n_head * head_dim");
+  const bool dh_ok = s.dtype == DT_F32 ? (s.Dh == 32 || s.Dh == 64) : (s.Dh == 64 || s.Dh == 128);
+  if (!dh_ok) return fail(GPT_EINVAL, "unsupported head_dim for this precision");
+  if (s.d % 64 || s.F % 64) return fail(GPT_EINVAL, "d_model and mlp_hidden must be multiples of 64");
+  if (s.V % 8 || s.V > 65536) return fail(GPT_EINVAL, "vocab must be a multiple of 8 and <= 65536");
+  if ((long)s.B * s.T > 32768) return fail(GPT_EINVAL, "batch * seq_len must be <= 32768");
+  if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(GPT_EINVAL, "bad norm_eps or rope_base");
+  s.BT = s.B * s.T;
+  s.Tp = (s.T + 63) / 64 * 64;
+  const char* pat = c->window_pattern;
+  size_t plen = strnlen(pat, sizeof(c->window_pattern));
+  if (plen == 0 || plen == sizeof(c->window_pattern)) return fail(GPT_EINVAL, "window_pattern must be 1..7 chars");
+  for (size_t k = 0; k < plen; ++k)
+    if (pat[k] != 'S' && pat[k] != 'L') return fail(GPT_EINVAL, "window_pattern chars must be 'S' or 'L'");
+  s.win.assign(s.L, s.T);
+  for (int l = 0; l < s.L; ++l) {
+    char ch = pat[l % plen];
+    if (l == s.L - 1) ch = 'L';
+    if (ch == 'S') {
+      if (c->window < 1) return fail(GPT_EINVAL, "window must be >= 1 when the pattern has 'S'");
+      s.win[l] = c->window < s.T ? c->window : s.T;
+    } else if (ch != 'L') {
+      return fail(GPT_EINVAL, "window_pattern chars must be 'S' or 'L'");
+    }
+  }
+  return GPT_OK;
+}
+
+struct ParamOffsets {
+  long E, U;
+  std::vector<long> Wqkv, Wo, W1, W2;
+  long total;
+  std::vector<gpt_tensor_desc> descs;
+};
+
+void param_offsets(const Shape& s, ParamOffsets& p) {
+  long off = 0;
+  auto add = [&](const char* name, int rows, int cols) {
+    gpt_tensor_desc t;
+    memset(&t, 0, sizeof(t));
+    snprintf(t.name, sizeof(t.name), "%s", name);
+    t.offset = off;
+    t.rows = rows;
+    t.cols = cols;
+    p.descs.push_back(t);
+    long o = off;
+    off += (long)rows * cols;
+    off = (off + 127) / 128 * 128;
+    return o;
+  };
+  p.descs.clear();
+  p.Wqkv.resize(s.L); p.Wo.resize(s.L); p.W1.resize(s.L); p.W2.resize(s.L);
+  p.E = add("E", s.V, s.d);
+  char nm[24];
+  for (int l = 0; l < s.L; ++l) {
+    snprintf(nm, sizeof nm, "L%d.Wq", l); p.Wqkv[l] = add(nm, s.d, s.d);
+    snprintf(nm, sizeof nm, "L%d.Wk", l); add(nm, s.d, s.d);
+    snprintf(nm, sizeof nm, "L%d.Wv", l); add(nm, s.d, s.d);
+    snprintf(nm, sizeof nm, "L%d.Wo", l); p.Wo[l] = add(nm, s.d, s.d);
+    snprintf(nm, sizeof nm, "L%d.W1", l); p.W1[l] = add(nm, s.F, s.d);
+    snprintf(nm, sizeof nm, "L%d.W2", l); p.W2[l] = add(nm, s.d, s.F);
+  }
+  p.U = add("U", s.V, s.d);
+  p.total = off;
+}
+
+// ------------------------------------------------------------------ GEMM planning
+struct GemmPlan {
+  int tile, splits, k_split;
+};
+
+int tile_bm(int tile) { return tile == TILE_256x256 || tile == TILE_256x128 ? 256 : (tile == TILE_128x128 ? 128 : 64); }
+int tile_bn(int tile) { return tile == TILE_256x256 ? 256 : (tile == TILE_64x64 ? 64 : 128); }
+
+GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
+  GemmPlan g{TILE_64x64, 1, K};
+  const int bk = dtype == DT_F32 ? 32 : 64;
+  if (dtype == DT_F32) {
+    g.tile = (long)M * N >= 256L * 128 * 128 ? TILE_128x128 : TILE_64x64;
+  } else {
+    const int cand[3] = {TILE_256x256, TILE_256x128, TILE_128x128};
+    const double eff[3] = {1.0, 0.9, 0.75};
+    double best = 1e300;
+    for (int c = 0; c < 3; ++c) {
+      const long tiles = (long)((M + tile_bm(cand[c]) - 1) / tile_bm(cand[c])) *
+                         ((N + tile_bn(cand[c]) - 1) / tile_bn(cand[c]));
+      const long waves = (tiles + 255) / 256;
+      const double cost = (double)waves * tile_bm(cand[c]) * tile_bn(cand[c]) / eff[c];
+      if (cost < best) { best = cost; g.tile = cand[c]; }
+    }
+  }
+  if (layout == LAYOUT_MN || layout == LAYOUT_KN) {
+    const long tiles = (long)((M + tile_bm(g.tile) - 1) / tile_bm(g.tile)) * ((N + tile_bn(g.tile) - 1) / tile_bn(g.tile));
+    if (tiles < 192 && K >= 4 * bk * 4) {
+      int splits = (int)((256 + tiles - 1) / tiles);
+      if (splits > 16) splits = 16;
+      const int maxs = K / (4 * bk);
+      if (splits > maxs) splits = maxs;
+      if (splits > 1) {
+        int ks = (K + splits - 1) / splits;
+        ks = (ks + bk - 1) / bk * bk;
+        g.splits = (K + ks - 1) / ks;
+        g.k_split = ks;
+      }
+    }
+  }
+  if (g.splits == 1) g.k_split = K;
+  return g;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ model
+struct gpt_model {
+  gpt_config cfg;
+  Shape s;
+  ParamOffsets po;
+  hipStream_t st;
+  char* ws;
+  const char* W;
+  // workspace offsets (bytes)
+  struct Layer {
+    size_t n1, rstd1, qkv, rqk, qT, kT, vT, o, lse2, n2, rstd2, u, g;
+  };
+  std::vector<Layer> lay;
+  size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
+      cosb, sinb, keys, total;
+  size_t splitk_floats;
+  int xent_tile, xent_nblk;
+};
+
+namespace {
+
+int build_layout(gpt_model& m) {
+  const Shape& s = m.s;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t A = s.es;  // activation element size
+  const size_t BT = s.BT;
+  m.lay.resize(s.L);
+  for (int l = 0; l < s.L; ++l) {
+    auto& L = m.lay[l];
+    L.n1 = take(BT * s.d * A);
+    L.rstd1 = take(BT * 4);
+    L.qkv = take(BT * 3 * s.d * A);
+    L.rqk = take(BT * 2 * s.H * 4);
+    L.qT = take((size_t)s.B * s.H * s.Dh * s.Tp * A);
+    L.kT = take((size_t)s.B * s.H * s.Dh * s.Tp * A);
+    L.vT = take((size_t)s.B * s.H * s.Dh * s.Tp * A);
+    L.o = take(BT * s.d * A);
+    L.lse2 = take((size_t)s.B * s.H * s.Tp * 4);
+    L.n2 = take(BT * s.d * A);
+    L.rstd2 = take(BT * 4);
+    L.u = take(BT * s.F * A);
+    L.g = take(BT * s.F * A);
+  }
+  m.h = take(BT * s.d * 4);
+  m.nL = take(BT * s.d * A);
+  m.rstdL = take(BT * 4);
+  m.xent_tile = s.dtype == DT_F32 ? TILE_64x64 : TILE_256x256;
+  const int wn = tile_bn(m.xent_tile) / 2;
+  m.xent_nblk = (s.V + wn - 1) / wn;
+  m.part = take(BT * m.xent_nblk * 2 * 4);
+  m.tgt = take(BT * 4);
+  m.lse = take(BT * 4);
+  m.rowloss = take(BT * 4);
+  m.lossdev = take(64);
+  m.flag = take(64);
+  m.dz = take(BT * s.V * A);
+  m.dm = take(BT * s.d * 4);
+  m.dh = take(BT * s.d * 4);
+  m.dhA = take(BT * s.d * A);
+  m.du = take(BT * s.F * A);
+  m.dO = take(BT * s.d * A);
+  m.dOT = take((size_t)s.B * s.H * s.Dh * s.Tp * A);
+  m.Dv = take((size_t)s.B * s.H * s.Tp * 4);
+  m.dqkv = take(BT * 3 * s.d * A);
+  // split-K partials: the largest need among the planned products
+  size_t need = 0;
+  auto consider = [&](int layout, int M, int N, int K) {
+    GemmPlan g = plan_gemm(s.dtype, layout, M, N, K);
+    if (g.splits > 1) need = std::max(need, (size_t)g.splits * M * N);
+  };
+  consider(LAYOUT_KN, s.BT, s.d, s.V);
+  consider(LAYOUT_MN, s.V, s.d, s.BT);
+  consider(LAYOUT_KN, s.BT, s.F, s.d);
+  consider(LAYOUT_MN, s.d, s.F, s.BT);
+  consider(LAYOUT_KN, s.BT, s.d, s.F);
+  consider(LAYOUT_MN, s.F, s.d, s.BT);
+  consider(LAYOUT_KN, s.BT, s.d, s.d);
+  consider(LAYOUT_MN, s.d, s.d, s.BT);
+  consider(LAYOUT_KN, s.BT, s.d, 3 * s.d);
+  consider(LAYOUT_MN, 3 * s.d, s.d, s.BT);
+  m.splitk_floats = need;
+  m.splitk = take(std::max<size_t>(need, 1) * 4);
+  m.cosb = take((size_t)s.T * (s.Dh / 2) * 4);
+  m.sinb = take((size_t)s.T * (s.Dh / 2) * 4);
+  m.keys = take(BT * 4);
+  m.total = off;
+  return GPT_OK;
+}
+
+template <typename P>
+P* at(gpt_model& m, size_t off) { return (P*)(m.ws + off); }
+
+// One product with the planned tiling; splits go through the partial buffer
+// and an ordered reduction into C (fp32).
+int gemm(gpt_model& m, int layout, int epi, int M, int N, int K, const void* A, long lda, const void* B, long ldb,
+         void* C, long ldc, GemmArgs extra = GemmArgs{}) {
+  GemmArgs a = extra;
+  a.A = A; a.B = B; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = ldb; a.C = C; a.ldc = ldc;
+  if (a.alpha == 0.f) a.alpha = 1.f;
+  GemmPlan g = plan_gemm(m.s.dtype, layout, M, N, K);
+  if (epi == EPI_XENT_FWD) g = GemmPlan{m.xent_tile, 1, K};
+  if (epi != EPI_STORE_F32) g.splits = 1, g.k_split = K;
+  if (g.splits > 1 && ldc != N) g.splits = 1, g.k_split = K;
+  if (g.splits > 1) {
+    a.part = at<float>(m, m.splitk);
+    a.k_split = g.k_split;
+    if (gemm_launch(a, m.s.dtype, layout, EPI_PARTIAL, g.tile, g.splits, m.st))
+      return fail(GPT_EINVAL, "gemm variant not instantiated (partial)");
+    splitk_reduce(a.part, g.splits, (long)M * N, (float*)C, 0, m.st);
+    return GPT_OK;
+  }
+  a.k_split = K;
+  if (gemm_launch(a, m.s.dtype, layout, epi, g.tile, 1, m.st))
+    return fail(GPT_EINVAL, "gemm variant not instantiated");
+  return GPT_OK;
+}
+
+int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float* grads) {
+  const Shape& s = m.s;
+  const ParamOffsets& P = m.po;
+  const int dt = s.dtype;
+  const size_t es = s.es;
+  const char* W = m.W;
+  auto wp = [&](long off) { return (const void*)(W + off * es); };
+  hipStream_t st = m.st;
+  const int BT = s.BT, d = s.d, F = s.F, V = s.V, H = s.H, Dh = s.Dh;
+  float* h = at<float>(m, m.h);
+  int* flag = at<int>(m, m.flag);
+  const float* cosb = at<float>(m, m.cosb);
+  const float* sinb = at<float>(m, m.sinb);
+  int rc;
+
+  fill_f32((float*)flag, 1, 0.f, st);
+  embed_fwd(dt, tokens, targets, wp(P.E), h, BT, d, V, flag, st);
+  for (int l = 0; l < s.L; ++l) {
+    auto& Ly = m.lay[l];
+    rmsnorm_fwd(dt, h, m.ws + Ly.n1, at<float>(m, Ly.rstd1), BT, d, s.eps, st);
+    if ((rc = gemm(m, LAYOUT_KK, EPI_STORE, BT, 3 * d, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d, m.ws + Ly.qkv, 3 * d)))
+      return rc;
+    rope_qknorm_fwd(dt, m.ws + Ly.qkv, at<float>(m, Ly.rqk), m.ws + Ly.qT, m.ws + Ly.kT, m.ws + Ly.vT, cosb, sinb,
+                    s.B, s.T, s.Tp, H, Dh, s.eps, st);
+    AttnArgs aa{};
+    aa.qkv = m.ws + Ly.qkv; aa.qT = m.ws + Ly.qT; aa.kT = m.ws + Ly.kT; aa.vT = m.ws + Ly.vT;
+    aa.o = m.ws + Ly.o; aa.lse2 = at<float>(m, Ly.lse2);
+    aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.d = d; aa.window = s.win[l];
+    aa.scale = 1.0f / std::sqrt((float)Dh);
+    aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
+    if (attn_fwd(dt, Dh, aa, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
+    if ((rc = gemm(m, LAYOUT_KK, EPI_ACCUM_F32, BT, d, d, m.ws + Ly.o, d, wp(P.Wo[l]), d, h, d))) return rc;
+    rmsnorm_fwd(dt, h, m.ws + Ly.n2, at<float>(m, Ly.rstd2), BT, d, s.eps, st);
+    GemmArgs ex{};
+    ex.C2 = m.ws + Ly.g;
+    if ((rc = gemm(m, LAYOUT_KK, EPI_RELU2, BT, F, d, m.ws + Ly.n2, d, wp(P.W1[l]), d, m.ws + Ly.u, F, ex)))
+      return rc;
+    if ((rc = gemm(m, LAYOUT_KK, EPI_ACCUM_F32, BT, d, F, m.ws + Ly.g, F, wp(P.W2[l]), F, h, d))) return rc;
+  }
+  rmsnorm_fwd(dt, h, m.ws + m.nL, at<float>(m, m.rstdL), BT, d, s.eps, st);
+  {
+    GemmArgs ex{};
+    ex.aux = targets;
+    ex.part = at<float>(m, m.part);
+    ex.tgt = at<float>(m, m.tgt);
+    ex.nblk = m.xent_nblk;
+    if ((rc = gemm(m, LAYOUT_KK, EPI_XENT_FWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, nullptr, V, ex))) return rc;
+  }
+  xent_reduce(at<float>(m, m.part), at<float>(m, m.tgt), BT, m.xent_nblk, at<float>(m, m.lse),
+              at<float>(m, m.rowloss), st);
+  mean_reduce(at<float>(m, m.rowloss), BT, at<float>(m, m.lossdev), st);
+
+  // ---------------------------------------------------------------- backward
+  {
+    GemmArgs ex{};
+    ex.aux = targets;
+    ex.auxf = at<float>(m, m.lse);
+    ex.beta = 1.0f / (float)BT;
+    if ((rc = gemm(m, LAYOUT_KK, EPI_XENT_BWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, m.ws + m.dz, V, ex))) return rc;
+  }
+  float* dm = at<float>(m, m.dm);
+  float* dh = at<float>(m, m.dh);
+  void* dhA = m.ws + m.dhA;
+  if ((rc = gemm(m, LAYOUT_KN, EPI_STORE_F32, BT, d, V, m.ws + m.dz, V, wp(P.U), d, dm, d))) return rc;
+  if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, V, d, BT, m.ws + m.dz, V, m.ws + m.nL, d, grads + P.U, d))) return rc;
+  rmsnorm_bwd(dt, dm, m.ws + m.nL, at<float>(m, m.rstdL), dh, dhA, BT, d, 0, st);
+  for (int l = s.L - 1; l >= 0; --l) {
+    auto& Ly = m.lay[l];
+    GemmArgs ex{};
+    ex.aux = m.ws + Ly.u;
+    if ((rc = gemm(m, LAYOUT_KN, EPI_DRELU2, BT, F, d, dhA, d, wp(P.W2[l]), F, m.ws + m.du, F, ex))) return rc;
+    if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F))) return rc;
+    if ((rc = gemm(m, LAYOUT_KN, EPI_STORE_F32, BT, d, F, m.ws + m.du, F, wp(P.W1[l]), d, dm, d))) return rc;
+    if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d, grads + P.W1[l], d)))
+      return rc;
+    rmsnorm_bwd(dt, dm, m.ws + Ly.n2, at<float>(m, Ly.rstd2), dh, dhA, BT, d, 1, st);
+    if ((rc = gemm(m, LAYOUT_KN, EPI_STORE, BT, d, d, dhA, d, wp(P.Wo[l]), d, m.ws + m.dO, d))) return rc;
+    if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d))) return rc;
+    attn_bwd_pre(dt, m.ws + m.dO, m.ws + Ly.o, at<float>(m, m.Dv), m.ws + m.dOT, s.B, s.T, s.Tp, H, Dh, st);
+    AttnArgs aa{};
+    aa.qkv = m.ws + Ly.qkv; aa.qT = m.ws + Ly.qT; aa.kT = m.ws + Ly.kT; aa.vT = m.ws + Ly.vT;
+    aa.o = m.ws + Ly.o; aa.lse2 = at<float>(m, Ly.lse2);
+    aa.dO = m.ws + m.dO; aa.dOT = m.ws + m.dOT; aa.Dv = at<float>(m, m.Dv); aa.dqkv = m.ws + m.dqkv;
+    aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.d = d; aa.window = s.win[l];
+    aa.scale = 1.0f / std::sqrt((float)Dh);
+    aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
+    if (attn_bwd(dt, Dh, aa, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
+    rope_qknorm_bwd(dt, m.ws + m.dqkv, m.ws + Ly.qkv, at<float>(m, Ly.rqk), cosb, sinb, s.B, s.T, H, Dh, st);
+    if ((rc = gemm(m, LAYOUT_KN, EPI_STORE_F32, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d, dm, d)))
+      return rc;
+    if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d,
+                   grads + P.Wqkv[l], d)))
+      return rc;
+    rmsnorm_bwd(dt, dm, m.ws + Ly.n1, at<float>(m, Ly.rstd1), dh, dhA, BT, d, 1, st);
+  }
+  embed_bwd(tokens, dh, grads + P.E, BT, d, V, at<uint32_t>(m, m.keys), nullptr, nullptr, st);
+  HIP_TRY(hipGetLastError());
+  return GPT_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+extern "C" {
+
+int gpt_param_layout(const gpt_config* cfg, gpt_tensor_desc* out, int capacity, int* n_tensors,
+                     int64_t* total_elems) {
+  Shape s;
+  int rc = check_config(cfg, s);
+  if (rc) return rc;
+  ParamOffsets p;
+  param_offsets(s, p);
+  if (n_tensors) *n_tensors = (int)p.descs.size();
+  if (total_elems) *total_elems = p.total;
+  if (out) {
+    if (capacity < (int)p.descs.size()) return fail(GPT_EINVAL, "capacity too small for the layout");
+    for (size_t i = 0; i < p.descs.size(); ++i) out[i] = p.descs[i];
+  }
+  return GPT_OK;
+}
+
+int gpt_workspace_bytes(const gpt_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(GPT_ENULL, "bytes is NULL");
+  gpt_model m{};
+  int rc = check_config(cfg, m.s);
+  if (rc) return rc;
+  build_layout(m);
+  *bytes = m.total;
+  return GPT_OK;
+}
+
+int gpt_create(const gpt_config* cfg, gpt_model** out) {
+  if (!out) return fail(GPT_ENULL, "out is NULL");
+  *out = nullptr;
+  gpt_model* m = new (std::nothrow) gpt_model();
+  if (!m) return fail(GPT_EINVAL, "host allocation failed");
+  int rc = check_config(cfg, m->s);
+  if (rc) { delete m; return rc; }
+  if (!cfg->weights || !cfg->workspace) { delete m; return fail(GPT_ENULL, "weights and workspace are required"); }
+  if (((uintptr_t)cfg->weights | (uintptr_t)cfg->workspace) & (ALIGN - 1)) {
+    delete m;
+    return fail(GPT_EALIGN, "weights and workspace must be 256-byte aligned");
+  }
+  m->cfg = *cfg;
+  param_offsets(m->s, m->po);
+  build_layout(*m);
+  if (cfg->workspace_bytes < m->total) {
+    size_t need = m->total;
+    delete m;
+    return fail(GPT_ESPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  }
+  m->st = (hipStream_t)cfg->stream;
+  m->ws = (char*)cfg->workspace;
+  m->W = (const char*)cfg->weights;
+  // RoPE table: t * base^(-2i/Dh) evaluated in double, stored as fp32.
+  const int half = m->s.Dh / 2;
+  std::vector<float> c((size_t)m->s.T * half), sn((size_t)m->s.T * half);
+  for (int t = 0; t < m->s.T; ++t)
+    for (int i = 0; i < half; ++i) {
+      const double th = std::pow((double)m->s.base, -2.0 * i / m->s.Dh);
+      c[(size_t)t * half + i] = (float)std::cos(t * th);
+      sn[(size_t)t * half + i] = (float)std::sin(t * th);
+    }
+  hipError_t e1 = hipMemcpyAsync(m->ws + m->cosb, c.data(), c.size() * 4, hipMemcpyHostToDevice, m->st);
+  hipError_t e2 = hipMemcpyAsync(m->ws + m->sinb, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, m->st);
+  hipError_t e3 = hipStreamSynchronize(m->st);
+  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
+    delete m;
+    return fail(GPT_EHIP, "RoPE table upload failed");
+  }
+  *out = m;
+  return GPT_OK;
+}
+
+int gpt_step(gpt_model* m, const int32_t* tokens, const int32_t* targets, float* grads, float* loss) {
+  if (!m || !tokens || !targets || !grads || !loss) return fail(GPT_ENULL, "gpt_step: NULL argument");
+  if ((uintptr_t)grads & (ALIGN - 1)) return fail(GPT_EALIGN, "grads must be 256-byte aligned");
+  int rc = run_step(*m, tokens, targets, grads);
+  if (rc) return rc;
+  float lossv = 0.f;
+  int flag = 0;
+  HIP_TRY(hipMemcpyAsync(&lossv, m->ws + m->lossdev, 4, hipMemcpyDeviceToHost, m->st));
+  HIP_TRY(hipMemcpyAsync(&flag, m->ws + m->flag, 4, hipMemcpyDeviceToHost, m->st));
+  HIP_TRY(hipStreamSynchronize(m->st));
+  *loss = lossv;
+  if (flag) return fail(GPT_ETOKEN, "a token or target id is outside [0, vocab)");
+  if (!std::isfinite(lossv)) return fail(GPT_ENONFINITE, "loss is not finite");
+  return GPT_OK;
+}
+
+void gpt_destroy(gpt_model* m) { delete m; }
+
+int gpt_debug_tensor(gpt_model* m, int which, int layer, void** ptr, int64_t* rows, int64_t* cols,
+                     int* elem_bytes) {
+  if (!m || !ptr || !rows || !cols || !elem_bytes) return fail(GPT_ENULL, "NULL argument");
+  const Shape& s = m->s;
+  if ((which == 1 || which == 2 || which == 5) && (layer < 0 || layer >= s.L))
+    return fail(GPT_EINVAL, "layer out of range");
+  *rows = s.BT;
+  *elem_bytes = s.es;
+  switch (which) {
+    case 0: *ptr = m->ws + m->h; *cols = s.d; *elem_bytes = 4; break;
+    case 1: *ptr = m->ws + m->lay[layer].qkv; *cols = 3 * s.d; break;
+    case 2: *ptr = m->ws + m->lay[layer].o; *cols = s.d; break;
+    case 3: *ptr = m->ws + m->rowloss; *cols = 1; *elem_bytes = 4; break;
+    case 4: *ptr = m->ws + m->lse; *cols = 1; *elem_bytes = 4; break;
+    case 5: *ptr = m->ws + m->lay[layer].u; *cols = s.F; break;
+    default: return fail(GPT_EINVAL, "unknown tensor id");
+  }
+  return GPT_OK;
+}
+
+int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const void* B, float* C, float* workspace,
+             int splits, int tile, void* stream) {
+  if (!A || !B || !C) return fail(GPT_ENULL, "gpt_gemm: NULL operand");
+  if (dtype != DT_F32 && dtype != DT_BF16) return fail(GPT_EINVAL, "gpt_gemm: dtype");
+  if (layout < 0 || layout > 2) return fail(GPT_EINVAL, "gpt_gemm: layout");
+  if (M < 1 || N < 1 || K < 1 || M % 8 || N % 8 || K % 8) return fail(GPT_EINVAL, "gpt_gemm: sizes");
+  if (splits < 1 || (splits > 1 && (!workspace || layout == LAYOUT_KK)))
+    return fail(GPT_EINVAL, "gpt_gemm: splits");
+  if (tile < 0) tile = plan_gemm(dtype, layout, M, N, K).tile;
+  if (dtype == DT_F32 && tile != TILE_128x128 && tile != TILE_64x64) return fail(GPT_EINVAL, "gpt_gemm: tile");
+  if (dtype == DT_BF16 && tile == TILE_64x64) return fail(GPT_EINVAL, "gpt_gemm: tile");
+  GemmArgs a{};
+  a.A = A; a.B = B; a.M = M; a.N = N; a.K = K;
+  a.lda = layout == LAYOUT_MN ? M : K;
+  a.ldb = layout == LAYOUT_KK ? K : N;
+  a.C = C; a.ldc = N; a.alpha = 1.f;
+  hipStream_t st = (hipStream_t)stream;
+  const int bk = dtype == DT_F32 ? 32 : 64;
+  if (splits > 1) {
+    int ks = (K + splits - 1) / splits;
+    ks = (ks + bk - 1) / bk * bk;
+    splits = (K + ks - 1) / ks;
+    a.k_split = ks;
+    a.part = workspace;
+    if (gemm_launch(a, dtype, layout, EPI_PARTIAL, tile, splits, st)) return fail(GPT_EINVAL, "gpt_gemm: variant");
+    splitk_reduce(workspace, splits, (long)M * N, C, 0, st);
+  } else {
+    a.k_split = K;
+    if (gemm_launch(a, dtype, layout, EPI_STORE_F32, tile, 1, st)) return fail(GPT_EINVAL, "gpt_gemm: variant");
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_EHIP, std::string("launch: ") + hipGetErrorString(e));
+  return GPT_OK;
+}
+
+const char* gpt_strerror(int code) {
+  switch (code) {
+    case GPT_OK: return "ok";
+    case GPT_EINVAL: return "invalid configuration or argument";
+    case GPT_ENULL: return "NULL pointer";
+    case GPT_ETOKEN: return "token id out of range";
+    case GPT_EHIP: return "HIP runtime error";
+    case GPT_ENONFINITE: return "non-finite loss";
+    case GPT_ESPACE: return "workspace too small";
+    case GPT_EALIGN: return "misaligned pointer";
+    default: return "unknown error";
+  }
+}
+
+const char* gpt_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+// Shared device-side definitions for the gfx950 kernels of the GPT step.
+//
+// Element types: float (fp32 configuration), bf16 (stored as __bf16), and the
+// OCP fp8 formats (stored as uint8).  MFMA traits describe, per operand type,
+// how many elements one lane feeds into a 32x32 MFMA (EPL) and the K depth
+// of one instruction (KM).  For every 32x32 MFMA used here the A operand of
+// lane l is row (l % 32) and the B operand is column (l % 32); lane group
+// g = l / 32 supplies a fixed K subset, the same for A and B.  The 16 fp32
+// accumulators of lane l hold D[8*(r/4) + 4*g + r%4][l % 32], r = 0..15.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gk {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct fp8e4 { uint8_t v; };   // OCP E4M3FN code
+struct fp8e5 { uint8_t v; };   // OCP E5M2 code
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Store 4 consecutive fp32 values as T (8 or 16 bytes, naturally aligned).
+__device__ __forceinline__ void store4(float* p, floatx4 v) { *(floatx4*)p = v; }
+__device__ __forceinline__ void store4(bf16* p, floatx4 v) {
+  bf16x4 r = __builtin_convertvector(v, bf16x4);
+  *(bf16x4*)p = r;
+}
+__device__ __forceinline__ floatx4 load4(const float* p) { return *(const floatx4*)p; }
+__device__ __forceinline__ floatx4 load4(const bf16* p) {
+  bf16x4 r = *(const bf16x4*)p;
+  return __builtin_convertvector(r, floatx4);
+}
+
+// ---------------------------------------------------------------- MFMA traits
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  static constexpr int KM = 16;   // K per instruction
+  static constexpr int EPL = 8;   // elements per lane per operand
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static floatx16 mma(frag a, frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KM = 2;
+  static constexpr int EPL = 1;
+  typedef float frag;
+  __device__ __forceinline__ static floatx16 mma(frag a, frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// fp8 x fp8 with neutral (2^0) block scales: format codes 0 = E4M3, 1 = E5M2.
+template <int FA, int FB> struct MfmaF8 {
+  static constexpr int KM = 64;
+  static constexpr int EPL = 32;
+  typedef intx8 frag;
+  __device__ __forceinline__ static floatx16 mma(frag a, frag b, floatx16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
+  }
+};
+
+// ---------------------------------------------------------------- LDS layout
+// Tiles are stored row by row; each row is cut into 16-byte chunks and chunk c
+// of row r lives at chunk slot c ^ swz(r) so that 16 consecutive rows read at
+// the same chunk hit distinct bank groups (64 banks x 4 bytes).
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int row) {
+  constexpr int NCH = ROW_BYTES / 16;
+  constexpr int RP = (256 / ROW_BYTES) > 0 ? (256 / ROW_BYTES) : 1;
+  return (row / RP) & (NCH - 1);
+}
+template <int ROW_BYTES>
+__device__ __forceinline__ int lds_off(int row, int byte_in_row) {
+  const int c = byte_in_row >> 4;
+  return row * ROW_BYTES + (((c ^ swz<ROW_BYTES>(row))) << 4) + (byte_in_row & 15);
+}
+
+// Read `bytes` (4, 8, 16 or 32) at (row, byte) of a swizzled LDS tile.
+template <int ROW_BYTES, int BYTES>
+__device__ __forceinline__ void lds_read(const char* base, int row, int byte, void* out) {
+  if constexpr (BYTES == 32) {
+    *(u32x4*)out = *(const u32x4*)(base + lds_off<ROW_BYTES>(row, byte));
+    *((u32x4*)out + 1) = *(const u32x4*)(base + lds_off<ROW_BYTES>(row, byte + 16));
+  } else if constexpr (BYTES == 16) {
+    *(u32x4*)out = *(const u32x4*)(base + lds_off<ROW_BYTES>(row, byte));
+  } else if constexpr (BYTES == 8) {
+    *(u32x2*)out = *(const u32x2*)(base + lds_off<ROW_BYTES>(row, byte));
+  } else {
+    *(uint32_t*)out = *(const uint32_t*)(base + lds_off<ROW_BYTES>(row, byte));
+  }
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// Sum over aligned groups of W lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace gk

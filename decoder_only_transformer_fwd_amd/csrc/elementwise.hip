@@ -1,0 +1,430 @@
+// Bandwidth-bound kernels of the GPT step: embedding, RMSNorm, rotary + QK
+// norm, attention-backward preparation, cross-entropy row reduction and the
+// embedding-gradient segmented sum.  Each kernel reads and writes every byte
+// once with 8- or 16-byte accesses; per-row statistics are wave reductions.
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+
+// ------------------------------------------------------------------ embedding
+// h[r, :] = E[tokens[r], :] (fp32).  An id outside [0, vocab) sets *flag and
+// writes a zero row.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restrict__ tok,
+                                                        const int32_t* __restrict__ tgt,
+                                                        const T* __restrict__ E, float* __restrict__ h,
+                                                        int rows, int d, int vocab, int* flag) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int id = tok[row];
+  const int y = tgt[row];
+  const bool ok = id >= 0 && id < vocab;
+  if ((!ok || y < 0 || y >= vocab) && lane == 0) atomicOr(flag, 1);
+  for (int c = lane * 4; c < d; c += 256) {
+    floatx4 v = {0.f, 0.f, 0.f, 0.f};
+    if (ok) v = load4(E + (long)id * d + c);
+    store4(h + (long)row * d + c, v);
+  }
+}
+
+// ------------------------------------------------------------------ rmsnorm
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ y,
+                                                          float* __restrict__ rstd, int rows, int d,
+                                                          float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* xr = x + (long)row * d;
+  float ss = 0.f;
+  for (int c = lane * 4; c < d; c += 256) {
+    const floatx4 v = load4(xr + c);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int c = lane * 4; c < d; c += 256) store4(y + (long)row * d + c, load4(xr + c) * r);
+  if (lane == 0) rstd[row] = r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __restrict__ y,
+                                                          const float* __restrict__ rstd, float* __restrict__ dx,
+                                                          T* __restrict__ dxa, int rows, int d, int accumulate) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const long base = (long)row * d;
+  float dot = 0.f;
+  for (int c = lane * 4; c < d; c += 256) {
+    const floatx4 a = load4(dy + base + c);
+    const floatx4 b = load4(y + base + c);
+    dot += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+  }
+  dot = wave_sum(dot) / (float)d;
+  const float r = rstd[row];
+  for (int c = lane * 4; c < d; c += 256) {
+    floatx4 g = (load4(dy + base + c) - load4(y + base + c) * dot) * r;
+    if (accumulate) g += load4(dx + base + c);
+    store4(dx + base + c, g);
+    store4(dxa + base + c, g);
+  }
+}
+
+// ------------------------------------------------------------------ rotary + QK norm
+// Grid (ceil(T/64), H, B); 256 threads.  For q and k of head h: rotate the
+// half-split pairs (x[i], x[i+Dh/2]) by t*theta_i, RMS-normalise the head
+// vector, write it back in place and into the transposed copy [B][H][Dh][Tp];
+// v is only transposed.  Tokens t >= T are written as zeros in the copies.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rstd_qk,
+                                                              T* __restrict__ qT, T* __restrict__ kT,
+                                                              T* __restrict__ vT, const float* __restrict__ cosb,
+                                                              const float* __restrict__ sinb, int Tn, int Tp,
+                                                              int H, float eps) {
+  constexpr int HALF = DH / 2;
+  constexpr int TPP = 64 / HALF;      // tokens per wave pass
+  constexpr int LDW = 64 + 16 / sizeof(T) * 2;  // padded tile row (elements), 16-byte multiple
+  __shared__ __attribute__((aligned(16))) T tile[DH * LDW];
+  const int t0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / HALF, i = lane % HALF;
+  const int d = H * DH;
+  const long row3 = 3L * d;
+  for (int part = 0; part < 3; ++part) {
+    const int col = part * d + h * DH;
+    for (int tt = wave * 16; tt < wave * 16 + 16; tt += TPP) {
+      const int tl = tt + sub;
+      const int t = t0 + tl;
+      const bool ok = t < Tn;
+      float y1 = 0.f, y2 = 0.f;
+      T* px = qkv + ((long)b * Tn + t) * row3 + col;
+      if (ok) {
+        y1 = to_f32(px[i]);
+        y2 = to_f32(px[i + HALF]);
+      }
+      if (part < 2) {
+        float c = 0.f, s = 0.f;
+        if (ok) {
+          c = cosb[t * HALF + i];
+          s = sinb[t * HALF + i];
+        }
+        const float r1 = y1 * c - y2 * s;
+        const float r2 = y1 * s + y2 * c;
+        const float ss = group_sum<HALF>(r1 * r1 + r2 * r2);
+        const float r = 1.0f / sqrtf(ss / (float)DH + eps);
+        y1 = r1 * r;
+        y2 = r2 * r;
+        if (ok) {
+          px[i] = from_f32<T>(y1);
+          px[i + HALF] = from_f32<T>(y2);
+          if (i == 0) rstd_qk[((long)b * Tn + t) * 2 * H + part * H + h] = r;
+        }
+      }
+      tile[i * LDW + tl] = from_f32<T>(ok ? y1 : 0.f);
+      tile[(i + HALF) * LDW + tl] = from_f32<T>(ok ? y2 : 0.f);
+    }
+    __syncthreads();
+    T* dst = part == 0 ? qT : (part == 1 ? kT : vT);
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int CPR = 64 / EPC;    // chunks per row
+    for (int c = threadIdx.x; c < DH * CPR; c += 256) {
+      const int r = c / CPR, cc = c % CPR;
+      if (t0 + cc * EPC < Tp)
+        *(u32x4*)(dst + (((long)b * H + h) * DH + r) * Tp + t0 + cc * EPC) =
+            *(const u32x4*)(tile + r * LDW + cc * EPC);
+    }
+    __syncthreads();
+  }
+}
+
+// dq' = r * (g - y * mean(g*y)), then the inverse rotation; in place on the
+// q and k columns of dqkv.  One wave per token row.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv,
+                                                              const float* __restrict__ rstd_qk,
+                                                              const float* __restrict__ cosb,
+                                                              const float* __restrict__ sinb, int rows, int Tn,
+                                                              int H) {
+  constexpr int HALF = DH / 2;
+  constexpr int VPP = 64 / HALF;   // head vectors per pass
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int t = row % Tn;
+  const int sub = lane / HALF, i = lane % HALF;
+  const int d = H * DH;
+  const float c = cosb[t * HALF + i], s = sinb[t * HALF + i];
+  for (int v0 = 0; v0 < 2 * H; v0 += VPP) {
+    const int v = v0 + sub;       // 0..2H-1: q heads then k heads
+    if (v >= 2 * H) continue;
+    const long off = (long)row * 3 * d + (long)v * DH;  // q at h*DH, k at d + h*DH
+    const float g1 = to_f32(dqkv[off + i]), g2 = to_f32(dqkv[off + i + HALF]);
+    const float y1 = to_f32(qkv[off + i]), y2 = to_f32(qkv[off + i + HALF]);
+    const float dot = group_sum<HALF>(g1 * y1 + g2 * y2) / (float)DH;
+    const float r = rstd_qk[(long)row * 2 * H + v];
+    const float d1 = r * (g1 - y1 * dot), d2 = r * (g2 - y2 * dot);
+    dqkv[off + i] = from_f32<T>(d1 * c + d2 * s);
+    dqkv[off + i + HALF] = from_f32<T>(-d1 * s + d2 * c);
+  }
+}
+
+// D[b,h,t] = sum_c dO[t, h*Dh + c] * O[t, h*Dh + c]; dO^T copy [B][H][Dh][Tp].
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const T* __restrict__ dO, const T* __restrict__ O,
+                                                           float* __restrict__ Dv, T* __restrict__ dOT, int Tn,
+                                                           int Tp, int H) {
+  constexpr int HALF = DH / 2;
+  constexpr int TPP = 64 / HALF;
+  constexpr int LDW = 64 + 16 / sizeof(T) * 2;
+  __shared__ __attribute__((aligned(16))) T tile[DH * LDW];
+  const int t0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / HALF, i = lane % HALF;
+  const int d = H * DH;
+  for (int tt = wave * 16; tt < wave * 16 + 16; tt += TPP) {
+    const int tl = tt + sub;
+    const int t = t0 + tl;
+    const bool ok = t < Tn;
+    float g1 = 0.f, g2 = 0.f, o1 = 0.f, o2 = 0.f;
+    if (ok) {
+      const long off = ((long)b * Tn + t) * d + h * DH;
+      g1 = to_f32(dO[off + i]);
+      g2 = to_f32(dO[off + i + HALF]);
+      o1 = to_f32(O[off + i]);
+      o2 = to_f32(O[off + i + HALF]);
+    }
+    const float s = group_sum<HALF>(g1 * o1 + g2 * o2);
+    if (i == 0 && t < Tp) Dv[((long)b * H + h) * Tp + t] = ok ? s : 0.f;
+    tile[i * LDW + tl] = from_f32<T>(g1);
+    tile[(i + HALF) * LDW + tl] = from_f32<T>(g2);
+  }
+  __syncthreads();
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int CPR = 64 / EPC;
+  for (int c = threadIdx.x; c < DH * CPR; c += 256) {
+    const int r = c / CPR, cc = c % CPR;
+    if (t0 + cc * EPC < Tp)
+      *(u32x4*)(dOT + (((long)b * H + h) * DH + r) * Tp + t0 + cc * EPC) =
+          *(const u32x4*)(tile + r * LDW + cc * EPC);
+  }
+}
+
+// ------------------------------------------------------------------ cross-entropy rows
+// lse[m] = log sum_b se_b * exp(mx_b - M), row_loss[m] = lse[m] - z[m, y_m].
+__global__ __launch_bounds__(256) void xent_reduce_kernel(const float* __restrict__ part,
+                                                          const float* __restrict__ tgt, int rows, int nblk,
+                                                          float* __restrict__ lse, float* __restrict__ row_loss) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* p = part + (long)row * nblk * 2;
+  float mx = -INFINITY;
+  for (int b = lane; b < nblk; b += 64) mx = fmaxf(mx, p[2 * b]);
+  mx = wave_max(mx);
+  float s = 0.f;
+  for (int b = lane; b < nblk; b += 64) {
+    const float m = p[2 * b];
+    if (m > -INFINITY) s += p[2 * b + 1] * expf(m - mx);
+  }
+  s = wave_sum(s);
+  if (lane == 0) {
+    const float l = mx + logf(s);
+    lse[row] = l;
+    row_loss[row] = l - tgt[row];
+  }
+}
+
+// out[0] = (sum x) / n, summed in a fixed order by one work-group.
+__global__ __launch_bounds__(1024) void mean_reduce_kernel(const float* __restrict__ x, int n, float* out) {
+  __shared__ double red[1024];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += 1024) s += (double)x[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = (float)(red[0] / (double)n);
+}
+
+// ------------------------------------------------------------------ embedding gradient
+// Sort keys (id << PB | position) in one work-group (bitonic, in LDS), so
+// that equal ids form runs in position order.  Then one work-group per run
+// head and 256-column slice sums the run's rows in order: deterministic.
+// Ids outside [0, vocab) get the key 0xFFFFFFFF and are skipped by the sum
+// (vocab <= 65536 and rows <= 32768 keep every valid key below 2^31).
+__global__ __launch_bounds__(1024) void sort_keys_kernel(const int32_t* __restrict__ tok, int rows, int pbits,
+                                                         int n2, int vocab, uint32_t* __restrict__ keys_out) {
+  extern __shared__ uint32_t sk[];
+  for (int i = threadIdx.x; i < n2; i += 1024) {
+    uint32_t k = 0xFFFFFFFFu;
+    if (i < rows) {
+      const int id = tok[i];
+      if (id >= 0 && id < vocab) k = (((uint32_t)id) << pbits) | (uint32_t)i;
+    }
+    sk[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += 1024) {
+        const int p = i ^ j;
+        if (p > i) {
+          const uint32_t a = sk[i], b = sk[p];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) {
+            sk[i] = b;
+            sk[p] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < rows; i += 1024) keys_out[i] = sk[i];
+}
+
+__global__ __launch_bounds__(64) void embed_bwd_runs_kernel(const uint32_t* __restrict__ keys,
+                                                            const float* __restrict__ dh, float* __restrict__ dE,
+                                                            int rows, int d, int pbits, int vocab) {
+  const int i = blockIdx.x;
+  const uint32_t id = keys[i] >> pbits;
+  if (id >= (uint32_t)vocab) return;                     // invalid id
+  if (i > 0 && (keys[i - 1] >> pbits) == id) return;   // not a run head
+  const uint32_t pmask = (1u << pbits) - 1u;
+  const int c = blockIdx.y * 256 + threadIdx.x * 4;
+  if (c >= d) return;
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int j = i; j < rows; ++j) {
+    const uint32_t kk = keys[j];
+    if ((kk >> pbits) != id) break;
+    s += load4(dh + (long)(kk & pmask) * d + c);
+  }
+  store4(dE + (long)id * d + c, s);
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* p, long n, float v) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ------------------------------------------------------------------ launchers
+void embed_fwd(int dtype, const int32_t* tokens, const int32_t* targets, const void* E, float* h, int rows, int d,
+               int vocab, int* flag, hipStream_t st) {
+  dim3 g((rows + 3) / 4);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(embed_fwd_kernel<bf16>, g, dim3(256), 0, st, tokens, targets, (const bf16*)E, h, rows, d,
+                       vocab, flag);
+  else
+    hipLaunchKernelGGL(embed_fwd_kernel<float>, g, dim3(256), 0, st, tokens, targets, (const float*)E, h, rows, d,
+                       vocab, flag);
+}
+
+void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps, hipStream_t st) {
+  dim3 g((rows + 3) / 4);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, g, dim3(256), 0, st, x, (bf16*)y, rstd, rows, d, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, g, dim3(256), 0, st, x, (float*)y, rstd, rows, d, eps);
+}
+
+void rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* rstd, float* dx, void* dxa, int rows,
+                 int d, int accumulate, hipStream_t st) {
+  dim3 g((rows + 3) / 4);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, g, dim3(256), 0, st, dy, (const bf16*)y, rstd, dx, (bf16*)dxa,
+                       rows, d, accumulate);
+  else
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, g, dim3(256), 0, st, dy, (const float*)y, rstd, dx,
+                       (float*)dxa, rows, d, accumulate);
+}
+
+template <typename T, int DH>
+static void rope_fwd_t(void* qkv, float* rq, void* qT, void* kT, void* vT, const float* c, const float* s, int B,
+                       int T_, int Tp, int H, float eps, hipStream_t st) {
+  dim3 g((T_ + 63) / 64, H, B);
+  hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, DH>), g, dim3(256), 0, st, (T*)qkv, rq, (T*)qT, (T*)kT, (T*)vT, c,
+                     s, T_, Tp, H, eps);
+}
+
+void rope_qknorm_fwd(int dtype, void* qkv, float* rq, void* qT, void* kT, void* vT, const float* c,
+                     const float* s, int B, int T_, int Tp, int H, int Dh, float eps, hipStream_t st) {
+#define RF(TT, D) \
+  if (Dh == D) return rope_fwd_t<TT, D>(qkv, rq, qT, kT, vT, c, s, B, T_, Tp, H, eps, st);
+  if (dtype == DT_BF16) { RF(bf16, 32) RF(bf16, 64) RF(bf16, 128) }
+  else { RF(float, 32) RF(float, 64) RF(float, 128) }
+#undef RF
+}
+
+template <typename T, int DH>
+static void rope_bwd_t(void* dqkv, const void* qkv, const float* rq, const float* c, const float* s, int B, int T_,
+                       int H, hipStream_t st) {
+  const int rows = B * T_;
+  hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, DH>), dim3((rows + 3) / 4), dim3(256), 0, st, (T*)dqkv,
+                     (const T*)qkv, rq, c, s, rows, T_, H);
+}
+
+void rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const float* rq, const float* c, const float* s,
+                     int B, int T_, int H, int Dh, hipStream_t st) {
+#define RB(TT, D) \
+  if (Dh == D) return rope_bwd_t<TT, D>(dqkv, qkv, rq, c, s, B, T_, H, st);
+  if (dtype == DT_BF16) { RB(bf16, 32) RB(bf16, 64) RB(bf16, 128) }
+  else { RB(float, 32) RB(float, 64) RB(float, 128) }
+#undef RB
+}
+
+template <typename T, int DH>
+static void pre_t(const void* dO, const void* O, float* Dv, void* dOT, int B, int T_, int Tp, int H, hipStream_t st) {
+  dim3 g((T_ + 63) / 64, H, B);
+  hipLaunchKernelGGL((attn_bwd_pre_kernel<T, DH>), g, dim3(256), 0, st, (const T*)dO, (const T*)O, Dv, (T*)dOT, T_,
+                     Tp, H);
+}
+
+void attn_bwd_pre(int dtype, const void* dO, const void* O, float* Dv, void* dOT, int B, int T_, int Tp, int H,
+                  int Dh, hipStream_t st) {
+#define PB(TT, D) \
+  if (Dh == D) return pre_t<TT, D>(dO, O, Dv, dOT, B, T_, Tp, H, st);
+  if (dtype == DT_BF16) { PB(bf16, 32) PB(bf16, 64) PB(bf16, 128) }
+  else { PB(float, 32) PB(float, 64) PB(float, 128) }
+#undef PB
+}
+
+void xent_reduce(const float* part, const float* tgt, int rows, int nblk, float* lse, float* row_loss,
+                 hipStream_t st) {
+  hipLaunchKernelGGL(xent_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, part, tgt, rows, nblk, lse,
+                     row_loss);
+}
+
+void mean_reduce(const float* x, int n, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(mean_reduce_kernel, dim3(1), dim3(1024), 0, st, x, n, out);
+}
+
+void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab, uint32_t* keys,
+               int32_t* runs, int* nruns, hipStream_t st) {
+  (void)runs;
+  (void)nruns;
+  int pbits = 0;
+  while ((1 << pbits) < rows) ++pbits;
+  int n2 = 1;
+  while (n2 < rows) n2 <<= 1;
+  fill_f32(dE, (long)vocab * d, 0.f, st);
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)sort_keys_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), n2 * sizeof(uint32_t), st, tokens, rows, pbits, n2,
+                     vocab, keys);
+  hipLaunchKernelGGL(embed_bwd_runs_kernel, dim3(rows, (d + 255) / 256), dim3(64), 0, st, keys, dh, dE, rows, d,
+                     pbits, vocab);
+}
+
+void fill_f32(float* p, long n, float v, hipStream_t st) {
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+}
+
+}  // namespace gk

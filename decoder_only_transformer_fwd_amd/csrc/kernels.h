@@ -1,0 +1,96 @@
+// Launcher interface between the host runtime (api.cpp) and the gfx950
+// kernels.  Plain structs and functions; every launcher enqueues on the given
+// stream and returns without synchronising.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gk {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+
+enum Layout {
+  LAYOUT_KK = 0,  // A [M][K], B [N][K]
+  LAYOUT_KN = 1,  // A [M][K], B [K][N]
+  LAYOUT_MN = 2,  // A [K][M], B [K][N]
+};
+
+enum Epi {
+  EPI_STORE = 0,      // C (activation type) = acc
+  EPI_STORE_F32 = 1,  // C (fp32) = acc
+  EPI_ACCUM_F32 = 2,  // C (fp32) += acc
+  EPI_RELU2 = 3,      // C = acc (u), C2 = relu(acc)^2 (g)
+  EPI_DRELU2 = 4,     // C = acc * 2 * relu(aux)
+  EPI_XENT_FWD = 5,   // per-row partial (max, sum exp) + target logit
+  EPI_XENT_BWD = 6,   // C = (exp(acc - lse) - onehot(target)) * beta
+  EPI_PARTIAL = 7,    // part[split][M][N] = acc (split-K)
+};
+
+enum Tile { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, TILE_64x64 = 3 };
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  int M, N, K;
+  long lda, ldb;   // leading dimensions, in elements
+  void* C;
+  long ldc;
+  void* C2;        // EPI_RELU2: g
+  const void* aux; // EPI_DRELU2: u; EPI_XENT_*: int32 targets
+  const float* auxf; // EPI_XENT_BWD: per-row logsumexp
+  float* part;     // EPI_XENT_FWD: [M][nblk][2]; EPI_PARTIAL: [splits][M][N]
+  float* tgt;      // EPI_XENT_FWD: target logit per row
+  float alpha;     // scales the accumulator before the epilogue
+  float beta;      // EPI_XENT_BWD: 1 / rows
+  int k_split;     // K elements handled per blockIdx.z
+  int nblk;        // EPI_XENT_FWD: number of column blocks of width BN/2
+};
+
+int gemm_launch(const GemmArgs& a, int dtype, int layout, int epi, int tile, int splits,
+                hipStream_t st);
+void splitk_reduce(const float* part, int splits, long mn, float* out, int accumulate,
+                   hipStream_t st);
+
+// ---------------------------------------------------------------- elementwise
+// Also checks that every token and target id is in [0, vocab) (sets *flag).
+void embed_fwd(int dtype, const int32_t* tokens, const int32_t* targets, const void* E, float* h, int rows, int d,
+               int vocab, int* flag, hipStream_t st);
+void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps,
+                 hipStream_t st);
+// dx (+)= r * (dy - y * mean(dy*y)); also writes dx in the activation type.
+void rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* rstd, float* dx,
+                 void* dx_act, int rows, int d, int accumulate, hipStream_t st);
+void rope_qknorm_fwd(int dtype, void* qkv, float* rstd_qk, void* qT, void* kT, void* vT,
+                     const float* cosb, const float* sinb, int B, int T, int Tp, int H, int Dh,
+                     float eps, hipStream_t st);
+void rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const float* rstd_qk, const float* cosb,
+                     const float* sinb, int B, int T, int H, int Dh, hipStream_t st);
+void attn_bwd_pre(int dtype, const void* dO, const void* O, float* Dv, void* dOT, int B, int T, int Tp,
+                  int H, int Dh, hipStream_t st);
+void xent_reduce(const float* part, const float* tgt, int rows, int nblk, float* lse, float* row_loss,
+                 hipStream_t st);
+void mean_reduce(const float* x, int n, float* out, hipStream_t st);
+void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab,
+               uint32_t* keys, int32_t* runs, int* nruns, hipStream_t st);
+void fill_f32(float* p, long n, float v, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const void* qkv;   // [B*T][3*d]: q^ at col h*Dh, k^ at d + h*Dh, v at 2d + h*Dh
+  const void* qT;    // [B][H][Dh][Tp]
+  const void* kT;
+  const void* vT;
+  void* o;           // [B*T][d]
+  float* lse2;       // [B][H][Tp], log2 domain
+  const void* dO;    // [B*T][d]
+  const void* dOT;   // [B][H][Dh][Tp]
+  const float* Dv;   // [B][H][Tp] rowsum(dO * O)
+  void* dqkv;        // [B*T][3*d]
+  int B, T, Tp, H, d, window;
+  float scale_log2;  // log2(e) / sqrt(Dh)
+  float scale;       // 1 / sqrt(Dh)
+};
+int attn_fwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st);
+int attn_bwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st);
+
+}  // namespace gk

@@ -1,0 +1,144 @@
+/* gpt.h - C ABI of one GPT forward+backward training step on an MI355X (gfx950).
+ *
+ * The step computes, for one batch of token rows, the mean next-token
+ * cross-entropy of a decoder-only transformer and the gradient of that loss
+ * with respect to every weight.  The network is the one the nanochat pages
+ * describe:
+ *   - "Introducing nanochat" (github.com/karpathy/nanochat/discussions/1),
+ *     pretraining log and the paragraph after it: untied embedding and
+ *     lm_head, separate Q, K, V, O projections, a 4*d MLP, no biases and no
+ *     norm gains;
+ *   - nanochat User Guide, section 10 "How It Works", base model paragraph:
+ *     rotary embeddings, QK-norm, ReLU^2 MLP, sliding-window pattern;
+ *   - "supa beginna nanochat" (discussions/677), troubleshooting: mean
+ *     cross-entropy over rows of T+1 tokens split into inputs and targets.
+ * Per layer: a = N(h); q,k,v = a Wq^T, a Wk^T, a Wv^T; q^ = N_h(RoPE(q)),
+ * k^ = N_h(RoPE(k)); o = softmax(q^ k^T / sqrt(Dh) | window mask) v;
+ * h += o Wo^T; h += relu(N(h) W1^T)^2 W2^T.  Then loss = mean CE(N(h) U^T, y).
+ * N is parameter-free RMSNorm with eps = norm_eps; RoPE rotates the pairs
+ * (x[i], x[i+Dh/2]) by t * base^(-2i/Dh); a layer of window W lets query i
+ * see keys j with 0 <= i - j <= W - 1.
+ *
+ * Conventions.  All tensors are row-major and contiguous.  Pointers are
+ * device pointers unless marked "host".  No function throws, aborts or
+ * exits; every failure is a negative return code, with details available
+ * from gpt_last_error() on the calling thread.  A model handle is not
+ * thread-safe: use one handle per stream.
+ */
+#ifndef GPT_MI355X_H
+#define GPT_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- codes */
+#define GPT_OK 0
+#define GPT_EINVAL (-1)      /* bad configuration or argument value            */
+#define GPT_ENULL (-2)       /* a required pointer is NULL                     */
+#define GPT_ETOKEN (-3)      /* a token id outside [0, vocab) (device check)   */
+#define GPT_EHIP (-4)        /* a HIP runtime call failed                      */
+#define GPT_ENONFINITE (-5)  /* the loss came out NaN or infinite              */
+#define GPT_ESPACE (-6)      /* workspace smaller than gpt_workspace_bytes()   */
+#define GPT_EALIGN (-7)      /* a pointer is not 256-byte aligned              */
+
+typedef enum { GPT_FP32 = 0, GPT_BF16 = 1, GPT_FP8 = 2 } gpt_precision;
+
+typedef struct gpt_config {
+  int32_t depth;        /* L, number of blocks                                */
+  int32_t d_model;      /* d = n_head * head_dim, multiple of 64              */
+  int32_t n_head;       /* H                                                  */
+  int32_t head_dim;     /* Dh: 32 or 64 (GPT_FP32); 64 or 128 (GPT_BF16)       */
+  int32_t mlp_hidden;   /* F, multiple of 64                                  */
+  int32_t vocab;        /* V, multiple of 8, <= 65536                         */
+  int32_t seq_len;      /* T >= 1                                             */
+  int32_t batch;        /* B >= 1, with B*T <= 32768                          */
+  int32_t window;       /* keys per 'S' layer incl. the query itself (>= 1)   */
+  char window_pattern[8]; /* NUL-terminated, chars 'S'/'L', cycled over layers;
+                             the last layer is always 'L' (full causal)       */
+  float rope_base;      /* RoPE base (10000)                                  */
+  float norm_eps;       /* RMSNorm epsilon for every norm (1e-6)              */
+  int32_t precision;    /* gpt_precision: storage/compute policy, see below   */
+  const void* weights;  /* device, caller-owned parameter buffer: see layout  */
+  void* workspace;      /* device, caller-owned, >= gpt_workspace_bytes()     */
+  size_t workspace_bytes;
+  void* stream;         /* hipStream_t on which all work is enqueued (NULL = default) */
+} gpt_config;
+/* Precision policy.  GPT_FP32: weights, activations and every product in
+ * fp32 (fp32 MFMA).  GPT_BF16: bf16 weights and activations, fp32
+ * accumulation, fp32 residual stream, fp32 norm/softmax statistics.
+ * GPT_FP8 is reserved (rejected with GPT_EINVAL). */
+
+/* Parameter layout.  One contiguous buffer, tensors in this order:
+ *   E [V, d]; for l in 0..L-1: Wq, Wk, Wv [d, d], Wo [d, d], W1 [F, d],
+ *   W2 [d, F]; U [V, d].
+ * Shapes are [out, in].  Each tensor starts at an element offset that is a
+ * multiple of 128; Wq, Wk, Wv of a layer are adjacent (one [3d, d] block).
+ * The weight buffer holds elements of the parameter type (fp32 for GPT_FP32,
+ * bf16 otherwise); the gradient buffer uses the same element offsets with
+ * fp32 elements. */
+typedef struct gpt_model gpt_model;  /* opaque handle ("params" of a step) */
+
+typedef struct gpt_tensor_desc {
+  char name[24];        /* "E", "L3.Wq", ..., "U"                             */
+  int64_t offset;       /* element offset in the weight / gradient buffer     */
+  int32_t rows, cols;
+} gpt_tensor_desc;
+
+/* Number of parameter tensors (2 + 6*depth) and total elements of the
+ * buffer including alignment gaps.  Returns GPT_EINVAL for a bad config. */
+int gpt_param_layout(const gpt_config* cfg, gpt_tensor_desc* out, int capacity, int* n_tensors,
+                     int64_t* total_elems);
+
+/* Bytes of device workspace gpt_create needs for this config. */
+int gpt_workspace_bytes(const gpt_config* cfg, size_t* bytes);
+
+/* Validate cfg, build the launch plan and write the RoPE table into the
+ * workspace (one small host->device copy on cfg->stream).  The handle keeps
+ * cfg->weights, cfg->workspace and cfg->stream; the caller keeps them alive
+ * and unchanged until gpt_destroy.  No device memory is allocated. */
+int gpt_create(const gpt_config* cfg, gpt_model** out_model);
+
+/* One forward+backward step.
+ *   tokens, targets: device int32 [B, T], ids in [0, V) (checked on device).
+ *   grads: device fp32 buffer in the parameter layout; every element is
+ *          overwritten with d(loss)/d(weight) (not accumulated).
+ *   loss:  host float, receives the mean cross-entropy.
+ * Enqueues on cfg->stream, then waits for the stream; buffers may be reused
+ * as soon as it returns.  Returns GPT_ETOKEN (grads undefined) for an
+ * out-of-range id and GPT_ENONFINITE for a NaN/inf loss. */
+int gpt_step(gpt_model* model, const int32_t* tokens, const int32_t* targets, float* grads, float* loss);
+
+/* Release the handle (host memory only). */
+void gpt_destroy(gpt_model* model);
+
+/* Inspect a saved intermediate of the last step (device pointer into the
+ * workspace).  which: 0 residual h after the forward [B*T, d] fp32,
+ * 1 normalised q/k + raw v of `layer` [B*T, 3d], 2 attention output of
+ * `layer` [B*T, d], 3 per-row loss [B*T] fp32, 4 per-row logsumexp [B*T] fp32,
+ * 5 u (MLP pre-activation) of `layer` [B*T, F].  Activation-typed buffers
+ * hold the parameter type.  *elem_bytes receives the element size. */
+int gpt_debug_tensor(gpt_model* model, int which, int layer, void** ptr, int64_t* rows, int64_t* cols,
+                     int* elem_bytes);
+
+/* A single product through the step's GEMM kernel, for testing and
+ * measurement: C[M,N] = A B^T with A [M,K], B [N,K] (layout 0), A [M,K],
+ * B [K,N] (layout 1) or A [K,M], B [K,N] (layout 2).  dtype 0 = fp32,
+ * 1 = bf16 inputs; C is fp32 [M, N].  M, N, K multiples of 8.  splits >= 1
+ * splits K (needs a workspace of splits*M*N floats, else pass splits = 1).
+ * Enqueued on `stream`; does not synchronise. */
+int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const void* B, float* C,
+             float* workspace, int splits, int tile, void* stream);
+
+/* Static description of a return code. */
+const char* gpt_strerror(int code);
+/* Details of the last failure on this thread ("" if none). */
+const char* gpt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT_MI355X_H */

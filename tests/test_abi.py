@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+entry point, and validates configurations without touching a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gpt_inputs as gi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gpt.h")
+
+
+@pytest.fixture(scope="module")
+def M():
+    import decoder_only_transformer_fwd_amd as M
+    return M
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gpt_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_step_entry_points():
+    fns = declared_functions()
+    for f in ("gpt_create", "gpt_step", "gpt_destroy", "gpt_workspace_bytes", "gpt_param_layout"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(M):
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+    assert sorted(M.EXPORTED) == declared_functions()
+
+
+@pytest.mark.parametrize("name", ["tiny", "d12", "d20", "d24"])
+def test_param_layout_matches_workload_shapes(M, name):
+    s = gi.preset(name)
+    layout, total = M.gpt_param_layout(M.make_config(s))
+    want = gi.param_shapes(s)
+    assert [(n, (r, c)) for n, _, r, c in layout] == want
+    prev_end = 0
+    for n, off, r, c in layout:
+        assert off % 128 == 0 and off >= prev_end
+        prev_end = off + r * c
+    assert total >= prev_end
+    # Wq, Wk, Wv of a layer are adjacent: one [3d, d] operand
+    offs = {n: o for n, o, _, _ in layout}
+    d = s.d_model
+    for l in range(s.depth):
+        assert offs[f"L{l}.Wk"] == offs[f"L{l}.Wq"] + d * d
+        assert offs[f"L{l}.Wv"] == offs[f"L{l}.Wq"] + 2 * d * d
+
+
+def test_d20_parameter_total(M):
+    layout, _ = M.gpt_param_layout(M.make_config(gi.preset("d20")))
+    assert sum(r * c for _, _, r, c in layout) == 560_988_160
+
+
+@pytest.mark.parametrize("name", ["tiny", "d12", "d20", "d24"])
+def test_workspace_bytes_is_sane(M, name):
+    s = gi.preset(name)
+    b = M.gpt_workspace_bytes(M.make_config(s))
+    assert b % 256 == 0
+    # at least the saved activations: per layer qkv + u + g in the parameter type
+    es = 4 if s.precision == "fp32" else 2
+    assert b > s.depth * s.bt * (3 * s.d_model + 2 * s.mlp_hidden) * es
+    assert b < 200 * 2 ** 30
+
+
+BAD = [
+    dict(head_dim=48, d_model=96, n_head=2),     # unsupported head_dim
+    dict(n_head=3),                              # d != H * Dh
+    dict(vocab=1001),                            # vocab not a multiple of 8
+    dict(batch=20, seq_len=2048),                # B*T too large
+    dict(window_pattern="SX"),                   # bad pattern char
+    dict(window=0, window_pattern="SL"),         # S layer without a window
+    dict(mlp_hidden=100),                        # F not a multiple of 64
+    dict(depth=0),
+    dict(precision="fp8"),                       # not built
+]
+
+
+@pytest.mark.parametrize("bad", BAD)
+def test_bad_configs_are_rejected(M, bad):
+    s = gi.preset("tiny").replace(**bad)
+    with pytest.raises(M.GPTError) as e:
+        M.gpt_workspace_bytes(M.make_config(s))
+    assert e.value.code == M.GPT_EINVAL
+    assert M.gpt_create_rc(M.make_config(s, weights=256, workspace=512, workspace_bytes=1 << 40)) == M.GPT_EINVAL
+
+
+def test_create_argument_errors(M):
+    s = gi.preset("tiny")
+    need = M.gpt_workspace_bytes(M.make_config(s))
+    assert M.gpt_create_rc(M.make_config(s)) == M.GPT_ENULL
+    assert M.gpt_create_rc(M.make_config(s, weights=0x1000, workspace=0x1010, workspace_bytes=need)) == M.GPT_EALIGN
+    assert M.gpt_create_rc(M.make_config(s, weights=0x1000, workspace=0x2000, workspace_bytes=need - 256)) == M.GPT_ESPACE
+
+
+def test_gemm_argument_errors(M):
+    with pytest.raises(M.GPTError):
+        M.gpt_gemm(1, 0, 100, 64, 64, 256, 256, 256)   # M not a multiple of 8
+    with pytest.raises(M.GPTError):
+        M.gpt_gemm(1, 3, 64, 64, 64, 256, 256, 256)    # bad layout
+    with pytest.raises(M.GPTError):
+        M.gpt_gemm(1, 0, 64, 64, 64, 0, 256, 256)      # NULL operand
+
+
+def test_strerror(M):
+    assert M.gpt_strerror(M.GPT_ETOKEN) == "token id out of range"
+    assert M.gpt_strerror(12345) == "unknown error"

@@ -1,0 +1,176 @@
+"""GPU parity of the whole training step against the fp64 oracle.
+
+Small workloads are compared tensor by tensor (loss relative error and
+per-tensor gradient cosine); the full-size workloads are compared against the
+oracle results stored by ``tests/golden/make_full_size_golden.py`` (loss,
+per-tensor norms and seeded gradient samples), in the same launch
+configuration the benchmark times.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import gpt_inputs as gi
+from tests.gpu_common import SMALL, TOL, cosine, log, oracle_step
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _session(s, W8, X, Y):
+    import decoder_only_transformer_fwd_amd as G
+    sess = G.Session(s, W8)
+    sess.set_tokens(X, Y)
+    return sess
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_step_matches_oracle(name):
+    s = SMALL[name]
+    W8, X, Y, loss_ref, G_ref = oracle_step(s)
+    log(f"step parity: {name} {s}")
+    sess = _session(s, W8, X, Y)
+    loss = sess.step()
+    G = sess.grads_numpy()
+    tol = TOL[s.precision]
+    rel = abs(loss - loss_ref) / abs(loss_ref)
+    log(f"  loss gpu={loss:.8f} oracle={loss_ref:.8f} rel={rel:.2e}")
+    worst = (2.0, None)
+    for n, g_ref in G_ref.items():
+        if not np.any(g_ref):
+            continue
+        c = cosine(G[n], g_ref)
+        worst = min(worst, (c, n))
+        if tol["maxrel"] is not None:
+            err = np.max(np.abs(G[n] - g_ref)) / np.max(np.abs(g_ref))
+            assert err <= tol["maxrel"], (n, err)
+    log(f"  worst grad cosine {worst[0]:.7f} ({worst[1]})")
+    assert rel <= tol["loss_rel"]
+    assert worst[0] >= tol["cos"], worst
+    # gradients of embedding rows that no token uses are exactly zero
+    unseen = np.setdiff1d(np.arange(s.vocab), np.unique(X))
+    assert np.all(G["E"][unseen] == 0.0)
+    sess.close()
+
+
+def test_forward_intermediates_match_oracle():
+    """Final residual stream and per-row losses of the bf16 step."""
+    from oracle import gpt_oracle as O
+    s = SMALL["bf16_mid"]
+    W8 = gi.make_weights(s)
+    W = gi.weights_f64(s, W8)
+    X, Y = gi.make_tokens(s)
+    h, _, _ = O.forward(s, W, X)
+    _, _, _, row_loss, lse = O._xent(s, W, h, Y, 1024, want_grads=False)
+    log("forward intermediates: bf16_mid")
+    sess = _session(s, W8, X, Y)
+    sess.step()
+    h_gpu = sess.debug_tensor(0)
+    assert cosine(h_gpu, h) > 0.9995
+    assert np.max(np.abs(sess.debug_tensor(3)[:, 0] - row_loss)) < 3e-2
+    assert np.max(np.abs(sess.debug_tensor(4)[:, 0] - lse)) < 3e-2
+    sess.close()
+
+
+def test_step_is_bitwise_deterministic():
+    s = SMALL["bf16_mid"]
+    W8 = gi.make_weights(s)
+    X, Y = gi.make_tokens(s)
+    log("determinism: bf16_mid twice")
+    sess = _session(s, W8, X, Y)
+    l1 = sess.step()
+    g1 = sess.grads.clone()
+    l2 = sess.step()
+    assert l1 == l2
+    assert bool((g1 == sess.grads).all())
+    sess.close()
+
+
+def test_causality_of_row_losses():
+    """Changing tokens after position i leaves every row loss at t <= i
+    bit-identical (the forward has no cross-row reduction order effects)."""
+    s = SMALL["bf16_mid"]
+    W8 = gi.make_weights(s)
+    X, Y = gi.make_tokens(s)
+    log("causality: bf16_mid")
+    sess = _session(s, W8, X, Y)
+    sess.step()
+    r1 = sess.debug_tensor(3)[:, 0].reshape(s.batch, s.seq_len)
+    i = 77
+    X2 = X.copy()
+    X2[:, i + 1:] = (X2[:, i + 1:] * 5 + 11) % s.vocab
+    sess.set_tokens(X2, Y)
+    sess.step()
+    r2 = sess.debug_tensor(3)[:, 0].reshape(s.batch, s.seq_len)
+    assert np.array_equal(r1[:, :i + 1], r2[:, :i + 1])
+    assert not np.array_equal(r1[:, i + 1:], r2[:, i + 1:])
+    sess.close()
+
+
+def test_zero_lm_head_gives_ln_vocab():
+    s = SMALL["bf16_mid"]
+    W8 = gi.make_weights(s, zero_lm_head=True)
+    X, Y = gi.make_tokens(s)
+    log("zero lm_head: bf16_mid")
+    sess = _session(s, W8, X, Y)
+    loss = sess.step()
+    assert abs(loss - np.log(s.vocab)) < 1e-5
+    G = sess.grads_numpy()
+    for n, g in G.items():
+        if n != "U":
+            assert not np.any(g), n
+    sess.close()
+
+
+def test_out_of_range_token_is_reported():
+    import decoder_only_transformer_fwd_amd as G
+    s = SMALL["tiny"]
+    W8 = gi.make_weights(s)
+    X, Y = gi.make_tokens(s)
+    X = X.copy()
+    X[0, 5] = s.vocab + 3
+    log("token range check: tiny")
+    sess = _session(s, W8, X, Y)
+    rc, _ = sess.step_rc()
+    assert rc == G.GPT_ETOKEN
+    Y2 = Y.copy()
+    Y2[0, 0] = -1
+    sess.set_tokens(gi.make_tokens(s)[0], Y2)
+    rc, _ = sess.step_rc()
+    assert rc == G.GPT_ETOKEN
+    sess.set_tokens(*gi.make_tokens(s))
+    rc, loss = sess.step_rc()
+    assert rc == G.GPT_OK and np.isfinite(loss)
+    sess.close()
+
+
+@pytest.mark.parametrize("name", ["d12", "d24", "d20"])
+def test_full_size_step_matches_stored_oracle(name):
+    path = os.path.join(GOLDEN, f"oracle_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    ref = np.load(path, allow_pickle=False)
+    s = gi.preset(name)
+    W8 = gi.make_weights(s)
+    X, Y = gi.make_tokens(s)
+    log(f"full-size parity: {name}")
+    sess = _session(s, W8, X, Y)
+    loss = sess.step()
+    rel = abs(loss - float(ref["loss"])) / float(ref["loss"])
+    log(f"  loss gpu={loss:.7f} oracle={float(ref['loss']):.7f} rel={rel:.2e}")
+    assert rel <= TOL["bf16"]["loss_rel"]
+    idx = gi.grad_sample_indices(s, int(ref["n_samples"]))
+    samples = sess.grad_samples(idx)
+    norms = sess.grad_norms()
+    worst = (2.0, None)
+    for k, n in enumerate(ref["names"]):
+        n = str(n)
+        c = cosine(samples[n], ref["samples"][k])
+        worst = min(worst, (c, n))
+        nr = norms[n] / ref["norms"][k]
+        assert 0.98 < nr < 1.02, (n, nr)
+    log(f"  worst sampled cosine {worst[0]:.6f} ({worst[1]})")
+    assert worst[0] >= TOL["bf16"]["cos"], worst
+    sess.close()
