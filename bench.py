@@ -1,0 +1,156 @@
+"""Benchmark: tokens/s and MFU of one GPT forward+backward training step on
+one MI355X, through the C ABI (``gpt_step``).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d24]
+
+A step is one ``gpt_step`` call on one batch of seeded synthetic tokens with
+seeded random weights (inputs resident in HBM before the timed region); the
+timed region is K steps bracketed by device synchronisation.  The JSON line
+also carries the roofline of the dominant kernel (HIP-event timing of every
+launch site inside the timed region) and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gpt_inputs as gi  # noqa: E402
+
+METRIC = "training tokens/sec + MFU, d20/d24 GPT fwd+bwd step on 1×MI355X"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(s, budget_rows: int = 1) -> dict:
+    """Time the fp64 oracle on one batch row (T tokens) of the workload."""
+    from oracle import gpt_oracle as O
+    try:
+        import threadpoolctl
+        cores = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:
+        cores = os.cpu_count()
+    sample = s.replace(batch=budget_rows)
+    W = gi.weights_f64(sample, gi.make_weights(sample))
+    X, Y = gi.make_tokens(sample)
+    t0 = time.perf_counter()
+    O.forward_backward(sample, W, X, Y)
+    dt = time.perf_counter() - t0
+    return {"value": sample.bt / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one forward+backward of the full {s.name} model on {budget_rows} of its {s.batch} "
+                      f"rows ({sample.bt} tokens), fp64 numpy, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="d24", choices=sorted(gi.PRESETS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sites", action="store_true", help="print per-site timings to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        log("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)")
+        return 2
+
+    import torch
+    import decoder_only_transformer_fwd_amd as G
+    from decoder_only_transformer_fwd_amd import metrics as Mx
+
+    s = gi.preset(args.config)
+    if s.precision == "fp8":
+        log("the fp8 workload is not built yet")
+        return 2
+    log(f"bench: {s}")
+    W8 = gi.make_weights(s)
+    X, Y = gi.make_tokens(s)
+    sess = G.Session(s, W8)
+    sess.set_tokens(X, Y)
+    del W8
+    for _ in range(args.warmup):
+        sess.step()
+    sess.profile(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loss = 0.0
+    for _ in range(args.steps):
+        loss = sess.step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    sites = sess.profile_sites()
+    sess.profile(False)
+
+    tok_s = s.bt * args.steps / dt
+    peak = Mx.PEAK_FP32_MFMA if s.precision == "fp32" else Mx.PEAK_BF16
+    mfu = tok_s * Mx.flops_per_token(s) / peak
+    total_site_ms = sum(x["total_ms"] for x in sites)
+    if args.sites:
+        for x in sorted(sites, key=lambda x: -x["total_ms"]):
+            per = x["total_ms"] / max(1, x["launches"])
+            rate = x["work"] / max(1, x["launches"]) / (per * 1e-3) if per > 0 else 0.0
+            unit = "TFLOP/s" if x["work_kind"] == "flops" else "GB/s"
+            scale = 1e12 if unit == "TFLOP/s" else 1e9
+            log(f"  {x['name']:28s} {x['launches']:6d} launches {x['total_ms'] / args.steps:9.3f} ms/step "
+                f"{100 * x['total_ms'] / total_site_ms:5.1f}%  {rate / scale:9.1f} {unit}")
+    dom = max(sites, key=lambda x: x["total_ms"])
+    per_launch_s = dom["total_ms"] / dom["launches"] * 1e-3
+    work_per_launch = dom["work"] / dom["launches"]
+    if dom["work_kind"] == "flops":
+        kpeak = Mx.PEAK_FP32_MFMA if s.precision == "fp32" else Mx.PEAK_BF16
+        roof = {"bound": "mfma", "kernel": dom["name"], "achieved": work_per_launch / per_launch_s / 1e12,
+                "peak": kpeak / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "kernel": dom["name"], "achieved": work_per_launch / per_launch_s / 1e9,
+                "peak": Mx.PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["share_of_step"] = dom["total_ms"] / total_site_ms
+
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if s.precision == "fp32" else "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, seeded token ids)",
+        "config": {"workload": s.name, "depth": s.depth, "d_model": s.d_model, "n_head": s.n_head,
+                   "head_dim": s.head_dim, "mlp_hidden": s.mlp_hidden, "vocab": s.vocab,
+                   "seq_len": s.seq_len, "batch": s.batch, "tokens_per_step": s.bt,
+                   "window": s.window, "window_pattern": s.window_pattern, "token_dist": s.token_dist},
+        "mfu": mfu,
+        "mfu_peak_tflops": peak / 1e12,
+        "model_flops_per_token": Mx.flops_per_token(s),
+        "loss": loss,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        sess.close()
+        del sess
+        torch.cuda.empty_cache()
+        log("cpu baseline: timing the oracle on one batch row")
+        out["cpu_baseline"] = cpu_baseline(s)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

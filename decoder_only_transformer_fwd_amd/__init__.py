@@ -20,7 +20,8 @@ GPT_OK, GPT_EINVAL, GPT_ENULL, GPT_ETOKEN, GPT_EHIP, GPT_ENONFINITE, GPT_ESPACE,
 GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 
 EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_destroy",
-            "gpt_debug_tensor", "gpt_gemm", "gpt_strerror", "gpt_last_error"]
+            "gpt_debug_tensor", "gpt_gemm", "gpt_profile_enable", "gpt_profile_sites", "gpt_profile_get",
+            "gpt_strerror", "gpt_last_error"]
 
 
 class gpt_config(ctypes.Structure):
@@ -40,6 +41,10 @@ class gpt_tensor_desc(ctypes.Structure):
 
 
 def _load():
+    # One HIP runtime per process: torch ships its own libamdhip64 with the
+    # same soname as ROCm's.  Loading torch first makes this library bind to
+    # that already-loaded runtime instead of pulling in a second copy.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: run decoder_only_transformer_fwd_amd/build.py "
                           "(or __graft_entry__.build()) first")
@@ -55,12 +60,17 @@ def _load():
     lib.gpt_debug_tensor.argtypes = [P, I, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I64),
                                      ctypes.POINTER(I)]
     lib.gpt_gemm.argtypes = [I, I, I, I, I, P, P, P, P, I, I, P]
+    D = ctypes.c_double
+    lib.gpt_profile_enable.argtypes = [P, I]
+    lib.gpt_profile_sites.argtypes = [P, ctypes.POINTER(I)]
+    lib.gpt_profile_get.argtypes = [P, I, ctypes.c_char_p, I, ctypes.POINTER(I64), ctypes.POINTER(D),
+                                    ctypes.POINTER(D), ctypes.POINTER(I)]
     lib.gpt_strerror.argtypes = [I]
     lib.gpt_strerror.restype = ctypes.c_char_p
     lib.gpt_last_error.argtypes = []
     lib.gpt_last_error.restype = ctypes.c_char_p
     for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step",
-                 "gpt_debug_tensor", "gpt_gemm"):
+                 "gpt_debug_tensor", "gpt_gemm", "gpt_profile_enable", "gpt_profile_sites", "gpt_profile_get"):
         getattr(lib, name).restype = I
     return lib
 
@@ -151,6 +161,25 @@ def gpt_gemm(dtype: int, layout: int, M: int, N: int, K: int, A: int, B: int, C:
              workspace: int = 0, splits: int = 1, tile: int = -1, stream: int = 0) -> None:
     _check(_lib.gpt_gemm(dtype, layout, M, N, K, A, B, C, workspace or None, splits, tile, stream or None),
            "gpt_gemm")
+
+
+def gpt_profile_enable(model: int, on: bool) -> None:
+    _check(_lib.gpt_profile_enable(model, 1 if on else 0), "gpt_profile_enable")
+
+
+def gpt_profile_sites(model: int) -> int:
+    n = ctypes.c_int()
+    _check(_lib.gpt_profile_sites(model, ctypes.byref(n)), "gpt_profile_sites")
+    return n.value
+
+
+def gpt_profile_get(model: int, index: int) -> dict:
+    name = ctypes.create_string_buffer(64)
+    la, ms, wk, kind = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    _check(_lib.gpt_profile_get(model, index, name, 64, ctypes.byref(la), ctypes.byref(ms), ctypes.byref(wk),
+                                ctypes.byref(kind)), "gpt_profile_get")
+    return dict(name=name.value.decode(), launches=la.value, total_ms=ms.value, work=wk.value,
+                work_kind="flops" if kind.value == 0 else "bytes")
 
 
 def gpt_strerror(code: int) -> str:
@@ -246,6 +275,12 @@ class Session:
         if rc != 0:
             raise RuntimeError(f"hipMemcpy failed: {rc}")
         return buf.float().cpu().numpy().reshape(rows, cols)
+
+    def profile(self, on: bool = True) -> None:
+        gpt_profile_enable(self.handle, on)
+
+    def profile_sites(self) -> List[dict]:
+        return [gpt_profile_get(self.handle, i) for i in range(gpt_profile_sites(self.handle))]
 
     def close(self) -> None:
         if self.handle:

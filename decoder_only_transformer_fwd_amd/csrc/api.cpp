@@ -180,6 +180,28 @@ struct gpt_model {
       cosb, sinb, keys, total;
   size_t splitk_floats;
   int xent_tile, xent_nblk;
+  // optional per-launch-site timing with HIP events on the step's stream
+  struct Site {
+    std::string name;
+    long launches = 0;
+    double ms = 0.0, work = 0.0;
+    int work_kind = 0;  // 0 = flops, 1 = bytes
+  };
+  struct Pending {
+    int site;
+    double work;
+    hipEvent_t a, b;
+  };
+  bool prof_on = false;
+  std::vector<Site> sites;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<Pending> pend;
+  int cur_site = -1;
+  double cur_work = 0.0;
+  ~gpt_model() {
+    for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -260,10 +282,64 @@ int build_layout(gpt_model& m) {
 template <typename P>
 P* at(gpt_model& m, size_t off) { return (P*)(m.ws + off); }
 
+// Site timing: prof_begin records an event before a launch, prof_end after
+// it; gpt_step resolves the pairs once the stream has been synchronised.
+hipEvent_t next_event(gpt_model& m) {
+  if (m.ev_used == m.ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    m.ev_pool.push_back(e);
+  }
+  return m.ev_pool[m.ev_used++];
+}
+
+void prof_begin(gpt_model& m, const char* name, double work, int kind) {
+  if (!m.prof_on) return;
+  int idx = -1;
+  for (size_t i = 0; i < m.sites.size(); ++i)
+    if (m.sites[i].name == name) { idx = (int)i; break; }
+  if (idx < 0) {
+    gpt_model::Site st;
+    st.name = name;
+    st.work_kind = kind;
+    m.sites.push_back(st);
+    idx = (int)m.sites.size() - 1;
+  }
+  hipEvent_t a = next_event(m), b = next_event(m);
+  if (!a || !b) return;
+  (void)hipEventRecord(a, m.st);
+  m.pend.push_back(gpt_model::Pending{idx, work, a, b});
+}
+
+void prof_end(gpt_model& m) {
+  if (!m.prof_on || m.pend.empty()) return;
+  (void)hipEventRecord(m.pend.back().b, m.st);
+}
+
+void prof_collect(gpt_model& m) {
+  for (auto& p : m.pend) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      m.sites[p.site].ms += ms;
+      m.sites[p.site].launches += 1;
+      m.sites[p.site].work += p.work;
+    }
+  }
+  m.pend.clear();
+  m.ev_used = 0;
+}
+
+// Causal / windowed visible (query, key) pairs of one sequence.
+double visible_pairs(long T, long W) {
+  if (W >= T) return 0.5 * (double)T * (double)(T + 1);
+  return 0.5 * (double)W * (double)(W + 1) + (double)(T - W) * (double)W;
+}
+
 // One product with the planned tiling; splits go through the partial buffer
 // and an ordered reduction into C (fp32).
-int gemm(gpt_model& m, int layout, int epi, int M, int N, int K, const void* A, long lda, const void* B, long ldb,
-         void* C, long ldc, GemmArgs extra = GemmArgs{}) {
+int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int K, const void* A, long lda,
+         const void* B, long ldb, void* C, long ldc, GemmArgs extra = GemmArgs{}) {
+  const double flops = 2.0 * M * N * (double)K;
   GemmArgs a = extra;
   a.A = A; a.B = B; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = ldb; a.C = C; a.ldc = ldc;
   if (a.alpha == 0.f) a.alpha = 1.f;
@@ -274,14 +350,20 @@ int gemm(gpt_model& m, int layout, int epi, int M, int N, int K, const void* A, 
   if (g.splits > 1) {
     a.part = at<float>(m, m.splitk);
     a.k_split = g.k_split;
+    prof_begin(m, site, flops, 0);
     if (gemm_launch(a, m.s.dtype, layout, EPI_PARTIAL, g.tile, g.splits, m.st))
       return fail(GPT_EINVAL, "gemm variant not instantiated (partial)");
+    prof_end(m);
+    prof_begin(m, "splitk_reduce", (g.splits + 1.0) * M * N * 4.0, 1);
     splitk_reduce(a.part, g.splits, (long)M * N, (float*)C, 0, m.st);
+    prof_end(m);
     return GPT_OK;
   }
   a.k_split = K;
+  prof_begin(m, site, flops, 0);
   if (gemm_launch(a, m.s.dtype, layout, epi, g.tile, 1, m.st))
     return fail(GPT_EINVAL, "gemm variant not instantiated");
+  prof_end(m);
   return GPT_OK;
 }
 
@@ -300,13 +382,20 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   const float* sinb = at<float>(m, m.sinb);
   int rc;
 
+  const double es_d = (double)es;
   fill_f32((float*)flag, 1, 0.f, st);
+  prof_begin(m, "embed_fwd", (double)BT * d * (es_d + 4.0) + BT * 8.0, 1);
   embed_fwd(dt, tokens, targets, wp(P.E), h, BT, d, V, flag, st);
+  prof_end(m);
   for (int l = 0; l < s.L; ++l) {
     auto& Ly = m.lay[l];
+    const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
+    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1);
     rmsnorm_fwd(dt, h, m.ws + Ly.n1, at<float>(m, Ly.rstd1), BT, d, s.eps, st);
-    if ((rc = gemm(m, LAYOUT_KK, EPI_STORE, BT, 3 * d, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d, m.ws + Ly.qkv, 3 * d)))
+    prof_end(m);
+    if ((rc = gemm(m, "gemm_qkv", LAYOUT_KK, EPI_STORE, BT, 3 * d, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d, m.ws + Ly.qkv, 3 * d)))
       return rc;
+    prof_begin(m, "rope_qknorm_fwd", (double)BT * d * 8.0 * es_d + BT * 2.0 * H * 4.0, 1);
     rope_qknorm_fwd(dt, m.ws + Ly.qkv, at<float>(m, Ly.rqk), m.ws + Ly.qT, m.ws + Ly.kT, m.ws + Ly.vT, cosb, sinb,
                     s.B, s.T, s.Tp, H, Dh, s.eps, st);
     AttnArgs aa{};
@@ -315,27 +404,36 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.d = d; aa.window = s.win[l];
     aa.scale = 1.0f / std::sqrt((float)Dh);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
+    prof_end(m);
+    prof_begin(m, s.win[l] < s.T ? "attn_fwd_window" : "attn_fwd_causal", 4.0 * Dh * pairs, 0);
     if (attn_fwd(dt, Dh, aa, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
-    if ((rc = gemm(m, LAYOUT_KK, EPI_ACCUM_F32, BT, d, d, m.ws + Ly.o, d, wp(P.Wo[l]), d, h, d))) return rc;
+    prof_end(m);
+    if ((rc = gemm(m, "gemm_o", LAYOUT_KK, EPI_ACCUM_F32, BT, d, d, m.ws + Ly.o, d, wp(P.Wo[l]), d, h, d))) return rc;
+    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1);
     rmsnorm_fwd(dt, h, m.ws + Ly.n2, at<float>(m, Ly.rstd2), BT, d, s.eps, st);
+    prof_end(m);
     GemmArgs ex{};
     ex.C2 = m.ws + Ly.g;
-    if ((rc = gemm(m, LAYOUT_KK, EPI_RELU2, BT, F, d, m.ws + Ly.n2, d, wp(P.W1[l]), d, m.ws + Ly.u, F, ex)))
+    if ((rc = gemm(m, "gemm_w1_relu2", LAYOUT_KK, EPI_RELU2, BT, F, d, m.ws + Ly.n2, d, wp(P.W1[l]), d, m.ws + Ly.u, F, ex)))
       return rc;
-    if ((rc = gemm(m, LAYOUT_KK, EPI_ACCUM_F32, BT, d, F, m.ws + Ly.g, F, wp(P.W2[l]), F, h, d))) return rc;
+    if ((rc = gemm(m, "gemm_w2", LAYOUT_KK, EPI_ACCUM_F32, BT, d, F, m.ws + Ly.g, F, wp(P.W2[l]), F, h, d))) return rc;
   }
+  prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1);
   rmsnorm_fwd(dt, h, m.ws + m.nL, at<float>(m, m.rstdL), BT, d, s.eps, st);
+  prof_end(m);
   {
     GemmArgs ex{};
     ex.aux = targets;
     ex.part = at<float>(m, m.part);
     ex.tgt = at<float>(m, m.tgt);
     ex.nblk = m.xent_nblk;
-    if ((rc = gemm(m, LAYOUT_KK, EPI_XENT_FWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, nullptr, V, ex))) return rc;
+    if ((rc = gemm(m, "gemm_lm_head_xent_fwd", LAYOUT_KK, EPI_XENT_FWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, nullptr, V, ex))) return rc;
   }
+  prof_begin(m, "xent_reduce", (double)BT * m.xent_nblk * 8.0 + BT * 12.0, 1);
   xent_reduce(at<float>(m, m.part), at<float>(m, m.tgt), BT, m.xent_nblk, at<float>(m, m.lse),
               at<float>(m, m.rowloss), st);
   mean_reduce(at<float>(m, m.rowloss), BT, at<float>(m, m.lossdev), st);
+  prof_end(m);
 
   // ---------------------------------------------------------------- backward
   {
@@ -343,27 +441,41 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     ex.aux = targets;
     ex.auxf = at<float>(m, m.lse);
     ex.beta = 1.0f / (float)BT;
-    if ((rc = gemm(m, LAYOUT_KK, EPI_XENT_BWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, m.ws + m.dz, V, ex))) return rc;
+    if ((rc = gemm(m, "gemm_lm_head_xent_bwd", LAYOUT_KK, EPI_XENT_BWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, m.ws + m.dz, V, ex))) return rc;
   }
   float* dm = at<float>(m, m.dm);
   float* dh = at<float>(m, m.dh);
   void* dhA = m.ws + m.dhA;
-  if ((rc = gemm(m, LAYOUT_KN, EPI_STORE_F32, BT, d, V, m.ws + m.dz, V, wp(P.U), d, dm, d))) return rc;
-  if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, V, d, BT, m.ws + m.dz, V, m.ws + m.nL, d, grads + P.U, d))) return rc;
+  if ((rc = gemm(m, "dgrad_lm_head", LAYOUT_KN, EPI_STORE_F32, BT, d, V, m.ws + m.dz, V, wp(P.U), d, dm, d))) return rc;
+  if ((rc = gemm(m, "wgrad_lm_head", LAYOUT_MN, EPI_STORE_F32, V, d, BT, m.ws + m.dz, V, m.ws + m.nL, d, grads + P.U,
+                 d)))
+    return rc;
+  prof_begin(m, "rmsnorm_bwd", (double)BT * d * (8.0 + 2.0 * es_d), 1);
   rmsnorm_bwd(dt, dm, m.ws + m.nL, at<float>(m, m.rstdL), dh, dhA, BT, d, 0, st);
+  prof_end(m);
   for (int l = s.L - 1; l >= 0; --l) {
     auto& Ly = m.lay[l];
     GemmArgs ex{};
     ex.aux = m.ws + Ly.u;
-    if ((rc = gemm(m, LAYOUT_KN, EPI_DRELU2, BT, F, d, dhA, d, wp(P.W2[l]), F, m.ws + m.du, F, ex))) return rc;
-    if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F))) return rc;
-    if ((rc = gemm(m, LAYOUT_KN, EPI_STORE_F32, BT, d, F, m.ws + m.du, F, wp(P.W1[l]), d, dm, d))) return rc;
-    if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d, grads + P.W1[l], d)))
+    const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
+    if ((rc = gemm(m, "dgrad_w2_drelu2", LAYOUT_KN, EPI_DRELU2, BT, F, d, dhA, d, wp(P.W2[l]), F, m.ws + m.du, F, ex)))
       return rc;
+    if ((rc = gemm(m, "wgrad_w2", LAYOUT_MN, EPI_STORE_F32, d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F)))
+      return rc;
+    if ((rc = gemm(m, "dgrad_w1", LAYOUT_KN, EPI_STORE_F32, BT, d, F, m.ws + m.du, F, wp(P.W1[l]), d, dm, d)))
+      return rc;
+    if ((rc = gemm(m, "wgrad_w1", LAYOUT_MN, EPI_STORE_F32, F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d,
+                   grads + P.W1[l], d)))
+      return rc;
+    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1);
     rmsnorm_bwd(dt, dm, m.ws + Ly.n2, at<float>(m, Ly.rstd2), dh, dhA, BT, d, 1, st);
-    if ((rc = gemm(m, LAYOUT_KN, EPI_STORE, BT, d, d, dhA, d, wp(P.Wo[l]), d, m.ws + m.dO, d))) return rc;
-    if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d))) return rc;
+    prof_end(m);
+    if ((rc = gemm(m, "dgrad_o", LAYOUT_KN, EPI_STORE, BT, d, d, dhA, d, wp(P.Wo[l]), d, m.ws + m.dO, d))) return rc;
+    if ((rc = gemm(m, "wgrad_o", LAYOUT_MN, EPI_STORE_F32, d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d)))
+      return rc;
+    prof_begin(m, "attn_bwd_pre", (double)BT * d * 3.0 * es_d + (double)s.B * H * s.Tp * 4.0, 1);
     attn_bwd_pre(dt, m.ws + m.dO, m.ws + Ly.o, at<float>(m, m.Dv), m.ws + m.dOT, s.B, s.T, s.Tp, H, Dh, st);
+    prof_end(m);
     AttnArgs aa{};
     aa.qkv = m.ws + Ly.qkv; aa.qT = m.ws + Ly.qT; aa.kT = m.ws + Ly.kT; aa.vT = m.ws + Ly.vT;
     aa.o = m.ws + Ly.o; aa.lse2 = at<float>(m, Ly.lse2);
@@ -371,16 +483,29 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.d = d; aa.window = s.win[l];
     aa.scale = 1.0f / std::sqrt((float)Dh);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
-    if (attn_bwd(dt, Dh, aa, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
+    const bool win = s.win[l] < s.T;
+    prof_begin(m, win ? "attn_bwd_dkdv_window" : "attn_bwd_dkdv_causal", 6.0 * Dh * pairs, 0);
+    if (attn_bwd(dt, Dh, aa, 0, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
+    prof_end(m);
+    prof_begin(m, win ? "attn_bwd_dq_window" : "attn_bwd_dq_causal", 2.0 * Dh * pairs, 0);
+    if (attn_bwd(dt, Dh, aa, 1, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
+    prof_end(m);
+    prof_begin(m, "rope_qknorm_bwd", (double)BT * d * 6.0 * es_d + BT * 2.0 * H * 4.0, 1);
     rope_qknorm_bwd(dt, m.ws + m.dqkv, m.ws + Ly.qkv, at<float>(m, Ly.rqk), cosb, sinb, s.B, s.T, H, Dh, st);
-    if ((rc = gemm(m, LAYOUT_KN, EPI_STORE_F32, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d, dm, d)))
+    prof_end(m);
+    if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, EPI_STORE_F32, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d,
+                   dm, d)))
       return rc;
-    if ((rc = gemm(m, LAYOUT_MN, EPI_STORE_F32, 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d,
+    if ((rc = gemm(m, "wgrad_qkv", LAYOUT_MN, EPI_STORE_F32, 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d,
                    grads + P.Wqkv[l], d)))
       return rc;
+    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1);
     rmsnorm_bwd(dt, dm, m.ws + Ly.n1, at<float>(m, Ly.rstd1), dh, dhA, BT, d, 1, st);
+    prof_end(m);
   }
+  prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * 4.0 + BT * 8.0, 1);
   embed_bwd(tokens, dh, grads + P.E, BT, d, V, at<uint32_t>(m, m.keys), nullptr, nullptr, st);
+  prof_end(m);
   HIP_TRY(hipGetLastError());
   return GPT_OK;
 }
@@ -453,7 +578,8 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   hipError_t e3 = hipStreamSynchronize(m->st);
   if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
     delete m;
-    return fail(GPT_EHIP, "RoPE table upload failed");
+    return fail(GPT_EHIP, std::string("RoPE table upload failed: ") + hipGetErrorString(e1) + " / " +
+                              hipGetErrorString(e2) + " / " + hipGetErrorString(e3));
   }
   *out = m;
   return GPT_OK;
@@ -469,6 +595,7 @@ int gpt_step(gpt_model* m, const int32_t* tokens, const int32_t* targets, float*
   HIP_TRY(hipMemcpyAsync(&lossv, m->ws + m->lossdev, 4, hipMemcpyDeviceToHost, m->st));
   HIP_TRY(hipMemcpyAsync(&flag, m->ws + m->flag, 4, hipMemcpyDeviceToHost, m->st));
   HIP_TRY(hipStreamSynchronize(m->st));
+  if (m->prof_on) prof_collect(*m);
   *loss = lossv;
   if (flag) return fail(GPT_ETOKEN, "a token or target id is outside [0, vocab)");
   if (!std::isfinite(lossv)) return fail(GPT_ENONFINITE, "loss is not finite");
@@ -529,6 +656,34 @@ int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const vo
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GPT_EHIP, std::string("launch: ") + hipGetErrorString(e));
+  return GPT_OK;
+}
+
+int gpt_profile_enable(gpt_model* m, int on) {
+  if (!m) return fail(GPT_ENULL, "model is NULL");
+  m->prof_on = on != 0;
+  m->sites.clear();
+  m->pend.clear();
+  m->ev_used = 0;
+  return GPT_OK;
+}
+
+int gpt_profile_sites(gpt_model* m, int* n) {
+  if (!m || !n) return fail(GPT_ENULL, "NULL argument");
+  *n = (int)m->sites.size();
+  return GPT_OK;
+}
+
+int gpt_profile_get(gpt_model* m, int i, char* name, int name_len, int64_t* launches, double* total_ms,
+                    double* work, int* work_kind) {
+  if (!m || !name || !launches || !total_ms || !work || !work_kind) return fail(GPT_ENULL, "NULL argument");
+  if (i < 0 || i >= (int)m->sites.size()) return fail(GPT_EINVAL, "site index out of range");
+  const auto& st = m->sites[i];
+  snprintf(name, name_len, "%s", st.name.c_str());
+  *launches = st.launches;
+  *total_ms = st.ms;
+  *work = st.work;
+  *work_kind = st.work_kind;
   return GPT_OK;
 }
 

@@ -516,10 +516,12 @@ static void fwd_t(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((attn_fwd_kernel<T, DH>), g, dim3(256), 0, st, a);
 }
 template <typename T, int DH>
-static void bwd_t(const AttnArgs& a, hipStream_t st) {
+static void bwd_t(const AttnArgs& a, int part, hipStream_t st) {
   dim3 g((a.T + 127) / 128, a.H, a.B);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH>), g, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DH>), g, dim3(256), 0, st, a);
+  if (part == 0)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH>), g, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DH>), g, dim3(256), 0, st, a);
 }
 
 int attn_fwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st) {
@@ -530,8 +532,8 @@ int attn_fwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st) {
   return -1;
 }
 
-int attn_bwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st) {
-#define AB(TT, D) if (Dh == D) { bwd_t<TT, D>(a, st); return 0; }
+int attn_bwd(int dtype, int Dh, const AttnArgs& a, int part, hipStream_t st) {
+#define AB(TT, D) if (Dh == D) { bwd_t<TT, D>(a, part, st); return 0; }
   if (dtype == DT_BF16) { AB(bf16, 64) AB(bf16, 128) }
   else { AB(float, 32) AB(float, 64) }
 #undef AB

@@ -91,6 +91,7 @@ struct AttnArgs {
   float scale;       // 1 / sqrt(Dh)
 };
 int attn_fwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st);
-int attn_bwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st);
+// part 0: dK/dV kernel (one work-group per 128-key tile); part 1: dQ kernel.
+int attn_bwd(int dtype, int Dh, const AttnArgs& a, int part, hipStream_t st);
 
 }  // namespace gk

@@ -133,6 +133,19 @@ int gpt_debug_tensor(gpt_model* model, int which, int layer, void** ptr, int64_t
 int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const void* B, float* C,
              float* workspace, int splits, int tile, void* stream);
 
+/* Per-launch-site timing, for measurement.  When enabled, every kernel
+ * launch of gpt_step is bracketed by HIP events on the step's stream; after
+ * each step the elapsed times are added to named sites ("gemm_qkv",
+ * "attn_fwd_causal", "rmsnorm_fwd", ...).  gpt_profile_enable(m, 1) also
+ * resets the counters; 0 turns timing off.  For each site, `work` is the
+ * summed algorithmic work of its launches: FLOPs (work_kind 0: 2*M*N*K for a
+ * product, 4*Dh per visible (query, key) pair for the attention forward) or
+ * HBM bytes (work_kind 1: each input read once, each output written once). */
+int gpt_profile_enable(gpt_model* model, int on);
+int gpt_profile_sites(gpt_model* model, int* n_sites);
+int gpt_profile_get(gpt_model* model, int index, char* name, int name_len, int64_t* launches,
+                    double* total_ms, double* work, int* work_kind);
+
 /* Static description of a return code. */
 const char* gpt_strerror(int code);
 /* Details of the last failure on this thread ("" if none). */

@@ -1,0 +1,32 @@
+"""The FLOP convention used for MFU reproduces the pages' printed estimates."""
+import json
+import os
+
+import gpt_inputs as gi
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _page(key):
+    with open(os.path.join(GOLDEN, "page_values.json")) as f:
+        return json.load(f)[key]
+
+
+def test_flops_per_token_matches_d20_log():
+    from decoder_only_transformer_fwd_amd import metrics as M
+    for key in ("d20_flops_per_token_T2048", "d20_flops_per_token_T1024"):
+        pv = _page(key)
+        s = gi.preset("d20", seq_len=pv["config"]["seq_len"])
+        assert abs(M.flops_per_token(s) - pv["value"]) <= pv["rel_tol"] * pv["value"]
+
+
+def test_algorithmic_flops_count_visible_pairs():
+    from decoder_only_transformer_fwd_amd import metrics as M
+    assert M.visible_pairs(4, 4) == 10 and M.visible_pairs(5, 2) == 3 + 3 * 2
+    s = gi.preset("d24")
+    # windowed layers: algorithmic < conventional; no window: ratio (T+1)/(2T)
+    assert M.algorithmic_flops_per_token(s) < M.flops_per_token(s)
+    t = gi.preset("d12")
+    attn_conv = M.flops_per_token(t) - 6 * M.scaling_params(t)
+    attn_alg = M.algorithmic_flops_per_token(t) - 6 * M.scaling_params(t)
+    assert abs(attn_alg / attn_conv - (t.seq_len + 1) / (2 * t.seq_len)) < 1e-12
