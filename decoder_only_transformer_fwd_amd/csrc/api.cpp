@@ -122,8 +122,6 @@ struct GemmPlan {
   int tile, splits, k_split;
 };
 
-int tile_bm(int tile) { return tile == TILE_256x256 || tile == TILE_256x128 ? 256 : (tile == TILE_128x128 ? 128 : 64); }
-int tile_bn(int tile) { return tile == TILE_256x256 ? 256 : (tile == TILE_64x64 ? 64 : 128); }
 
 GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   GemmPlan g{TILE_64x64, 1, K};
@@ -131,10 +129,10 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   if (dtype == DT_F32) {
     g.tile = (long)M * N >= 256L * 128 * 128 ? TILE_128x128 : TILE_64x64;
   } else {
-    const int cand[3] = {TILE_256x256, TILE_256x128, TILE_128x128};
-    const double eff[3] = {1.0, 0.9, 0.75};
+    const int cand[5] = {TILE_256x256_W8, TILE_256x256, TILE_256x128_W8, TILE_256x128, TILE_128x128};
+    const double eff[5] = {1.0, 0.85, 0.9, 0.8, 0.8};
     double best = 1e300;
-    for (int c = 0; c < 3; ++c) {
+    for (int c = 0; c < 5; ++c) {
       const long tiles = (long)((M + tile_bm(cand[c]) - 1) / tile_bm(cand[c])) *
                          ((N + tile_bn(cand[c]) - 1) / tile_bn(cand[c]));
       const long waves = (tiles + 255) / 256;
@@ -236,8 +234,8 @@ int build_layout(gpt_model& m) {
   m.h = take(BT * s.d * 4);
   m.nL = take(BT * s.d * A);
   m.rstdL = take(BT * 4);
-  m.xent_tile = s.dtype == DT_F32 ? TILE_64x64 : TILE_256x256;
-  const int wn = tile_bn(m.xent_tile) / 2;
+  m.xent_tile = s.dtype == DT_F32 ? TILE_64x64 : TILE_256x256_W8;
+  const int wn = tile_wn(m.xent_tile);
   m.xent_nblk = (s.V + wn - 1) / wn;
   m.part = take(BT * m.xent_nblk * 2 * 4);
   m.tgt = take(BT * 4);
@@ -634,7 +632,7 @@ int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const vo
     return fail(GPT_EINVAL, "gpt_gemm: splits");
   if (tile < 0) tile = plan_gemm(dtype, layout, M, N, K).tile;
   if (dtype == DT_F32 && tile != TILE_128x128 && tile != TILE_64x64) return fail(GPT_EINVAL, "gpt_gemm: tile");
-  if (dtype == DT_BF16 && tile == TILE_64x64) return fail(GPT_EINVAL, "gpt_gemm: tile");
+  if (dtype == DT_BF16 && (tile == TILE_64x64 || tile > TILE_256x128_W8)) return fail(GPT_EINVAL, "gpt_gemm: tile");
   GemmArgs a{};
   a.A = A; a.B = B; a.M = M; a.N = N; a.K = K;
   a.lda = layout == LAYOUT_MN ? M : K;

@@ -1,124 +1,141 @@
 // Tiled MFMA GEMM for gfx950 with fused epilogues.
 //
 // C[M,N] = alpha * sum_k A(m,k) B(n,k), where A is stored either K-contiguous
-// ([M][K], "row") or M-contiguous ([K][M]), and B either K-contiguous ([N][K],
-// a linear layer's weight) or N-contiguous ([K][N]).  These three layouts
-// cover the forward (activation x weight^T), the input-gradient
-// (grad x weight) and the weight-gradient (grad^T x activation) products of
-// every linear layer of the step.
+// ([M][K]) or M-contiguous ([K][M]), and B either K-contiguous ([N][K], a
+// linear layer's weight) or N-contiguous ([K][N]).  These three layouts cover
+// the forward (activation x weight^T), the input-gradient (grad x weight) and
+// the weight-gradient (grad^T x activation) products of every linear layer.
 //
-// Structure: 256 threads = 4 waves in a 2x2 arrangement; each wave owns a
-// (BM/2)x(BN/2) block of 32x32 MFMA tiles.  K advances in steps of 128 bytes
-// per row (64 bf16, 32 fp32, 128 fp8).  Global tiles are fetched into
-// registers one step ahead, written to a double-buffered, XOR-swizzled LDS
-// tile, and consumed by MFMA with one barrier per step.  An M-contiguous or
-// N-contiguous operand is transposed in registers (blocks of 16 bytes x 16
-// bytes) on its way into LDS so that every MFMA fragment is a contiguous LDS
-// read.  The MFMA is issued with the B tile as its first operand, so each
-// lane's accumulators hold one output row and 4-wide runs of columns, which
-// keeps every epilogue store vectorised and every row reduction in-lane.
+// Structure: WGM x WGN waves (4 or 8) per work-group, each owning a
+// (BM/WGM) x (BN/WGN) block of 32x32 MFMA tiles.  K advances in steps of 128
+// bytes per row (64 bf16, 32 fp32).  A K-contiguous operand tile travels
+// straight from global memory into LDS (buffer loads with the LDS bit, no
+// registers); an M/N-contiguous one is loaded into registers, transposed in
+// 16x16-byte blocks and written to LDS, so every MFMA fragment is one
+// contiguous LDS read.  LDS is double-buffered with one barrier per K step;
+// within a step the fragment reads for sub-step kk+1 are issued before the
+// MFMAs of sub-step kk.  The MFMA takes the B tile as its first operand, so
+// each lane's accumulators hold one output row and 4-wide runs of columns:
+// epilogue stores are vectorised and row reductions stay in-lane.
 //
-// Work-group order is remapped so that the tiles one XCD (a group of 32 CUs
-// with its own L2) runs are neighbours, and grouped along M so that a band of
-// A rows is reused from L2 by several column tiles.
+// Work-group order is remapped so that the tiles one XCD (32 CUs sharing an
+// L2) runs are neighbours, grouped along M so a band of A rows is reused from
+// L2 by several column tiles.
 #include "common.h"
 #include "kernels.h"
 
 namespace gk {
 
-template <int ES, int ROWS, bool KC>
-struct TileLoader {
-  static constexpr int EPC = 16 / ES;                      // elements per 16 bytes
-  static constexpr int NBLK_TOTAL = 8 * ROWS / EPC;        // MN-contiguous blocks
-  static constexpr int NREG = KC ? (ROWS * 8) / 256 : ((NBLK_TOTAL + 255) / 256) * EPC;
-  u32x4 reg[NREG];
+constexpr uint32_t BUF_DWORD3 = 0x00020000u;   // raw buffer, 32-bit data format
 
-  // base: operand base pointer; ld: leading dimension in elements; r0/nrows:
-  // first row of the tile and the operand's row count (M or N); k0/K: the
-  // same along K.
-  __device__ __forceinline__ void load(const char* __restrict__ base, long ld, int r0, int nrows,
-                                       int k0, int K, int t) {
-    if constexpr (KC) {
+// M/N-contiguous operand: blocks of 16 bytes (EPC elements) along the rows
+// x EPC K-rows, transposed in registers, then stored K-contiguous in LDS.
+template <int ES, int ROWS, int THREADS>
+struct TransLoader {
+  static constexpr int EPC = 16 / ES;
+  static constexpr int NBLK_TOTAL = 8 * ROWS / EPC;
+  static constexpr int NB = (NBLK_TOTAL + THREADS - 1) / THREADS;
+  u32x4 reg[NB * EPC];
+
+  // base: operand [K][ld]; rows r0.. of the tile are its contiguous index.
+  __device__ __forceinline__ void load(const char* __restrict__ base, long ld, int r0, int nrows, int k0, int K,
+                                       int t) {
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int row = i * 32 + (t >> 3);
-        const int c = t & 7;
-        const int gr = r0 + row;
-        const int gk = k0 + c * EPC;
+    for (int bi = 0; bi < NB; ++bi) {
+      const int blk = t + bi * THREADS;
+      const int kb = blk / (ROWS / EPC);
+      const int rb = blk % (ROWS / EPC);
+      const int gr = r0 + rb * EPC;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const int gk = k0 + kb * EPC + e;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (gr < nrows && gk < K) v = *(const u32x4*)(base + ((long)gr * ld + gk) * ES);
-        reg[i] = v;
-      }
-    } else {
-#pragma unroll
-      for (int bi = 0; bi < NREG / EPC; ++bi) {
-        const int blk = t + bi * 256;
-        const int kb = blk / (ROWS / EPC);
-        const int rb = blk % (ROWS / EPC);
-        const int gr = r0 + rb * EPC;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const int gk = k0 + kb * EPC + e;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (blk < NBLK_TOTAL && gk < K && gr < nrows)
-            v = *(const u32x4*)(base + ((long)gk * ld + gr) * ES);
-          reg[bi * EPC + e] = v;
-        }
+        if (blk < NBLK_TOTAL && gk < K && gr < nrows) v = *(const u32x4*)(base + ((long)gk * ld + gr) * ES);
+        reg[bi * EPC + e] = v;
       }
     }
   }
 
   __device__ __forceinline__ void store(char* __restrict__ lds, int t) const {
-    if constexpr (KC) {
 #pragma unroll
-      for (int i = 0; i < NREG; ++i) {
-        const int row = i * 32 + (t >> 3);
-        *(u32x4*)(lds + lds_off<128>(row, (t & 7) * 16)) = reg[i];
-      }
-    } else {
+    for (int bi = 0; bi < NB; ++bi) {
+      const int blk = t + bi * THREADS;
+      if (blk >= NBLK_TOTAL) continue;
+      const int kb = blk / (ROWS / EPC);
+      const int rb = blk % (ROWS / EPC);
+      const u32x4* in = &reg[bi * EPC];
 #pragma unroll
-      for (int bi = 0; bi < NREG / EPC; ++bi) {
-        const int blk = t + bi * 256;
-        if (blk >= NBLK_TOTAL) continue;
-        const int kb = blk / (ROWS / EPC);
-        const int rb = blk % (ROWS / EPC);
-        const u32x4* in = &reg[bi * EPC];
+      for (int e2 = 0; e2 < EPC; ++e2) {
+        u32x4 o;
+        if constexpr (ES == 4) {
 #pragma unroll
-        for (int e2 = 0; e2 < EPC; ++e2) {
-          u32x4 o;
-          if constexpr (ES == 4) {
+          for (int w = 0; w < 4; ++w) o[w] = in[w][e2];
+        } else if constexpr (ES == 2) {
+          const uint32_t sel = (e2 & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) o[w] = in[w][e2];
-          } else if constexpr (ES == 2) {
-            const uint32_t sel = (e2 & 1) ? 0x07060302u : 0x05040100u;
+          for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][e2 >> 1], in[2 * w][e2 >> 1], sel);
+        } else {
+          const int sh = (e2 & 3) * 8;
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-              o[w] = __builtin_amdgcn_perm(in[2 * w + 1][e2 >> 1], in[2 * w][e2 >> 1], sel);
-          } else {
-            const int sh = (e2 & 3) * 8;
+          for (int w = 0; w < 4; ++w) {
+            uint32_t x = 0;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              uint32_t x = 0;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) x |= ((in[4 * w + q][e2 >> 2] >> sh) & 0xFFu) << (8 * q);
-              o[w] = x;
-            }
+            for (int q = 0; q < 4; ++q) x |= ((in[4 * w + q][e2 >> 2] >> sh) & 0xFFu) << (8 * q);
+            o[w] = x;
           }
-          *(u32x4*)(lds + lds_off<128>(rb * EPC + e2, kb * 16)) = o;
         }
+        *(u32x4*)(lds + lds_off<128>(rb * EPC + e2, kb * 16)) = o;
       }
+    }
+  }
+};
+
+// K-contiguous operand tile fetched straight from global memory into LDS.
+// Each wave instruction fills 8 consecutive 128-byte LDS rows, lane l writing
+// slot l%8 of row l/8; the swizzle is applied on the source side (the lane
+// owning LDS slot p of row r fetches K-chunk p ^ swz(r)).  Rows past the
+// operand and K-chunks past the end of the K range are outside the buffer's
+// range and arrive as zeros.
+template <int ES, int ROWS, int NWAVES>
+struct DmaLoader {
+  static constexpr int EPC = 16 / ES;
+  static constexpr int RPW = ROWS / NWAVES;       // rows per wave
+  static constexpr int PER_WAVE = RPW / 8;
+  static_assert(RPW % 8 == 0, "tile rows must cover 8 rows per wave instruction");
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff[PER_WAVE];
+  int kel[PER_WAVE];
+
+  __device__ __forceinline__ void init(const char* base, long ld, int r0, int nrows, int wave, int lane) {
+    const long rows_left = nrows > r0 ? (long)(nrows - r0) : 0;
+    long bytes = rows_left * ld * ES;
+    if (bytes > 0x7FFFFFF0L) bytes = 0x7FFFFFF0L;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (long)r0 * ld * ES), 0, (int)bytes, BUF_DWORD3);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int r = wave * RPW + i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz<128>(r);
+      voff[i] = (int)(r * ld * ES) + c * 16;
+      kel[i] = c * EPC;
+    }
+  }
+  __device__ __forceinline__ void issue(char* lds, int k0, int kend, int wave) const {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int off = (k0 + kel[i] < kend) ? voff[i] + k0 * ES : (int)0x80000000;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(lds + (wave * RPW + i * 8) * 128), 16, off, 0, 0, 0);
     }
   }
 };
 
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int nwg = tiles_m * tiles_n;
-  // XCD remap: hardware deals work-groups round-robin over 8 XCDs; give each
-  // XCD a contiguous range of tile ids.
+  // Hardware deals work-groups round-robin over 8 XCDs; give each XCD a
+  // contiguous range of tile ids.
   int tile = wg;
   const int per = nwg / 8;
   if (per > 0 && wg < per * 8) tile = (wg & 7) * per + (wg >> 3);
-  // Grouped order along M.
   constexpr int GROUP_M = 8;
   const int group = tile / (GROUP_M * tiles_n);
   const int first_m = group * GROUP_M;
@@ -128,23 +145,24 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
   tn = in_group / gsize;
 }
 
-template <typename TA, typename MF, int BM, int BN, bool A_KC, bool B_KC, int EPI, typename TC>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
+template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, bool A_KC, bool B_KC, int EPI, typename TC>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
+  constexpr int THREADS = 64 * WGM * WGN;
+  constexpr int NW = WGM * WGN;
   constexpr int ES = sizeof(TA);
   constexpr int BK = 128 / ES;
   constexpr int KM = MF::KM;
   constexpr int EPL = MF::EPL;
   constexpr int FB = EPL * ES;         // fragment bytes per lane
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
-
   constexpr int STAGE = (BM + BN) * 128;   // A tile, then B tile
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int g = lane >> 5, l32 = lane & 31;
 
   const int tiles_m = (p.M + BM - 1) / BM;
@@ -157,10 +175,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
   const int kend = min(p.K, kbeg + p.k_split);
   const int nk = (kend - kbeg + BK - 1) / BK;
 
-  TileLoader<ES, BM, A_KC> la;
-  TileLoader<ES, BN, B_KC> lb;
+  TransLoader<ES, BM, THREADS> la;
+  TransLoader<ES, BN, THREADS> lb;
+  DmaLoader<ES, BM, NW> da;
+  DmaLoader<ES, BN, NW> db;
   const char* Ab = (const char*)p.A;
   const char* Bb = (const char*)p.B;
+  if constexpr (A_KC) da.init(Ab, p.lda, m0, p.M, wave, lane);
+  if constexpr (B_KC) db.init(Bb, p.ldb, n0, p.N, wave, lane);
 
   floatx16 acc[MB][NB];
 #pragma unroll
@@ -170,41 +192,59 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  auto fetch = [&](int k0, int stage) {
+    char* st = smem + stage * STAGE;
+    if constexpr (A_KC) da.issue(st, k0, kend, wave);
+    else la.load(Ab, p.lda, m0, p.M, k0, kend, t);
+    if constexpr (B_KC) db.issue(st + BM * 128, k0, kend, wave);
+    else lb.load(Bb, p.ldb, n0, p.N, k0, kend, t);
+  };
+  auto commit = [&](int stage) {   // register-staged operands into LDS
+    char* st = smem + stage * STAGE;
+    if constexpr (!A_KC) la.store(st, t);
+    if constexpr (!B_KC) lb.store(st + BM * 128, t);
+  };
+
   if (nk > 0) {
-    la.load(Ab, p.lda, m0, p.M, kbeg, kend, t);
-    lb.load(Bb, p.ldb, n0, p.N, kbeg, kend, t);
-    la.store(smem, t);
-    lb.store(smem + BM * 128, t);
+    fetch(kbeg, 0);
+    commit(0);
   }
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): this thread's LDS traffic has landed
   __syncthreads();
 
+  constexpr int KK = BK / KM;
   for (int kt = 0; kt < nk; ++kt) {
     const int s = kt & 1;
     const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      la.load(Ab, p.lda, m0, p.M, k0, kend, t);
-      lb.load(Bb, p.ldb, n0, p.N, k0, kend, t);
-    }
+    if (more) fetch(kbeg + (kt + 1) * BK, s ^ 1);
     const char* a_s = smem + s * STAGE;
     const char* b_s = a_s + BM * 128;
+    typename MF::frag af[2][MB], bfr[2][NB];
 #pragma unroll
-    for (int kk = 0; kk < BK / KM; ++kk) {
-      typename MF::frag af[MB], bfr[NB];
-      const int kb = (kk * KM + g * EPL) * ES;
+    for (int i = 0; i < MB; ++i) lds_read<128, FB>(a_s, wm * WM + i * 32 + l32, (g * EPL) * ES, &af[0][i]);
 #pragma unroll
-      for (int i = 0; i < MB; ++i) lds_read<128, FB>(a_s, wm * WM + i * 32 + l32, kb, &af[i]);
+    for (int j = 0; j < NB; ++j) lds_read<128, FB>(b_s, wn * WN + j * 32 + l32, (g * EPL) * ES, &bfr[0][j]);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) lds_read<128, FB>(b_s, wn * WN + j * 32 + l32, kb, &bfr[j]);
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1;
+      // fragment reads for the next sub-step go out before this sub-step's
+      // MFMAs (the fences keep the scheduler from sinking them to their uses)
+      if (kk + 1 < KK) {
+        const int kb = ((kk + 1) * KM + g * EPL) * ES;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) lds_read<128, FB>(a_s, wm * WM + i * 32 + l32, kb, &af[cur ^ 1][i]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) lds_read<128, FB>(b_s, wn * WN + j * 32 + l32, kb, &bfr[cur ^ 1][j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = MF::mma(bfr[j], af[i], acc[i][j]);
+        for (int j = 0; j < NB; ++j) acc[i][j] = MF::mma(bfr[cur][j], af[cur][i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      la.store(smem + (s ^ 1) * STAGE, t);
-      lb.store(smem + (s ^ 1) * STAGE + BM * 128, t);
-    }
+    if (more) commit(s ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
   }
 
@@ -252,8 +292,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * g;
         if (!mok || n >= p.N) continue;
-        floatx4 v = {acc[i][j][4 * q] * alpha, acc[i][j][4 * q + 1] * alpha,
-                     acc[i][j][4 * q + 2] * alpha, acc[i][j][4 * q + 3] * alpha};
+        floatx4 v = {acc[i][j][4 * q] * alpha, acc[i][j][4 * q + 1] * alpha, acc[i][j][4 * q + 2] * alpha,
+                     acc[i][j][4 * q + 3] * alpha};
         const long off = (long)m * p.ldc + n;
         if constexpr (EPI == EPI_STORE) {
           store4((TC*)p.C + off, v);
@@ -266,7 +306,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
           store4((TC*)p.C + off, v);
           floatx4 r;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { const float x = fmaxf(v[e], 0.f); r[e] = x * x; }
+          for (int e = 0; e < 4; ++e) {
+            const float x = fmaxf(v[e], 0.f);
+            r[e] = x * x;
+          }
           store4((TC*)p.C2 + off, r);
         } else if constexpr (EPI == EPI_DRELU2) {
           const floatx4 u = load4((const TC*)p.aux + off);
@@ -280,8 +323,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
           const int y = ((const int*)p.aux)[m];
           floatx4 r;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            r[e] = (fast_exp2((v[e] - lse) * L2E) - (n + e == y ? 1.f : 0.f)) * p.beta;
+          for (int e = 0; e < 4; ++e) r[e] = (fast_exp2((v[e] - lse) * L2E) - (n + e == y ? 1.f : 0.f)) * p.beta;
           store4((TC*)p.C + off, r);
         } else if constexpr (EPI == EPI_PARTIAL) {
           store4(p.part + (long)blockIdx.z * p.M * p.N + (long)m * p.N + n, v);
@@ -292,9 +334,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs p) {
 }
 
 // Sum split-K partials in split order: out[m, n] (+)= sum_z part[z, m, n].
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
-                                                            long mn, float* __restrict__ out,
-                                                            int accumulate) {
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, long mn,
+                                                            float* __restrict__ out, int accumulate) {
   const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= mn) return;
   floatx4 s = accumulate ? *(const floatx4*)(out + i) : floatx4{0.f, 0.f, 0.f, 0.f};
@@ -304,30 +345,57 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // ------------------------------------------------------------------ dispatch
 
-template <typename TA, typename MF, int BM, int BN, bool AK, bool BK_, int EPI, typename TC>
+int tile_bm(int tile) {
+  switch (tile) {
+    case TILE_256x256: case TILE_256x128: case TILE_256x256_W8: case TILE_256x128_W8: return 256;
+    case TILE_128x128: return 128;
+    default: return 64;
+  }
+}
+int tile_bn(int tile) {
+  switch (tile) {
+    case TILE_256x256: case TILE_256x256_W8: return 256;
+    case TILE_256x128: case TILE_128x128: case TILE_256x128_W8: return 128;
+    default: return 64;
+  }
+}
+int tile_wn(int tile) {   // columns per wave (the cross-entropy partial block width)
+  switch (tile) {
+    case TILE_256x256_W8: return 64;
+    case TILE_256x128_W8: return 32;
+    default: return tile_bn(tile) / 2;
+  }
+}
+
+template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, bool AK, bool BK_, int EPI, typename TC>
 static void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
   dim3 grid(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN), 1, splits);
-  hipLaunchKernelGGL((gemm_kernel<TA, MF, BM, BN, AK, BK_, EPI, TC>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((gemm_kernel<TA, MF, BM, BN, WGM, WGN, AK, BK_, EPI, TC>), grid, dim3(64 * WGM * WGN), 0, st,
+                     a);
 }
 
 template <typename TA, typename MF, bool AK, bool BK_, int EPI, typename TC>
 static void launch_tiles(const GemmArgs& a, int tile, int splits, hipStream_t st) {
   if constexpr (sizeof(TA) == 4) {
-    if (tile == TILE_128x128) launch_cfg<TA, MF, 128, 128, AK, BK_, EPI, TC>(a, splits, st);
-    else launch_cfg<TA, MF, 64, 64, AK, BK_, EPI, TC>(a, splits, st);
+    if (tile == TILE_128x128) launch_cfg<TA, MF, 128, 128, 2, 2, AK, BK_, EPI, TC>(a, splits, st);
+    else launch_cfg<TA, MF, 64, 64, 2, 2, AK, BK_, EPI, TC>(a, splits, st);
   } else {
-    if (tile == TILE_256x256) launch_cfg<TA, MF, 256, 256, AK, BK_, EPI, TC>(a, splits, st);
-    else if (tile == TILE_256x128) launch_cfg<TA, MF, 256, 128, AK, BK_, EPI, TC>(a, splits, st);
-    else launch_cfg<TA, MF, 128, 128, AK, BK_, EPI, TC>(a, splits, st);
+    switch (tile) {
+      case TILE_256x256: launch_cfg<TA, MF, 256, 256, 2, 2, AK, BK_, EPI, TC>(a, splits, st); break;
+      case TILE_256x128: launch_cfg<TA, MF, 256, 128, 2, 2, AK, BK_, EPI, TC>(a, splits, st); break;
+      case TILE_256x256_W8: launch_cfg<TA, MF, 256, 256, 2, 4, AK, BK_, EPI, TC>(a, splits, st); break;
+      case TILE_256x128_W8: launch_cfg<TA, MF, 256, 128, 2, 4, AK, BK_, EPI, TC>(a, splits, st); break;
+      default: launch_cfg<TA, MF, 128, 128, 2, 2, AK, BK_, EPI, TC>(a, splits, st); break;
+    }
   }
 }
 
 template <typename TA, typename MF, typename TC>
 static int launch_epi(const GemmArgs& a, int layout, int epi, int tile, int splits, hipStream_t st) {
-#define GK_CASE(L, AK, BK_, E)                                             \
-  if (layout == L && epi == E) {                                           \
-    launch_tiles<TA, MF, AK, BK_, E, TC>(a, tile, splits, st);             \
-    return 0;                                                              \
+#define GK_CASE(L, AK, BK_, E)                                 \
+  if (layout == L && epi == E) {                               \
+    launch_tiles<TA, MF, AK, BK_, E, TC>(a, tile, splits, st); \
+    return 0;                                                  \
   }
   // forward products: activation [M][K] x weight [N][K]
   GK_CASE(LAYOUT_KK, true, true, EPI_STORE)
@@ -348,18 +416,16 @@ static int launch_epi(const GemmArgs& a, int layout, int epi, int tile, int spli
   return -1;
 }
 
-int gemm_launch(const GemmArgs& a, int dtype, int layout, int epi, int tile, int splits,
-                hipStream_t st) {
+int gemm_launch(const GemmArgs& a, int dtype, int layout, int epi, int tile, int splits, hipStream_t st) {
   if (dtype == DT_BF16) return launch_epi<bf16, Mfma<bf16>, bf16>(a, layout, epi, tile, splits, st);
   if (dtype == DT_F32) return launch_epi<float, Mfma<float>, float>(a, layout, epi, tile, splits, st);
   return -1;
 }
 
-void splitk_reduce(const float* part, int splits, long mn, float* out, int accumulate,
-                   hipStream_t st) {
+void splitk_reduce(const float* part, int splits, long mn, float* out, int accumulate, hipStream_t st) {
   const long n4 = (mn + 3) / 4;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part,
-                     splits, mn, out, accumulate);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, splits, mn,
+                     out, accumulate);
 }
 
 }  // namespace gk

@@ -26,7 +26,14 @@ enum Epi {
   EPI_PARTIAL = 7,    // part[split][M][N] = acc (split-K)
 };
 
-enum Tile { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, TILE_64x64 = 3 };
+// Work-group tiles (M x N); _W8 variants use 8 waves (2 x 4) instead of 4 (2 x 2).
+enum Tile {
+  TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, TILE_64x64 = 3,
+  TILE_256x256_W8 = 4, TILE_256x128_W8 = 5,
+};
+int tile_bm(int tile);
+int tile_bn(int tile);
+int tile_wn(int tile);   // output columns owned by one wave
 
 struct GemmArgs {
   const void* A;

@@ -9,7 +9,7 @@ from tests.gpu_common import log
 pytestmark = pytest.mark.gpu
 
 LAYOUT_KK, LAYOUT_KN, LAYOUT_MN = 0, 1, 2
-TILES_BF16 = [0, 1, 2]      # 256x256, 256x128, 128x128
+TILES_BF16 = [0, 1, 2, 4, 5]    # 256x256, 256x128, 128x128 (4 waves); 256x256, 256x128 (8 waves)
 TILES_F32 = [2, 3]          # 128x128, 64x64
 
 
