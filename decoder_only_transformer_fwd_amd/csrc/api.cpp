@@ -123,36 +123,34 @@ struct GemmPlan {
 };
 
 
+// Tile and split-K choice, set from measurements of this kernel on MI355X at
+// the step's shapes.  Small-N products are limited by L2->CU bandwidth less
+// than by latency and do best with 128x128 tiles (two work-groups per CU);
+// very wide products use the 8-wave 256x256 tile.  Weight gradients (K = B*T)
+// are split along K until about two waves of work-groups exist.
 GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   GemmPlan g{TILE_64x64, 1, K};
   const int bk = dtype == DT_F32 ? 32 : 64;
   if (dtype == DT_F32) {
     g.tile = (long)M * N >= 256L * 128 * 128 ? TILE_128x128 : TILE_64x64;
+  } else if (layout == LAYOUT_KK) {
+    g.tile = N >= 8192 ? TILE_256x256_W8 : TILE_128x128;
+  } else if (layout == LAYOUT_KN) {
+    g.tile = N >= 6144 ? TILE_256x256 : TILE_128x128;
   } else {
-    const int cand[5] = {TILE_256x256_W8, TILE_256x256, TILE_256x128_W8, TILE_256x128, TILE_128x128};
-    const double eff[5] = {1.0, 0.85, 0.9, 0.8, 0.8};
-    double best = 1e300;
-    for (int c = 0; c < 5; ++c) {
-      const long tiles = (long)((M + tile_bm(cand[c]) - 1) / tile_bm(cand[c])) *
-                         ((N + tile_bn(cand[c]) - 1) / tile_bn(cand[c]));
-      const long waves = (tiles + 255) / 256;
-      const double cost = (double)waves * tile_bm(cand[c]) * tile_bn(cand[c]) / eff[c];
-      if (cost < best) { best = cost; g.tile = cand[c]; }
-    }
+    g.tile = (long)M * N >= 4L * 1024 * 1024 ? TILE_256x256 : TILE_128x128;
   }
-  if (layout == LAYOUT_MN || layout == LAYOUT_KN) {
+  if (layout == LAYOUT_MN) {
     const long tiles = (long)((M + tile_bm(g.tile) - 1) / tile_bm(g.tile)) * ((N + tile_bn(g.tile) - 1) / tile_bn(g.tile));
-    if (tiles < 192 && K >= 4 * bk * 4) {
-      int splits = (int)((256 + tiles - 1) / tiles);
-      if (splits > 16) splits = 16;
-      const int maxs = K / (4 * bk);
-      if (splits > maxs) splits = maxs;
-      if (splits > 1) {
-        int ks = (K + splits - 1) / splits;
-        ks = (ks + bk - 1) / bk * bk;
-        g.splits = (K + ks - 1) / ks;
-        g.k_split = ks;
-      }
+    int splits = (int)((512 + tiles - 1) / tiles);
+    if (splits > 8) splits = 8;
+    const int maxs = K / (4 * bk);
+    if (splits > maxs) splits = maxs;
+    if (splits > 1) {
+      int ks = (K + splits - 1) / splits;
+      ks = (ks + bk - 1) / bk * bk;
+      g.splits = (K + ks - 1) / ks;
+      g.k_split = ks;
     }
   }
   if (g.splits == 1) g.k_split = K;
@@ -632,7 +630,8 @@ int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const vo
     return fail(GPT_EINVAL, "gpt_gemm: splits");
   if (tile < 0) tile = plan_gemm(dtype, layout, M, N, K).tile;
   if (dtype == DT_F32 && tile != TILE_128x128 && tile != TILE_64x64) return fail(GPT_EINVAL, "gpt_gemm: tile");
-  if (dtype == DT_BF16 && (tile == TILE_64x64 || tile > TILE_256x128_W8)) return fail(GPT_EINVAL, "gpt_gemm: tile");
+  if (dtype == DT_BF16 && (tile == TILE_64x64 || tile >= TILE_COUNT || (tile_needs_kc(tile) && layout != LAYOUT_KK)))
+    return fail(GPT_EINVAL, "gpt_gemm: tile");
   GemmArgs a{};
   a.A = A; a.B = B; a.M = M; a.N = N; a.K = K;
   a.lda = layout == LAYOUT_MN ? M : K;

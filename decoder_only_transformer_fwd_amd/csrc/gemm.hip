@@ -96,12 +96,14 @@ struct TransLoader {
 // owning LDS slot p of row r fetches K-chunk p ^ swz(r)).  Rows past the
 // operand and K-chunks past the end of the K range are outside the buffer's
 // range and arrive as zeros.
-template <int ES, int ROWS, int NWAVES>
+template <int ES, int ROWS, int NWAVES, int RB>
 struct DmaLoader {
   static constexpr int EPC = 16 / ES;
+  static constexpr int CPR = RB / 16;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;            // rows per wave instruction
   static constexpr int RPW = ROWS / NWAVES;       // rows per wave
-  static constexpr int PER_WAVE = RPW / 8;
-  static_assert(RPW % 8 == 0, "tile rows must cover 8 rows per wave instruction");
+  static constexpr int PER_WAVE = RPW / RPI;
+  static_assert(RPW % RPI == 0, "tile rows must be a multiple of the rows one wave instruction fills");
   __amdgpu_buffer_rsrc_t rsrc;
   int voff[PER_WAVE];
   int kel[PER_WAVE];
@@ -113,8 +115,8 @@ struct DmaLoader {
     rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (long)r0 * ld * ES), 0, (int)bytes, BUF_DWORD3);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int r = wave * RPW + i * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz<128>(r);
+      const int r = wave * RPW + i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<RB>(r);
       voff[i] = (int)(r * ld * ES) + c * 16;
       kel[i] = c * EPC;
     }
@@ -124,10 +126,14 @@ struct DmaLoader {
     for (int i = 0; i < PER_WAVE; ++i) {
       const int off = (k0 + kel[i] < kend) ? voff[i] + k0 * ES : (int)0x80000000;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(lds + (wave * RPW + i * 8) * 128), 16, off, 0, 0, 0);
+          rsrc, (__attribute__((address_space(3))) void*)(lds + (wave * RPW + i * RPI) * RB), 16, off, 0, 0, 0);
     }
   }
 };
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int nwg = tiles_m * tiles_n;
@@ -145,19 +151,22 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
   tn = in_group / gsize;
 }
 
-template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, bool A_KC, bool B_KC, int EPI, typename TC>
+template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, int RB, int NS, bool A_KC, bool B_KC, int EPI,
+          typename TC>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
   constexpr int THREADS = 64 * WGM * WGN;
   constexpr int NW = WGM * WGN;
   constexpr int ES = sizeof(TA);
-  constexpr int BK = 128 / ES;
+  constexpr int BK = RB / ES;         // K elements per step
+  static_assert(NS == 2 || (A_KC && B_KC), "deeper pipelines need both operands on the direct-to-LDS path");
+  static_assert(RB == 128 || (A_KC && B_KC), "register-transposed operands use 128-byte rows");
   constexpr int KM = MF::KM;
   constexpr int EPL = MF::EPL;
   constexpr int FB = EPL * ES;         // fragment bytes per lane
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int STAGE = (BM + BN) * 128;   // A tile, then B tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int STAGE = (BM + BN) * RB;   // A tile, then B tile
+  __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -177,8 +186,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
 
   TransLoader<ES, BM, THREADS> la;
   TransLoader<ES, BN, THREADS> lb;
-  DmaLoader<ES, BM, NW> da;
-  DmaLoader<ES, BN, NW> db;
+  DmaLoader<ES, BM, NW, RB> da;
+  DmaLoader<ES, BN, NW, RB> db;
   const char* Ab = (const char*)p.A;
   const char* Bb = (const char*)p.B;
   if constexpr (A_KC) da.init(Ab, p.lda, m0, p.M, wave, lane);
@@ -196,34 +205,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
     char* st = smem + stage * STAGE;
     if constexpr (A_KC) da.issue(st, k0, kend, wave);
     else la.load(Ab, p.lda, m0, p.M, k0, kend, t);
-    if constexpr (B_KC) db.issue(st + BM * 128, k0, kend, wave);
+    if constexpr (B_KC) db.issue(st + BM * RB, k0, kend, wave);
     else lb.load(Bb, p.ldb, n0, p.N, k0, kend, t);
   };
   auto commit = [&](int stage) {   // register-staged operands into LDS
     char* st = smem + stage * STAGE;
     if constexpr (!A_KC) la.store(st, t);
-    if constexpr (!B_KC) lb.store(st + BM * 128, t);
+    if constexpr (!B_KC) lb.store(st + BM * RB, t);
   };
-
-  if (nk > 0) {
-    fetch(kbeg, 0);
-    commit(0);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): this thread's LDS traffic has landed
-  __syncthreads();
-
   constexpr int KK = BK / KM;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) fetch(kbeg + (kt + 1) * BK, s ^ 1);
-    const char* a_s = smem + s * STAGE;
-    const char* b_s = a_s + BM * 128;
+  auto compute = [&](int stage) {
+    const char* a_s = smem + stage * STAGE;
+    const char* b_s = a_s + BM * RB;
     typename MF::frag af[2][MB], bfr[2][NB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) lds_read<128, FB>(a_s, wm * WM + i * 32 + l32, (g * EPL) * ES, &af[0][i]);
+    for (int i = 0; i < MB; ++i) lds_read<RB, FB>(a_s, wm * WM + i * 32 + l32, (g * EPL) * ES, &af[0][i]);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) lds_read<128, FB>(b_s, wn * WN + j * 32 + l32, (g * EPL) * ES, &bfr[0][j]);
+    for (int j = 0; j < NB; ++j) lds_read<RB, FB>(b_s, wn * WN + j * 32 + l32, (g * EPL) * ES, &bfr[0][j]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
@@ -232,9 +230,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
       if (kk + 1 < KK) {
         const int kb = ((kk + 1) * KM + g * EPL) * ES;
 #pragma unroll
-        for (int i = 0; i < MB; ++i) lds_read<128, FB>(a_s, wm * WM + i * 32 + l32, kb, &af[cur ^ 1][i]);
+        for (int i = 0; i < MB; ++i) lds_read<RB, FB>(a_s, wm * WM + i * 32 + l32, kb, &af[cur ^ 1][i]);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) lds_read<128, FB>(b_s, wn * WN + j * 32 + l32, kb, &bfr[cur ^ 1][j]);
+        for (int j = 0; j < NB; ++j) lds_read<RB, FB>(b_s, wn * WN + j * 32 + l32, kb, &bfr[cur ^ 1][j]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -243,9 +241,40 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
         for (int j = 0; j < NB; ++j) acc[i][j] = MF::mma(bfr[cur][j], af[cur][i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) commit(s ^ 1);
-    __builtin_amdgcn_s_waitcnt(0x0070);
+  };
+
+  if constexpr (NS == 2) {
+    // Two stages: the next tile is requested at the top of a step and must
+    // have landed (vmcnt 0) by the barrier that ends it.
+    if (nk > 0) {
+      fetch(kbeg, 0);
+      commit(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int s = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) fetch(kbeg + (kt + 1) * BK, s ^ 1);
+      compute(s);
+      if (more) commit(s ^ 1);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      __syncthreads();
+    }
+  } else {
+    // NS stages, all by direct-to-LDS loads: NS-1 steps are in flight.  Every
+    // step issues its loads (past the K range they fetch zeros), so a fixed
+    // vmcnt threshold waits for exactly the stage about to be consumed.
+    constexpr int LPS = DmaLoader<ES, BM, NW, RB>::PER_WAVE + DmaLoader<ES, BN, NW, RB>::PER_WAVE;
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) fetch(kbeg + st * BK, st);
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
+      __syncthreads();
+      fetch(kbeg + (kt + NS - 1) * BK, (kt + NS - 1) % NS);
+      compute(kt % NS);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);
   }
 
   // ------------------------------------------------------------ epilogue
@@ -345,48 +374,54 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // ------------------------------------------------------------------ dispatch
 
-int tile_bm(int tile) {
-  switch (tile) {
-    case TILE_256x256: case TILE_256x128: case TILE_256x256_W8: case TILE_256x128_W8: return 256;
-    case TILE_128x128: return 128;
-    default: return 64;
-  }
-}
-int tile_bn(int tile) {
-  switch (tile) {
-    case TILE_256x256: case TILE_256x256_W8: return 256;
-    case TILE_256x128: case TILE_128x128: case TILE_256x128_W8: return 128;
-    default: return 64;
-  }
-}
-int tile_wn(int tile) {   // columns per wave (the cross-entropy partial block width)
-  switch (tile) {
-    case TILE_256x256_W8: return 64;
-    case TILE_256x128_W8: return 32;
-    default: return tile_bn(tile) / 2;
-  }
-}
+// Tile table: id -> (BM, BN, waves M x N, bytes per K step per row, stages).
+struct TileCfg {
+  int bm, bn, wgm, wgn, rb, ns;
+};
+static constexpr TileCfg TILES[] = {
+    {256, 256, 2, 2, 128, 2},  // TILE_256x256
+    {256, 128, 2, 2, 128, 2},  // TILE_256x128
+    {128, 128, 2, 2, 128, 2},  // TILE_128x128
+    {64, 64, 2, 2, 128, 2},    // TILE_64x64
+    {256, 256, 2, 4, 128, 2},  // TILE_256x256_W8
+    {256, 128, 2, 4, 128, 2},  // TILE_256x128_W8
+    {256, 256, 2, 4, 64, 4},   // TILE_256x256_W8_S4
+    {256, 256, 2, 2, 64, 4},   // TILE_256x256_S4
+    {256, 128, 2, 4, 128, 3},  // TILE_256x128_W8_S3
+    {128, 128, 2, 2, 64, 4},   // TILE_128x128_S4
+};
+int tile_bm(int tile) { return TILES[tile].bm; }
+int tile_bn(int tile) { return TILES[tile].bn; }
+int tile_wn(int tile) { return TILES[tile].bn / TILES[tile].wgn; }
+bool tile_needs_kc(int tile) { return TILES[tile].ns > 2 || TILES[tile].rb != 128; }
 
-template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, bool AK, bool BK_, int EPI, typename TC>
+template <typename TA, typename MF, int T, bool AK, bool BK_, int EPI, typename TC>
 static void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
-  dim3 grid(((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN), 1, splits);
-  hipLaunchKernelGGL((gemm_kernel<TA, MF, BM, BN, WGM, WGN, AK, BK_, EPI, TC>), grid, dim3(64 * WGM * WGN), 0, st,
-                     a);
+  constexpr TileCfg c = TILES[T];
+  dim3 grid(((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn), 1, splits);
+  hipLaunchKernelGGL((gemm_kernel<TA, MF, c.bm, c.bn, c.wgm, c.wgn, c.rb, c.ns, AK, BK_, EPI, TC>), grid,
+                     dim3(64 * c.wgm * c.wgn), 0, st, a);
 }
 
 template <typename TA, typename MF, bool AK, bool BK_, int EPI, typename TC>
 static void launch_tiles(const GemmArgs& a, int tile, int splits, hipStream_t st) {
   if constexpr (sizeof(TA) == 4) {
-    if (tile == TILE_128x128) launch_cfg<TA, MF, 128, 128, 2, 2, AK, BK_, EPI, TC>(a, splits, st);
-    else launch_cfg<TA, MF, 64, 64, 2, 2, AK, BK_, EPI, TC>(a, splits, st);
+    if (tile == TILE_128x128) launch_cfg<TA, MF, TILE_128x128, AK, BK_, EPI, TC>(a, splits, st);
+    else launch_cfg<TA, MF, TILE_64x64, AK, BK_, EPI, TC>(a, splits, st);
   } else {
+#define GK_T(T) case T: launch_cfg<TA, MF, T, AK, BK_, EPI, TC>(a, splits, st); return;
     switch (tile) {
-      case TILE_256x256: launch_cfg<TA, MF, 256, 256, 2, 2, AK, BK_, EPI, TC>(a, splits, st); break;
-      case TILE_256x128: launch_cfg<TA, MF, 256, 128, 2, 2, AK, BK_, EPI, TC>(a, splits, st); break;
-      case TILE_256x256_W8: launch_cfg<TA, MF, 256, 256, 2, 4, AK, BK_, EPI, TC>(a, splits, st); break;
-      case TILE_256x128_W8: launch_cfg<TA, MF, 256, 128, 2, 4, AK, BK_, EPI, TC>(a, splits, st); break;
-      default: launch_cfg<TA, MF, 128, 128, 2, 2, AK, BK_, EPI, TC>(a, splits, st); break;
+      GK_T(TILE_256x256) GK_T(TILE_256x128) GK_T(TILE_256x256_W8) GK_T(TILE_256x128_W8)
+      default: break;
     }
+    if constexpr (AK && BK_) {
+      switch (tile) {
+        GK_T(TILE_256x256_W8_S4) GK_T(TILE_256x256_S4) GK_T(TILE_256x128_W8_S3) GK_T(TILE_128x128_S4)
+        default: break;
+      }
+    }
+#undef GK_T
+    launch_cfg<TA, MF, TILE_128x128, AK, BK_, EPI, TC>(a, splits, st);
   }
 }
 

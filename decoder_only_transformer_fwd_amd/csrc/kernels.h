@@ -30,7 +30,12 @@ enum Epi {
 enum Tile {
   TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2, TILE_64x64 = 3,
   TILE_256x256_W8 = 4, TILE_256x128_W8 = 5,
+  // deeper pipelines (K-contiguous operands only): 4 stages of 64-byte rows
+  // or 3 stages of 128-byte rows
+  TILE_256x256_W8_S4 = 6, TILE_256x256_S4 = 7, TILE_256x128_W8_S3 = 8, TILE_128x128_S4 = 9,
+  TILE_COUNT = 10,
 };
+bool tile_needs_kc(int tile);   // usable only when both operands are K-contiguous
 int tile_bm(int tile);
 int tile_bn(int tile);
 int tile_wn(int tile);   // output columns owned by one wave

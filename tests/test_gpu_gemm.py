@@ -77,6 +77,15 @@ def test_gemm_split_k(layout):
     _check(c, ref, 2048)
 
 
-def test_gemm_bf16_multi_tile():
-    c, ref = run_gemm(1, LAYOUT_KK, 1024, 768, 512, 0, seed=3)
+@pytest.mark.parametrize("tile", [0, 4, 6, 7, 8, 9])
+def test_gemm_bf16_multi_tile(tile):
+    c, ref = run_gemm(1, LAYOUT_KK, 1024, 768, 512, tile, seed=3)
     _check(c, ref, 512)
+
+
+@pytest.mark.parametrize("tile", [6, 7, 8, 9])
+def test_gemm_bf16_deep_pipeline_ragged(tile):
+    # K not a multiple of the 32- or 64-element step, fewer steps than stages
+    for K in (40, 328):
+        c, ref = run_gemm(1, LAYOUT_KK, 264, 200, K, tile)
+        _check(c, ref, K)
