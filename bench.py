@@ -103,19 +103,37 @@ def main() -> int:
             scale = 1e12 if unit == "TFLOP/s" else 1e9
             log(f"  {x['name']:28s} {x['launches']:6d} launches {x['total_ms'] / args.steps:9.3f} ms/step "
                 f"{100 * x['total_ms'] / total_site_ms:5.1f}%  {rate / scale:9.1f} {unit}")
-    dom = max(sites, key=lambda x: x["total_ms"])
-    per_launch_s = dom["total_ms"] / dom["launches"] * 1e-3
+    # Roofline of the dominant kernel: sites launching the same kernel
+    # (template instantiation) are aggregated, as a profiler's per-kernel
+    # statistics are.
+    kernels = {}
+    for x in sites:
+        k = kernels.setdefault(x["kernel"], {"kernel": x["kernel"], "sites": [], "launches": 0, "total_ms": 0.0,
+                                             "work": 0.0, "work_kind": x["work_kind"]})
+        k["sites"].append(x["name"])
+        k["launches"] += x["launches"]
+        k["total_ms"] += x["total_ms"]
+        k["work"] += x["work"]
+    dom = max(kernels.values(), key=lambda k: k["total_ms"])
+    avg_s = dom["total_ms"] / dom["launches"] * 1e-3
     work_per_launch = dom["work"] / dom["launches"]
     if dom["work_kind"] == "flops":
         kpeak = Mx.PEAK_FP32_MFMA if s.precision == "fp32" else Mx.PEAK_BF16
-        roof = {"bound": "mfma", "kernel": dom["name"], "achieved": work_per_launch / per_launch_s / 1e12,
-                "peak": kpeak / 1e12, "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": work_per_launch / avg_s / 1e12, "peak": kpeak / 1e12,
+                "unit": "TFLOP/s"}
     else:
-        roof = {"bound": "hbm", "kernel": dom["name"], "achieved": work_per_launch / per_launch_s / 1e9,
-                "peak": Mx.PEAK_HBM / 1e9, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": work_per_launch / avg_s / 1e9, "peak": Mx.PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
+    roof["kernel"] = dom["kernel"]
+    roof["sites"] = dom["sites"]
+    roof["avg_launch_us"] = avg_s * 1e6
     roof["share_of_step"] = dom["total_ms"] / total_site_ms
+    if args.sites:
+        log("per kernel:")
+        for k in sorted(kernels.values(), key=lambda k: -k["total_ms"])[:12]:
+            log(f"  {k['total_ms'] / args.steps:9.3f} ms/step {k['launches'] // args.steps:5d}/step "
+                f"avg {k['total_ms'] / k['launches'] * 1e3:9.1f} us  {k['kernel']}  [{', '.join(k['sites'])}]")
 
     out = {
         "metric": METRIC,

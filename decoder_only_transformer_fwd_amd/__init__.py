@@ -63,8 +63,8 @@ def _load():
     D = ctypes.c_double
     lib.gpt_profile_enable.argtypes = [P, I]
     lib.gpt_profile_sites.argtypes = [P, ctypes.POINTER(I)]
-    lib.gpt_profile_get.argtypes = [P, I, ctypes.c_char_p, I, ctypes.POINTER(I64), ctypes.POINTER(D),
-                                    ctypes.POINTER(D), ctypes.POINTER(I)]
+    lib.gpt_profile_get.argtypes = [P, I, ctypes.c_char_p, I, ctypes.c_char_p, I, ctypes.POINTER(I64),
+                                    ctypes.POINTER(D), ctypes.POINTER(D), ctypes.POINTER(I)]
     lib.gpt_strerror.argtypes = [I]
     lib.gpt_strerror.restype = ctypes.c_char_p
     lib.gpt_last_error.argtypes = []
@@ -175,11 +175,12 @@ def gpt_profile_sites(model: int) -> int:
 
 def gpt_profile_get(model: int, index: int) -> dict:
     name = ctypes.create_string_buffer(64)
+    kern = ctypes.create_string_buffer(160)
     la, ms, wk, kind = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
-    _check(_lib.gpt_profile_get(model, index, name, 64, ctypes.byref(la), ctypes.byref(ms), ctypes.byref(wk),
-                                ctypes.byref(kind)), "gpt_profile_get")
-    return dict(name=name.value.decode(), launches=la.value, total_ms=ms.value, work=wk.value,
-                work_kind="flops" if kind.value == 0 else "bytes")
+    _check(_lib.gpt_profile_get(model, index, name, 64, kern, 160, ctypes.byref(la), ctypes.byref(ms),
+                                ctypes.byref(wk), ctypes.byref(kind)), "gpt_profile_get")
+    return dict(name=name.value.decode(), kernel=kern.value.decode(), launches=la.value, total_ms=ms.value,
+                work=wk.value, work_kind="flops" if kind.value == 0 else "bytes")
 
 
 def gpt_strerror(code: int) -> str:

@@ -179,6 +179,7 @@ struct gpt_model {
   // optional per-launch-site timing with HIP events on the step's stream
   struct Site {
     std::string name;
+    std::string kernel;   // template signature of the launched kernel
     long launches = 0;
     double ms = 0.0, work = 0.0;
     int work_kind = 0;  // 0 = flops, 1 = bytes
@@ -289,7 +290,7 @@ hipEvent_t next_event(gpt_model& m) {
   return m.ev_pool[m.ev_used++];
 }
 
-void prof_begin(gpt_model& m, const char* name, double work, int kind) {
+void prof_begin(gpt_model& m, const char* name, double work, int kind, const std::string& kernel) {
   if (!m.prof_on) return;
   int idx = -1;
   for (size_t i = 0; i < m.sites.size(); ++i)
@@ -297,6 +298,7 @@ void prof_begin(gpt_model& m, const char* name, double work, int kind) {
   if (idx < 0) {
     gpt_model::Site st;
     st.name = name;
+    st.kernel = kernel;
     st.work_kind = kind;
     m.sites.push_back(st);
     idx = (int)m.sites.size() - 1;
@@ -346,17 +348,21 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   if (g.splits > 1) {
     a.part = at<float>(m, m.splitk);
     a.k_split = g.k_split;
-    prof_begin(m, site, flops, 0);
+    char label[128];
+    gemm_kernel_label(m.s.dtype, layout, EPI_PARTIAL, g.tile, label, sizeof label);
+    prof_begin(m, site, flops, 0, label);
     if (gemm_launch(a, m.s.dtype, layout, EPI_PARTIAL, g.tile, g.splits, m.st))
       return fail(GPT_EINVAL, "gemm variant not instantiated (partial)");
     prof_end(m);
-    prof_begin(m, "splitk_reduce", (g.splits + 1.0) * M * N * 4.0, 1);
+    prof_begin(m, "splitk_reduce", (g.splits + 1.0) * M * N * 4.0, 1, "splitk_reduce_kernel");
     splitk_reduce(a.part, g.splits, (long)M * N, (float*)C, 0, m.st);
     prof_end(m);
     return GPT_OK;
   }
   a.k_split = K;
-  prof_begin(m, site, flops, 0);
+  char label[128];
+  gemm_kernel_label(m.s.dtype, layout, epi, g.tile, label, sizeof label);
+  prof_begin(m, site, flops, 0, label);
   if (gemm_launch(a, m.s.dtype, layout, epi, g.tile, 1, m.st))
     return fail(GPT_EINVAL, "gemm variant not instantiated");
   prof_end(m);
@@ -379,19 +385,24 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   int rc;
 
   const double es_d = (double)es;
+  const std::string tname = dt == DT_BF16 ? "bf16" : "float";
+  auto KL = [&](const char* k) { return std::string(k) + "<" + tname + ">"; };
+  auto KLD = [&](const char* k, const char* extra = "") {
+    return std::string(k) + "<" + tname + ", " + std::to_string(Dh) + extra + ">";
+  };
   fill_f32((float*)flag, 1, 0.f, st);
-  prof_begin(m, "embed_fwd", (double)BT * d * (es_d + 4.0) + BT * 8.0, 1);
+  prof_begin(m, "embed_fwd", (double)BT * d * (es_d + 4.0) + BT * 8.0, 1, KL("embed_fwd_kernel"));
   embed_fwd(dt, tokens, targets, wp(P.E), h, BT, d, V, flag, st);
   prof_end(m);
   for (int l = 0; l < s.L; ++l) {
     auto& Ly = m.lay[l];
     const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
-    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1);
+    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
     rmsnorm_fwd(dt, h, m.ws + Ly.n1, at<float>(m, Ly.rstd1), BT, d, s.eps, st);
     prof_end(m);
     if ((rc = gemm(m, "gemm_qkv", LAYOUT_KK, EPI_STORE, BT, 3 * d, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d, m.ws + Ly.qkv, 3 * d)))
       return rc;
-    prof_begin(m, "rope_qknorm_fwd", (double)BT * d * 8.0 * es_d + BT * 2.0 * H * 4.0, 1);
+    prof_begin(m, "rope_qknorm_fwd", (double)BT * d * 8.0 * es_d + BT * 2.0 * H * 4.0, 1, KLD("rope_qknorm_fwd_kernel"));
     rope_qknorm_fwd(dt, m.ws + Ly.qkv, at<float>(m, Ly.rqk), m.ws + Ly.qT, m.ws + Ly.kT, m.ws + Ly.vT, cosb, sinb,
                     s.B, s.T, s.Tp, H, Dh, s.eps, st);
     AttnArgs aa{};
@@ -401,11 +412,12 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     aa.scale = 1.0f / std::sqrt((float)Dh);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
     prof_end(m);
-    prof_begin(m, s.win[l] < s.T ? "attn_fwd_window" : "attn_fwd_causal", 4.0 * Dh * pairs, 0);
+    prof_begin(m, s.win[l] < s.T ? "attn_fwd_window" : "attn_fwd_causal", 4.0 * Dh * pairs, 0,
+               KLD("attn_fwd_kernel"));
     if (attn_fwd(dt, Dh, aa, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
     prof_end(m);
     if ((rc = gemm(m, "gemm_o", LAYOUT_KK, EPI_ACCUM_F32, BT, d, d, m.ws + Ly.o, d, wp(P.Wo[l]), d, h, d))) return rc;
-    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1);
+    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
     rmsnorm_fwd(dt, h, m.ws + Ly.n2, at<float>(m, Ly.rstd2), BT, d, s.eps, st);
     prof_end(m);
     GemmArgs ex{};
@@ -414,7 +426,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
       return rc;
     if ((rc = gemm(m, "gemm_w2", LAYOUT_KK, EPI_ACCUM_F32, BT, d, F, m.ws + Ly.g, F, wp(P.W2[l]), F, h, d))) return rc;
   }
-  prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1);
+  prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
   rmsnorm_fwd(dt, h, m.ws + m.nL, at<float>(m, m.rstdL), BT, d, s.eps, st);
   prof_end(m);
   {
@@ -425,7 +437,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     ex.nblk = m.xent_nblk;
     if ((rc = gemm(m, "gemm_lm_head_xent_fwd", LAYOUT_KK, EPI_XENT_FWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, nullptr, V, ex))) return rc;
   }
-  prof_begin(m, "xent_reduce", (double)BT * m.xent_nblk * 8.0 + BT * 12.0, 1);
+  prof_begin(m, "xent_reduce", (double)BT * m.xent_nblk * 8.0 + BT * 12.0, 1, "xent_reduce_kernel + mean_reduce_kernel");
   xent_reduce(at<float>(m, m.part), at<float>(m, m.tgt), BT, m.xent_nblk, at<float>(m, m.lse),
               at<float>(m, m.rowloss), st);
   mean_reduce(at<float>(m, m.rowloss), BT, at<float>(m, m.lossdev), st);
@@ -446,7 +458,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   if ((rc = gemm(m, "wgrad_lm_head", LAYOUT_MN, EPI_STORE_F32, V, d, BT, m.ws + m.dz, V, m.ws + m.nL, d, grads + P.U,
                  d)))
     return rc;
-  prof_begin(m, "rmsnorm_bwd", (double)BT * d * (8.0 + 2.0 * es_d), 1);
+  prof_begin(m, "rmsnorm_bwd", (double)BT * d * (8.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
   rmsnorm_bwd(dt, dm, m.ws + m.nL, at<float>(m, m.rstdL), dh, dhA, BT, d, 0, st);
   prof_end(m);
   for (int l = s.L - 1; l >= 0; --l) {
@@ -463,13 +475,13 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     if ((rc = gemm(m, "wgrad_w1", LAYOUT_MN, EPI_STORE_F32, F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d,
                    grads + P.W1[l], d)))
       return rc;
-    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1);
+    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
     rmsnorm_bwd(dt, dm, m.ws + Ly.n2, at<float>(m, Ly.rstd2), dh, dhA, BT, d, 1, st);
     prof_end(m);
     if ((rc = gemm(m, "dgrad_o", LAYOUT_KN, EPI_STORE, BT, d, d, dhA, d, wp(P.Wo[l]), d, m.ws + m.dO, d))) return rc;
     if ((rc = gemm(m, "wgrad_o", LAYOUT_MN, EPI_STORE_F32, d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d)))
       return rc;
-    prof_begin(m, "attn_bwd_pre", (double)BT * d * 3.0 * es_d + (double)s.B * H * s.Tp * 4.0, 1);
+    prof_begin(m, "attn_bwd_pre", (double)BT * d * 3.0 * es_d + (double)s.B * H * s.Tp * 4.0, 1, KLD("attn_bwd_pre_kernel"));
     attn_bwd_pre(dt, m.ws + m.dO, m.ws + Ly.o, at<float>(m, m.Dv), m.ws + m.dOT, s.B, s.T, s.Tp, H, Dh, st);
     prof_end(m);
     AttnArgs aa{};
@@ -480,13 +492,19 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     aa.scale = 1.0f / std::sqrt((float)Dh);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
     const bool win = s.win[l] < s.T;
-    prof_begin(m, win ? "attn_bwd_dkdv_window" : "attn_bwd_dkdv_causal", 6.0 * Dh * pairs, 0);
+    prof_begin(m, win ? "attn_bwd_dv_window" : "attn_bwd_dv_causal", 2.0 * Dh * pairs, 0,
+               KLD("attn_bwd_dkdv_kernel", ", 32, 1"));
     if (attn_bwd(dt, Dh, aa, 0, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
     prof_end(m);
-    prof_begin(m, win ? "attn_bwd_dq_window" : "attn_bwd_dq_causal", 2.0 * Dh * pairs, 0);
+    prof_begin(m, win ? "attn_bwd_dk_window" : "attn_bwd_dk_causal", 4.0 * Dh * pairs, 0,
+               KLD("attn_bwd_dkdv_kernel", ", 32, 2"));
     if (attn_bwd(dt, Dh, aa, 1, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
     prof_end(m);
-    prof_begin(m, "rope_qknorm_bwd", (double)BT * d * 6.0 * es_d + BT * 2.0 * H * 4.0, 1);
+    prof_begin(m, win ? "attn_bwd_dq_window" : "attn_bwd_dq_causal", 2.0 * Dh * pairs, 0,
+               KLD("attn_bwd_dq_kernel"));
+    if (attn_bwd(dt, Dh, aa, 2, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
+    prof_end(m);
+    prof_begin(m, "rope_qknorm_bwd", (double)BT * d * 6.0 * es_d + BT * 2.0 * H * 4.0, 1, KLD("rope_qknorm_bwd_kernel"));
     rope_qknorm_bwd(dt, m.ws + m.dqkv, m.ws + Ly.qkv, at<float>(m, Ly.rqk), cosb, sinb, s.B, s.T, H, Dh, st);
     prof_end(m);
     if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, EPI_STORE_F32, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d,
@@ -495,11 +513,11 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     if ((rc = gemm(m, "wgrad_qkv", LAYOUT_MN, EPI_STORE_F32, 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d,
                    grads + P.Wqkv[l], d)))
       return rc;
-    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1);
+    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
     rmsnorm_bwd(dt, dm, m.ws + Ly.n1, at<float>(m, Ly.rstd1), dh, dhA, BT, d, 1, st);
     prof_end(m);
   }
-  prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * 4.0 + BT * 8.0, 1);
+  prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * 4.0 + BT * 8.0, 1, "sort_keys_kernel + embed_bwd_runs_kernel");
   embed_bwd(tokens, dh, grads + P.E, BT, d, V, at<uint32_t>(m, m.keys), nullptr, nullptr, st);
   prof_end(m);
   HIP_TRY(hipGetLastError());
@@ -671,12 +689,13 @@ int gpt_profile_sites(gpt_model* m, int* n) {
   return GPT_OK;
 }
 
-int gpt_profile_get(gpt_model* m, int i, char* name, int name_len, int64_t* launches, double* total_ms,
-                    double* work, int* work_kind) {
-  if (!m || !name || !launches || !total_ms || !work || !work_kind) return fail(GPT_ENULL, "NULL argument");
+int gpt_profile_get(gpt_model* m, int i, char* name, int name_len, char* kernel, int kernel_len, int64_t* launches,
+                    double* total_ms, double* work, int* work_kind) {
+  if (!m || !name || !kernel || !launches || !total_ms || !work || !work_kind) return fail(GPT_ENULL, "NULL argument");
   if (i < 0 || i >= (int)m->sites.size()) return fail(GPT_EINVAL, "site index out of range");
   const auto& st = m->sites[i];
   snprintf(name, name_len, "%s", st.name.c_str());
+  snprintf(kernel, kernel_len, "%s", st.kernel.c_str());
   *launches = st.launches;
   *total_ms = st.ms;
   *work = st.work;

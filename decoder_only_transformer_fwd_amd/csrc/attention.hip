@@ -16,39 +16,14 @@
 // come from transposed copies [B][H][Dh][Tp] written by the producing kernels,
 // so every LDS read is one contiguous 8- or 16-byte access.
 //
-// Backward: D_i = rowsum(dO*O) comes from a separate pass; dK/dV are produced
-// by one kernel per 128-key tile iterating over query tiles, dQ by one kernel
-// per 128-query tile iterating over key tiles.  No atomics: the result is
-// bitwise reproducible.
+// Backward: D_i = rowsum(dO*O) comes from a separate pass; dV and dK are
+// produced by two passes over 128-key tiles iterating over query tiles, dQ by
+// one pass over 128-query tiles iterating over key tiles.  No atomics: the
+// result is bitwise reproducible.
 #include "common.h"
 #include "kernels.h"
 
 namespace gk {
-
-template <int ROWS, int ROW_BYTES>
-struct RowTile {
-  static constexpr int NCH = ROW_BYTES / 16;
-  static constexpr int TOTAL = ROWS * NCH;
-  static constexpr int PER = (TOTAL + 255) / 256;
-  u32x4 reg[PER];
-  __device__ __forceinline__ void load(const char* __restrict__ base, long stride, int nvalid, int t) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = t + p * 256;
-      const int row = c / NCH, ch = c % NCH;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (c < TOTAL && row < nvalid) v = *(const u32x4*)(base + (long)row * stride + ch * 16);
-      reg[p] = v;
-    }
-  }
-  __device__ __forceinline__ void store(char* __restrict__ lds, int t) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = t + p * 256;
-      if (c < TOTAL) *(u32x4*)(lds + lds_off<ROW_BYTES>(c / NCH, (c % NCH) * 16)) = reg[p];
-    }
-  }
-};
 
 // Fragment of a row-major operand: EPL contiguous elements at K offset
 // s*KM + g*EPL of `row`.
@@ -106,8 +81,12 @@ __device__ __forceinline__ bool visible(int i, int j, int W, int Tn) {
 }
 
 // ------------------------------------------------------------------ forward
+// Work-group: 4 waves x 32 queries; key tiles of 64 (K rows and V^T columns)
+// arrive by direct-to-LDS loads one tile ahead.  Two work-groups fit per CU
+// (64 KB LDS, <= 256 registers per lane) so one work-group's softmax overlaps
+// the other's MFMAs.
 template <typename T, int DH>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
   constexpr int ES = sizeof(T);
   constexpr int BQ = 128, BKV = 64;
@@ -141,33 +120,36 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
   const int jend = min(Tn, i0 + BQ);
   const int nt = jend > jb0 ? (jend - jb0 + BKV - 1) / BKV : 0;
 
-  const char* kbase = qkv + (((long)b * Tn) * row3 + d + h * DH) * ES;
-  const char* vtbase = (const char*)a.vT + (((long)b * a.H + h) * DH) * (long)a.Tp * ES;
-  RowTile<BKV, KROW> lk;
-  RowTile<DH, VROW> lv;
+  RowDma<BKV, KROW, 4> lk;
+  RowDma<DH, VROW, 4> lv;
+  {
+    const char* kbase = qkv + (((long)b * Tn) * row3 + d + h * DH) * ES;
+    lk.init(kbase, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + KROW, wave, lane);
+    const char* vtbase = (const char*)a.vT + (((long)b * a.H + h) * DH) * (long)a.Tp * ES;
+    lv.init(vtbase, a.Tp * ES, (long)DH * a.Tp * ES, wave, lane);
+  }
 
   floatx16 acc[DB];
 #pragma unroll
   for (int x = 0; x < DB; ++x)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
-  float m = -1e30f, l = 0.f;
+  float m = -1e30f, l = 0.f;   // running max of raw scores, running sum (this lane's keys)
+  const float c = a.scale_log2;
 
   if (nt > 0) {
-    lk.load(kbase + (long)jb0 * row3 * ES, row3 * ES, Tn - jb0, t);
-    lv.load(vtbase + (long)jb0 * ES, (long)a.Tp * ES, DH, t);
-    lk.store(smem, t);
-    lv.store(smem + BKV * KROW, t);
+    lk.issue(smem, jb0 * (int)(row3 * ES), wave);
+    lv.issue(smem + BKV * KROW, jb0 * ES, wave);
   }
-  __syncthreads();
-
   for (int it = 0; it < nt; ++it) {
     const int j0 = jb0 + it * BKV;
     const int s = it & 1;
-    const bool more = it + 1 < nt;
-    if (more) {
-      lk.load(kbase + (long)(j0 + BKV) * row3 * ES, row3 * ES, Tn - j0 - BKV, t);
-      lv.load(vtbase + (long)(j0 + BKV) * ES, (long)a.Tp * ES, DH, t);
+    __builtin_amdgcn_s_waitcnt(0x0070);   // this tile's loads have landed
+    __syncthreads();                      // ... for every wave; stage s^1 is free
+    if (it + 1 < nt) {
+      char* nx = smem + (s ^ 1) * STAGE;
+      lk.issue(nx, (j0 + BKV) * (int)(row3 * ES), wave);
+      lv.issue(nx + BKV * KROW, (j0 + BKV) * ES, wave);
     }
     const char* ks = smem + s * STAGE;
     const char* vs = ks + BKV * KROW;
@@ -181,27 +163,29 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < KS; ++k) sc[jb] = MF::mma(row_frag<T, KROW>(ks, jb * 32 + l32, k, g), qf[k], sc[jb]);
       }
-      const bool need_mask = (j0 + BKV - 1 > iw0) || (iw0 + 31 - j0 >= W) || (j0 + BKV > Tn);
-      float mloc = -1e30f;
+      const bool need_mask = (j0 + BKV - 1 > iw0) || (iw0 + 31 - j0 >= W) || (j0 + BKV > Tn) || (iw0 + 31 >= Tn);
+      if (need_mask) {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!visible(i, j0 + jb * 32 + acc_row(r, g), W, Tn)) sc[jb][r] = -INFINITY;
+      }
+      float mloc = m;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sc[jb][r] * a.scale_log2;
-          if (need_mask && !visible(i, j0 + jb * 32 + acc_row(r, g), W, Tn)) x = -INFINITY;
-          sc[jb][r] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float mnew = fmaxf(m, mloc);
-      const float alpha = fast_exp2(m - mnew);
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[jb][r]);
+      const float mnew = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float alpha = fast_exp2((m - mnew) * c);
       m = mnew;
+      const float mc = mnew * c;
       float ps = 0.f;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sc[jb][r] - mnew);
+          const float p = fast_exp2(__builtin_fmaf(sc[jb][r], c, -mc));
           sc[jb][r] = p;
           ps += p;
         }
@@ -217,11 +201,6 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
         for (int x = 0; x < DB; ++x) acc[x] = MF::mma(perm_frag<T, VROW>(vs, x * 32 + l32, k, g), pf, acc[x]);
       }
     }
-    if (more) {
-      lk.store(smem + (s ^ 1) * STAGE, t);
-      lv.store(smem + (s ^ 1) * STAGE + BKV * KROW, t);
-    }
-    __syncthreads();
   }
 
   const float lt = l + __shfl_xor(l, 32, 64);
@@ -236,20 +215,36 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs a) {
         store4(orow + x * 32 + 8 * q + 4 * g, v);
       }
   }
-  if (g == 0 && i < a.Tp) a.lse2[((long)b * a.H + h) * a.Tp + i] = i < Tn ? m + fast_log2(lt) : 0.f;
+  // log-sum-exp of the scaled scores, base 2
+  if (g == 0 && i < a.Tp) a.lse2[((long)b * a.H + h) * a.Tp + i] = i < Tn ? m * c + fast_log2(lt) : 0.f;
 }
 
 // ------------------------------------------------------------------ backward: dK, dV
-template <typename T, int DH>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
+// Work-group: 4 waves x 32 keys (K and V fragments held in registers), looping
+// over query tiles of BQ that arrive by direct-to-LDS loads one tile ahead (Q
+// and dO rows, and their transposed copies for the dV / dK products); the
+// per-query lse and D values are 16-byte loads issued as a tile starts.
+// MODE 1 produces dV and MODE 2 dK: each pass is small enough for two or
+// three waves per SIMD, which on MI355X beats a single pass holding both
+// accumulators at one wave per SIMD, even though the scores are computed in
+// both passes.
+template <typename T, int DH, int BQ, int MODE>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
+  static_assert(MODE == 1 || MODE == 2, "MODE 1 = dV pass, MODE 2 = dK pass");
+  constexpr bool DO_DV = MODE == 1, DO_DK = MODE == 2;
   constexpr int ES = sizeof(T);
-  constexpr int BKV = 128, BQ = 32;
+  constexpr int BKV = 128;
+  constexpr int QB = BQ / 32;                 // 32-query blocks per tile
   constexpr int RROW = DH * ES, TROW = BQ * ES;
   constexpr int KS = DH / MF::KM;
   constexpr int PS = BQ / MF::KM;
   constexpr int DB = DH / 32;
-  constexpr int STAGE = 2 * BQ * RROW + 2 * DH * TROW + 2 * BQ * 4;
+  // stage layout: Q rows | dO rows (dK) | Q^T (dK) | dO^T (dV)
+  constexpr int OFF_DO = BQ * RROW;
+  constexpr int OFF_QT = OFF_DO + (DO_DK ? BQ * RROW : 0);
+  constexpr int OFF_DOT = OFF_QT + (DO_DK ? DH * TROW : 0);
+  constexpr int STAGE = OFF_DOT + (DO_DV ? DH * TROW : 0);
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
@@ -257,9 +252,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   const int Tn = a.T, W = a.window, d = a.d, Tp = a.Tp;
   const long row3 = 3L * d;
   const int j0 = kb * BKV, jw0 = j0 + wave * 32, j = jw0 + l32;
+  const float c = a.scale_log2;
 
   const char* qkv = (const char*)a.qkv;
-  typename MF::frag kf[KS], vf[KS];
+  typename MF::frag kf[KS], vf[DO_DK ? KS : 1];
   {
     const char* krow = qkv + (((long)b * Tn + j) * row3 + d + h * DH) * ES;
     const char* vrow = krow + (long)d * ES;
@@ -267,10 +263,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
     for (int s = 0; s < KS; ++s) {
       if (j < Tn) {
         kf[s] = *(const typename MF::frag*)(krow + (s * MF::KM + g * MF::EPL) * ES);
-        vf[s] = *(const typename MF::frag*)(vrow + (s * MF::KM + g * MF::EPL) * ES);
+        if constexpr (DO_DK) vf[s] = *(const typename MF::frag*)(vrow + (s * MF::KM + g * MF::EPL) * ES);
       } else {
         __builtin_memset(&kf[s], 0, sizeof(kf[s]));
-        __builtin_memset(&vf[s], 0, sizeof(vf[s]));
+        if constexpr (DO_DK) __builtin_memset(&vf[s], 0, sizeof(vf[s]));
       }
     }
   }
@@ -278,96 +274,97 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
   const int ib = j0;
   const int iend = min(Tn, j0 + BKV - 1 + W);
   const int nq = iend > ib ? (iend - ib + BQ - 1) / BQ : 0;
-
-  const char* qbase = qkv + (((long)b * Tn) * row3 + h * DH) * ES;
-  const char* dobase = (const char*)a.dO + (((long)b * Tn) * d + h * DH) * ES;
   const long hoff = ((long)b * a.H + h);
-  const char* qtbase = (const char*)a.qT + hoff * DH * Tp * ES;
-  const char* dotbase = (const char*)a.dOT + hoff * DH * Tp * ES;
-  const float* lseb = a.lse2 + hoff * Tp;
-  const float* Db = a.Dv + hoff * Tp;
 
-  RowTile<BQ, RROW> lq, ldo;
-  RowTile<DH, TROW> lqt, ldot;
-  float lse_r = 0.f, d_r = 0.f;   // thread t < BQ stages lse/D of query i0 + t
+  RowDma<BQ, RROW, 4> lq, ldo;
+  RowDma<DH, TROW, 4> lqt, ldot;
+  lq.init(qkv + (((long)b * Tn) * row3 + h * DH) * ES, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + RROW, wave,
+          lane);
+  if constexpr (DO_DK) {
+    ldo.init((const char*)a.dO + (((long)b * Tn) * d + h * DH) * ES, d * ES, (long)(Tn - 1) * d * ES + RROW, wave,
+             lane);
+    lqt.init((const char*)a.qT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
+  }
+  if constexpr (DO_DV) ldot.init((const char*)a.dOT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
+  // lse / D of the queries this lane's accumulator rows cover: i0 + 32qb + 8q + 4g + e
+  const float* lseb = a.lse2 + hoff * Tp + 4 * g;
+  const float* Db = a.Dv + hoff * Tp + 4 * g;
 
-  floatx16 dk[DB], dv[DB];
+  floatx16 dk[DO_DK ? DB : 1], dv[DO_DV ? DB : 1];
 #pragma unroll
   for (int x = 0; x < DB; ++x)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk[x][r] = dv[x][r] = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (DO_DK) dk[x][r] = 0.f;
+      if constexpr (DO_DV) dv[x][r] = 0.f;
+    }
 
-  auto load = [&](int i0) {
-    lq.load(qbase + (long)i0 * row3 * ES, row3 * ES, Tn - i0, t);
-    ldo.load(dobase + (long)i0 * d * ES, (long)d * ES, Tn - i0, t);
-    lqt.load(qtbase + (long)i0 * ES, (long)Tp * ES, DH, t);
-    ldot.load(dotbase + (long)i0 * ES, (long)Tp * ES, DH, t);
-    if (t < BQ) {
-      lse_r = i0 + t < Tp ? lseb[i0 + t] : 0.f;
-      d_r = i0 + t < Tp ? Db[i0 + t] : 0.f;
+  auto issue = [&](int i0, int stage) {
+    char* st = smem + stage * STAGE;
+    lq.issue(st, i0 * (int)(row3 * ES), wave);
+    if constexpr (DO_DK) {
+      ldo.issue(st + OFF_DO, i0 * d * ES, wave);
+      lqt.issue(st + OFF_QT, i0 * ES, wave);
     }
-  };
-  auto store = [&](char* st) {
-    lq.store(st, t);
-    ldo.store(st + BQ * RROW, t);
-    lqt.store(st + 2 * BQ * RROW, t);
-    ldot.store(st + 2 * BQ * RROW + DH * TROW, t);
-    float* f = (float*)(st + 2 * BQ * RROW + 2 * DH * TROW);
-    if (t < BQ) {
-      f[t] = lse_r;
-      f[BQ + t] = d_r;
-    }
+    if constexpr (DO_DV) ldot.issue(st + OFF_DOT, i0 * ES, wave);
   };
 
-  if (nq > 0) {
-    load(ib);
-    store(smem);
-  }
-  __syncthreads();
-
+  if (nq > 0) issue(ib, 0);
   for (int it = 0; it < nq; ++it) {
     const int i0 = ib + it * BQ;
     const int s = it & 1;
-    const bool more = it + 1 < nq;
-    if (more) load(i0 + BQ);
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();
+    floatx4 lse_c[QB][4], D_c[DO_DK ? QB : 1][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lse_c[qb][q] = *(const floatx4*)(lseb + i0 + 32 * qb + 8 * q);
+        if constexpr (DO_DK) D_c[qb][q] = *(const floatx4*)(Db + i0 + 32 * qb + 8 * q);
+      }
+    if (it + 1 < nq) issue(i0 + BQ, s ^ 1);
     const char* qs = smem + s * STAGE;
-    const char* dos = qs + BQ * RROW;
-    const char* qts = qs + 2 * BQ * RROW;
-    const char* dots = qts + DH * TROW;
-    const float* lses = (const float*)(dots + DH * TROW);
-    const float* Ds = lses + BQ;
     const bool skip = i0 + BQ - 1 < jw0 || i0 - (jw0 + 31) >= W || jw0 >= Tn || i0 >= Tn;
     if (!skip) {
-      floatx16 sc[1], dp[1];
+      floatx16 sc[QB], dp[DO_DK ? QB : 1];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[0][r] = dp[0][r] = 0.f;
+      for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        sc[0] = MF::mma(row_frag<T, RROW>(qs, l32, k, g), kf[k], sc[0]);
-        dp[0] = MF::mma(row_frag<T, RROW>(dos, l32, k, g), vf[k], dp[0]);
+        for (int r = 0; r < 16; ++r) {
+          sc[qb][r] = 0.f;
+          if constexpr (DO_DK) dp[qb][r] = 0.f;
+        }
       }
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          sc[qb] = MF::mma(row_frag<T, RROW>(qs, qb * 32 + l32, k, g), kf[k], sc[qb]);
+          if constexpr (DO_DK) dp[qb] = MF::mma(row_frag<T, RROW>(qs + OFF_DO, qb * 32 + l32, k, g), vf[k], dp[qb]);
+        }
       const bool need_mask = (i0 < jw0 + 31) || (i0 + BQ - 1 - jw0 >= W) || (i0 + BQ > Tn) || (jw0 + 31 >= Tn);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = acc_row(r, g);
-        const float p0 = fast_exp2(sc[0][r] * a.scale_log2 - lses[il]);
-        const float p = (!need_mask || visible(i0 + il, j, W, Tn)) ? p0 : 0.f;
-        sc[0][r] = p;
-        dp[0][r] = p * (dp[0][r] - Ds[il]);
-      }
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int il = qb * 32 + acc_row(r, g);
+          const float p0 = fast_exp2(__builtin_fmaf(sc[qb][r], c, -lse_c[qb][r >> 2][r & 3]));
+          const float p = (!need_mask || visible(i0 + il, j, W, Tn)) ? p0 : 0.f;
+          sc[qb][r] = p;
+          if constexpr (DO_DK) dp[qb][r] = p * (dp[qb][r] - D_c[qb][r >> 2][r & 3]);
+        }
 #pragma unroll
       for (int k = 0; k < PS; ++k) {
-        const typename MF::frag pf = acc_frag<T, 1>(sc, k);
-        const typename MF::frag sf = acc_frag<T, 1>(dp, k);
 #pragma unroll
         for (int x = 0; x < DB; ++x) {
-          dv[x] = MF::mma(perm_frag<T, TROW>(dots, x * 32 + l32, k, g), pf, dv[x]);
-          dk[x] = MF::mma(perm_frag<T, TROW>(qts, x * 32 + l32, k, g), sf, dk[x]);
+          if constexpr (DO_DV)
+            dv[x] = MF::mma(perm_frag<T, TROW>(qs + OFF_DOT, x * 32 + l32, k, g), acc_frag<T, QB>(sc, k), dv[x]);
+          if constexpr (DO_DK)
+            dk[x] = MF::mma(perm_frag<T, TROW>(qs + OFF_QT, x * 32 + l32, k, g), acc_frag<T, QB>(dp, k), dk[x]);
         }
       }
     }
-    if (more) store(smem + (s ^ 1) * STAGE);
-    __syncthreads();
   }
 
   if (j < Tn) {
@@ -376,21 +373,28 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(AttnArgs a) {
     for (int x = 0; x < DB; ++x)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int c = x * 32 + 8 * q + 4 * g;
-        floatx4 vk = {dk[x][4 * q], dk[x][4 * q + 1], dk[x][4 * q + 2], dk[x][4 * q + 3]};
-        floatx4 vv = {dv[x][4 * q], dv[x][4 * q + 1], dv[x][4 * q + 2], dv[x][4 * q + 3]};
-        store4(base + d + c, vk * a.scale);
-        store4(base + 2 * d + c, vv);
+        const int cc = x * 32 + 8 * q + 4 * g;
+        if constexpr (DO_DK) {
+          floatx4 vk = {dk[x][4 * q], dk[x][4 * q + 1], dk[x][4 * q + 2], dk[x][4 * q + 3]};
+          store4(base + d + cc, vk * a.scale);
+        }
+        if constexpr (DO_DV) {
+          floatx4 vv = {dv[x][4 * q], dv[x][4 * q + 1], dv[x][4 * q + 2], dv[x][4 * q + 3]};
+          store4(base + 2 * d + cc, vv);
+        }
       }
   }
 }
 
 // ------------------------------------------------------------------ backward: dQ
+// Work-group: 4 waves x 32 queries (Q and dO fragments in registers), looping
+// over key tiles of 32 (K and V rows plus K^T columns) that arrive by
+// direct-to-LDS loads one tile ahead.
 template <typename T, int DH>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
   constexpr int ES = sizeof(T);
-  constexpr int BQ = 128, BKV = 64;
+  constexpr int BQ = 128, BKV = 32;
   constexpr int RROW = DH * ES, TROW = BKV * ES;
   constexpr int KS = DH / MF::KM;
   constexpr int PS = BKV / MF::KM;
@@ -404,6 +408,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   const long row3 = 3L * d;
   const int i0 = qb * BQ, iw0 = i0 + wave * 32, i = iw0 + l32;
   const long hoff = ((long)b * a.H + h);
+  const float c = a.scale_log2;
 
   const char* qkv = (const char*)a.qkv;
   typename MF::frag qf[KS], df[KS];
@@ -428,11 +433,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
   const int jend = min(Tn, i0 + BQ);
   const int nt = jend > jb0 ? (jend - jb0 + BKV - 1) / BKV : 0;
 
-  const char* kbase = qkv + (((long)b * Tn) * row3 + d + h * DH) * ES;
-  const char* vbase = kbase + (long)d * ES;
-  const char* ktbase = (const char*)a.kT + hoff * DH * Tp * ES;
-  RowTile<BKV, RROW> lk, lv;
-  RowTile<DH, TROW> lkt;
+  RowDma<BKV, RROW, 4> lk, lv;
+  RowDma<DH, TROW, 4> lkt;
+  {
+    const char* kbase = qkv + (((long)b * Tn) * row3 + d + h * DH) * ES;
+    lk.init(kbase, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + RROW, wave, lane);
+    lv.init(kbase + (long)d * ES, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + RROW, wave, lane);
+    lkt.init((const char*)a.kT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
+  }
 
   floatx16 dq[DB];
 #pragma unroll
@@ -440,61 +448,46 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[x][r] = 0.f;
 
-  auto load = [&](int j0) {
-    lk.load(kbase + (long)j0 * row3 * ES, row3 * ES, Tn - j0, t);
-    lv.load(vbase + (long)j0 * row3 * ES, row3 * ES, Tn - j0, t);
-    lkt.load(ktbase + (long)j0 * ES, (long)Tp * ES, DH, t);
+  auto issue = [&](int j0, int stage) {
+    char* st = smem + stage * STAGE;
+    lk.issue(st, j0 * (int)(row3 * ES), wave);
+    lv.issue(st + BKV * RROW, j0 * (int)(row3 * ES), wave);
+    lkt.issue(st + 2 * BKV * RROW, j0 * ES, wave);
   };
-  auto store = [&](char* st) {
-    lk.store(st, t);
-    lv.store(st + BKV * RROW, t);
-    lkt.store(st + 2 * BKV * RROW, t);
-  };
-  if (nt > 0) {
-    load(jb0);
-    store(smem);
-  }
-  __syncthreads();
-
+  if (nt > 0) issue(jb0, 0);
   for (int it = 0; it < nt; ++it) {
     const int j0 = jb0 + it * BKV;
     const int s = it & 1;
-    const bool more = it + 1 < nt;
-    if (more) load(j0 + BKV);
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();
+    if (it + 1 < nt) issue(j0 + BKV, s ^ 1);
     const char* ks = smem + s * STAGE;
     const char* vs = ks + BKV * RROW;
     const char* kts = vs + BKV * RROW;
     const bool skip = j0 > iw0 + 31 || iw0 - (j0 + BKV - 1) >= W || iw0 >= Tn;
     if (!skip) {
-      floatx16 sc[2], dp[2];
+      floatx16 sc[1], dp[1];
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
+      for (int r = 0; r < 16; ++r) sc[0][r] = dp[0][r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[jb][r] = dp[jb][r] = 0.f;
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          sc[jb] = MF::mma(row_frag<T, RROW>(ks, jb * 32 + l32, k, g), qf[k], sc[jb]);
-          dp[jb] = MF::mma(row_frag<T, RROW>(vs, jb * 32 + l32, k, g), df[k], dp[jb]);
-        }
+      for (int k = 0; k < KS; ++k) {
+        sc[0] = MF::mma(row_frag<T, RROW>(ks, l32, k, g), qf[k], sc[0]);
+        dp[0] = MF::mma(row_frag<T, RROW>(vs, l32, k, g), df[k], dp[0]);
       }
       const bool need_mask = (j0 + BKV - 1 > iw0) || (iw0 + 31 - j0 >= W) || (j0 + BKV > Tn) || (iw0 + 31 >= Tn);
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p0 = fast_exp2(sc[jb][r] * a.scale_log2 - lse_i);
-          const float p = (!need_mask || visible(i, j0 + jb * 32 + acc_row(r, g), W, Tn)) ? p0 : 0.f;
-          dp[jb][r] = p * (dp[jb][r] - D_i);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const float p0 = fast_exp2(__builtin_fmaf(sc[0][r], c, -lse_i));
+        const float p = (!need_mask || visible(i, j0 + acc_row(r, g), W, Tn)) ? p0 : 0.f;
+        dp[0][r] = p * (dp[0][r] - D_i);
+      }
 #pragma unroll
       for (int k = 0; k < PS; ++k) {
-        const typename MF::frag sf = acc_frag<T, 2>(dp, k);
+        const typename MF::frag sf = acc_frag<T, 1>(dp, k);
 #pragma unroll
         for (int x = 0; x < DB; ++x) dq[x] = MF::mma(perm_frag<T, TROW>(kts, x * 32 + l32, k, g), sf, dq[x]);
       }
     }
-    if (more) store(smem + (s ^ 1) * STAGE);
-    __syncthreads();
   }
 
   if (i < Tn) {
@@ -518,10 +511,9 @@ static void fwd_t(const AttnArgs& a, hipStream_t st) {
 template <typename T, int DH>
 static void bwd_t(const AttnArgs& a, int part, hipStream_t st) {
   dim3 g((a.T + 127) / 128, a.H, a.B);
-  if (part == 0)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH>), g, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DH>), g, dim3(256), 0, st, a);
+  if (part == 0) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH, 32, 1>), g, dim3(256), 0, st, a);
+  else if (part == 1) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH, 32, 2>), g, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DH>), g, dim3(256), 0, st, a);
 }
 
 int attn_fwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st) {

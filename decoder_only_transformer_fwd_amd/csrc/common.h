@@ -109,6 +109,44 @@ __device__ __forceinline__ void lds_read(const char* base, int row, int byte, vo
   }
 }
 
+// Rows of a global matrix copied straight into a swizzled LDS tile by buffer
+// loads with the LDS bit (no registers).  One wave instruction writes 64
+// lanes x 16 bytes = RPI consecutive LDS rows of RB bytes; the lane owning
+// LDS slot p of row r fetches source chunk p ^ swz(r).  Source row r of the
+// tile starts at base + row_off + r * stride; bytes at or past `nbytes` from
+// base read as zero.
+// One wave instruction: 64 lanes x 16 bytes from the buffer into LDS at
+// lds + 16 * lane.  Bytes at or past the buffer's size read as zero.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+
+template <int ROWS, int RB, int NW>
+struct RowDma {
+  static constexpr int CPR = RB / 16;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int PER_WAVE = ROWS / (RPI * NW);
+  static_assert(ROWS % (RPI * NW) == 0, "tile rows must split evenly over the waves");
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff[PER_WAVE];
+  __device__ __forceinline__ void init(const void* base, int stride, long nbytes, int wave, int lane) {
+    if (nbytes > 0x7FFFFFF0L) nbytes = 0x7FFFFFF0L;
+    if (nbytes < 0) nbytes = 0;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)nbytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int r = (wave * PER_WAVE + i) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<RB>(r);
+      voff[i] = r * stride + c * 16;
+    }
+  }
+  __device__ __forceinline__ void issue(char* lds, int row_off, int wave) const {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      dma16(rsrc, lds + (wave * PER_WAVE + i) * RPI * RB, voff[i] + row_off);
+  }
+};
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

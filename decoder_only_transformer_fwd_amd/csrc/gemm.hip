@@ -24,6 +24,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <cstdio>
+
 namespace gk {
 
 constexpr uint32_t BUF_DWORD3 = 0x00020000u;   // raw buffer, 32-bit data format
@@ -125,8 +127,7 @@ struct DmaLoader {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int off = (k0 + kel[i] < kend) ? voff[i] + k0 * ES : (int)0x80000000;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(lds + (wave * RPW + i * RPI) * RB), 16, off, 0, 0, 0);
+      dma16(rsrc, lds + (wave * RPW + i * RPI) * RB, off);
     }
   }
 };
@@ -394,6 +395,13 @@ int tile_bm(int tile) { return TILES[tile].bm; }
 int tile_bn(int tile) { return TILES[tile].bn; }
 int tile_wn(int tile) { return TILES[tile].bn / TILES[tile].wgn; }
 bool tile_needs_kc(int tile) { return TILES[tile].ns > 2 || TILES[tile].rb != 128; }
+
+void gemm_kernel_label(int dtype, int layout, int epi, int tile, char* buf, int n) {
+  const TileCfg& c = TILES[tile];
+  snprintf(buf, n, "gemm_kernel<%s, %d, %d, %d, %d, %d, %d, %s, %s, %d>", dtype == DT_BF16 ? "bf16" : "float", c.bm,
+           c.bn, c.wgm, c.wgn, c.rb, c.ns, layout == LAYOUT_MN ? "false" : "true", layout == LAYOUT_KK ? "true" : "false",
+           epi);
+}
 
 template <typename TA, typename MF, int T, bool AK, bool BK_, int EPI, typename TC>
 static void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {

@@ -36,6 +36,9 @@ enum Tile {
   TILE_COUNT = 10,
 };
 bool tile_needs_kc(int tile);   // usable only when both operands are K-contiguous
+// Readable template signature of the kernel a product launches (as profilers
+// print it, without the MFMA-traits and output-type arguments).
+void gemm_kernel_label(int dtype, int layout, int epi, int tile, char* buf, int n);
 int tile_bm(int tile);
 int tile_bn(int tile);
 int tile_wn(int tile);   // output columns owned by one wave
@@ -103,7 +106,7 @@ struct AttnArgs {
   float scale;       // 1 / sqrt(Dh)
 };
 int attn_fwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st);
-// part 0: dK/dV kernel (one work-group per 128-key tile); part 1: dQ kernel.
+// part 0: dV, part 1: dK (one work-group per 128-key tile); part 2: dQ (per 128-query tile).
 int attn_bwd(int dtype, int Dh, const AttnArgs& a, int part, hipStream_t st);
 
 }  // namespace gk

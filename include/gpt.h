@@ -143,8 +143,8 @@ int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const vo
  * HBM bytes (work_kind 1: each input read once, each output written once). */
 int gpt_profile_enable(gpt_model* model, int on);
 int gpt_profile_sites(gpt_model* model, int* n_sites);
-int gpt_profile_get(gpt_model* model, int index, char* name, int name_len, int64_t* launches,
-                    double* total_ms, double* work, int* work_kind);
+int gpt_profile_get(gpt_model* model, int index, char* name, int name_len, char* kernel, int kernel_len,
+                    int64_t* launches, double* total_ms, double* work, int* work_kind);
 
 /* Static description of a return code. */
 const char* gpt_strerror(int code);
