@@ -124,10 +124,11 @@ struct GemmPlan {
 
 
 // Tile and split-K choice, set from measurements of this kernel on MI355X at
-// the step's shapes.  Small-N products are limited by L2->CU bandwidth less
-// than by latency and do best with 128x128 tiles (two work-groups per CU);
-// very wide products use the 8-wave 256x256 tile.  Weight gradients (K = B*T)
-// are split along K until about two waves of work-groups exist.
+// the step's shapes: 128x128 tiles (two work-groups per CU) except for very
+// wide forward products (8-wave 256x256).  Weight gradients (K = B*T, few
+// output tiles) are split along K by a cost model: waves of work-groups
+// (512 resident at two per CU) times K steps per split, plus the fp32
+// partial-sum reduction at ~5 TB/s.
 GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   GemmPlan g{TILE_64x64, 1, K};
   const int bk = dtype == DT_F32 ? 32 : 64;
@@ -135,22 +136,29 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
     g.tile = (long)M * N >= 256L * 128 * 128 ? TILE_128x128 : TILE_64x64;
   } else if (layout == LAYOUT_KK) {
     g.tile = N >= 8192 ? TILE_256x256_W8 : TILE_128x128;
-  } else if (layout == LAYOUT_KN) {
-    g.tile = N >= 6144 ? TILE_256x256 : TILE_128x128;
   } else {
-    g.tile = (long)M * N >= 4L * 1024 * 1024 ? TILE_256x256 : TILE_128x128;
+    g.tile = TILE_128x128;
   }
   if (layout == LAYOUT_MN) {
     const long tiles = (long)((M + tile_bm(g.tile) - 1) / tile_bm(g.tile)) * ((N + tile_bn(g.tile) - 1) / tile_bn(g.tile));
-    int splits = (int)((512 + tiles - 1) / tiles);
-    if (splits > 8) splits = 8;
-    const int maxs = K / (4 * bk);
-    if (splits > maxs) splits = maxs;
-    if (splits > 1) {
-      int ks = (K + splits - 1) / splits;
+    const long slots = dtype == DT_F32 ? 256 : 512;
+    const double t_step = dtype == DT_F32 ? 4e-6 : 1.34e-6;   // one K step of one tile, seconds
+    double best = 1e300;
+    const int cand[6] = {1, 2, 3, 4, 6, 8};
+    for (int c = 0; c < 6; ++c) {
+      const int sp = cand[c];
+      int ks = (K + sp - 1) / sp;
       ks = (ks + bk - 1) / bk * bk;
-      g.splits = (K + ks - 1) / ks;
-      g.k_split = ks;
+      const int real = (K + ks - 1) / ks;
+      if (real != sp && sp > 1) continue;
+      const long waves = (tiles * sp + slots - 1) / slots;
+      double t = (double)waves * ((ks + bk - 1) / bk) * t_step;
+      if (sp > 1) t += (sp + 1.0) * M * (double)N * 4.0 / 5e12;
+      if (t < best) {
+        best = t;
+        g.splits = sp;
+        g.k_split = ks;
+      }
     }
   }
   if (g.splits == 1) g.k_split = K;

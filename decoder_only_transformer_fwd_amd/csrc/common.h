@@ -147,6 +147,14 @@ struct RowDma {
   }
 };
 
+// Transposing LDS read (16-bit elements).  Within each group of 16 lanes,
+// lane 4a+b receives as its element e the b-th 16-bit value of the 8 bytes
+// addressed by lane 4e+a of the same group (measured on gfx950).
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ shortx4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)p);
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -8,15 +8,17 @@
 //
 // Structure: WGM x WGN waves (4 or 8) per work-group, each owning a
 // (BM/WGM) x (BN/WGN) block of 32x32 MFMA tiles.  K advances in steps of 128
-// bytes per row (64 bf16, 32 fp32).  A K-contiguous operand tile travels
-// straight from global memory into LDS (buffer loads with the LDS bit, no
-// registers); an M/N-contiguous one is loaded into registers, transposed in
-// 16x16-byte blocks and written to LDS, so every MFMA fragment is one
-// contiguous LDS read.  LDS is double-buffered with one barrier per K step;
+// bytes per row (64 bf16, 32 fp32).  Operand tiles travel straight from global
+// memory into LDS (buffer loads with the LDS bit, no registers): a
+// K-contiguous tile is read back as one contiguous 16-byte fragment per lane,
+// a 16-bit M/N-contiguous tile with two transposing LDS reads per fragment.
+// 32-bit M/N-contiguous operands (fp32 workloads) are instead transposed in
+// registers on their way into LDS.  LDS is double-buffered with one barrier per K step;
 // within a step the fragment reads for sub-step kk+1 are issued before the
 // MFMAs of sub-step kk.  The MFMA takes the B tile as its first operand, so
 // each lane's accumulators hold one output row and 4-wide runs of columns:
-// epilogue stores are vectorised and row reductions stay in-lane.
+// row reductions (the cross-entropy statistics) stay in-lane, and the other
+// epilogues stage 32-row blocks through LDS to load and store whole rows.
 //
 // Work-group order is remapped so that the tiles one XCD (32 CUs sharing an
 // L2) runs are neighbours, grouped along M so a band of A rows is reused from
@@ -132,6 +134,69 @@ struct DmaLoader {
   }
 };
 
+// M/N-contiguous 16-bit operand ([K][rows]) copied row-for-row into LDS by
+// direct-to-LDS loads: the tile holds BK K-rows of ROWS*2 bytes, 16-byte
+// chunk c of K-row k at slot c ^ swz_tr(k).  Each stage re-bases the buffer
+// at K-row k0 so offsets stay small, and K-rows at or past the end of the K
+// range fall outside the buffer and arrive as zeros.  MFMA fragments are then
+// assembled with transposing LDS reads (tr_frag).
+template <int RBT>
+__device__ __forceinline__ int swz_tr(int k) {
+  return (4 * (k & 3)) & (RBT / 16 - 1);
+}
+
+template <int ES, int ROWS, int NWAVES, int BK>
+struct DmaTrLoader {
+  static constexpr int RBT = ROWS * ES;            // bytes per K-row in LDS
+  static constexpr int TOTAL = BK * RBT / 1024;    // wave instructions per stage
+  static constexpr int PER_WAVE = TOTAL / NWAVES;
+  static_assert(TOTAL % NWAVES == 0 && RBT <= 1024 && 1024 % RBT == 0, "tile shape");
+  const char* base;     // operand + r0 columns
+  long ldb;             // leading dimension in bytes
+  long col_bytes_left;  // bytes of a K-row from column r0 to the end of the row
+  int voff[PER_WAVE];   // offset of this lane's chunk relative to K-row k0
+  int krow[PER_WAVE];
+
+  __device__ __forceinline__ void init(const char* op, long ld, int r0, int wave, int lane) {
+    base = op + (long)r0 * ES;
+    ldb = ld * ES;
+    col_bytes_left = ldb - (long)r0 * ES;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int pos = (wave * PER_WAVE + i) * 1024 + lane * 16;
+      const int k = pos / RBT, p = (pos % RBT) / 16;
+      krow[i] = k;
+      voff[i] = (int)(k * ldb) + ((p ^ swz_tr<RBT>(k)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(char* lds, int k0, int kend, int wave) const {
+    long bytes = (long)(kend - k0 - 1) * ldb + col_bytes_left;
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7FFFFFF0L) bytes = 0x7FFFFFF0L;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (long)k0 * ldb), 0, (int)bytes, BUF_DWORD3);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      dma16(r, lds + (wave * PER_WAVE + i) * 1024, k0 + krow[i] < kend ? voff[i] : (int)0x80000000);
+  }
+};
+
+// Fragment of 32 rows (M or N indices rb..rb+31) x 16 K values from a
+// [K][rows] tile: lane (row rb + l%32, group g) gets K-rows kbase + 8g + e,
+// e = 0..7 -- the same K order as a K-contiguous fragment.
+template <int RBT>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int rb, int kbase, int lane) {
+  const int s = lane & 15, q = (lane >> 4) & 1, g = lane >> 5;
+  const int byte = (rb + 16 * q + 4 * (s & 3)) * 2;
+  shortx4 v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = kbase + 8 * g + 4 * h + (s >> 2);
+    v[h] = lds_read_tr16(tile + k * RBT + (((byte >> 4) ^ swz_tr<RBT>(k)) << 4) + (byte & 15));
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -159,8 +224,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
   constexpr int NW = WGM * WGN;
   constexpr int ES = sizeof(TA);
   constexpr int BK = RB / ES;         // K elements per step
-  static_assert(NS == 2 || (A_KC && B_KC), "deeper pipelines need both operands on the direct-to-LDS path");
-  static_assert(RB == 128 || (A_KC && B_KC), "register-transposed operands use 128-byte rows");
+  // 16-bit M/N-contiguous operands take the direct-to-LDS path with
+  // transposing fragment reads; 32-bit ones are transposed in registers.
+  constexpr bool A_TR = !A_KC && ES == 2, B_TR = !B_KC && ES == 2;
+  constexpr bool A_REG = !A_KC && !A_TR, B_REG = !B_KC && !B_TR;
+  static_assert(NS == 2 || (!A_REG && !B_REG), "deeper pipelines need both operands on the direct-to-LDS path");
+  static_assert(RB == 128 || (A_KC && B_KC), "transposed operands use 128-byte K steps");
   constexpr int KM = MF::KM;
   constexpr int EPL = MF::EPL;
   constexpr int FB = EPL * ES;         // fragment bytes per lane
@@ -189,10 +258,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
   TransLoader<ES, BN, THREADS> lb;
   DmaLoader<ES, BM, NW, RB> da;
   DmaLoader<ES, BN, NW, RB> db;
+  DmaTrLoader<ES, BM, NW, BK> ta;
+  DmaTrLoader<ES, BN, NW, BK> tb;
   const char* Ab = (const char*)p.A;
   const char* Bb = (const char*)p.B;
   if constexpr (A_KC) da.init(Ab, p.lda, m0, p.M, wave, lane);
   if constexpr (B_KC) db.init(Bb, p.ldb, n0, p.N, wave, lane);
+  if constexpr (A_TR) ta.init(Ab, p.lda, m0, wave, lane);
+  if constexpr (B_TR) tb.init(Bb, p.ldb, n0, wave, lane);
 
   floatx16 acc[MB][NB];
 #pragma unroll
@@ -205,14 +278,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
   auto fetch = [&](int k0, int stage) {
     char* st = smem + stage * STAGE;
     if constexpr (A_KC) da.issue(st, k0, kend, wave);
+    else if constexpr (A_TR) ta.issue(st, k0, kend, wave);
     else la.load(Ab, p.lda, m0, p.M, k0, kend, t);
     if constexpr (B_KC) db.issue(st + BM * RB, k0, kend, wave);
+    else if constexpr (B_TR) tb.issue(st + BM * RB, k0, kend, wave);
     else lb.load(Bb, p.ldb, n0, p.N, k0, kend, t);
   };
   auto commit = [&](int stage) {   // register-staged operands into LDS
     char* st = smem + stage * STAGE;
-    if constexpr (!A_KC) la.store(st, t);
-    if constexpr (!B_KC) lb.store(st + BM * RB, t);
+    if constexpr (A_REG) la.store(st, t);
+    if constexpr (B_REG) lb.store(st + BM * RB, t);
+  };
+  // fragment of 32 A rows / B columns at K sub-step kk
+  auto frag_a = [&](const char* a_s, int i, int kk, typename MF::frag* out) {
+    if constexpr (A_TR) *out = tr_frag<BM * ES>(a_s, wm * WM + i * 32, kk * KM, lane);
+    else lds_read<RB, FB>(a_s, wm * WM + i * 32 + l32, (kk * KM + g * EPL) * ES, out);
+  };
+  auto frag_b = [&](const char* b_s, int j, int kk, typename MF::frag* out) {
+    if constexpr (B_TR) *out = tr_frag<BN * ES>(b_s, wn * WN + j * 32, kk * KM, lane);
+    else lds_read<RB, FB>(b_s, wn * WN + j * 32 + l32, (kk * KM + g * EPL) * ES, out);
   };
   constexpr int KK = BK / KM;
   auto compute = [&](int stage) {
@@ -220,20 +304,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
     const char* b_s = a_s + BM * RB;
     typename MF::frag af[2][MB], bfr[2][NB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) lds_read<RB, FB>(a_s, wm * WM + i * 32 + l32, (g * EPL) * ES, &af[0][i]);
+    for (int i = 0; i < MB; ++i) frag_a(a_s, i, 0, &af[0][i]);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) lds_read<RB, FB>(b_s, wn * WN + j * 32 + l32, (g * EPL) * ES, &bfr[0][j]);
+    for (int j = 0; j < NB; ++j) frag_b(b_s, j, 0, &bfr[0][j]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int cur = kk & 1;
       // fragment reads for the next sub-step go out before this sub-step's
       // MFMAs (the fences keep the scheduler from sinking them to their uses)
       if (kk + 1 < KK) {
-        const int kb = ((kk + 1) * KM + g * EPL) * ES;
 #pragma unroll
-        for (int i = 0; i < MB; ++i) lds_read<RB, FB>(a_s, wm * WM + i * 32 + l32, kb, &af[cur ^ 1][i]);
+        for (int i = 0; i < MB; ++i) frag_a(a_s, i, kk + 1, &af[cur ^ 1][i]);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) lds_read<RB, FB>(b_s, wn * WN + j * 32 + l32, kb, &bfr[cur ^ 1][j]);
+        for (int j = 0; j < NB; ++j) frag_b(b_s, j, kk + 1, &bfr[cur ^ 1][j]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -266,7 +349,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
     // NS stages, all by direct-to-LDS loads: NS-1 steps are in flight.  Every
     // step issues its loads (past the K range they fetch zeros), so a fixed
     // vmcnt threshold waits for exactly the stage about to be consumed.
-    constexpr int LPS = DmaLoader<ES, BM, NW, RB>::PER_WAVE + DmaLoader<ES, BN, NW, RB>::PER_WAVE;
+    constexpr int LPS = (A_KC ? DmaLoader<ES, BM, NW, RB>::PER_WAVE : DmaTrLoader<ES, BM, NW, BK>::PER_WAVE) +
+                        (B_KC ? DmaLoader<ES, BN, NW, RB>::PER_WAVE : DmaTrLoader<ES, BN, NW, BK>::PER_WAVE);
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st) fetch(kbeg + st * BK, st);
     for (int kt = 0; kt < nk; ++kt) {
@@ -280,11 +364,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
 
   // ------------------------------------------------------------ epilogue
   const float alpha = p.alpha;
+  if constexpr (EPI == EPI_XENT_FWD) {
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = m0 + wm * WM + i * 32 + l32;
-    const bool mok = m < p.M;
-    if constexpr (EPI == EPI_XENT_FWD) {
+    for (int i = 0; i < MB; ++i) {
+      const int m = m0 + wm * WM + i * 32 + l32;
+      const bool mok = m < p.M;
       // per-row partial (max, sum of exp) over this wave's WN columns
       const int ncol0 = n0 + wn * WN;
       float mx = -INFINITY;
@@ -314,16 +398,39 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
         p.part[((long)m * p.nblk + blk) * 2 + 0] = mx;
         p.part[((long)m * p.nblk + blk) * 2 + 1] = se;
       }
-      continue;
     }
+  } else {
+    // Each wave stages its 32-row blocks of fp32 results through its own LDS
+    // region and reads them back as whole rows, so that every global load and
+    // store of the epilogue covers contiguous row segments (64 consecutive
+    // columns per 16 lanes).
+    constexpr int RBY = WN * 4;              // bytes per staged row
+    constexpr int LPR = WN / 4;              // lanes per staged row (16 bytes each)
+    constexpr int RPS = 64 / LPR;            // rows per read step
+    static_assert(NW * 32 * RBY <= NS * STAGE, "epilogue staging must fit in the operand stages");
+    char* region = smem + wave * 32 * RBY;
+    __syncthreads();   // every wave is done with the operand stages
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int i = 0; i < MB; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * g;
-        if (!mok || n >= p.N) continue;
-        floatx4 v = {acc[i][j][4 * q] * alpha, acc[i][j][4 * q + 1] * alpha, acc[i][j][4 * q + 2] * alpha,
-                     acc[i][j][4 * q + 3] * alpha};
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = j * 32 + 8 * q + 4 * g;
+          floatx4 v = {acc[i][j][4 * q] * alpha, acc[i][j][4 * q + 1] * alpha, acc[i][j][4 * q + 2] * alpha,
+                       acc[i][j][4 * q + 3] * alpha};
+          *(floatx4*)(region + lds_off<RBY>(l32, col * 4)) = v;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int st = 0; st < 32 / RPS; ++st) {
+        const int r = st * RPS + lane / LPR;
+        const int c4 = lane % LPR;
+        const floatx4 v = *(const floatx4*)(region + lds_off<RBY>(r, c4 * 16));
+        const int m = m0 + wm * WM + i * 32 + r;
+        const int n = n0 + wn * WN + c4 * 4;
+        if (m >= p.M || n >= p.N) continue;
         const long off = (long)m * p.ldc + n;
         if constexpr (EPI == EPI_STORE) {
           store4((TC*)p.C + off, v);
@@ -334,31 +441,33 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
           store4(c, load4(c) + v);
         } else if constexpr (EPI == EPI_RELU2) {
           store4((TC*)p.C + off, v);
-          floatx4 r;
+          floatx4 rr;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float x = fmaxf(v[e], 0.f);
-            r[e] = x * x;
+            rr[e] = x * x;
           }
-          store4((TC*)p.C2 + off, r);
+          store4((TC*)p.C2 + off, rr);
         } else if constexpr (EPI == EPI_DRELU2) {
           const floatx4 u = load4((const TC*)p.aux + off);
-          floatx4 r;
+          floatx4 rr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = v[e] * 2.f * fmaxf(u[e], 0.f);
-          store4((TC*)p.C + off, r);
+          for (int e = 0; e < 4; ++e) rr[e] = v[e] * 2.f * fmaxf(u[e], 0.f);
+          store4((TC*)p.C + off, rr);
         } else if constexpr (EPI == EPI_XENT_BWD) {
           const float L2E = 1.4426950408889634f;
           const float lse = p.auxf[m];
           const int y = ((const int*)p.aux)[m];
-          floatx4 r;
+          floatx4 rr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = (fast_exp2((v[e] - lse) * L2E) - (n + e == y ? 1.f : 0.f)) * p.beta;
-          store4((TC*)p.C + off, r);
+          for (int e = 0; e < 4; ++e) rr[e] = (fast_exp2((v[e] - lse) * L2E) - (n + e == y ? 1.f : 0.f)) * p.beta;
+          store4((TC*)p.C + off, rr);
         } else if constexpr (EPI == EPI_PARTIAL) {
           store4(p.part + (long)blockIdx.z * p.M * p.N + (long)m * p.N + n, v);
         }
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // staging reads done before the region is rewritten
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
