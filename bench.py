@@ -69,9 +69,6 @@ def main() -> int:
     from decoder_only_transformer_fwd_amd import metrics as Mx
 
     s = gi.preset(args.config)
-    if s.precision == "fp8":
-        log("the fp8 workload is not built yet")
-        return 2
     log(f"bench: {s}")
     W8 = gi.make_weights(s)
     X, Y = gi.make_tokens(s)
@@ -118,7 +115,9 @@ def main() -> int:
     avg_s = dom["total_ms"] / dom["launches"] * 1e-3
     work_per_launch = dom["work"] / dom["launches"]
     if dom["work_kind"] == "flops":
-        kpeak = Mx.PEAK_FP32_MFMA if s.precision == "fp32" else Mx.PEAK_BF16
+        # a product is priced at the MFMA peak of its own operand type
+        kpeak = (Mx.PEAK_FP32_MFMA if s.precision == "fp32" else
+                 Mx.PEAK_FP8 if "fp8" in dom["kernel"] else Mx.PEAK_BF16)
         roof = {"bound": "mfma", "achieved": work_per_launch / avg_s / 1e12, "peak": kpeak / 1e12,
                 "unit": "TFLOP/s"}
     else:
@@ -135,6 +134,14 @@ def main() -> int:
             log(f"  {k['total_ms'] / args.steps:9.3f} ms/step {k['launches'] // args.steps:5d}/step "
                 f"avg {k['total_ms'] / k['launches'] * 1e3:9.1f} us  {k['kernel']}  [{', '.join(k['sites'])}]")
 
+    extra = {}
+    if s.precision == "fp8":
+        f8 = [x for x in sites if "fp8" in x["kernel"] and x["work_kind"] == "flops"]
+        f8_ms = sum(x["total_ms"] for x in f8)
+        f8_rate = sum(x["work"] for x in f8) / (f8_ms * 1e-3) if f8_ms > 0 else 0.0
+        extra["fp8_gemm"] = {"tflops": f8_rate / 1e12, "frac_of_fp8_peak": f8_rate / Mx.PEAK_FP8,
+                             "share_of_step": f8_ms / total_site_ms}
+    dtype = {"fp32": "f32", "bf16": "bf16", "fp8": "fp8+bf16"}[s.precision]
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -146,17 +153,19 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if s.precision == "fp32" else "bf16",
+        "dtype": dtype,
         "data": "synthetic (seeded N(0,0.02) weights, seeded token ids)",
         "config": {"workload": s.name, "depth": s.depth, "d_model": s.d_model, "n_head": s.n_head,
                    "head_dim": s.head_dim, "mlp_hidden": s.mlp_hidden, "vocab": s.vocab,
                    "seq_len": s.seq_len, "batch": s.batch, "tokens_per_step": s.bt,
-                   "window": s.window, "window_pattern": s.window_pattern, "token_dist": s.token_dist},
+                   "window": s.window, "window_pattern": s.window_pattern, "token_dist": s.token_dist,
+                   "precision": s.precision},
         "mfu": mfu,
         "mfu_peak_tflops": peak / 1e12,
         "model_flops_per_token": Mx.flops_per_token(s),
         "loss": loss,
         "roofline": roof,
+        **extra,
     }
     if not args.no_cpu_baseline:
         sess.close()

@@ -20,8 +20,8 @@ GPT_OK, GPT_EINVAL, GPT_ENULL, GPT_ETOKEN, GPT_EHIP, GPT_ENONFINITE, GPT_ESPACE,
 GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 
 EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_destroy",
-            "gpt_debug_tensor", "gpt_gemm", "gpt_profile_enable", "gpt_profile_sites", "gpt_profile_get",
-            "gpt_strerror", "gpt_last_error"]
+            "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
+            "gpt_profile_sites", "gpt_profile_get", "gpt_strerror", "gpt_last_error"]
 
 
 class gpt_config(ctypes.Structure):
@@ -60,6 +60,8 @@ def _load():
     lib.gpt_debug_tensor.argtypes = [P, I, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I64),
                                      ctypes.POINTER(I)]
     lib.gpt_gemm.argtypes = [I, I, I, I, I, P, P, P, P, I, I, P]
+    lib.gpt_fp8_quantize.argtypes = [I, P, I, I, P, P, P, P, P]
+    lib.gpt_gemm_fp8.argtypes = [I, I, I, I, P, P, P, P, P, P, I, P]
     D = ctypes.c_double
     lib.gpt_profile_enable.argtypes = [P, I]
     lib.gpt_profile_sites.argtypes = [P, ctypes.POINTER(I)]
@@ -70,7 +72,8 @@ def _load():
     lib.gpt_last_error.argtypes = []
     lib.gpt_last_error.restype = ctypes.c_char_p
     for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step",
-                 "gpt_debug_tensor", "gpt_gemm", "gpt_profile_enable", "gpt_profile_sites", "gpt_profile_get"):
+                 "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
+                 "gpt_profile_sites", "gpt_profile_get"):
         getattr(lib, name).restype = I
     return lib
 
@@ -161,6 +164,17 @@ def gpt_gemm(dtype: int, layout: int, M: int, N: int, K: int, A: int, B: int, C:
              workspace: int = 0, splits: int = 1, tile: int = -1, stream: int = 0) -> None:
     _check(_lib.gpt_gemm(dtype, layout, M, N, K, A, B, C, workspace or None, splits, tile, stream or None),
            "gpt_gemm")
+
+
+def gpt_fp8_quantize(fmt: int, x: int, rows: int, cols: int, amax: int, scale: int, q: int, qT: int = 0,
+                     stream: int = 0) -> None:
+    _check(_lib.gpt_fp8_quantize(fmt, x, rows, cols, amax, scale, q, qT or None, stream or None), "gpt_fp8_quantize")
+
+
+def gpt_gemm_fp8(fmt_a: int, M: int, N: int, K: int, A: int, B: int, scale_a: int, scale_b: int, C: int,
+                 workspace: int = 0, splits: int = 1, stream: int = 0) -> None:
+    _check(_lib.gpt_gemm_fp8(fmt_a, M, N, K, A, B, scale_a, scale_b, C, workspace or None, splits, stream or None),
+           "gpt_gemm_fp8")
 
 
 def gpt_profile_enable(model: int, on: bool) -> None:

@@ -36,14 +36,16 @@ size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 
 struct Shape {
   int L, d, H, Dh, F, V, T, B, BT, Tp, dtype, es;
+  bool fp8;   // linear layers (QKV, O, W1, W2) in fp8; everything else as bf16
   float eps, base;
   std::vector<int> win;   // keys visible per layer
 };
 
 int check_config(const gpt_config* c, Shape& s) {
   if (!c) return fail(GPT_ENULL, "cfg is NULL");
-  if (c->precision == GPT_FP8) return fail(GPT_EINVAL, "GPT_FP8 is not supported by this build");
-  if (c->precision != GPT_FP32 && c->precision != GPT_BF16) return fail(GPT_EINVAL, "unknown precision");
+  if (c->precision != GPT_FP32 && c->precision != GPT_BF16 && c->precision != GPT_FP8)
+    return fail(GPT_EINVAL, "unknown precision");
+  s.fp8 = c->precision == GPT_FP8;
   s.dtype = c->precision == GPT_FP32 ? DT_F32 : DT_BF16;
   s.es = s.dtype == DT_F32 ? 4 : 2;
   s.L = c->depth; s.d = c->d_model; s.H = c->n_head; s.Dh = c->head_dim; s.F = c->mlp_hidden;
@@ -60,6 +62,7 @@ int check_config(const gpt_config* c, Shape& s) {
   if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(GPT_EINVAL, "bad norm_eps or rope_base");
   s.BT = s.B * s.T;
   s.Tp = (s.T + 63) / 64 * 64;
+  if (s.fp8 && s.BT % 64) return fail(GPT_EINVAL, "GPT_FP8 needs batch * seq_len to be a multiple of 64");
   const char* pat = c->window_pattern;
   size_t plen = strnlen(pat, sizeof(c->window_pattern));
   if (plen == 0 || plen == sizeof(c->window_pattern)) return fail(GPT_EINVAL, "window_pattern must be 1..7 chars");
@@ -131,18 +134,22 @@ struct GemmPlan {
 // partial-sum reduction at ~5 TB/s.
 GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   GemmPlan g{TILE_64x64, 1, K};
-  const int bk = dtype == DT_F32 ? 32 : 64;
-  if (dtype == DT_F32) {
+  const bool f8 = dtype == DT_FP8_A4B4 || dtype == DT_FP8_A5B4;
+  const int bk = dtype == DT_F32 ? 32 : f8 ? 128 : 64;
+  if (f8) {
+    g.tile = TILE_128x128;
+  } else if (dtype == DT_F32) {
     g.tile = (long)M * N >= 256L * 128 * 128 ? TILE_128x128 : TILE_64x64;
   } else if (layout == LAYOUT_KK) {
     g.tile = N >= 8192 ? TILE_256x256_W8 : TILE_128x128;
   } else {
     g.tile = TILE_128x128;
   }
-  if (layout == LAYOUT_MN) {
+  // fp8 weight gradients are K-contiguous products with K = B*T
+  if (layout == LAYOUT_MN || (f8 && K >= 4096)) {
     const long tiles = (long)((M + tile_bm(g.tile) - 1) / tile_bm(g.tile)) * ((N + tile_bn(g.tile) - 1) / tile_bn(g.tile));
     const long slots = dtype == DT_F32 ? 256 : 512;
-    const double t_step = dtype == DT_F32 ? 4e-6 : 1.34e-6;   // one K step of one tile, seconds
+    const double t_step = dtype == DT_F32 ? 4e-6 : f8 ? 1.5e-6 : 1.34e-6;   // one K step of one tile, seconds
     double best = 1e300;
     const int cand[6] = {1, 2, 3, 4, 6, 8};
     for (int c = 0; c < 6; ++c) {
@@ -178,11 +185,16 @@ struct gpt_model {
   // workspace offsets (bytes)
   struct Layer {
     size_t n1, rstd1, qkv, rqk, qT, kT, vT, o, lse2, n2, rstd2, u, g;
+    // fp8: transposed activation codes kept for the weight gradients, and the
+    // step's weight codes (row-major and transposed) for QKV, O, W1, W2
+    size_t n1T, oT, n2T, gT, wq[4], wqT[4];
   };
   std::vector<Layer> lay;
   size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
       cosb, sinb, keys, total;
   size_t splitk_floats;
+  size_t q8row, q8T, amax, scales;   // fp8: transient codes, per-tensor amax / scale slots
+  int n_slots;
   int xent_tile, xent_nblk;
   // optional per-launch-site timing with HIP events on the step's stream
   struct Site {
@@ -275,6 +287,37 @@ int build_layout(gpt_model& m) {
   consider(LAYOUT_MN, s.d, s.d, s.BT);
   consider(LAYOUT_KN, s.BT, s.d, 3 * s.d);
   consider(LAYOUT_MN, 3 * s.d, s.d, s.BT);
+  if (s.fp8) {
+    for (int dty : {DT_FP8_A4B4, DT_FP8_A5B4}) {
+      for (int K : {s.d, s.F, 3 * s.d}) {
+        GemmPlan g = plan_gemm(dty, LAYOUT_KK, s.BT, s.d, K);
+        if (g.splits > 1) need = std::max(need, (size_t)g.splits * s.BT * s.d);
+      }
+      const int MN[4][2] = {{3 * s.d, s.d}, {s.d, s.d}, {s.F, s.d}, {s.d, s.F}};
+      for (auto& mn : MN) {
+        GemmPlan g = plan_gemm(dty, LAYOUT_KK, mn[0], mn[1], s.BT);
+        if (g.splits > 1) need = std::max(need, (size_t)g.splits * mn[0] * mn[1]);
+      }
+    }
+    const size_t wide = (size_t)std::max(s.F, 3 * s.d);
+    for (int l = 0; l < s.L; ++l) {
+      auto& L = m.lay[l];
+      L.n1T = take(BT * s.d);
+      L.oT = take(BT * s.d);
+      L.n2T = take(BT * s.d);
+      L.gT = take(BT * s.F);
+      const size_t wsz[4] = {(size_t)3 * s.d * s.d, (size_t)s.d * s.d, (size_t)s.F * s.d, (size_t)s.d * s.F};
+      for (int k = 0; k < 4; ++k) {
+        L.wq[k] = take(wsz[k]);
+        L.wqT[k] = take(wsz[k]);
+      }
+    }
+    m.q8row = take(BT * wide);
+    m.q8T = take(BT * wide);
+    m.n_slots = 12 * s.L;
+    m.amax = take((size_t)m.n_slots * 4);
+    m.scales = take((size_t)m.n_slots * 4);
+  }
   m.splitk_floats = need;
   m.splitk = take(std::max<size_t>(need, 1) * 4);
   m.cosb = take((size_t)s.T * (s.Dh / 2) * 4);
@@ -344,12 +387,13 @@ double visible_pairs(long T, long W) {
 // One product with the planned tiling; splits go through the partial buffer
 // and an ordered reduction into C (fp32).
 int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int K, const void* A, long lda,
-         const void* B, long ldb, void* C, long ldc, GemmArgs extra = GemmArgs{}) {
+         const void* B, long ldb, void* C, long ldc, GemmArgs extra = GemmArgs{}, int dtype = -1) {
   const double flops = 2.0 * M * N * (double)K;
+  const int dty = dtype < 0 ? m.s.dtype : dtype;
   GemmArgs a = extra;
   a.A = A; a.B = B; a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = ldb; a.C = C; a.ldc = ldc;
   if (a.alpha == 0.f) a.alpha = 1.f;
-  GemmPlan g = plan_gemm(m.s.dtype, layout, M, N, K);
+  GemmPlan g = plan_gemm(dty, layout, M, N, K);
   if (epi == EPI_XENT_FWD) g = GemmPlan{m.xent_tile, 1, K};
   if (epi != EPI_STORE_F32) g.splits = 1, g.k_split = K;
   if (g.splits > 1 && ldc != N) g.splits = 1, g.k_split = K;
@@ -357,9 +401,9 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
     a.part = at<float>(m, m.splitk);
     a.k_split = g.k_split;
     char label[128];
-    gemm_kernel_label(m.s.dtype, layout, EPI_PARTIAL, g.tile, label, sizeof label);
+    gemm_kernel_label(dty, layout, EPI_PARTIAL, g.tile, label, sizeof label);
     prof_begin(m, site, flops, 0, label);
-    if (gemm_launch(a, m.s.dtype, layout, EPI_PARTIAL, g.tile, g.splits, m.st))
+    if (gemm_launch(a, dty, layout, EPI_PARTIAL, g.tile, g.splits, m.st))
       return fail(GPT_EINVAL, "gemm variant not instantiated (partial)");
     prof_end(m);
     prof_begin(m, "splitk_reduce", (g.splits + 1.0) * M * N * 4.0, 1, "splitk_reduce_kernel");
@@ -369,9 +413,9 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   }
   a.k_split = K;
   char label[128];
-  gemm_kernel_label(m.s.dtype, layout, epi, g.tile, label, sizeof label);
+  gemm_kernel_label(dty, layout, epi, g.tile, label, sizeof label);
   prof_begin(m, site, flops, 0, label);
-  if (gemm_launch(a, m.s.dtype, layout, epi, g.tile, 1, m.st))
+  if (gemm_launch(a, dty, layout, epi, g.tile, 1, m.st))
     return fail(GPT_EINVAL, "gemm variant not instantiated");
   prof_end(m);
   return GPT_OK;
@@ -398,7 +442,39 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   auto KLD = [&](const char* k, const char* extra = "") {
     return std::string(k) + "<" + tname + ", " + std::to_string(Dh) + extra + ">";
   };
+  // fp8 linear layers: per-tensor scale slots (12 per layer), transient codes
+  enum { SL_N1, SL_O, SL_N2, SL_G, SL_WQKV, SL_WO, SL_W1, SL_W2, SL_DH2, SL_DU, SL_DH1, SL_DQKV };
+  const bool f8 = s.fp8;
+  unsigned* amax8 = f8 ? at<unsigned>(m, m.amax) : nullptr;
+  float* sc8 = f8 ? at<float>(m, m.scales) : nullptr;
+  void* q8row = f8 ? m.ws + m.q8row : nullptr;
+  void* q8T = f8 ? m.ws + m.q8T : nullptr;
+  auto slot = [](int l, int k) { return 12 * l + k; };
+  auto quant = [&](const char* site, int fmt, const void* x, int R, int C, int sl, void* q, void* qT) {
+    prof_begin(m, site, (double)R * C * (qT ? 4.0 : 3.0), 1,
+               std::string("amax_kernel + quant_kernel<") + (fmt == FP8_E4M3 ? "e4m3" : "e5m2") + ">");
+    fp8_amax(x, (long)R * C, amax8 + sl, st);
+    fp8_quantize(fmt, x, R, C, amax8 + sl, sc8 + sl, q, qT, st);
+    prof_end(m);
+  };
+  auto gemm8 = [&](const char* site, int dty, int epi, int M, int N, int K, const void* A, const void* B, void* C,
+                   long ldc, int sa, int sb, GemmArgs ex = GemmArgs{}) {
+    ex.scale_a = sc8 + sa;
+    ex.scale_b = sc8 + sb;
+    return gemm(m, site, LAYOUT_KK, epi, M, N, K, A, K, B, K, C, ldc, ex, dty);
+  };
+
   fill_f32((float*)flag, 1, 0.f, st);
+  if (f8) {
+    zero_u32(amax8, m.n_slots, st);
+    for (int l = 0; l < s.L; ++l) {
+      auto& Ly = m.lay[l];
+      quant("fp8_quant_weights", FP8_E4M3, wp(P.Wqkv[l]), 3 * d, d, slot(l, SL_WQKV), m.ws + Ly.wq[0], m.ws + Ly.wqT[0]);
+      quant("fp8_quant_weights", FP8_E4M3, wp(P.Wo[l]), d, d, slot(l, SL_WO), m.ws + Ly.wq[1], m.ws + Ly.wqT[1]);
+      quant("fp8_quant_weights", FP8_E4M3, wp(P.W1[l]), F, d, slot(l, SL_W1), m.ws + Ly.wq[2], m.ws + Ly.wqT[2]);
+      quant("fp8_quant_weights", FP8_E4M3, wp(P.W2[l]), d, F, slot(l, SL_W2), m.ws + Ly.wq[3], m.ws + Ly.wqT[3]);
+    }
+  }
   prof_begin(m, "embed_fwd", (double)BT * d * (es_d + 4.0) + BT * 8.0, 1, KL("embed_fwd_kernel"));
   embed_fwd(dt, tokens, targets, wp(P.E), h, BT, d, V, flag, st);
   prof_end(m);
@@ -408,8 +484,15 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
     rmsnorm_fwd(dt, h, m.ws + Ly.n1, at<float>(m, Ly.rstd1), BT, d, s.eps, st);
     prof_end(m);
-    if ((rc = gemm(m, "gemm_qkv", LAYOUT_KK, EPI_STORE, BT, 3 * d, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d, m.ws + Ly.qkv, 3 * d)))
-      return rc;
+    if (f8) {
+      quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.n1, BT, d, slot(l, SL_N1), q8row, m.ws + Ly.n1T);
+      rc = gemm8("gemm_qkv", DT_FP8_A4B4, EPI_STORE, BT, 3 * d, d, q8row, m.ws + Ly.wq[0], m.ws + Ly.qkv, 3 * d,
+                 slot(l, SL_N1), slot(l, SL_WQKV));
+    } else {
+      rc = gemm(m, "gemm_qkv", LAYOUT_KK, EPI_STORE, BT, 3 * d, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d, m.ws + Ly.qkv,
+                3 * d);
+    }
+    if (rc) return rc;
     prof_begin(m, "rope_qknorm_fwd", (double)BT * d * 8.0 * es_d + BT * 2.0 * H * 4.0, 1, KLD("rope_qknorm_fwd_kernel"));
     rope_qknorm_fwd(dt, m.ws + Ly.qkv, at<float>(m, Ly.rqk), m.ws + Ly.qT, m.ws + Ly.kT, m.ws + Ly.vT, cosb, sinb,
                     s.B, s.T, s.Tp, H, Dh, s.eps, st);
@@ -424,15 +507,34 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                KLD("attn_fwd_kernel"));
     if (attn_fwd(dt, Dh, aa, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
     prof_end(m);
-    if ((rc = gemm(m, "gemm_o", LAYOUT_KK, EPI_ACCUM_F32, BT, d, d, m.ws + Ly.o, d, wp(P.Wo[l]), d, h, d))) return rc;
+    if (f8) {
+      quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.o, BT, d, slot(l, SL_O), q8row, m.ws + Ly.oT);
+      rc = gemm8("gemm_o", DT_FP8_A4B4, EPI_ACCUM_F32, BT, d, d, q8row, m.ws + Ly.wq[1], h, d, slot(l, SL_O),
+                 slot(l, SL_WO));
+    } else {
+      rc = gemm(m, "gemm_o", LAYOUT_KK, EPI_ACCUM_F32, BT, d, d, m.ws + Ly.o, d, wp(P.Wo[l]), d, h, d);
+    }
+    if (rc) return rc;
     prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
     rmsnorm_fwd(dt, h, m.ws + Ly.n2, at<float>(m, Ly.rstd2), BT, d, s.eps, st);
     prof_end(m);
     GemmArgs ex{};
     ex.C2 = m.ws + Ly.g;
-    if ((rc = gemm(m, "gemm_w1_relu2", LAYOUT_KK, EPI_RELU2, BT, F, d, m.ws + Ly.n2, d, wp(P.W1[l]), d, m.ws + Ly.u, F, ex)))
-      return rc;
-    if ((rc = gemm(m, "gemm_w2", LAYOUT_KK, EPI_ACCUM_F32, BT, d, F, m.ws + Ly.g, F, wp(P.W2[l]), F, h, d))) return rc;
+    if (f8) {
+      quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.n2, BT, d, slot(l, SL_N2), q8row, m.ws + Ly.n2T);
+      if ((rc = gemm8("gemm_w1_relu2", DT_FP8_A4B4, EPI_RELU2, BT, F, d, q8row, m.ws + Ly.wq[2], m.ws + Ly.u, F,
+                      slot(l, SL_N2), slot(l, SL_W1), ex)))
+        return rc;
+      quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.g, BT, F, slot(l, SL_G), q8row, m.ws + Ly.gT);
+      rc = gemm8("gemm_w2", DT_FP8_A4B4, EPI_ACCUM_F32, BT, d, F, q8row, m.ws + Ly.wq[3], h, d, slot(l, SL_G),
+                 slot(l, SL_W2));
+    } else {
+      if ((rc = gemm(m, "gemm_w1_relu2", LAYOUT_KK, EPI_RELU2, BT, F, d, m.ws + Ly.n2, d, wp(P.W1[l]), d, m.ws + Ly.u,
+                     F, ex)))
+        return rc;
+      rc = gemm(m, "gemm_w2", LAYOUT_KK, EPI_ACCUM_F32, BT, d, F, m.ws + Ly.g, F, wp(P.W2[l]), F, h, d);
+    }
+    if (rc) return rc;
   }
   prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
   rmsnorm_fwd(dt, h, m.ws + m.nL, at<float>(m, m.rstdL), BT, d, s.eps, st);
@@ -474,21 +576,50 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     GemmArgs ex{};
     ex.aux = m.ws + Ly.u;
     const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
-    if ((rc = gemm(m, "dgrad_w2_drelu2", LAYOUT_KN, EPI_DRELU2, BT, F, d, dhA, d, wp(P.W2[l]), F, m.ws + m.du, F, ex)))
-      return rc;
-    if ((rc = gemm(m, "wgrad_w2", LAYOUT_MN, EPI_STORE_F32, d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F)))
-      return rc;
-    if ((rc = gemm(m, "dgrad_w1", LAYOUT_KN, EPI_STORE_F32, BT, d, F, m.ws + m.du, F, wp(P.W1[l]), d, dm, d)))
-      return rc;
-    if ((rc = gemm(m, "wgrad_w1", LAYOUT_MN, EPI_STORE_F32, F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d,
-                   grads + P.W1[l], d)))
-      return rc;
+    if (f8) {
+      quant("fp8_quant_grad", FP8_E5M2, dhA, BT, d, slot(l, SL_DH2), q8row, q8T);
+      if ((rc = gemm8("dgrad_w2_drelu2", DT_FP8_A5B4, EPI_DRELU2, BT, F, d, q8row, m.ws + Ly.wqT[3], m.ws + m.du, F,
+                      slot(l, SL_DH2), slot(l, SL_W2), ex)))
+        return rc;
+      if ((rc = gemm8("wgrad_w2", DT_FP8_A5B4, EPI_STORE_F32, d, F, BT, q8T, m.ws + Ly.gT, grads + P.W2[l], F,
+                      slot(l, SL_DH2), slot(l, SL_G))))
+        return rc;
+      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.du, BT, F, slot(l, SL_DU), q8row, q8T);
+      if ((rc = gemm8("dgrad_w1", DT_FP8_A5B4, EPI_STORE_F32, BT, d, F, q8row, m.ws + Ly.wqT[2], dm, d,
+                      slot(l, SL_DU), slot(l, SL_W1))))
+        return rc;
+      if ((rc = gemm8("wgrad_w1", DT_FP8_A5B4, EPI_STORE_F32, F, d, BT, q8T, m.ws + Ly.n2T, grads + P.W1[l], d,
+                      slot(l, SL_DU), slot(l, SL_N2))))
+        return rc;
+    } else {
+      if ((rc = gemm(m, "dgrad_w2_drelu2", LAYOUT_KN, EPI_DRELU2, BT, F, d, dhA, d, wp(P.W2[l]), F, m.ws + m.du, F,
+                     ex)))
+        return rc;
+      if ((rc = gemm(m, "wgrad_w2", LAYOUT_MN, EPI_STORE_F32, d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F)))
+        return rc;
+      if ((rc = gemm(m, "dgrad_w1", LAYOUT_KN, EPI_STORE_F32, BT, d, F, m.ws + m.du, F, wp(P.W1[l]), d, dm, d)))
+        return rc;
+      if ((rc = gemm(m, "wgrad_w1", LAYOUT_MN, EPI_STORE_F32, F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d,
+                     grads + P.W1[l], d)))
+        return rc;
+    }
     prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
     rmsnorm_bwd(dt, dm, m.ws + Ly.n2, at<float>(m, Ly.rstd2), dh, dhA, BT, d, 1, st);
     prof_end(m);
-    if ((rc = gemm(m, "dgrad_o", LAYOUT_KN, EPI_STORE, BT, d, d, dhA, d, wp(P.Wo[l]), d, m.ws + m.dO, d))) return rc;
-    if ((rc = gemm(m, "wgrad_o", LAYOUT_MN, EPI_STORE_F32, d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d)))
-      return rc;
+    if (f8) {
+      quant("fp8_quant_grad", FP8_E5M2, dhA, BT, d, slot(l, SL_DH1), q8row, q8T);
+      if ((rc = gemm8("dgrad_o", DT_FP8_A5B4, EPI_STORE, BT, d, d, q8row, m.ws + Ly.wqT[1], m.ws + m.dO, d,
+                      slot(l, SL_DH1), slot(l, SL_WO))))
+        return rc;
+      if ((rc = gemm8("wgrad_o", DT_FP8_A5B4, EPI_STORE_F32, d, d, BT, q8T, m.ws + Ly.oT, grads + P.Wo[l], d,
+                      slot(l, SL_DH1), slot(l, SL_O))))
+        return rc;
+    } else {
+      if ((rc = gemm(m, "dgrad_o", LAYOUT_KN, EPI_STORE, BT, d, d, dhA, d, wp(P.Wo[l]), d, m.ws + m.dO, d)))
+        return rc;
+      if ((rc = gemm(m, "wgrad_o", LAYOUT_MN, EPI_STORE_F32, d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d)))
+        return rc;
+    }
     prof_begin(m, "attn_bwd_pre", (double)BT * d * 3.0 * es_d + (double)s.B * H * s.Tp * 4.0, 1, KLD("attn_bwd_pre_kernel"));
     attn_bwd_pre(dt, m.ws + m.dO, m.ws + Ly.o, at<float>(m, m.Dv), m.ws + m.dOT, s.B, s.T, s.Tp, H, Dh, st);
     prof_end(m);
@@ -515,12 +646,22 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     prof_begin(m, "rope_qknorm_bwd", (double)BT * d * 6.0 * es_d + BT * 2.0 * H * 4.0, 1, KLD("rope_qknorm_bwd_kernel"));
     rope_qknorm_bwd(dt, m.ws + m.dqkv, m.ws + Ly.qkv, at<float>(m, Ly.rqk), cosb, sinb, s.B, s.T, H, Dh, st);
     prof_end(m);
-    if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, EPI_STORE_F32, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d,
-                   dm, d)))
-      return rc;
-    if ((rc = gemm(m, "wgrad_qkv", LAYOUT_MN, EPI_STORE_F32, 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d,
-                   grads + P.Wqkv[l], d)))
-      return rc;
+    if (f8) {
+      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.dqkv, BT, 3 * d, slot(l, SL_DQKV), q8row, q8T);
+      if ((rc = gemm8("dgrad_qkv", DT_FP8_A5B4, EPI_STORE_F32, BT, d, 3 * d, q8row, m.ws + Ly.wqT[0], dm, d,
+                      slot(l, SL_DQKV), slot(l, SL_WQKV))))
+        return rc;
+      if ((rc = gemm8("wgrad_qkv", DT_FP8_A5B4, EPI_STORE_F32, 3 * d, d, BT, q8T, m.ws + Ly.n1T, grads + P.Wqkv[l], d,
+                      slot(l, SL_DQKV), slot(l, SL_N1))))
+        return rc;
+    } else {
+      if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, EPI_STORE_F32, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d,
+                     dm, d)))
+        return rc;
+      if ((rc = gemm(m, "wgrad_qkv", LAYOUT_MN, EPI_STORE_F32, 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d,
+                     grads + P.Wqkv[l], d)))
+        return rc;
+    }
     prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
     rmsnorm_bwd(dt, dm, m.ws + Ly.n1, at<float>(m, Ly.rstd1), dh, dhA, BT, d, 1, st);
     prof_end(m);
@@ -676,6 +817,51 @@ int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const vo
   } else {
     a.k_split = K;
     if (gemm_launch(a, dtype, layout, EPI_STORE_F32, tile, 1, st)) return fail(GPT_EINVAL, "gpt_gemm: variant");
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_EHIP, std::string("launch: ") + hipGetErrorString(e));
+  return GPT_OK;
+}
+
+int gpt_fp8_quantize(int fmt, const void* x, int rows, int cols, uint32_t* amax, float* scale, void* q, void* qT,
+                     void* stream) {
+  if (!x || !amax || !scale || !q) return fail(GPT_ENULL, "gpt_fp8_quantize: NULL argument");
+  if (fmt != FP8_E4M3 && fmt != FP8_E5M2) return fail(GPT_EINVAL, "gpt_fp8_quantize: fmt");
+  if (rows < 1 || cols < 64 || cols % 64 || (long)rows * cols > (1L << 31))
+    return fail(GPT_EINVAL, "gpt_fp8_quantize: sizes");
+  hipStream_t st = (hipStream_t)stream;
+  zero_u32(amax, 1, st);
+  fp8_amax(x, (long)rows * cols, amax, st);
+  fp8_quantize(fmt, x, rows, cols, amax, scale, q, qT, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_EHIP, std::string("launch: ") + hipGetErrorString(e));
+  return GPT_OK;
+}
+
+int gpt_gemm_fp8(int fmt_a, int M, int N, int K, const void* A, const void* B, const float* scale_a,
+                 const float* scale_b, float* C, float* workspace, int splits, void* stream) {
+  if (!A || !B || !C || !scale_a || !scale_b) return fail(GPT_ENULL, "gpt_gemm_fp8: NULL argument");
+  if (fmt_a != FP8_E4M3 && fmt_a != FP8_E5M2) return fail(GPT_EINVAL, "gpt_gemm_fp8: fmt_a");
+  if (M < 1 || N < 1 || K < 16 || M % 8 || N % 8 || K % 16) return fail(GPT_EINVAL, "gpt_gemm_fp8: sizes");
+  if (splits < 1 || (splits > 1 && !workspace)) return fail(GPT_EINVAL, "gpt_gemm_fp8: splits");
+  const int dtype = fmt_a == FP8_E4M3 ? DT_FP8_A4B4 : DT_FP8_A5B4;
+  GemmArgs a{};
+  a.A = A; a.B = B; a.M = M; a.N = N; a.K = K; a.lda = K; a.ldb = K;
+  a.C = C; a.ldc = N; a.alpha = 1.f; a.scale_a = scale_a; a.scale_b = scale_b;
+  hipStream_t st = (hipStream_t)stream;
+  if (splits > 1) {
+    int ks = (K + splits - 1) / splits;
+    ks = (ks + 127) / 128 * 128;
+    splits = (K + ks - 1) / ks;
+    a.k_split = ks;
+    a.part = workspace;
+    if (gemm_launch(a, dtype, LAYOUT_KK, EPI_PARTIAL, TILE_128x128, splits, st))
+      return fail(GPT_EINVAL, "gpt_gemm_fp8: variant");
+    splitk_reduce(workspace, splits, (long)M * N, C, 0, st);
+  } else {
+    a.k_split = K;
+    if (gemm_launch(a, dtype, LAYOUT_KK, EPI_STORE_F32, TILE_128x128, 1, st))
+      return fail(GPT_EINVAL, "gpt_gemm_fp8: variant");
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GPT_EHIP, std::string("launch: ") + hipGetErrorString(e));

@@ -68,7 +68,9 @@ template <> struct Mfma<float> {
   }
 };
 
-// fp8 x fp8 with neutral (2^0) block scales: format codes 0 = E4M3, 1 = E5M2.
+// fp8 x fp8 with neutral (2^0) block scales: format codes 0 = E4M3, 1 = E5M2
+// (FA for the first operand, FB for the second).  Each lane supplies 32
+// codes of one row (first operand) / column (second operand).
 template <int FA, int FB> struct MfmaF8 {
   static constexpr int KM = 64;
   static constexpr int EPL = 32;

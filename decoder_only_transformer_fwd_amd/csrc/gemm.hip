@@ -363,7 +363,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
   }
 
   // ------------------------------------------------------------ epilogue
-  const float alpha = p.alpha;
+  float alpha = p.alpha;
+  if constexpr (ES == 1) alpha = alpha / p.scale_a[0] / p.scale_b[0];
   if constexpr (EPI == EPI_XENT_FWD) {
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
@@ -507,7 +508,8 @@ bool tile_needs_kc(int tile) { return TILES[tile].ns > 2 || TILES[tile].rb != 12
 
 void gemm_kernel_label(int dtype, int layout, int epi, int tile, char* buf, int n) {
   const TileCfg& c = TILES[tile];
-  snprintf(buf, n, "gemm_kernel<%s, %d, %d, %d, %d, %d, %d, %s, %s, %d>", dtype == DT_BF16 ? "bf16" : "float", c.bm,
+  const char* ty = dtype == DT_BF16 ? "bf16" : dtype == DT_F32 ? "float" : dtype == DT_FP8_A4B4 ? "fp8 e4m3 x e4m3" : "fp8 e5m2 x e4m3";
+  snprintf(buf, n, "gemm_kernel<%s, %d, %d, %d, %d, %d, %d, %s, %s, %d>", ty, c.bm,
            c.bn, c.wgm, c.wgn, c.rb, c.ns, layout == LAYOUT_MN ? "false" : "true", layout == LAYOUT_KK ? "true" : "false",
            epi);
 }
@@ -568,9 +570,33 @@ static int launch_epi(const GemmArgs& a, int layout, int epi, int tile, int spli
   return -1;
 }
 
+// FP8 products: both operands K-contiguous (the quantiser provides
+// transposed copies), bf16 / fp32 outputs.  The MFMA is issued with the B
+// tile first, so its first format code is B's.
+template <typename MF>
+static int launch_fp8(const GemmArgs& a, int layout, int epi, int tile, int splits, hipStream_t st) {
+  if (layout != LAYOUT_KK) return -1;
+#define GK_F8(E)                                                                    \
+  if (epi == E) {                                                                   \
+    if (tile == TILE_256x256_W8) launch_cfg<uint8_t, MF, TILE_256x256_W8, true, true, E, bf16>(a, splits, st); \
+    else launch_cfg<uint8_t, MF, TILE_128x128, true, true, E, bf16>(a, splits, st); \
+    return 0;                                                                       \
+  }
+  GK_F8(EPI_STORE)
+  GK_F8(EPI_STORE_F32)
+  GK_F8(EPI_ACCUM_F32)
+  GK_F8(EPI_RELU2)
+  GK_F8(EPI_DRELU2)
+  GK_F8(EPI_PARTIAL)
+#undef GK_F8
+  return -1;
+}
+
 int gemm_launch(const GemmArgs& a, int dtype, int layout, int epi, int tile, int splits, hipStream_t st) {
   if (dtype == DT_BF16) return launch_epi<bf16, Mfma<bf16>, bf16>(a, layout, epi, tile, splits, st);
   if (dtype == DT_F32) return launch_epi<float, Mfma<float>, float>(a, layout, epi, tile, splits, st);
+  if (dtype == DT_FP8_A4B4) return launch_fp8<MfmaF8<FP8_E4M3, FP8_E4M3>>(a, layout, epi, tile, splits, st);
+  if (dtype == DT_FP8_A5B4) return launch_fp8<MfmaF8<FP8_E4M3, FP8_E5M2>>(a, layout, epi, tile, splits, st);
   return -1;
 }
 

@@ -7,7 +7,13 @@
 
 namespace gk {
 
-enum DType { DT_F32 = 0, DT_BF16 = 1 };
+enum DType {
+  DT_F32 = 0,
+  DT_BF16 = 1,
+  DT_FP8_A4B4 = 2,   // fp8 GEMM: A E4M3, B E4M3 (forward)
+  DT_FP8_A5B4 = 3,   // fp8 GEMM: A E5M2 (a gradient), B E4M3
+};
+enum Fp8Fmt { FP8_E4M3 = 0, FP8_E5M2 = 1 };   // also the MFMA operand format codes
 
 enum Layout {
   LAYOUT_KK = 0,  // A [M][K], B [N][K]
@@ -56,6 +62,8 @@ struct GemmArgs {
   float* part;     // EPI_XENT_FWD: [M][nblk][2]; EPI_PARTIAL: [splits][M][N]
   float* tgt;      // EPI_XENT_FWD: target logit per row
   float alpha;     // scales the accumulator before the epilogue
+  const float* scale_a;  // fp8 products: quantisation scales of A and B (device);
+  const float* scale_b;  // the accumulator is multiplied by alpha / (scale_a * scale_b)
   float beta;      // EPI_XENT_BWD: 1 / rows
   int k_split;     // K elements handled per blockIdx.z
   int nblk;        // EPI_XENT_FWD: number of column blocks of width BN/2
@@ -88,6 +96,14 @@ void mean_reduce(const float* x, int n, float* out, hipStream_t st);
 void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab,
                uint32_t* keys, int32_t* runs, int* nruns, hipStream_t st);
 void fill_f32(float* p, long n, float v, hipStream_t st);
+
+// ---------------------------------------------------------------- fp8
+void zero_u32(unsigned* p, int n, hipStream_t st);
+// *amax (zeroed beforehand) = max |x| over n bf16 values, as float bits.
+void fp8_amax(const void* x, long n, unsigned* amax, hipStream_t st);
+// x [R][C] bf16 (C a multiple of 64) -> codes q [R][C] and, if qT, [C][R].
+void fp8_quantize(int fmt, const void* x, int R, int C, const unsigned* amax, float* scale_out, void* q, void* qT,
+                  hipStream_t st);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

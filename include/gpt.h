@@ -51,7 +51,7 @@ typedef struct gpt_config {
   int32_t depth;        /* L, number of blocks                                */
   int32_t d_model;      /* d = n_head * head_dim, multiple of 64              */
   int32_t n_head;       /* H                                                  */
-  int32_t head_dim;     /* Dh: 32 or 64 (GPT_FP32); 64 or 128 (GPT_BF16)       */
+  int32_t head_dim;     /* Dh: 32 or 64 (GPT_FP32); 64 or 128 (GPT_BF16, GPT_FP8) */
   int32_t mlp_hidden;   /* F, multiple of 64                                  */
   int32_t vocab;        /* V, multiple of 8, <= 65536                         */
   int32_t seq_len;      /* T >= 1                                             */
@@ -70,7 +70,14 @@ typedef struct gpt_config {
 /* Precision policy.  GPT_FP32: weights, activations and every product in
  * fp32 (fp32 MFMA).  GPT_BF16: bf16 weights and activations, fp32
  * accumulation, fp32 residual stream, fp32 norm/softmax statistics.
- * GPT_FP8 is reserved (rejected with GPT_EINVAL). */
+ * GPT_FP8: as GPT_BF16, except that the four linear layers of every block
+ * (QKV, O, W1, W2) multiply fp8 operands with fp32 accumulation: weights and
+ * activations in OCP E4M3, gradients in OCP E5M2, each tensor quantised in
+ * every step with its own current scale (see gpt_fp8_quantize); embedding,
+ * attention, norms, lm_head and the loss stay bf16/fp32.  B*T must be a
+ * multiple of 64.  The "FP8 matrix products" of the d24 speedrun ("supa
+ * beginna nanochat" discussion) and the alpha-nanochat-d24 model card are the
+ * prior art; the format split and scaling rule are this library's. */
 
 /* Parameter layout.  One contiguous buffer, tensors in this order:
  *   E [V, d]; for l in 0..L-1: Wq, Wk, Wv [d, d], Wo [d, d], W1 [F, d],
@@ -132,6 +139,28 @@ int gpt_debug_tensor(gpt_model* model, int which, int layer, void** ptr, int64_t
  * Enqueued on `stream`; does not synchronise. */
 int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const void* B, float* C,
              float* workspace, int splits, int tile, void* stream);
+
+/* Per-tensor fp8 quantisation, as used by GPT_FP8 (current scaling):
+ *   s = fmax / max|x| (fmax 448 for E4M3, 57344 for E5M2; s = 1 if x is all
+ *   zero; s capped at 2^64), computed in fp32;
+ *   q[r][c] = OCP code of x[r][c] * s (fp32 product) rounded to nearest even
+ *   with saturation to +-fmax.
+ * fmt: 0 = E4M3, 1 = E5M2.  x: device bf16 [rows, cols], cols a multiple of
+ * 64.  amax: device uint32 scratch (one element, overwritten).  scale: device
+ * float, receives s.  q: device uint8 [rows, cols]; qT: NULL or device uint8
+ * [cols, rows] receiving the transposed codes.  Enqueued on `stream`; does
+ * not synchronise. */
+int gpt_fp8_quantize(int fmt, const void* x, int rows, int cols, uint32_t* amax, float* scale, void* q, void* qT,
+                     void* stream);
+
+/* A single fp8 product through the step's fp8 GEMM kernel:
+ *   C[M,N] = (A B^T) / (scale_a * scale_b), A [M,K] codes in E4M3 (fmt_a = 0)
+ *   or E5M2 (fmt_a = 1), B [N,K] E4M3 codes, fp32 accumulation, C fp32.
+ * scale_a, scale_b: device floats (as written by gpt_fp8_quantize).  M, N
+ * multiples of 8, K a multiple of 16.  splits >= 1 splits K (workspace of
+ * splits*M*N floats).  Enqueued on `stream`; does not synchronise. */
+int gpt_gemm_fp8(int fmt_a, int M, int N, int K, const void* A, const void* B, const float* scale_a,
+                 const float* scale_b, float* C, float* workspace, int splits, void* stream);
 
 /* Per-launch-site timing, for measurement.  When enabled, every kernel
  * launch of gpt_step is bracketed by HIP events on the step's stream; after

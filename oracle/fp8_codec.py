@@ -70,9 +70,21 @@ def encode(x: np.ndarray, fmt: str) -> np.ndarray:
     return (c | np.where(neg, 0x80, 0)).astype(np.uint8)
 
 
-def quantize_tensor(x: np.ndarray, fmt: str):
-    """Current per-tensor scaling: returns (codes, scale) with x ~ decode/scale."""
-    amax = float(np.max(np.abs(x))) if x.size else 0.0
-    fmax = FORMATS[fmt]["fmax"]
-    scale = fmax / amax if amax > 0 else 1.0
-    return encode(np.asarray(x, dtype=np.float64) * scale, fmt), scale
+SCALE_CAP = 2.0 ** 64
+
+
+def quantize_tensor(x: np.ndarray, fmt: str, dtype=np.float64):
+    """Current per-tensor scaling: returns (codes, scale) with x ~ decode/scale.
+
+    scale = fmax / amax (1 when amax = 0, at most 2**64), and each code is the
+    RNE-with-saturation encoding of x * scale.  ``dtype`` is the precision in
+    which the scale and the products x * scale are rounded before encoding
+    (float64 by default; float32 reproduces a quantiser that works in fp32,
+    where the rounded product decides the code)."""
+    x = np.asarray(x, dtype=dtype)
+    amax = dtype(np.max(np.abs(x))) if x.size else dtype(0.0)
+    fmax = dtype(FORMATS[fmt]["fmax"])
+    scale = min(fmax / amax, dtype(SCALE_CAP)) if amax > 0 else dtype(1.0)
+    scale = dtype(scale)
+    y = (x * scale).astype(dtype)
+    return encode(y.astype(np.float64), fmt), float(scale)

@@ -28,6 +28,17 @@ design notes of the repository):
   per-head QK RMSNorm; attention scale 1/sqrt(Dh); a window of W keys means
   0 <= i-j <= W-1; layer l uses pattern[l % len] with the last layer full.
 
+FP8 configuration (precision "fp8"): the "FP8 matrix products" of the d24
+speedrun ("supa beginna nanochat" discussion #677) and of the
+alpha-nanochat-d24 model card are an encoding of the four linear layers'
+operands, so the oracle takes that encoding as a step of the method
+(``Fp8Operands``): forward operands (weights and activations) are encoded in
+OCP E4M3 and gradient operands in E5M2, each tensor with its own current
+per-tensor scale (``fp8_codec.quantize_tensor``); the products of the decoded
+operands are then exact (fp64), and gradients pass the encoding unchanged
+(straight-through).  The fused QKV weight [3d, d] and its output gradient
+[BT, 3d] are one tensor each.  Everything else stays exact.
+
 Memory plan: the residual stream h is checkpointed (fp64) at each layer input;
 the backward recomputes the layer's internals from it.  Attention is done one
 batch row at a time, cross-entropy in chunks of rows, so neither the full
@@ -41,6 +52,8 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 import gpt_inputs as gi
+
+from . import fp8_codec
 
 # ---------------------------------------------------------------------------
 # Elementary operations (each one a plain definition)
@@ -143,17 +156,78 @@ def logsumexp_rows(z: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
+# ---------------------------------------------------------------------------
+# Operands of the linear layers (QKV, O, W1, W2)
+# ---------------------------------------------------------------------------
+
+
+class LinearOperands:
+    """Exact operands: the linear layers multiply the values themselves."""
+
+    def weights(self, s: gi.GPTShape, W: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+        return W
+
+    def act(self, x: np.ndarray) -> np.ndarray:
+        return x
+
+    def grad(self, g: np.ndarray) -> np.ndarray:
+        return g
+
+    def grad_fused(self, *parts: np.ndarray) -> Tuple[np.ndarray, ...]:
+        """Gradient operands of column blocks that form one tensor."""
+        return parts
+
+
+def fp8_value(x: np.ndarray, fmt: str) -> np.ndarray:
+    """The value an fp8-encoded tensor stands for: decode(code) / scale."""
+    codes, scale = fp8_codec.quantize_tensor(x, fmt)
+    return fp8_codec.decode(codes, fmt) / scale
+
+
+class Fp8Operands(LinearOperands):
+    """FP8 configuration: E4M3 weights and activations, E5M2 gradients, one
+    current scale per tensor (the fused QKV weight is one tensor)."""
+
+    def weights(self, s, W):
+        out = dict(W)
+        d = s.d_model
+        for l in range(s.depth):
+            qkv = fp8_value(np.concatenate([W[f"L{l}.Wq"], W[f"L{l}.Wk"], W[f"L{l}.Wv"]]), "e4m3")
+            out[f"L{l}.Wq"], out[f"L{l}.Wk"], out[f"L{l}.Wv"] = qkv[:d], qkv[d:2 * d], qkv[2 * d:]
+            for w in ("Wo", "W1", "W2"):
+                out[f"L{l}.{w}"] = fp8_value(W[f"L{l}.{w}"], "e4m3")
+        return out
+
+    def act(self, x):
+        return fp8_value(x, "e4m3")
+
+    def grad(self, g):
+        return fp8_value(g, "e5m2")
+
+    def grad_fused(self, *parts):
+        q = self.grad(np.concatenate(parts, axis=1))
+        cuts = np.cumsum([p.shape[1] for p in parts])[:-1]
+        return tuple(np.split(q, cuts, axis=1))
+
+
+def operands_for(s: gi.GPTShape) -> LinearOperands:
+    return Fp8Operands() if s.precision == "fp8" else LinearOperands()
+
+
 class _Layer:
-    """Forward internals of one block, recomputed from its input h."""
+    """Forward internals of one block, recomputed from its input h.  W holds
+    the linear weights as the operands encoder ``enc`` presents them."""
 
     def __init__(self, s: gi.GPTShape, W: Dict[str, np.ndarray], l: int,
-                 h: np.ndarray, cos: np.ndarray, sin: np.ndarray, window: int):
+                 h: np.ndarray, cos: np.ndarray, sin: np.ndarray, window: int,
+                 enc: LinearOperands):
         B, T, H, Dh, eps = s.batch, s.seq_len, s.n_head, s.head_dim, s.norm_eps
         self.h_in = h
         self.a, self.r1 = rmsnorm(h, eps)                          # [BT, d]
-        q = (self.a @ W[f"L{l}.Wq"].T).reshape(B, T, H, Dh)
-        k = (self.a @ W[f"L{l}.Wk"].T).reshape(B, T, H, Dh)
-        self.v = (self.a @ W[f"L{l}.Wv"].T).reshape(B, T, H, Dh)
+        self.aq = enc.act(self.a)
+        q = (self.aq @ W[f"L{l}.Wq"].T).reshape(B, T, H, Dh)
+        k = (self.aq @ W[f"L{l}.Wk"].T).reshape(B, T, H, Dh)
+        self.v = (self.aq @ W[f"L{l}.Wv"].T).reshape(B, T, H, Dh)
         self.qr, self.kr = rope(q, cos, sin), rope(k, cos, sin)
         self.qn, self.rq = rmsnorm(self.qr, eps)                   # QK-norm
         self.kn, self.rk = rmsnorm(self.kr, eps)
@@ -164,11 +238,14 @@ class _Layer:
             vb = self.v[b].transpose(1, 0, 2)
             o[b] = attention_fwd(qb, kb, vb, window).transpose(1, 0, 2)
         self.o = o.reshape(B * T, H * Dh)
-        self.h_mid = h + self.o @ W[f"L{l}.Wo"].T
+        self.oq = enc.act(self.o)
+        self.h_mid = h + self.oq @ W[f"L{l}.Wo"].T
         self.m, self.r2 = rmsnorm(self.h_mid, eps)
-        self.u = self.m @ W[f"L{l}.W1"].T
+        self.mq = enc.act(self.m)
+        self.u = self.mq @ W[f"L{l}.W1"].T
         self.g = np.maximum(self.u, 0.0) ** 2
-        self.h_out = self.h_mid + self.g @ W[f"L{l}.W2"].T
+        self.gq = enc.act(self.g)
+        self.h_out = self.h_mid + self.gq @ W[f"L{l}.W2"].T
 
 
 def param_count(s: gi.GPTShape) -> int:
@@ -180,18 +257,24 @@ def _embed(W, X):
 
 
 def forward(s: gi.GPTShape, W: Dict[str, np.ndarray], X: np.ndarray,
-            keep_layers: bool = False):
+            keep_layers: bool = False, enc: Optional[LinearOperands] = None):
     """Forward pass -> (final residual h [BT, d], list of layer inputs, layers).
 
     ``layers`` (the full internals) is only kept when keep_layers is set.
+    ``enc`` defaults to the workload's own operand encoding.
     """
+    enc = enc or operands_for(s)
+    return _forward(s, enc.weights(s, W), X, keep_layers, enc)
+
+
+def _forward(s, W, X, keep_layers, enc):
     cos, sin = rope_tables(s.seq_len, s.head_dim, s.rope_base)
     wins = gi.layer_windows(s)
     h = _embed(W, X)
     h_ins, layers = [], []
     for l in range(s.depth):
         h_ins.append(h)
-        lay = _Layer(s, W, l, h, cos, sin, wins[l])
+        lay = _Layer(s, W, l, h, cos, sin, wins[l], enc)
         h = lay.h_out
         if keep_layers:
             layers.append(lay)
@@ -240,21 +323,25 @@ def _xent(s, W, h, Y, chunk_rows: int, want_grads: bool):
 
 
 def loss_only(s: gi.GPTShape, W: Dict[str, np.ndarray], X: np.ndarray,
-              Y: np.ndarray, chunk_rows: int = 1024) -> float:
-    h, _, _ = forward(s, W, X)
+              Y: np.ndarray, chunk_rows: int = 1024, enc: Optional[LinearOperands] = None) -> float:
+    h, _, _ = forward(s, W, X, enc=enc)
     return _xent(s, W, h, Y, chunk_rows, want_grads=False)[0]
 
 
 def forward_backward(s: gi.GPTShape, W: Dict[str, np.ndarray], X: np.ndarray,
                      Y: np.ndarray, chunk_rows: int = 1024,
-                     want_grads: bool = True):
+                     want_grads: bool = True, enc: Optional[LinearOperands] = None):
     """One training step of the definition: returns (loss, grads dict).
 
     Gradients are of the mean loss, one fp64 array per parameter tensor in
-    the same [rows, cols] shape as the weight.
+    the same [rows, cols] shape as the weight.  ``enc`` defaults to the
+    workload's own operand encoding (fp8 for precision "fp8"); the gradient
+    of an encoded weight is taken as the gradient of the weight.
     """
     B, T, H, Dh, d = s.batch, s.seq_len, s.n_head, s.head_dim, s.d_model
-    h, h_ins, _ = forward(s, W, X)
+    enc = enc or operands_for(s)
+    Wl = enc.weights(s, W)
+    h, h_ins, _ = _forward(s, Wl, X, False, enc)
     loss, dh, dU, _, _ = _xent(s, W, h, Y, chunk_rows, want_grads)
     if not want_grads:
         return loss, {}
@@ -263,18 +350,21 @@ def forward_backward(s: gi.GPTShape, W: Dict[str, np.ndarray], X: np.ndarray,
     wins = gi.layer_windows(s)
     grads: Dict[str, np.ndarray] = {"U": dU}
     for l in reversed(range(s.depth)):
-        L = _Layer(s, W, l, h_ins[l], cos, sin, wins[l])
+        L = _Layer(s, Wl, l, h_ins[l], cos, sin, wins[l], enc)
         h_ins[l] = None
         # MLP: h_out = h_mid + g W2^T, g = relu(u)^2, u = m W1^T, m = N(h_mid)
-        grads[f"L{l}.W2"] = dh.T @ L.g
-        dg = dh @ W[f"L{l}.W2"]
+        dhq = enc.grad(dh)
+        grads[f"L{l}.W2"] = dhq.T @ L.gq
+        dg = dhq @ Wl[f"L{l}.W2"]
         du = dg * 2.0 * np.maximum(L.u, 0.0)
-        grads[f"L{l}.W1"] = du.T @ L.m
-        dm = du @ W[f"L{l}.W1"]
+        duq = enc.grad(du)
+        grads[f"L{l}.W1"] = duq.T @ L.mq
+        dm = duq @ Wl[f"L{l}.W1"]
         dh = dh + rmsnorm_bwd(dm, L.m, L.r2)
         # attention: h_mid = h_in + o Wo^T
-        grads[f"L{l}.Wo"] = dh.T @ L.o
-        do = (dh @ W[f"L{l}.Wo"]).reshape(B, T, H, Dh)
+        dhq = enc.grad(dh)
+        grads[f"L{l}.Wo"] = dhq.T @ L.oq
+        do = (dhq @ Wl[f"L{l}.Wo"]).reshape(B, T, H, Dh)
         dqn = np.empty_like(do)
         dkn = np.empty_like(do)
         dv = np.empty_like(do)
@@ -289,10 +379,11 @@ def forward_backward(s: gi.GPTShape, W: Dict[str, np.ndarray], X: np.ndarray,
         dq = rope_bwd(rmsnorm_bwd(dqn, L.qn, L.rq), cos, sin).reshape(B * T, d)
         dk = rope_bwd(rmsnorm_bwd(dkn, L.kn, L.rk), cos, sin).reshape(B * T, d)
         dv = dv.reshape(B * T, d)
-        grads[f"L{l}.Wq"] = dq.T @ L.a
-        grads[f"L{l}.Wk"] = dk.T @ L.a
-        grads[f"L{l}.Wv"] = dv.T @ L.a
-        da = dq @ W[f"L{l}.Wq"] + dk @ W[f"L{l}.Wk"] + dv @ W[f"L{l}.Wv"]
+        dq, dk, dv = enc.grad_fused(dq, dk, dv)   # the fused projection's output gradient
+        grads[f"L{l}.Wq"] = dq.T @ L.aq
+        grads[f"L{l}.Wk"] = dk.T @ L.aq
+        grads[f"L{l}.Wv"] = dv.T @ L.aq
+        da = dq @ Wl[f"L{l}.Wq"] + dk @ Wl[f"L{l}.Wk"] + dv @ Wl[f"L{l}.Wv"]
         dh = dh + rmsnorm_bwd(da, L.a, L.r1)
         del L
     dE = np.zeros((s.vocab, d))

@@ -1,12 +1,13 @@
 """Write the oracle's full-size results used by the GPU parity tests.
 
-For each full workload (d12, d20, d24; the fp8 workload shares d24's inputs and
-exact result) this runs the fp64 oracle once on the seeded inputs and stores:
+For each full workload (d12, d20, d24, and d24-fp8, whose linear-layer
+operands the oracle encodes in fp8 as that workload's method does) this runs
+the fp64 oracle once on the seeded inputs and stores:
 the loss, the L2 norm of every gradient tensor, and the gradient values at
 seeded sample positions (``gpt_inputs.grad_sample_indices``, 2048 per tensor).
 Only ``oracle/`` and ``gpt_inputs`` are used.
 
-Usage:  python tests/golden/make_full_size_golden.py d12 d20 d24
+Usage:  python tests/golden/make_full_size_golden.py d12 d20 d24 d24-fp8
 """
 import os
 import sys

@@ -44,6 +44,11 @@ SMALL = {
                             precision="bf16", token_dist="zipf"),
     "d12_short": gi.preset("d12", seq_len=256, batch=1),
     "d24_short": gi.preset("d24", seq_len=384, batch=1, window=128),
+    # fp8 linear layers (B*T a multiple of 64)
+    "fp8_mid": gi.GPTShape("fp8_mid", depth=2, d_model=256, n_head=2, head_dim=128, mlp_hidden=1024,
+                           vocab=1000, seq_len=224, batch=2, window=64, window_pattern="SL",
+                           precision="fp8", token_dist="zipf"),
+    "d24_fp8_short": gi.preset("d24-fp8", seq_len=384, batch=1, window=128),
 }
 
 

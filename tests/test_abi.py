@@ -62,7 +62,7 @@ def test_d20_parameter_total(M):
     assert sum(r * c for _, _, r, c in layout) == 560_988_160
 
 
-@pytest.mark.parametrize("name", ["tiny", "d12", "d20", "d24"])
+@pytest.mark.parametrize("name", ["tiny", "d12", "d20", "d24", "d24-fp8"])
 def test_workspace_bytes_is_sane(M, name):
     s = gi.preset(name)
     b = M.gpt_workspace_bytes(M.make_config(s))
@@ -82,7 +82,8 @@ BAD = [
     dict(window=0, window_pattern="SL"),         # S layer without a window
     dict(mlp_hidden=100),                        # F not a multiple of 64
     dict(depth=0),
-    dict(precision="fp8"),                       # not built
+    dict(precision="fp8", seq_len=100, batch=1),  # fp8 needs B*T % 64 == 0
+    dict(precision="fp8", head_dim=32, d_model=64, n_head=2),  # fp8 attention is bf16: Dh 64/128
 ]
 
 
@@ -110,6 +111,28 @@ def test_gemm_argument_errors(M):
         M.gpt_gemm(1, 3, 64, 64, 64, 256, 256, 256)    # bad layout
     with pytest.raises(M.GPTError):
         M.gpt_gemm(1, 0, 64, 64, 64, 0, 256, 256)      # NULL operand
+
+
+def test_fp8_argument_errors(M):
+    with pytest.raises(M.GPTError):
+        M.gpt_fp8_quantize(2, 256, 64, 64, 256, 256, 256)      # bad format
+    with pytest.raises(M.GPTError):
+        M.gpt_fp8_quantize(0, 256, 64, 100, 256, 256, 256)     # cols not a multiple of 64
+    with pytest.raises(M.GPTError):
+        M.gpt_fp8_quantize(0, 0, 64, 64, 256, 256, 256)        # NULL input
+    with pytest.raises(M.GPTError):
+        M.gpt_gemm_fp8(0, 64, 64, 40, 256, 256, 256, 256, 256)  # K not a multiple of 16
+    with pytest.raises(M.GPTError):
+        M.gpt_gemm_fp8(3, 64, 64, 64, 256, 256, 256, 256, 256)  # bad format
+
+
+def test_fp8_workspace_holds_the_codes(M):
+    s = gi.preset("d24")
+    b16 = M.gpt_workspace_bytes(M.make_config(s))
+    b8 = M.gpt_workspace_bytes(M.make_config(s.replace(precision="fp8")))
+    d, F, L, BT = s.d_model, s.mlp_hidden, s.depth, s.bt
+    # saved transposed activation codes + two copies of every weight's codes
+    assert b8 - b16 >= L * (3 * d * BT + F * BT + 2 * (4 * d * d + 2 * F * d))
 
 
 def test_strerror(M):

@@ -6,6 +6,7 @@ oracle results stored by ``tests/golden/make_full_size_golden.py`` (loss,
 per-tensor norms and seeded gradient samples), in the same launch
 configuration the benchmark times.
 """
+import json
 import os
 
 import numpy as np
@@ -17,6 +18,22 @@ from tests.gpu_common import SMALL, TOL, cosine, log, oracle_step
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def grad_cos_bar(workload: str, precision: str, tensor: str) -> float:
+    """Per-tensor gradient cosine bar.  fp8: 0.99, lowered for a tensor whose
+    gradient the fp8 recipe itself cannot reproduce that closely -- two
+    faithful fp64 evaluations of the recipe, one with its operands rounded to
+    bf16 before encoding, agree only to cosine c (tests/golden/
+    make_fp8_sensitivity.py) -- to 1 - 2 (1 - c), i.e. twice the recipe's own
+    disagreement."""
+    bar = TOL[precision]["cos"]
+    if precision != "fp8":
+        return bar
+    path = os.path.join(GOLDEN, "fp8_sensitivity.json")
+    sens = json.load(open(path)) if os.path.exists(path) else {}
+    c = sens.get(workload, {}).get("cosine", {}).get(tensor)
+    return bar if c is None else min(bar, 1.0 - 2.0 * (1.0 - c))
 
 
 def _session(s, W8, X, Y):
@@ -38,17 +55,23 @@ def test_step_matches_oracle(name):
     rel = abs(loss - loss_ref) / abs(loss_ref)
     log(f"  loss gpu={loss:.8f} oracle={loss_ref:.8f} rel={rel:.2e}")
     worst = (2.0, None)
+    below = []
     for n, g_ref in G_ref.items():
         if not np.any(g_ref):
             continue
         c = cosine(G[n], g_ref)
         worst = min(worst, (c, n))
+        bar = grad_cos_bar(name, s.precision, n)
+        if c < tol["cos"]:
+            log(f"  {n}: cosine {c:.5f} (bar {bar:.5f})")
+        if c < bar:
+            below.append((n, c, bar))
         if tol["maxrel"] is not None:
             err = np.max(np.abs(G[n] - g_ref)) / np.max(np.abs(g_ref))
             assert err <= tol["maxrel"], (n, err)
     log(f"  worst grad cosine {worst[0]:.7f} ({worst[1]})")
     assert rel <= tol["loss_rel"]
-    assert worst[0] >= tol["cos"], worst
+    assert not below, below
     # gradients of embedding rows that no token uses are exactly zero
     unseen = np.setdiff1d(np.arange(s.vocab), np.unique(X))
     assert np.all(G["E"][unseen] == 0.0)
@@ -146,13 +169,14 @@ def test_out_of_range_token_is_reported():
     sess.close()
 
 
-@pytest.mark.parametrize("name", ["d12", "d24", "d20"])
+@pytest.mark.parametrize("name", ["d12", "d24", "d20", "d24-fp8"])
 def test_full_size_step_matches_stored_oracle(name):
     path = os.path.join(GOLDEN, f"oracle_{name}.npz")
     if not os.path.exists(path):
         pytest.skip(f"{path} not generated")
     ref = np.load(path, allow_pickle=False)
     s = gi.preset(name)
+    tol = TOL[s.precision]
     W8 = gi.make_weights(s)
     X, Y = gi.make_tokens(s)
     log(f"full-size parity: {name}")
@@ -160,17 +184,24 @@ def test_full_size_step_matches_stored_oracle(name):
     loss = sess.step()
     rel = abs(loss - float(ref["loss"])) / float(ref["loss"])
     log(f"  loss gpu={loss:.7f} oracle={float(ref['loss']):.7f} rel={rel:.2e}")
-    assert rel <= TOL["bf16"]["loss_rel"]
+    assert rel <= tol["loss_rel"]
     idx = gi.grad_sample_indices(s, int(ref["n_samples"]))
     samples = sess.grad_samples(idx)
     norms = sess.grad_norms()
     worst = (2.0, None)
+    below = []
     for k, n in enumerate(ref["names"]):
         n = str(n)
         c = cosine(samples[n], ref["samples"][k])
         worst = min(worst, (c, n))
+        bar = grad_cos_bar(name, s.precision, n)
+        if c < tol["cos"]:
+            log(f"  {n}: sampled cosine {c:.5f} (bar {bar:.5f})")
+        if c < bar:
+            below.append((n, c, bar))
         nr = norms[n] / ref["norms"][k]
-        assert 0.98 < nr < 1.02, (n, nr)
+        band = 0.02 if s.precision == "bf16" else 0.05
+        assert abs(nr - 1.0) < band, (n, nr)
     log(f"  worst sampled cosine {worst[0]:.6f} ({worst[1]})")
-    assert worst[0] >= TOL["bf16"]["cos"], worst
+    assert not below, below
     sess.close()
