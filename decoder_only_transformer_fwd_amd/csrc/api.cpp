@@ -127,11 +127,12 @@ struct GemmPlan {
 
 
 // Tile and split-K choice, set from measurements of this kernel on MI355X at
-// the step's shapes: 128x128 tiles (two work-groups per CU) except for very
-// wide forward products (8-wave 256x256).  Weight gradients (K = B*T, few
-// output tiles) are split along K by a cost model: waves of work-groups
-// (512 resident at two per CU) times K steps per split, plus the fp32
-// partial-sum reduction at ~5 TB/s.
+// the step's shapes: 128x128 tiles (two work-groups per CU) for forward and
+// input-gradient products, 8-wave 256x256 for very wide forward products,
+// and the 256x256 ping-pong tile for bf16 weight gradients (K = B*T, few
+// output tiles), which are split along K by a cost model: waves of
+// work-groups (512 resident at two per CU, 256 at one) times K steps per
+// split, plus the fp32 partial-sum reduction at ~5 TB/s.
 GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   GemmPlan g{TILE_64x64, 1, K};
   const bool f8 = dtype == DT_FP8_A4B4 || dtype == DT_FP8_A5B4;
@@ -142,24 +143,30 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
     g.tile = (long)M * N >= 256L * 128 * 128 ? TILE_128x128 : TILE_64x64;
   } else if (layout == LAYOUT_KK) {
     g.tile = N >= 8192 ? TILE_256x256_W8 : TILE_128x128;
+  } else if (layout == LAYOUT_MN) {
+    g.tile = TILE_256x256_PP4;
   } else {
     g.tile = TILE_128x128;
   }
   // fp8 weight gradients are K-contiguous products with K = B*T
   if (layout == LAYOUT_MN || (f8 && K >= 4096)) {
+    const bool pp = g.tile == TILE_256x256_PP4;
     const long tiles = (long)((M + tile_bm(g.tile) - 1) / tile_bm(g.tile)) * ((N + tile_bn(g.tile) - 1) / tile_bn(g.tile));
-    const long slots = dtype == DT_F32 ? 256 : 512;
-    const double t_step = dtype == DT_F32 ? 4e-6 : f8 ? 1.5e-6 : 1.34e-6;   // one K step of one tile, seconds
+    const long slots = dtype == DT_F32 || pp ? 256 : 512;
+    // one K step of one tile, seconds (the ping-pong tile steps 32 deep)
+    const double t_step = dtype == DT_F32 ? 4e-6 : f8 ? 1.5e-6 : pp ? 0.95e-6 : 1.34e-6;
+    const int step = pp ? 32 : bk;
     double best = 1e300;
     const int cand[6] = {1, 2, 3, 4, 6, 8};
-    for (int c = 0; c < 6; ++c) {
+    const int ncand = pp ? 4 : 6;   // deeper splits lose to the reduction at 256x256
+    for (int c = 0; c < ncand; ++c) {
       const int sp = cand[c];
       int ks = (K + sp - 1) / sp;
       ks = (ks + bk - 1) / bk * bk;
       const int real = (K + ks - 1) / ks;
       if (real != sp && sp > 1) continue;
       const long waves = (tiles * sp + slots - 1) / slots;
-      double t = (double)waves * ((ks + bk - 1) / bk) * t_step;
+      double t = (double)waves * ((ks + step - 1) / step) * t_step;
       if (sp > 1) t += (sp + 1.0) * M * (double)N * 4.0 / 5e12;
       if (t < best) {
         best = t;

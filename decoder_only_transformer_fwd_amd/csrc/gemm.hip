@@ -197,6 +197,16 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int rb, int kbase, i
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Work-group barrier without the release/acquire fences of __syncthreads.
+// Those fences make every wave wait for all of its outstanding global->LDS
+// copies (vmcnt 0) at each barrier, which would drain a multi-stage pipeline;
+// callers wait for exactly the copies and LDS reads they depend on.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -218,7 +228,7 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 }
 
 template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, int RB, int NS, bool A_KC, bool B_KC, int EPI,
-          typename TC>
+          typename TC, bool PP>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
   constexpr int THREADS = 64 * WGM * WGN;
   constexpr int NW = WGM * WGN;
@@ -229,7 +239,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
   constexpr bool A_TR = !A_KC && ES == 2, B_TR = !B_KC && ES == 2;
   constexpr bool A_REG = !A_KC && !A_TR, B_REG = !B_KC && !B_TR;
   static_assert(NS == 2 || (!A_REG && !B_REG), "deeper pipelines need both operands on the direct-to-LDS path");
-  static_assert(RB == 128 || (A_KC && B_KC), "transposed operands use 128-byte K steps");
+  static_assert(RB == 128 || (A_KC && B_KC) || PP, "transposed operands use 128-byte K steps");
+  static_assert(!PP || (WGM * WGN == 8 && WGM % 2 == 0 && !A_REG && !B_REG), "ping-pong: two groups of four waves");
+  // waves that issue the global->LDS copies: all of them, or in the
+  // ping-pong schedule the first group only
+  constexpr int LW = PP ? WGM * WGN / 2 : WGM * WGN;
   constexpr int KM = MF::KM;
   constexpr int EPL = MF::EPL;
   constexpr int FB = EPL * ES;         // fragment bytes per lane
@@ -256,16 +270,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
 
   TransLoader<ES, BM, THREADS> la;
   TransLoader<ES, BN, THREADS> lb;
-  DmaLoader<ES, BM, NW, RB> da;
-  DmaLoader<ES, BN, NW, RB> db;
-  DmaTrLoader<ES, BM, NW, BK> ta;
-  DmaTrLoader<ES, BN, NW, BK> tb;
+  DmaLoader<ES, BM, LW, RB> da;
+  DmaLoader<ES, BN, LW, RB> db;
+  DmaTrLoader<ES, BM, LW, BK> ta;
+  DmaTrLoader<ES, BN, LW, BK> tb;
   const char* Ab = (const char*)p.A;
   const char* Bb = (const char*)p.B;
-  if constexpr (A_KC) da.init(Ab, p.lda, m0, p.M, wave, lane);
-  if constexpr (B_KC) db.init(Bb, p.ldb, n0, p.N, wave, lane);
-  if constexpr (A_TR) ta.init(Ab, p.lda, m0, wave, lane);
-  if constexpr (B_TR) tb.init(Bb, p.ldb, n0, wave, lane);
+  if (wave < LW) {
+    if constexpr (A_KC) da.init(Ab, p.lda, m0, p.M, wave, lane);
+    if constexpr (B_KC) db.init(Bb, p.ldb, n0, p.N, wave, lane);
+    if constexpr (A_TR) ta.init(Ab, p.lda, m0, wave, lane);
+    if constexpr (B_TR) tb.init(Bb, p.ldb, n0, wave, lane);
+  }
 
   floatx16 acc[MB][NB];
 #pragma unroll
@@ -299,51 +315,103 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
     else lds_read<RB, FB>(b_s, wn * WN + j * 32 + l32, (kk * KM + g * EPL) * ES, out);
   };
   constexpr int KK = BK / KM;
-  auto compute = [&](int stage) {
+  static_assert(KK % 2 == 0, "fragment double-buffering assumes an even number of K sub-steps");
+  // fragment buffers: two (double-buffered sub-steps), or in the ping-pong
+  // schedule one per sub-step of a whole K step
+  constexpr int FBUF = PP ? KK : 2;
+  typename MF::frag af[FBUF][MB], bfr[FBUF][NB];
+  auto read_frags = [&](const char* a_s, int kk, int buf) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) frag_a(a_s, i, kk, &af[buf][i]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) frag_b(a_s + BM * RB, j, kk, &bfr[buf][j]);
+  };
+  auto mma_step = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = MF::mma(bfr[buf][j], af[buf][i], acc[i][j]);
+  };
+  // Sub-steps 0 .. KK-2 of a stage whose sub-step-0 fragments are already in
+  // buffer 0; the fragment reads for the next sub-step go out before this
+  // sub-step's MFMAs (the fences keep the scheduler from sinking them to
+  // their uses).  Sub-step KK-1's fragments are left in buffer 1.
+  auto compute_head = [&](int stage) {
     const char* a_s = smem + stage * STAGE;
-    const char* b_s = a_s + BM * RB;
-    typename MF::frag af[2][MB], bfr[2][NB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) frag_a(a_s, i, 0, &af[0][i]);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) frag_b(b_s, j, 0, &bfr[0][j]);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int cur = kk & 1;
-      // fragment reads for the next sub-step go out before this sub-step's
-      // MFMAs (the fences keep the scheduler from sinking them to their uses)
-      if (kk + 1 < KK) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i) frag_a(a_s, i, kk + 1, &af[cur ^ 1][i]);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) frag_b(b_s, j, kk + 1, &bfr[cur ^ 1][j]);
-      }
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      read_frags(a_s, kk + 1, (kk + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = MF::mma(bfr[cur][j], af[cur][i], acc[i][j]);
+      mma_step(kk & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto compute = [&](int stage) {
+    read_frags(smem + stage * STAGE, 0, 0);
+    compute_head(stage);
+    mma_step(1);
+  };
 
-  if constexpr (NS == 2) {
+  if constexpr (PP) {
+    // Ping-pong: waves 0-3 (group 0, output rows 0..BM/2-1) and 4-7 (group 1,
+    // the other half)
+    // share the SIMDs pairwise and run half a step apart.  While one group
+    // multiplies fragments already in its registers, the other reads the
+    // next stage's fragments from LDS (and group 0 also issues the
+    // global->LDS copies for the stage NS-1 steps ahead), so each SIMD's
+    // matrix unit alternates between the two groups' MFMA blocks.  Every
+    // phase ends with a barrier of all 8 waves; group 1 starts one phase
+    // late, and group 0 ends with one extra barrier to match.
+    constexpr int LPS = (A_KC ? DmaLoader<ES, BM, LW, RB>::PER_WAVE : DmaTrLoader<ES, BM, LW, BK>::PER_WAVE) +
+                        (B_KC ? DmaLoader<ES, BN, LW, RB>::PER_WAVE : DmaTrLoader<ES, BN, LW, BK>::PER_WAVE);
+    const bool loader = wave < LW;
+    if (loader) {
+#pragma unroll
+      for (int st = 0; st < NS - 1; ++st) fetch(kbeg + st * BK, st);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
+    }
+    barrier_only();
+    if (!loader) barrier_only();
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* a_s = smem + (kt % NS) * STAGE;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) read_frags(a_s, kk, kk);
+      if (loader) fetch(kbeg + (kt + NS - 1) * BK, (kt + NS - 1) % NS);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): fragments are in registers
+      barrier_only();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) mma_step(kk);
+      __builtin_amdgcn_sched_barrier(0);
+      if (loader) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));   // the next stage has landed
+      barrier_only();
+    }
+    if (loader) barrier_only();
+    __builtin_amdgcn_s_waitcnt(0x0070);
+  } else if constexpr (NS == 2) {
     // Two stages: the next tile is requested at the top of a step and must
-    // have landed (vmcnt 0) by the barrier that ends it.
+    // have landed (vmcnt 0) by the barrier that ends it.  The last sub-step's
+    // MFMAs run after that barrier, behind the fragment reads of the next
+    // stage's first sub-step, so the LDS latency after each barrier is hidden.
     if (nk > 0) {
       fetch(kbeg, 0);
       commit(0);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __syncthreads();
+    if (nk > 0) read_frags(smem, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const int s = kt & 1;
       const bool more = kt + 1 < nk;
       if (more) fetch(kbeg + (kt + 1) * BK, s ^ 1);
-      compute(s);
+      compute_head(s);
       if (more) commit(s ^ 1);
       __builtin_amdgcn_s_waitcnt(0x0070);
       __syncthreads();
+      if (more) read_frags(smem + (s ^ 1) * STAGE, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     // NS stages, all by direct-to-LDS loads: NS-1 steps are in flight.  Every
@@ -355,7 +423,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
     for (int st = 0; st < NS - 1; ++st) fetch(kbeg + st * BK, st);
     for (int kt = 0; kt < nk; ++kt) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
-      __syncthreads();
+      barrier_only();
       fetch(kbeg + (kt + NS - 1) * BK, (kt + NS - 1) % NS);
       compute(kt % NS);
     }
@@ -488,6 +556,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // Tile table: id -> (BM, BN, waves M x N, bytes per K step per row, stages).
 struct TileCfg {
   int bm, bn, wgm, wgn, rb, ns;
+  bool pp;   // ping-pong schedule of two 4-wave groups
 };
 static constexpr TileCfg TILES[] = {
     {256, 256, 2, 2, 128, 2},  // TILE_256x256
@@ -500,25 +569,28 @@ static constexpr TileCfg TILES[] = {
     {256, 256, 2, 2, 64, 4},   // TILE_256x256_S4
     {256, 128, 2, 4, 128, 3},  // TILE_256x128_W8_S3
     {128, 128, 2, 2, 64, 4},   // TILE_128x128_S4
+    {256, 256, 2, 4, 64, 4, true},   // TILE_256x256_PP4
+    {256, 256, 2, 4, 64, 5, true},   // TILE_256x256_PP5
+    {256, 128, 4, 2, 128, 3, true},  // TILE_256x128_PP3
 };
 int tile_bm(int tile) { return TILES[tile].bm; }
 int tile_bn(int tile) { return TILES[tile].bn; }
 int tile_wn(int tile) { return TILES[tile].bn / TILES[tile].wgn; }
-bool tile_needs_kc(int tile) { return TILES[tile].ns > 2 || TILES[tile].rb != 128; }
+bool tile_needs_kc(int tile) { return !TILES[tile].pp && (TILES[tile].ns > 2 || TILES[tile].rb != 128); }
 
 void gemm_kernel_label(int dtype, int layout, int epi, int tile, char* buf, int n) {
   const TileCfg& c = TILES[tile];
   const char* ty = dtype == DT_BF16 ? "bf16" : dtype == DT_F32 ? "float" : dtype == DT_FP8_A4B4 ? "fp8 e4m3 x e4m3" : "fp8 e5m2 x e4m3";
-  snprintf(buf, n, "gemm_kernel<%s, %d, %d, %d, %d, %d, %d, %s, %s, %d>", ty, c.bm,
+  snprintf(buf, n, "gemm_kernel<%s, %d, %d, %d, %d, %d, %d, %s, %s, %d%s>", ty, c.bm,
            c.bn, c.wgm, c.wgn, c.rb, c.ns, layout == LAYOUT_MN ? "false" : "true", layout == LAYOUT_KK ? "true" : "false",
-           epi);
+           epi, c.pp ? ", ping-pong" : "");
 }
 
 template <typename TA, typename MF, int T, bool AK, bool BK_, int EPI, typename TC>
 static void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
   constexpr TileCfg c = TILES[T];
   dim3 grid(((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn), 1, splits);
-  hipLaunchKernelGGL((gemm_kernel<TA, MF, c.bm, c.bn, c.wgm, c.wgn, c.rb, c.ns, AK, BK_, EPI, TC>), grid,
+  hipLaunchKernelGGL((gemm_kernel<TA, MF, c.bm, c.bn, c.wgm, c.wgn, c.rb, c.ns, AK, BK_, EPI, TC, c.pp>), grid,
                      dim3(64 * c.wgm * c.wgn), 0, st, a);
 }
 
@@ -531,6 +603,7 @@ static void launch_tiles(const GemmArgs& a, int tile, int splits, hipStream_t st
 #define GK_T(T) case T: launch_cfg<TA, MF, T, AK, BK_, EPI, TC>(a, splits, st); return;
     switch (tile) {
       GK_T(TILE_256x256) GK_T(TILE_256x128) GK_T(TILE_256x256_W8) GK_T(TILE_256x128_W8)
+      GK_T(TILE_256x256_PP4) GK_T(TILE_256x256_PP5) GK_T(TILE_256x128_PP3)
       default: break;
     }
     if constexpr (AK && BK_) {

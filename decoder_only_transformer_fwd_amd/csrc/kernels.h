@@ -39,7 +39,9 @@ enum Tile {
   // deeper pipelines (K-contiguous operands only): 4 stages of 64-byte rows
   // or 3 stages of 128-byte rows
   TILE_256x256_W8_S4 = 6, TILE_256x256_S4 = 7, TILE_256x128_W8_S3 = 8, TILE_128x128_S4 = 9,
-  TILE_COUNT = 10,
+  // 8 waves in two ping-pong groups: 4 / 5 stages of 64-byte rows, 3 of 128
+  TILE_256x256_PP4 = 10, TILE_256x256_PP5 = 11, TILE_256x128_PP3 = 12,
+  TILE_COUNT = 13,
 };
 bool tile_needs_kc(int tile);   // usable only when both operands are K-contiguous
 // Readable template signature of the kernel a product launches (as profilers

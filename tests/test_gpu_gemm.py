@@ -9,7 +9,8 @@ from tests.gpu_common import log
 pytestmark = pytest.mark.gpu
 
 LAYOUT_KK, LAYOUT_KN, LAYOUT_MN = 0, 1, 2
-TILES_BF16 = [0, 1, 2, 4, 5]    # 256x256, 256x128, 128x128 (4 waves); 256x256, 256x128 (8 waves)
+# 256x256, 256x128, 128x128 (4 waves); 256x256, 256x128 (8 waves); ping-pong 256x256 (4, 5 stages), 256x128
+TILES_BF16 = [0, 1, 2, 4, 5, 10, 11, 12]
 TILES_F32 = [2, 3]          # 128x128, 64x64
 
 
@@ -72,20 +73,30 @@ def test_gemm_f32_ragged(layout, tile):
 
 
 @pytest.mark.parametrize("layout", [LAYOUT_KN, LAYOUT_MN])
-def test_gemm_split_k(layout):
-    c, ref = run_gemm(1, layout, 256, 192, 2048, 2, splits=5)
+@pytest.mark.parametrize("tile", [2, 10])
+def test_gemm_split_k(layout, tile):
+    c, ref = run_gemm(1, layout, 256, 192, 2048, tile, splits=5)
     _check(c, ref, 2048)
 
 
-@pytest.mark.parametrize("tile", [0, 4, 6, 7, 8, 9])
+@pytest.mark.parametrize("tile", [0, 4, 6, 7, 8, 9, 10, 11, 12])
 def test_gemm_bf16_multi_tile(tile):
     c, ref = run_gemm(1, LAYOUT_KK, 1024, 768, 512, tile, seed=3)
     _check(c, ref, 512)
 
 
-@pytest.mark.parametrize("tile", [6, 7, 8, 9])
+@pytest.mark.parametrize("layout", [LAYOUT_KN, LAYOUT_MN])
+@pytest.mark.parametrize("tile", [10, 11, 12])
+def test_gemm_bf16_ping_pong_multi_tile(layout, tile):
+    c, ref = run_gemm(1, layout, 768, 1024, 640, tile, seed=4)
+    _check(c, ref, 640)
+
+
+@pytest.mark.parametrize("tile", [6, 7, 8, 9, 10, 11, 12])
 def test_gemm_bf16_deep_pipeline_ragged(tile):
     # K not a multiple of the 32- or 64-element step, fewer steps than stages
-    for K in (40, 328):
-        c, ref = run_gemm(1, LAYOUT_KK, 264, 200, K, tile)
-        _check(c, ref, K)
+    layouts = [LAYOUT_KK, LAYOUT_KN, LAYOUT_MN] if tile >= 10 else [LAYOUT_KK]
+    for layout in layouts:
+        for K in (40, 328):
+            c, ref = run_gemm(1, layout, 264, 200, K, tile)
+            _check(c, ref, K)
