@@ -229,7 +229,9 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 
 template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, int RB, int NS, bool A_KC, bool B_KC, int EPI,
           typename TC, bool PP>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
+// Two waves per SIMD except for the 4-wave tiles whose accumulators need the
+// whole register file.
+__global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 * 128) ? 1 : 2) void gemm_kernel(GemmArgs p) {
   constexpr int THREADS = 64 * WGM * WGN;
   constexpr int NW = WGM * WGN;
   constexpr int ES = sizeof(TA);
@@ -479,8 +481,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
     static_assert(NW * 32 * RBY <= NS * STAGE, "epilogue staging must fit in the operand stages");
     char* region = smem + wave * 32 * RBY;
     __syncthreads();   // every wave is done with the operand stages
+    // Epilogues that read C (accumulate) or the saved pre-activation
+    // (dReLU^2) load those values for a whole 32-row block up front: the
+    // compiler cannot move a load above an earlier store that may alias it.
+    constexpr bool PRELOAD = EPI == EPI_ACCUM_F32 || EPI == EPI_DRELU2;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
+      floatx4 pre[PRELOAD ? 32 / RPS : 1];
+      if constexpr (PRELOAD) {
+        asm volatile("" ::: "memory");   // keep the next block's loads from being hoisted here
+#pragma unroll
+        for (int st = 0; st < 32 / RPS; ++st) {
+          // out-of-range positions load a clamped in-range address (no
+          // branches, so the array stays in registers) and are never stored
+          const int m = min(m0 + wm * WM + i * 32 + st * RPS + lane / LPR, p.M - 1);
+          const int n = min(n0 + wn * WN + (lane % LPR) * 4, p.N - 4);
+          const long off = (long)m * p.ldc + n;
+          if constexpr (EPI == EPI_ACCUM_F32) pre[st] = load4((const float*)p.C + off);
+          else pre[st] = load4((const TC*)p.aux + off);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -499,40 +519,40 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_kernel(GemmArgs p) {
         const floatx4 v = *(const floatx4*)(region + lds_off<RBY>(r, c4 * 16));
         const int m = m0 + wm * WM + i * 32 + r;
         const int n = n0 + wn * WN + c4 * 4;
-        if (m >= p.M || n >= p.N) continue;
-        const long off = (long)m * p.ldc + n;
-        if constexpr (EPI == EPI_STORE) {
-          store4((TC*)p.C + off, v);
-        } else if constexpr (EPI == EPI_STORE_F32) {
-          store4((float*)p.C + off, v);
-        } else if constexpr (EPI == EPI_ACCUM_F32) {
-          float* c = (float*)p.C + off;
-          store4(c, load4(c) + v);
-        } else if constexpr (EPI == EPI_RELU2) {
-          store4((TC*)p.C + off, v);
-          floatx4 rr;
+        if (m < p.M && n < p.N) {
+          const long off = (long)m * p.ldc + n;
+          if constexpr (EPI == EPI_STORE) {
+            store4((TC*)p.C + off, v);
+          } else if constexpr (EPI == EPI_STORE_F32) {
+            store4((float*)p.C + off, v);
+          } else if constexpr (EPI == EPI_ACCUM_F32) {
+            store4((float*)p.C + off, pre[st] + v);
+          } else if constexpr (EPI == EPI_RELU2) {
+            store4((TC*)p.C + off, v);
+            floatx4 rr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = fmaxf(v[e], 0.f);
-            rr[e] = x * x;
+            for (int e = 0; e < 4; ++e) {
+              const float x = fmaxf(v[e], 0.f);
+              rr[e] = x * x;
+            }
+            store4((TC*)p.C2 + off, rr);
+          } else if constexpr (EPI == EPI_DRELU2) {
+            const floatx4 u = pre[st];
+            floatx4 rr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[e] = v[e] * 2.f * fmaxf(u[e], 0.f);
+            store4((TC*)p.C + off, rr);
+          } else if constexpr (EPI == EPI_XENT_BWD) {
+            const float L2E = 1.4426950408889634f;
+            const float lse = p.auxf[m];
+            const int y = ((const int*)p.aux)[m];
+            floatx4 rr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[e] = (fast_exp2((v[e] - lse) * L2E) - (n + e == y ? 1.f : 0.f)) * p.beta;
+            store4((TC*)p.C + off, rr);
+          } else if constexpr (EPI == EPI_PARTIAL) {
+            store4(p.part + (long)blockIdx.z * p.M * p.N + (long)m * p.N + n, v);
           }
-          store4((TC*)p.C2 + off, rr);
-        } else if constexpr (EPI == EPI_DRELU2) {
-          const floatx4 u = load4((const TC*)p.aux + off);
-          floatx4 rr;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) rr[e] = v[e] * 2.f * fmaxf(u[e], 0.f);
-          store4((TC*)p.C + off, rr);
-        } else if constexpr (EPI == EPI_XENT_BWD) {
-          const float L2E = 1.4426950408889634f;
-          const float lse = p.auxf[m];
-          const int y = ((const int*)p.aux)[m];
-          floatx4 rr;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) rr[e] = (fast_exp2((v[e] - lse) * L2E) - (n + e == y ? 1.f : 0.f)) * p.beta;
-          store4((TC*)p.C + off, rr);
-        } else if constexpr (EPI == EPI_PARTIAL) {
-          store4(p.part + (long)blockIdx.z * p.M * p.N + (long)m * p.N + n, v);
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // staging reads done before the region is rewritten
@@ -651,8 +671,7 @@ static int launch_fp8(const GemmArgs& a, int layout, int epi, int tile, int spli
   if (layout != LAYOUT_KK) return -1;
 #define GK_F8(E)                                                                    \
   if (epi == E) {                                                                   \
-    if (tile == TILE_256x256_W8) launch_cfg<uint8_t, MF, TILE_256x256_W8, true, true, E, bf16>(a, splits, st); \
-    else launch_cfg<uint8_t, MF, TILE_128x128, true, true, E, bf16>(a, splits, st); \
+    launch_cfg<uint8_t, MF, TILE_128x128, true, true, E, bf16>(a, splits, st);      \
     return 0;                                                                       \
   }
   GK_F8(EPI_STORE)
