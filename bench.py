@@ -123,7 +123,15 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": work_per_launch / avg_s / 1e9, "peak": Mx.PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    # HBM bytes per launch of this kernel from the committed rocprofv3
+    # FETCH_SIZE / WRITE_SIZE summary, if it was taken from the current
+    # kernel sources
+    from decoder_only_transformer_fwd_amd import profiling as Pf
+    tr = Pf.traffic_lookup(os.path.join(ROOT, "profiles", f"gpt_step_{s.name}_{s.precision}_traffic.md"),
+                           dom["kernel"])
+    roof["traffic"] = None if tr is None else tr[0] + tr[1]
+    if tr is not None:
+        roof["traffic_read"], roof["traffic_written"] = tr
     roof["kernel"] = dom["kernel"]
     roof["sites"] = dom["sites"]
     roof["avg_launch_us"] = avg_s * 1e6
