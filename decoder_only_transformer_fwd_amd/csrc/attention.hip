@@ -25,6 +25,21 @@
 
 namespace gk {
 
+// Work-group -> (tile, head, batch).  Work-groups are dealt round-robin to
+// the 8 XCDs (each with its own L2); the linear id is remapped so that all
+// tiles of one (batch, head) run on the same XCD and share its K/V (or Q/dO)
+// reads from L2.  Tiles are taken in reverse so the longest causal rows
+// start first.
+__device__ __forceinline__ void attn_coords(int& tile, int& h, int& b) {
+  const int nt = gridDim.x, H = gridDim.y;
+  const int L = blockIdx.x + nt * (blockIdx.y + H * blockIdx.z);
+  const int per = nt * H * gridDim.z / 8;
+  const int Lp = (per > 0 && L < per * 8) ? (L & 7) * per + (L >> 3) : L;
+  tile = nt - 1 - Lp % nt;
+  h = (Lp / nt) % H;
+  b = Lp / nt / H;
+}
+
 // Fragment of a row-major operand: EPL contiguous elements at K offset
 // s*KM + g*EPL of `row`.
 template <typename T, int ROW_BYTES>
@@ -98,7 +113,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
-  const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int qb, h, b;
+  attn_coords(qb, h, b);
   const int Tn = a.T, W = a.window, d = a.d;
   const long row3 = 3L * d;
   const int i0 = qb * BQ, iw0 = i0 + wave * 32, i = iw0 + l32;
@@ -248,7 +264,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
-  const int kb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int kb, h, b;
+  attn_coords(kb, h, b);
   const int Tn = a.T, W = a.window, d = a.d, Tp = a.Tp;
   const long row3 = 3L * d;
   const int j0 = kb * BKV, jw0 = j0 + wave * 32, j = jw0 + l32;
@@ -403,7 +420,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
-  const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int qb, h, b;
+  attn_coords(qb, h, b);
   const int Tn = a.T, W = a.window, d = a.d, Tp = a.Tp;
   const long row3 = 3L * d;
   const int i0 = qb * BQ, iw0 = i0 + wave * 32, i = iw0 + l32;
