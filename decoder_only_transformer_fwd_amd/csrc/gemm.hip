@@ -211,6 +211,9 @@ __device__ __forceinline__ void barrier_only() {
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
+// Tiles are taken in groups of GROUP_M rows of tiles (about 1024 rows of A,
+// measured best at the step's shapes) across all tile columns.
+template <int GROUP_M>
 __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int nwg = tiles_m * tiles_n;
   // Hardware deals work-groups round-robin over 8 XCDs; give each XCD a
@@ -218,7 +221,6 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
   int tile = wg;
   const int per = nwg / 8;
   if (per > 0 && wg < per * 8) tile = (wg & 7) * per + (wg >> 3);
-  constexpr int GROUP_M = 8;
   const int group = tile / (GROUP_M * tiles_n);
   const int first_m = group * GROUP_M;
   const int gsize = min(tiles_m - first_m, GROUP_M);
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_coords<(BM >= 1024 ? 1 : 1024 / BM)>(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int kbeg = blockIdx.z * p.k_split;
