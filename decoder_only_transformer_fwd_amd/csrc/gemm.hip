@@ -394,28 +394,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
     __builtin_amdgcn_s_waitcnt(0x0070);
   } else if constexpr (NS == 2) {
     // Two stages: the next tile is requested at the top of a step and must
-    // have landed (vmcnt 0) by the barrier that ends it.  The last sub-step's
-    // MFMAs run after that barrier, behind the fragment reads of the next
-    // stage's first sub-step, so the LDS latency after each barrier is hidden.
+    // have landed (vmcnt 0) by the barrier that ends it.  (Moving the last
+    // sub-step's MFMAs behind that barrier, to overlap the next stage's first
+    // fragment reads, measured slower for the fp8 tiles and no faster for
+    // bf16.)
     if (nk > 0) {
       fetch(kbeg, 0);
       commit(0);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __syncthreads();
-    if (nk > 0) read_frags(smem, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const int s = kt & 1;
       const bool more = kt + 1 < nk;
       if (more) fetch(kbeg + (kt + 1) * BK, s ^ 1);
-      compute_head(s);
+      compute(s);
       if (more) commit(s ^ 1);
       __builtin_amdgcn_s_waitcnt(0x0070);
       __syncthreads();
-      if (more) read_frags(smem + (s ^ 1) * STAGE, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_step(1);
-      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     // NS stages, all by direct-to-LDS loads: NS-1 steps are in flight.  Every
