@@ -324,7 +324,7 @@ int build_layout(gpt_model& m) {
     m.q8row = take(BT * wide);
     m.q8T = take(BT * wide);
     m.n_slots = 12 * s.L;
-    m.amax = take((size_t)m.n_slots * 4);
+    m.amax = take((size_t)m.n_slots * AMAX_SLOT * 4);
     m.scales = take((size_t)m.n_slots * 4);
   }
   m.splitk_floats = need;
@@ -459,13 +459,19 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   void* q8row = f8 ? m.ws + m.q8row : nullptr;
   void* q8T = f8 ? m.ws + m.q8T : nullptr;
   auto slot = [](int l, int k) { return 12 * l + k; };
-  auto quant = [&](const char* site, int fmt, const void* x, int R, int C, int sl, void* q, void* qT) {
+  // Weights get their own amax pass; every activation and gradient operand's
+  // amax is folded in by the kernel that produces it (the slot's pointer is
+  // passed to that kernel), so its quantisation reads it once.
+  auto quant = [&](const char* site, int fmt, const void* x, int R, int C, int sl, void* q, void* qT,
+                   bool amax_done = true) {
     prof_begin(m, site, (double)R * C * (qT ? 4.0 : 3.0), 1,
-               std::string("amax_kernel + quant_kernel<") + (fmt == FP8_E4M3 ? "e4m3" : "e5m2") + ">");
-    fp8_amax(x, (long)R * C, amax8 + sl, st);
-    fp8_quantize(fmt, x, R, C, amax8 + sl, sc8 + sl, q, qT, st);
+               std::string(amax_done ? "" : "amax_kernel + ") + "quant_kernel<" + (fmt == FP8_E4M3 ? "0" : "1") + ">");
+    unsigned* am = amax8 + (size_t)sl * AMAX_SLOT;
+    if (!amax_done) fp8_amax(x, (long)R * C, am, st);
+    fp8_quantize(fmt, x, R, C, am, sc8 + sl, q, qT, st);
     prof_end(m);
   };
+  auto amx = [&](int l, int k) { return f8 && l >= 0 ? amax8 + (size_t)slot(l, k) * AMAX_SLOT : (unsigned*)nullptr; };
   auto gemm8 = [&](const char* site, int dty, int epi, int M, int N, int K, const void* A, const void* B, void* C,
                    long ldc, int sa, int sb, GemmArgs ex = GemmArgs{}) {
     ex.scale_a = sc8 + sa;
@@ -475,13 +481,13 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
 
   fill_f32((float*)flag, 1, 0.f, st);
   if (f8) {
-    zero_u32(amax8, m.n_slots, st);
+    zero_u32(amax8, m.n_slots * AMAX_SLOT, st);
     for (int l = 0; l < s.L; ++l) {
       auto& Ly = m.lay[l];
-      quant("fp8_quant_weights", FP8_E4M3, wp(P.Wqkv[l]), 3 * d, d, slot(l, SL_WQKV), m.ws + Ly.wq[0], m.ws + Ly.wqT[0]);
-      quant("fp8_quant_weights", FP8_E4M3, wp(P.Wo[l]), d, d, slot(l, SL_WO), m.ws + Ly.wq[1], m.ws + Ly.wqT[1]);
-      quant("fp8_quant_weights", FP8_E4M3, wp(P.W1[l]), F, d, slot(l, SL_W1), m.ws + Ly.wq[2], m.ws + Ly.wqT[2]);
-      quant("fp8_quant_weights", FP8_E4M3, wp(P.W2[l]), d, F, slot(l, SL_W2), m.ws + Ly.wq[3], m.ws + Ly.wqT[3]);
+      quant("fp8_quant_weights", FP8_E4M3, wp(P.Wqkv[l]), 3 * d, d, slot(l, SL_WQKV), m.ws + Ly.wq[0], m.ws + Ly.wqT[0], false);
+      quant("fp8_quant_weights", FP8_E4M3, wp(P.Wo[l]), d, d, slot(l, SL_WO), m.ws + Ly.wq[1], m.ws + Ly.wqT[1], false);
+      quant("fp8_quant_weights", FP8_E4M3, wp(P.W1[l]), F, d, slot(l, SL_W1), m.ws + Ly.wq[2], m.ws + Ly.wqT[2], false);
+      quant("fp8_quant_weights", FP8_E4M3, wp(P.W2[l]), d, F, slot(l, SL_W2), m.ws + Ly.wq[3], m.ws + Ly.wqT[3], false);
     }
   }
   prof_begin(m, "embed_fwd", (double)BT * d * (es_d + 4.0) + BT * 8.0, 1, KL("embed_fwd_kernel"));
@@ -491,7 +497,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     auto& Ly = m.lay[l];
     const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
     prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
-    rmsnorm_fwd(dt, h, m.ws + Ly.n1, at<float>(m, Ly.rstd1), BT, d, s.eps, st);
+    rmsnorm_fwd(dt, h, m.ws + Ly.n1, at<float>(m, Ly.rstd1), BT, d, s.eps, st, amx(l, SL_N1));
     prof_end(m);
     if (f8) {
       quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.n1, BT, d, slot(l, SL_N1), q8row, m.ws + Ly.n1T);
@@ -511,6 +517,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.d = d; aa.window = s.win[l];
     aa.scale = 1.0f / std::sqrt((float)Dh);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
+    aa.amax_o = amx(l, SL_O);
     prof_end(m);
     prof_begin(m, s.win[l] < s.T ? "attn_fwd_window" : "attn_fwd_causal", 4.0 * Dh * pairs, 0,
                KLD("attn_fwd_kernel"));
@@ -525,10 +532,11 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     }
     if (rc) return rc;
     prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
-    rmsnorm_fwd(dt, h, m.ws + Ly.n2, at<float>(m, Ly.rstd2), BT, d, s.eps, st);
+    rmsnorm_fwd(dt, h, m.ws + Ly.n2, at<float>(m, Ly.rstd2), BT, d, s.eps, st, amx(l, SL_N2));
     prof_end(m);
     GemmArgs ex{};
     ex.C2 = m.ws + Ly.g;
+    ex.amax = amx(l, SL_G);
     if (f8) {
       quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.n2, BT, d, slot(l, SL_N2), q8row, m.ws + Ly.n2T);
       if ((rc = gemm8("gemm_w1_relu2", DT_FP8_A4B4, EPI_RELU2, BT, F, d, q8row, m.ws + Ly.wq[2], m.ws + Ly.u, F,
@@ -578,12 +586,13 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                  d)))
     return rc;
   prof_begin(m, "rmsnorm_bwd", (double)BT * d * (8.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
-  rmsnorm_bwd(dt, dm, m.ws + m.nL, at<float>(m, m.rstdL), dh, dhA, BT, d, 0, st);
+  rmsnorm_bwd(dt, dm, m.ws + m.nL, at<float>(m, m.rstdL), dh, dhA, BT, d, 0, st, amx(s.L - 1, SL_DH2));
   prof_end(m);
   for (int l = s.L - 1; l >= 0; --l) {
     auto& Ly = m.lay[l];
     GemmArgs ex{};
     ex.aux = m.ws + Ly.u;
+    ex.amax = amx(l, SL_DU);
     const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
     if (f8) {
       quant("fp8_quant_grad", FP8_E5M2, dhA, BT, d, slot(l, SL_DH2), q8row, q8T);
@@ -613,7 +622,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
         return rc;
     }
     prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
-    rmsnorm_bwd(dt, dm, m.ws + Ly.n2, at<float>(m, Ly.rstd2), dh, dhA, BT, d, 1, st);
+    rmsnorm_bwd(dt, dm, m.ws + Ly.n2, at<float>(m, Ly.rstd2), dh, dhA, BT, d, 1, st, amx(l, SL_DH1));
     prof_end(m);
     if (f8) {
       quant("fp8_quant_grad", FP8_E5M2, dhA, BT, d, slot(l, SL_DH1), q8row, q8T);
@@ -636,6 +645,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     aa.qkv = m.ws + Ly.qkv; aa.qT = m.ws + Ly.qT; aa.kT = m.ws + Ly.kT; aa.vT = m.ws + Ly.vT;
     aa.o = m.ws + Ly.o; aa.lse2 = at<float>(m, Ly.lse2);
     aa.dO = m.ws + m.dO; aa.dOT = m.ws + m.dOT; aa.Dv = at<float>(m, m.Dv); aa.dqkv = m.ws + m.dqkv;
+    aa.amax_dv = amx(l, SL_DQKV);
     aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.d = d; aa.window = s.win[l];
     aa.scale = 1.0f / std::sqrt((float)Dh);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
@@ -653,7 +663,8 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     if (attn_bwd(dt, Dh, aa, 2, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
     prof_end(m);
     prof_begin(m, "rope_qknorm_bwd", (double)BT * d * 6.0 * es_d + BT * 2.0 * H * 4.0, 1, KLD("rope_qknorm_bwd_kernel"));
-    rope_qknorm_bwd(dt, m.ws + m.dqkv, m.ws + Ly.qkv, at<float>(m, Ly.rqk), cosb, sinb, s.B, s.T, H, Dh, st);
+    rope_qknorm_bwd(dt, m.ws + m.dqkv, m.ws + Ly.qkv, at<float>(m, Ly.rqk), cosb, sinb, s.B, s.T, H, Dh, st,
+                    amx(l, SL_DQKV));
     prof_end(m);
     if (f8) {
       quant("fp8_quant_grad", FP8_E5M2, m.ws + m.dqkv, BT, 3 * d, slot(l, SL_DQKV), q8row, q8T);
@@ -672,7 +683,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
         return rc;
     }
     prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
-    rmsnorm_bwd(dt, dm, m.ws + Ly.n1, at<float>(m, Ly.rstd1), dh, dhA, BT, d, 1, st);
+    rmsnorm_bwd(dt, dm, m.ws + Ly.n1, at<float>(m, Ly.rstd1), dh, dhA, BT, d, 1, st, amx(l - 1, SL_DH2));
     prof_end(m);
   }
   prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * 4.0 + BT * 8.0, 1, "sort_keys_kernel + embed_bwd_runs_kernel");
@@ -835,11 +846,12 @@ int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const vo
 int gpt_fp8_quantize(int fmt, const void* x, int rows, int cols, uint32_t* amax, float* scale, void* q, void* qT,
                      void* stream) {
   if (!x || !amax || !scale || !q) return fail(GPT_ENULL, "gpt_fp8_quantize: NULL argument");
+  if ((uintptr_t)x & 15) return fail(GPT_EALIGN, "gpt_fp8_quantize: x must be 16-byte aligned");
   if (fmt != FP8_E4M3 && fmt != FP8_E5M2) return fail(GPT_EINVAL, "gpt_fp8_quantize: fmt");
   if (rows < 1 || cols < 64 || cols % 64 || (long)rows * cols > (1L << 31))
     return fail(GPT_EINVAL, "gpt_fp8_quantize: sizes");
   hipStream_t st = (hipStream_t)stream;
-  zero_u32(amax, 1, st);
+  zero_u32(amax, AMAX_SLOT, st);
   fp8_amax(x, (long)rows * cols, amax, st);
   fp8_quantize(fmt, x, rows, cols, amax, scale, q, qT, st);
   hipError_t e = hipGetLastError();

@@ -220,6 +220,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 
   const float lt = l + __shfl_xor(l, 32, 64);
+  float om = 0.f;
   if (i < Tn) {
     const float inv = 1.0f / lt;
     T* orow = (T*)a.o + ((long)b * Tn + i) * d + h * DH;
@@ -229,7 +230,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       for (int q = 0; q < 4; ++q) {
         floatx4 v = {acc[x][4 * q] * inv, acc[x][4 * q + 1] * inv, acc[x][4 * q + 2] * inv, acc[x][4 * q + 3] * inv};
         store4(orow + x * 32 + 8 * q + 4 * g, v);
+        om = fmaxf(om, abs_max4<T>(v));
       }
+  }
+  if (a.amax_o) {
+    __syncthreads();   // every wave is done reading the K/V stages
+    block_amax<4>(a.amax_o, om, (float*)smem);
   }
   // log-sum-exp of the scaled scores, base 2
   if (g == 0 && i < a.Tp) a.lse2[((long)b * a.H + h) * a.Tp + i] = i < Tn ? m * c + fast_log2(lt) : 0.f;
@@ -384,6 +390,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnArgs a) {
     }
   }
 
+  float vm = 0.f;
   if (j < Tn) {
     T* base = (T*)a.dqkv + ((long)b * Tn + j) * row3 + h * DH;
 #pragma unroll
@@ -398,8 +405,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnArgs a) {
         if constexpr (DO_DV) {
           floatx4 vv = {dv[x][4 * q], dv[x][4 * q + 1], dv[x][4 * q + 2], dv[x][4 * q + 3]};
           store4(base + 2 * d + cc, vv);
+          vm = fmaxf(vm, abs_max4<T>(vv));
         }
       }
+  }
+  if constexpr (DO_DV) {
+    if (a.amax_dv) {
+      __syncthreads();   // every wave is done reading the stages
+      block_amax<4>(a.amax_dv, vm, (float*)smem);
+    }
   }
 }
 

@@ -176,6 +176,39 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// A tensor's running max |x| is kept in AMAX_WAYS words (bit patterns of
+// non-negative floats, all starting at 0); writers spread their atomics over
+// the words so that thousands of waves do not queue on one address, and the
+// reader takes the max of all of them.  Max is order-independent, so the
+// result is deterministic.
+constexpr int AMAX_WAYS = 64;
+__device__ __forceinline__ int amax_way() {
+  return (blockIdx.x + blockIdx.y * 17 + blockIdx.z * 31) & (AMAX_WAYS - 1);
+}
+// Fold the work-group's largest |value| in: one atomic per work-group of NW
+// waves, reduced through `red` (NW floats of LDS).  Every thread of the
+// work-group must call it.
+template <int NW>
+__device__ __forceinline__ void block_amax(unsigned* amax, float m, float* red) {
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) r = fmaxf(r, red[w]);
+    atomicMax(amax + amax_way(), __float_as_uint(r));
+  }
+}
+// Largest |x_e| of 4 values after rounding to T (the values actually stored).
+template <typename T>
+__device__ __forceinline__ float abs_max4(floatx4 v) {
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(to_f32(from_f32<T>(v[e]))));
+  return m;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -33,44 +33,58 @@ __global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restric
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ y,
                                                           float* __restrict__ rstd, int rows, int d,
-                                                          float eps) {
+                                                          float eps, unsigned* __restrict__ amax) {
+  __shared__ float red[4];
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const float* xr = x + (long)row * d;
-  float ss = 0.f;
-  for (int c = lane * 4; c < d; c += 256) {
-    const floatx4 v = load4(xr + c);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  float m = 0.f;
+  if (row < rows) {
+    const float* xr = x + (long)row * d;
+    float ss = 0.f;
+    for (int c = lane * 4; c < d; c += 256) {
+      const floatx4 v = load4(xr + c);
+      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int c = lane * 4; c < d; c += 256) {
+      const floatx4 v = load4(xr + c) * r;
+      store4(y + (long)row * d + c, v);
+      if (amax) m = fmaxf(m, abs_max4<T>(v));
+    }
+    if (lane == 0) rstd[row] = r;
   }
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = lane * 4; c < d; c += 256) store4(y + (long)row * d + c, load4(xr + c) * r);
-  if (lane == 0) rstd[row] = r;
+  if (amax) block_amax<4>(amax, m, red);
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __restrict__ y,
                                                           const float* __restrict__ rstd, float* __restrict__ dx,
-                                                          T* __restrict__ dxa, int rows, int d, int accumulate) {
+                                                          T* __restrict__ dxa, int rows, int d, int accumulate,
+                                                          unsigned* __restrict__ amax) {
+  __shared__ float red[4];
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const long base = (long)row * d;
-  float dot = 0.f;
-  for (int c = lane * 4; c < d; c += 256) {
-    const floatx4 a = load4(dy + base + c);
-    const floatx4 b = load4(y + base + c);
-    dot += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+  float m = 0.f;
+  if (row < rows) {
+    const long base = (long)row * d;
+    float dot = 0.f;
+    for (int c = lane * 4; c < d; c += 256) {
+      const floatx4 a = load4(dy + base + c);
+      const floatx4 b = load4(y + base + c);
+      dot += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+    }
+    dot = wave_sum(dot) / (float)d;
+    const float r = rstd[row];
+    for (int c = lane * 4; c < d; c += 256) {
+      floatx4 g = (load4(dy + base + c) - load4(y + base + c) * dot) * r;
+      if (accumulate) g += load4(dx + base + c);
+      store4(dx + base + c, g);
+      store4(dxa + base + c, g);
+      if (amax) m = fmaxf(m, abs_max4<T>(g));
+    }
   }
-  dot = wave_sum(dot) / (float)d;
-  const float r = rstd[row];
-  for (int c = lane * 4; c < d; c += 256) {
-    floatx4 g = (load4(dy + base + c) - load4(y + base + c) * dot) * r;
-    if (accumulate) g += load4(dx + base + c);
-    store4(dx + base + c, g);
-    store4(dxa + base + c, g);
-  }
+  if (amax) block_amax<4>(amax, m, red);
 }
 
 // ------------------------------------------------------------------ rotary + QK norm
@@ -147,17 +161,19 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(T* __restrict__ dq
                                                               const float* __restrict__ rstd_qk,
                                                               const float* __restrict__ cosb,
                                                               const float* __restrict__ sinb, int rows, int Tn,
-                                                              int H) {
+                                                              int H, unsigned* __restrict__ amax) {
   constexpr int HALF = DH / 2;
   constexpr int VPP = 64 / HALF;   // head vectors per pass
+  __shared__ float red[4];
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
   const int t = row % Tn;
   const int sub = lane / HALF, i = lane % HALF;
   const int d = H * DH;
-  const float c = cosb[t * HALF + i], s = sinb[t * HALF + i];
-  for (int v0 = 0; v0 < 2 * H; v0 += VPP) {
+  const bool ok = row < rows;
+  const float c = ok ? cosb[t * HALF + i] : 0.f, s = ok ? sinb[t * HALF + i] : 0.f;
+  float m = 0.f;
+  for (int v0 = 0; ok && v0 < 2 * H; v0 += VPP) {
     const int v = v0 + sub;       // 0..2H-1: q heads then k heads
     if (v >= 2 * H) continue;
     const long off = (long)row * 3 * d + (long)v * DH;  // q at h*DH, k at d + h*DH
@@ -166,9 +182,12 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(T* __restrict__ dq
     const float dot = group_sum<HALF>(g1 * y1 + g2 * y2) / (float)DH;
     const float r = rstd_qk[(long)row * 2 * H + v];
     const float d1 = r * (g1 - y1 * dot), d2 = r * (g2 - y2 * dot);
-    dqkv[off + i] = from_f32<T>(d1 * c + d2 * s);
-    dqkv[off + i + HALF] = from_f32<T>(-d1 * s + d2 * c);
+    const T o1 = from_f32<T>(d1 * c + d2 * s), o2 = from_f32<T>(-d1 * s + d2 * c);
+    dqkv[off + i] = o1;
+    dqkv[off + i + HALF] = o2;
+    m = fmaxf(m, fmaxf(fabsf(to_f32(o1)), fabsf(to_f32(o2))));
   }
+  if (amax) block_amax<4>(amax, m, red);
 }
 
 // D[b,h,t] = sum_c dO[t, h*Dh + c] * O[t, h*Dh + c]; dO^T copy [B][H][Dh][Tp].
@@ -324,23 +343,24 @@ void embed_fwd(int dtype, const int32_t* tokens, const int32_t* targets, const v
                        vocab, flag);
 }
 
-void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps, hipStream_t st) {
+void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps, hipStream_t st,
+                 unsigned* amax) {
   dim3 g((rows + 3) / 4);
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, g, dim3(256), 0, st, x, (bf16*)y, rstd, rows, d, eps);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, g, dim3(256), 0, st, x, (bf16*)y, rstd, rows, d, eps, amax);
   else
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, g, dim3(256), 0, st, x, (float*)y, rstd, rows, d, eps);
+    hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, g, dim3(256), 0, st, x, (float*)y, rstd, rows, d, eps, amax);
 }
 
 void rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* rstd, float* dx, void* dxa, int rows,
-                 int d, int accumulate, hipStream_t st) {
+                 int d, int accumulate, hipStream_t st, unsigned* amax) {
   dim3 g((rows + 3) / 4);
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, g, dim3(256), 0, st, dy, (const bf16*)y, rstd, dx, (bf16*)dxa,
-                       rows, d, accumulate);
+                       rows, d, accumulate, amax);
   else
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, g, dim3(256), 0, st, dy, (const float*)y, rstd, dx,
-                       (float*)dxa, rows, d, accumulate);
+                       (float*)dxa, rows, d, accumulate, amax);
 }
 
 template <typename T, int DH>
@@ -362,16 +382,16 @@ void rope_qknorm_fwd(int dtype, void* qkv, float* rq, void* qT, void* kT, void* 
 
 template <typename T, int DH>
 static void rope_bwd_t(void* dqkv, const void* qkv, const float* rq, const float* c, const float* s, int B, int T_,
-                       int H, hipStream_t st) {
+                       int H, hipStream_t st, unsigned* amax) {
   const int rows = B * T_;
   hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, DH>), dim3((rows + 3) / 4), dim3(256), 0, st, (T*)dqkv,
-                     (const T*)qkv, rq, c, s, rows, T_, H);
+                     (const T*)qkv, rq, c, s, rows, T_, H, amax);
 }
 
 void rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const float* rq, const float* c, const float* s,
-                     int B, int T_, int H, int Dh, hipStream_t st) {
+                     int B, int T_, int H, int Dh, hipStream_t st, unsigned* amax) {
 #define RB(TT, D) \
-  if (Dh == D) return rope_bwd_t<TT, D>(dqkv, qkv, rq, c, s, B, T_, H, st);
+  if (Dh == D) return rope_bwd_t<TT, D>(dqkv, qkv, rq, c, s, B, T_, H, st, amax);
   if (dtype == DT_BF16) { RB(bf16, 32) RB(bf16, 64) RB(bf16, 128) }
   else { RB(float, 32) RB(float, 64) RB(float, 128) }
 #undef RB

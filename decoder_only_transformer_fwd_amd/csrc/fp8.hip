@@ -15,6 +15,8 @@
 
 namespace gk {
 
+static_assert(AMAX_SLOT == AMAX_WAYS, "amax slot size must match the device-side spreading");
+
 __device__ __forceinline__ float fp8_max(int fmt) { return fmt == FP8_E4M3 ? 448.f : 57344.f; }
 
 // Two fp32 values -> two codes in the low 16 bits (round to nearest even).
@@ -23,9 +25,8 @@ __device__ __forceinline__ uint32_t cvt2(int fmt, float a, float b) {
                          : __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
 }
 
-// amax[0] = max |x| (as the bit pattern of a non-negative float; *amax must
-// start at 0).  Each work-group reduces its share through LDS and issues one
-// atomic; max is order-independent, so the result is deterministic.
+// Folds max |x| into the AMAX_WAYS words at amax (zeroed beforehand).  Each
+// work-group reduces its share through LDS and issues one atomic.
 __global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, long n, unsigned* amax) {
   __shared__ float red[4];
   float m = 0.f;
@@ -40,7 +41,8 @@ __global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, l
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) atomicMax(amax, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+  if (threadIdx.x == 0)
+    atomicMax(amax + (blockIdx.x & (AMAX_WAYS - 1)), __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 // Grid (C/64, ceil(R/64)), 256 threads: a 64x64 tile; thread t converts 16
@@ -51,8 +53,14 @@ __global__ __launch_bounds__(256) void quant_kernel(const bf16* __restrict__ x, 
                                                     const unsigned* __restrict__ amax, float* scale_out,
                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ qT) {
   __shared__ uint8_t tile[64][64 + 4];
+  __shared__ float amax_s;
   const float fmax = fp8_max(FMT);
-  const float a = __uint_as_float(amax[0]);
+  if (threadIdx.x < 64) {
+    const float w = wave_max(__uint_as_float(amax[threadIdx.x & (AMAX_WAYS - 1)]));
+    if (threadIdx.x == 0) amax_s = w;
+  }
+  __syncthreads();
+  const float a = amax_s;
   const float s = a > 0.f ? fminf(fmax / a, 0x1p64f) : 1.f;
   if (scale_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) scale_out[0] = s;
   const int t = threadIdx.x;

@@ -483,6 +483,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
     // (dReLU^2) load those values for a whole 32-row block up front: the
     // compiler cannot move a load above an earlier store that may alias it.
     constexpr bool PRELOAD = EPI == EPI_ACCUM_F32 || EPI == EPI_DRELU2;
+    float amax_acc = 0.f;   // RELU2 / DRELU2: largest |stored activation|
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       floatx4 pre[PRELOAD ? 32 / RPS : 1];
@@ -534,12 +535,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
               rr[e] = x * x;
             }
             store4((TC*)p.C2 + off, rr);
+            amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
           } else if constexpr (EPI == EPI_DRELU2) {
             const floatx4 u = pre[st];
             floatx4 rr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) rr[e] = v[e] * 2.f * fmaxf(u[e], 0.f);
             store4((TC*)p.C + off, rr);
+            amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
           } else if constexpr (EPI == EPI_XENT_BWD) {
             const float L2E = 1.4426950408889634f;
             const float lse = p.auxf[m];
@@ -555,6 +558,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // staging reads done before the region is rewritten
       __builtin_amdgcn_wave_barrier();
+    }
+    if constexpr (EPI == EPI_RELU2 || EPI == EPI_DRELU2) {
+      if (p.amax) {
+        __syncthreads();   // every wave is done with its staging region
+        block_amax<NW>(p.amax, amax_acc, (float*)smem);
+      }
     }
   }
 }

@@ -69,6 +69,7 @@ struct GemmArgs {
   float beta;      // EPI_XENT_BWD: 1 / rows
   int k_split;     // K elements handled per blockIdx.z
   int nblk;        // EPI_XENT_FWD: number of column blocks of width BN/2
+  unsigned* amax;  // EPI_RELU2 / EPI_DRELU2: if set, max |stored g / du| is folded in (float bits)
 };
 
 int gemm_launch(const GemmArgs& a, int dtype, int layout, int epi, int tile, int splits,
@@ -80,16 +81,17 @@ void splitk_reduce(const float* part, int splits, long mn, float* out, int accum
 // Also checks that every token and target id is in [0, vocab) (sets *flag).
 void embed_fwd(int dtype, const int32_t* tokens, const int32_t* targets, const void* E, float* h, int rows, int d,
                int vocab, int* flag, hipStream_t st);
+// amax (optional): max |stored value| folded in as float bits (for fp8 scaling)
 void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps,
-                 hipStream_t st);
+                 hipStream_t st, unsigned* amax = nullptr);
 // dx (+)= r * (dy - y * mean(dy*y)); also writes dx in the activation type.
 void rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* rstd, float* dx,
-                 void* dx_act, int rows, int d, int accumulate, hipStream_t st);
+                 void* dx_act, int rows, int d, int accumulate, hipStream_t st, unsigned* amax = nullptr);
 void rope_qknorm_fwd(int dtype, void* qkv, float* rstd_qk, void* qT, void* kT, void* vT,
                      const float* cosb, const float* sinb, int B, int T, int Tp, int H, int Dh,
                      float eps, hipStream_t st);
 void rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const float* rstd_qk, const float* cosb,
-                     const float* sinb, int B, int T, int H, int Dh, hipStream_t st);
+                     const float* sinb, int B, int T, int H, int Dh, hipStream_t st, unsigned* amax = nullptr);
 void attn_bwd_pre(int dtype, const void* dO, const void* O, float* Dv, void* dOT, int B, int T, int Tp,
                   int H, int Dh, hipStream_t st);
 void xent_reduce(const float* part, const float* tgt, int rows, int nblk, float* lse, float* row_loss,
@@ -101,7 +103,9 @@ void fill_f32(float* p, long n, float v, hipStream_t st);
 
 // ---------------------------------------------------------------- fp8
 void zero_u32(unsigned* p, int n, hipStream_t st);
-// *amax (zeroed beforehand) = max |x| over n bf16 values, as float bits.
+// Per-tensor amax: AMAX_SLOT words per tensor (see wave_amax), zeroed before
+// the tensor is produced; fp8_amax folds in max |x| over n bf16 values.
+constexpr int AMAX_SLOT = 64;
 void fp8_amax(const void* x, long n, unsigned* amax, hipStream_t st);
 // x [R][C] bf16 (C a multiple of 64) -> codes q [R][C] and, if qT, [C][R].
 void fp8_quantize(int fmt, const void* x, int R, int C, const unsigned* amax, float* scale_out, void* q, void* qT,
@@ -121,6 +125,8 @@ struct AttnArgs {
   void* dqkv;        // [B*T][3*d]
   int B, T, Tp, H, d, window;
   float scale_log2;  // log2(e) / sqrt(Dh)
+  unsigned* amax_o;   // forward: if set, max |stored o| (float bits)
+  unsigned* amax_dv;  // dV pass: if set, max |stored dv| (float bits)
   float scale;       // 1 / sqrt(Dh)
 };
 int attn_fwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st);

@@ -146,10 +146,11 @@ int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const vo
  *   q[r][c] = OCP code of x[r][c] * s (fp32 product) rounded to nearest even
  *   with saturation to +-fmax.
  * fmt: 0 = E4M3, 1 = E5M2.  x: device bf16 [rows, cols], cols a multiple of
- * 64.  amax: device uint32 scratch (one element, overwritten).  scale: device
- * float, receives s.  q: device uint8 [rows, cols]; qT: NULL or device uint8
- * [cols, rows] receiving the transposed codes.  Enqueued on `stream`; does
- * not synchronise. */
+ * 64, 16-byte aligned.  amax: device uint32 scratch of 64 elements
+ * (overwritten).  scale: device float, receives s.  q: device uint8
+ * [rows, cols]; qT: NULL or device uint8 [cols, rows] receiving the
+ * transposed codes.  Enqueued on `stream`; does not synchronise.
+ * GPT_EALIGN for a misaligned x. */
 int gpt_fp8_quantize(int fmt, const void* x, int rows, int cols, uint32_t* amax, float* scale, void* q, void* qT,
                      void* stream);
 

@@ -27,7 +27,7 @@ def _dev_bf16(torch, x64):
 def _quantize(torch, G, fmt, xt, R, C, transposed=True):
     q = torch.empty((R, C), dtype=torch.uint8, device="cuda")
     qT = torch.empty((C, R), dtype=torch.uint8, device="cuda") if transposed else None
-    amax = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    amax = torch.full((64,), 12345, dtype=torch.int32, device="cuda")   # scratch, overwritten
     scale = torch.zeros(1, dtype=torch.float32, device="cuda")
     G.gpt_fp8_quantize(fmt, xt.data_ptr(), R, C, amax.data_ptr(), scale.data_ptr(), q.data_ptr(),
                        qT.data_ptr() if transposed else 0, torch.cuda.current_stream().cuda_stream)
