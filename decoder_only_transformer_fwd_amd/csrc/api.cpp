@@ -127,9 +127,10 @@ struct GemmPlan {
 
 
 // Tile and split-K choice, set from measurements of this kernel on MI355X at
-// the step's shapes: 8-wave 256x256 tiles for forward products and wide
-// input-gradient products, 128x128 (two work-groups per CU) for the narrow
-// input gradients, and the 256x256 ping-pong tile for bf16 weight gradients (K = B*T, few
+// the step's shapes: 8-wave 256x256 tiles for wide products, the 256x256
+// ping-pong tile for narrow input gradients with a long K, 128x128 (two
+// work-groups per CU) for narrow short products, and the ping-pong tile for
+// bf16 weight gradients (K = B*T, few
 // output tiles), which are split along K by a cost model: waves of
 // work-groups (512 resident at two per CU, 256 at one) times K steps per
 // split, plus the fp32 partial-sum reduction at ~5 TB/s.
@@ -142,9 +143,11 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   } else if (dtype == DT_F32) {
     g.tile = (long)M * N >= 256L * 128 * 128 ? TILE_128x128 : TILE_64x64;
   } else if (layout == LAYOUT_KK) {
-    g.tile = TILE_256x256_W8;
+    // 8-wave 256x256 unless both N and K are short
+    g.tile = N >= 4096 || K >= 4096 ? TILE_256x256_W8 : TILE_128x128;
   } else if (layout == LAYOUT_KN) {
-    g.tile = N >= 4096 ? TILE_256x256_W8 : TILE_128x128;
+    // wide: 8-wave 256x256; narrow with a long K: ping-pong 256x256
+    g.tile = N >= 4096 ? TILE_256x256_W8 : K >= 6144 ? TILE_256x256_PP4 : TILE_128x128;
   } else if (layout == LAYOUT_MN) {
     g.tile = TILE_256x256_PP4;
   } else {

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       for (int q = 0; q < 4; ++q) {
         floatx4 v = {acc[x][4 * q] * inv, acc[x][4 * q + 1] * inv, acc[x][4 * q + 2] * inv, acc[x][4 * q + 3] * inv};
         store4(orow + x * 32 + 8 * q + 4 * g, v);
-        om = fmaxf(om, abs_max4<T>(v));
+        if (a.amax_o) om = fmaxf(om, abs_max4<T>(v));
       }
   }
   if (a.amax_o) {
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 // accumulators at one wave per SIMD, even though the scores are computed in
 // both passes.
 template <typename T, int DH, int BQ, int MODE>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(AttnArgs a) {
   typedef Mfma<T> MF;
   static_assert(MODE == 1 || MODE == 2, "MODE 1 = dV pass, MODE 2 = dK pass");
   constexpr bool DO_DV = MODE == 1, DO_DK = MODE == 2;
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnArgs a) {
         if constexpr (DO_DV) {
           floatx4 vv = {dv[x][4 * q], dv[x][4 * q + 1], dv[x][4 * q + 2], dv[x][4 * q + 3]};
           store4(base + 2 * d + cc, vv);
-          vm = fmaxf(vm, abs_max4<T>(vv));
+          if (a.amax_dv) vm = fmaxf(vm, abs_max4<T>(vv));
         }
       }
   }

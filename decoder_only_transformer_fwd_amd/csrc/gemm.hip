@@ -535,14 +535,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
               rr[e] = x * x;
             }
             store4((TC*)p.C2 + off, rr);
-            amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
+            if (p.amax) amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
           } else if constexpr (EPI == EPI_DRELU2) {
             const floatx4 u = pre[st];
             floatx4 rr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) rr[e] = v[e] * 2.f * fmaxf(u[e], 0.f);
             store4((TC*)p.C + off, rr);
-            amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
+            if (p.amax) amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
           } else if constexpr (EPI == EPI_XENT_BWD) {
             const float L2E = 1.4426950408889634f;
             const float lse = p.auxf[m];
