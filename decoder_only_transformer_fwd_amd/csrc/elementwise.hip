@@ -154,6 +154,99 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qk
   }
 }
 
+// The same for bf16 heads of 128: grid (ceil(T/64), H, B), 256 threads.
+// Thread (p, c) = (tid / 8, tid % 8) owns tokens 2p and 2p+1 of the tile and
+// the 16-byte chunks c and c+8 of each head vector (elements 8c.. and
+// 64+8c.., the rotation pairs).  The head's sum of squares is a reduction over
+// the 8 lanes sharing p.  The transposed copies go through LDS as 4-byte words
+// holding one dimension of two consecutive tokens; the word stride per
+// dimension is odd (33), so both the writes and the row reads are free of
+// bank conflicts.
+__global__ __launch_bounds__(256) void rope_qknorm_fwd128_kernel(bf16* __restrict__ qkv, float* __restrict__ rstd_qk,
+                                                                 bf16* __restrict__ qT, bf16* __restrict__ kT,
+                                                                 bf16* __restrict__ vT, const float* __restrict__ cosb,
+                                                                 const float* __restrict__ sinb, int Tn, int Tp,
+                                                                 int H, float eps) {
+  constexpr int DH = 128, HALF = 64, S = 33;
+  __shared__ uint32_t tile[DH * S];
+  const int t0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, p = tid >> 3, c = tid & 7;
+  const int d = H * DH;
+  const long row3 = 3L * d;
+  for (int part = 0; part < 3; ++part) {
+    const int col = part * d + h * DH;
+    float x[2][16];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = t0 + 2 * p + u;
+      bf16* px = qkv + ((long)b * Tn + t) * row3 + col;
+      bf16x8 lo, hi;
+      if (t < Tn) {
+        lo = *(const bf16x8*)(px + 8 * c);
+        hi = *(const bf16x8*)(px + HALF + 8 * c);
+      } else {
+        lo = hi = bf16x8{};
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[u][e] = (float)lo[e];
+        x[u][8 + e] = (float)hi[e];
+      }
+      if (part < 2) {
+        float cs[8], sn[8];
+        if (t < Tn) {
+          *(floatx4*)&cs[0] = *(const floatx4*)(cosb + (long)t * HALF + 8 * c);
+          *(floatx4*)&cs[4] = *(const floatx4*)(cosb + (long)t * HALF + 8 * c + 4);
+          *(floatx4*)&sn[0] = *(const floatx4*)(sinb + (long)t * HALF + 8 * c);
+          *(floatx4*)&sn[4] = *(const floatx4*)(sinb + (long)t * HALF + 8 * c + 4);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cs[e] = sn[e] = 0.f;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float r1 = x[u][e] * cs[e] - x[u][8 + e] * sn[e];
+          const float r2 = x[u][e] * sn[e] + x[u][8 + e] * cs[e];
+          x[u][e] = r1;
+          x[u][8 + e] = r2;
+          ss += r1 * r1 + r2 * r2;
+        }
+        ss = group_sum<8>(ss);
+        const float r = 1.0f / sqrtf(ss / (float)DH + eps);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[u][e] *= r;
+        if (t < Tn) {
+          bf16x8 ylo, yhi;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ylo[e] = (bf16)x[u][e];
+            yhi[e] = (bf16)x[u][8 + e];
+          }
+          *(bf16x8*)(px + 8 * c) = ylo;
+          *(bf16x8*)(px + HALF + 8 * c) = yhi;
+          if (c == 0) rstd_qk[((long)b * Tn + t) * 2 * H + part * H + h] = r;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int dim = (e < 8 ? 8 * c : HALF + 8 * c) + (e & 7);
+      const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[0][e]) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[1][e]) << 16);
+      tile[dim * S + p] = w;
+    }
+    __syncthreads();
+    bf16* dst = (part == 0 ? qT : (part == 1 ? kT : vT)) + ((long)b * H + h) * DH * Tp + t0;
+#pragma unroll
+    for (int k = 0; k < DH / 8; ++k) {
+      const int dim = (tid >> 5) + 8 * k, wd = tid & 31;
+      *(uint32_t*)(dst + (long)dim * Tp + 2 * wd) = tile[dim * S + wd];
+    }
+    __syncthreads();
+  }
+}
+
 // dq' = r * (g - y * mean(g*y)), then the inverse rotation; in place on the
 // q and k columns of dqkv.  One wave per token row.
 template <typename T, int DH>
@@ -307,23 +400,53 @@ __global__ __launch_bounds__(1024) void sort_keys_kernel(const int32_t* __restri
   for (int i = threadIdx.x; i < rows; i += 1024) keys_out[i] = sk[i];
 }
 
-__global__ __launch_bounds__(64) void embed_bwd_runs_kernel(const uint32_t* __restrict__ keys,
-                                                            const float* __restrict__ dh, float* __restrict__ dE,
-                                                            int rows, int d, int pbits, int vocab) {
+// One work-group per (run head, 256-column slice): the run's end is found by
+// binary search over the sorted keys, then wave w sums rows w, w+4, w+8, ...
+// of the run (four loads in flight per lane) and the four partial sums are
+// added in wave order, so the result does not depend on timing.
+__global__ __launch_bounds__(256) void embed_bwd_runs_kernel(const uint32_t* __restrict__ keys,
+                                                             const float* __restrict__ dh, float* __restrict__ dE,
+                                                             int rows, int d, int pbits, int vocab) {
+  __shared__ floatx4 part[3][64];
   const int i = blockIdx.x;
   const uint32_t id = keys[i] >> pbits;
-  if (id >= (uint32_t)vocab) return;                     // invalid id
+  if (id >= (uint32_t)vocab) return;                     // invalid id (uniform over the work-group)
   if (i > 0 && (keys[i - 1] >> pbits) == id) return;   // not a run head
-  const uint32_t pmask = (1u << pbits) - 1u;
-  const int c = blockIdx.y * 256 + threadIdx.x * 4;
-  if (c >= d) return;
-  floatx4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int j = i; j < rows; ++j) {
-    const uint32_t kk = keys[j];
-    if ((kk >> pbits) != id) break;
-    s += load4(dh + (long)(kk & pmask) * d + c);
+  const int c = blockIdx.y * 256 + (threadIdx.x & 63) * 4;
+  const int w = threadIdx.x >> 6;
+  // end of the run: first index whose key belongs to a larger id
+  const uint32_t bound = (id + 1u) << pbits;
+  int lo = i + 1, hi = rows;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (keys[mid] < bound) lo = mid + 1;
+    else hi = mid;
   }
-  store4(dE + (long)id * d + c, s);
+  const int end = lo;
+  const uint32_t pmask = (1u << pbits) - 1u;
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+  if (c < d) {
+    int j = i + w;
+    for (; j + 12 < end; j += 16) {
+      const floatx4 a0 = load4(dh + (long)(keys[j] & pmask) * d + c);
+      const floatx4 a1 = load4(dh + (long)(keys[j + 4] & pmask) * d + c);
+      const floatx4 a2 = load4(dh + (long)(keys[j + 8] & pmask) * d + c);
+      const floatx4 a3 = load4(dh + (long)(keys[j + 12] & pmask) * d + c);
+      s += a0;
+      s += a1;
+      s += a2;
+      s += a3;
+    }
+    for (; j < end; j += 4) s += load4(dh + (long)(keys[j] & pmask) * d + c);
+  }
+  if (w > 0) part[w - 1][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (w == 0 && c < d) {
+    s += part[0][threadIdx.x];
+    s += part[1][threadIdx.x];
+    s += part[2][threadIdx.x];
+    store4(dE + (long)id * d + c, s);
+  }
 }
 
 __global__ __launch_bounds__(256) void fill_f32_kernel(float* p, long n, float v) {
@@ -367,6 +490,11 @@ template <typename T, int DH>
 static void rope_fwd_t(void* qkv, float* rq, void* qT, void* kT, void* vT, const float* c, const float* s, int B,
                        int T_, int Tp, int H, float eps, hipStream_t st) {
   dim3 g((T_ + 63) / 64, H, B);
+  if constexpr (sizeof(T) == 2 && DH == 128) {
+    hipLaunchKernelGGL(rope_qknorm_fwd128_kernel, g, dim3(256), 0, st, (bf16*)qkv, rq, (bf16*)qT, (bf16*)kT,
+                       (bf16*)vT, c, s, T_, Tp, H, eps);
+    return;
+  }
   hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, DH>), g, dim3(256), 0, st, (T*)qkv, rq, (T*)qT, (T*)kT, (T*)vT, c,
                      s, T_, Tp, H, eps);
 }
@@ -439,7 +567,7 @@ void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int 
   }
   hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), n2 * sizeof(uint32_t), st, tokens, rows, pbits, n2,
                      vocab, keys);
-  hipLaunchKernelGGL(embed_bwd_runs_kernel, dim3(rows, (d + 255) / 256), dim3(64), 0, st, keys, dh, dE, rows, d,
+  hipLaunchKernelGGL(embed_bwd_runs_kernel, dim3(rows, (d + 255) / 256), dim3(256), 0, st, keys, dh, dE, rows, d,
                      pbits, vocab);
 }
 
