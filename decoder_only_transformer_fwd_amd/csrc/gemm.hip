@@ -320,9 +320,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
   };
   constexpr int KK = BK / KM;
   static_assert(KK % 2 == 0, "fragment double-buffering assumes an even number of K sub-steps");
-  // fragment buffers: two (double-buffered sub-steps), or in the ping-pong
-  // schedule one per sub-step of a whole K step
-  constexpr int FBUF = PP ? KK : 2;
+  // fragment buffers: two, double-buffering the sub-steps, or in the
+  // ping-pong schedule one per sub-step of a phase (two sub-steps)
+  constexpr int PSUB = 2;             // ping-pong: K sub-steps per phase
+  constexpr int FBUF = PP ? PSUB : 2;
   typename MF::frag af[FBUF][MB], bfr[FBUF][NB];
   auto read_frags = [&](const char* a_s, int kk, int buf) {
 #pragma unroll
@@ -369,6 +370,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
     constexpr int LPS = (A_KC ? DmaLoader<ES, BM, LW, RB>::PER_WAVE : DmaTrLoader<ES, BM, LW, BK>::PER_WAVE) +
                         (B_KC ? DmaLoader<ES, BN, LW, RB>::PER_WAVE : DmaTrLoader<ES, BN, LW, BK>::PER_WAVE);
     const bool loader = wave < LW;
+    static_assert(KK % PSUB == 0, "whole phases per K step");
     if (loader) {
 #pragma unroll
       for (int st = 0; st < NS - 1; ++st) fetch(kbeg + st * BK, st);
@@ -379,16 +381,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
     for (int kt = 0; kt < nk; ++kt) {
       const char* a_s = smem + (kt % NS) * STAGE;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) read_frags(a_s, kk, kk);
-      if (loader) fetch(kbeg + (kt + NS - 1) * BK, (kt + NS - 1) % NS);
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): fragments are in registers
-      barrier_only();
-      __builtin_amdgcn_sched_barrier(0);
+      for (int ph = 0; ph < KK / PSUB; ++ph) {
+        // memory phase: this phase's fragments into registers (and, at the
+        // start of a step, the copies for the stage NS-1 steps ahead)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) mma_step(kk);
-      __builtin_amdgcn_sched_barrier(0);
-      if (loader) __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));   // the next stage has landed
-      barrier_only();
+        for (int u = 0; u < PSUB; ++u) read_frags(a_s, ph * PSUB + u, u);
+        if (ph == 0 && loader) fetch(kbeg + (kt + NS - 1) * BK, (kt + NS - 1) % NS);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): fragments are in registers
+        barrier_only();
+        // compute phase
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < PSUB; ++u) mma_step(u);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ph == KK / PSUB - 1 && loader)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));   // the next stage has landed
+        barrier_only();
+      }
     }
     if (loader) barrier_only();
     __builtin_amdgcn_s_waitcnt(0x0070);
