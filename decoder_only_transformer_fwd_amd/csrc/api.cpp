@@ -153,30 +153,38 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   } else {
     g.tile = TILE_128x128;
   }
-  // fp8 weight gradients are K-contiguous products with K = B*T
+  // Weight gradients (and fp8 weight gradients, K-contiguous with K = B*T):
+  // split K by the cost model, over the candidate tiles (bf16: the ping-pong
+  // 256x256 tile, or 128x128 for small outputs that need many splits).
   if (layout == LAYOUT_MN || (f8 && K >= 4096)) {
-    const bool pp = g.tile == TILE_256x256_PP4;
-    const long tiles = (long)((M + tile_bm(g.tile) - 1) / tile_bm(g.tile)) * ((N + tile_bn(g.tile) - 1) / tile_bn(g.tile));
-    const long slots = dtype == DT_F32 || pp ? 256 : 512;
-    // one K step of one tile, seconds (the ping-pong tile steps 32 deep)
-    const double t_step = dtype == DT_F32 ? 4e-6 : f8 ? 1.5e-6 : pp ? 0.95e-6 : 1.34e-6;
-    const int step = pp ? 32 : bk;
     double best = 1e300;
-    const int cand[6] = {1, 2, 3, 4, 6, 8};
-    const int ncand = pp ? 4 : 6;   // deeper splits lose to the reduction at 256x256
-    for (int c = 0; c < ncand; ++c) {
-      const int sp = cand[c];
-      int ks = (K + sp - 1) / sp;
-      ks = (ks + bk - 1) / bk * bk;
-      const int real = (K + ks - 1) / ks;
-      if (real != sp && sp > 1) continue;
-      const long waves = (tiles * sp + slots - 1) / slots;
-      double t = (double)waves * ((ks + step - 1) / step) * t_step;
-      if (sp > 1) t += (sp + 1.0) * M * (double)N * 4.0 / 5e12;
-      if (t < best) {
-        best = t;
-        g.splits = sp;
-        g.k_split = ks;
+    const int tile_cand[2] = {g.tile, TILE_128x128};
+    const int ntile = (layout == LAYOUT_MN && dtype == DT_BF16) ? 2 : 1;
+    for (int ti = 0; ti < ntile; ++ti) {
+      const int tile = tile_cand[ti];
+      const bool pp = tile == TILE_256x256_PP4;
+      const long tiles = (long)((M + tile_bm(tile) - 1) / tile_bm(tile)) * ((N + tile_bn(tile) - 1) / tile_bn(tile));
+      const long slots = dtype == DT_F32 || pp ? 256 : 512;
+      // one K step of one tile, seconds (the ping-pong tile steps 32 deep)
+      const double t_step = dtype == DT_F32 ? 4e-6 : f8 ? 1.5e-6 : pp ? 0.95e-6 : 1.34e-6;
+      const int step = pp ? 32 : bk;
+      const int cand[9] = {1, 2, 3, 4, 6, 8, 12, 16, 24};
+      const int ncand = pp ? 4 : 9;   // deeper splits lose to the reduction at 256x256
+      for (int c = 0; c < ncand; ++c) {
+        const int sp = cand[c];
+        int ks = (K + sp - 1) / sp;
+        ks = (ks + bk - 1) / bk * bk;
+        const int real = (K + ks - 1) / ks;
+        if (real != sp && sp > 1) continue;
+        const long waves = (tiles * sp + slots - 1) / slots;
+        double t = (double)waves * ((ks + step - 1) / step) * t_step;
+        if (sp > 1) t += (sp + 1.0) * M * (double)N * 4.0 / 5e12;
+        if (t < best) {
+          best = t;
+          g.tile = tile;
+          g.splits = sp;
+          g.k_split = ks;
+        }
       }
     }
   }
