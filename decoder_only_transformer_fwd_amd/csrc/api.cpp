@@ -143,11 +143,13 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   } else if (dtype == DT_F32) {
     g.tile = (long)M * N >= 256L * 128 * 128 ? TILE_128x128 : TILE_64x64;
   } else if (layout == LAYOUT_KK) {
-    // 8-wave 256x256 unless both N and K are short
-    g.tile = N >= 4096 || K >= 4096 ? TILE_256x256_W8 : TILE_128x128;
+    // ping-pong 256x256 unless both N and K are short (measured at the
+    // step's shapes: 16384 x {1536, 4608, 6144, 32768} x {1536, 6144})
+    g.tile = N >= 4096 || K >= 4096 ? TILE_256x256_PP4 : TILE_128x128;
   } else if (layout == LAYOUT_KN) {
-    // wide: 8-wave 256x256; narrow with a long K: ping-pong 256x256
-    g.tile = N >= 4096 ? TILE_256x256_W8 : K >= 6144 ? TILE_256x256_PP4 : TILE_128x128;
+    // input gradients: the ping-pong 256x256 tile measured best at every
+    // step shape, narrow and wide
+    g.tile = TILE_256x256_PP4;
   } else if (layout == LAYOUT_MN) {
     g.tile = TILE_256x256_PP4;
   } else {

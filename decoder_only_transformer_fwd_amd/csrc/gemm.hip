@@ -245,9 +245,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
   static_assert(NS == 2 || (!A_REG && !B_REG), "deeper pipelines need both operands on the direct-to-LDS path");
   static_assert(RB == 128 || (A_KC && B_KC) || PP, "transposed operands use 128-byte K steps");
   static_assert(!PP || (WGM * WGN == 8 && WGM % 2 == 0 && !A_REG && !B_REG), "ping-pong: two groups of four waves");
-  // waves that issue the global->LDS copies: all of them, or in the
-  // ping-pong schedule the first group only
-  constexpr int LW = PP ? WGM * WGN / 2 : WGM * WGN;
+  // every wave issues its share of the global->LDS copies (in the ping-pong
+  // schedule, each group during its own memory phase: spreading the copies
+  // over 8 waves and two issue points per step keeps more of them in flight
+  // than one group issuing all of them)
+  constexpr int LW = WGM * WGN;
   constexpr int KM = MF::KM;
   constexpr int EPL = MF::EPL;
   constexpr int FB = EPL * ES;         // fragment bytes per lane
@@ -359,25 +361,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
 
   if constexpr (PP) {
     // Ping-pong: waves 0-3 (group 0, output rows 0..BM/2-1) and 4-7 (group 1,
-    // the other half)
-    // share the SIMDs pairwise and run half a step apart.  While one group
-    // multiplies fragments already in its registers, the other reads the
-    // next stage's fragments from LDS (and group 0 also issues the
-    // global->LDS copies for the stage NS-1 steps ahead), so each SIMD's
-    // matrix unit alternates between the two groups' MFMA blocks.  Every
-    // phase ends with a barrier of all 8 waves; group 1 starts one phase
-    // late, and group 0 ends with one extra barrier to match.
+    // the other half) share the SIMDs pairwise and run one phase apart.  While
+    // one group multiplies fragments already in its registers, the other
+    // reads the next phase's fragments from LDS and, at the start of a step,
+    // issues its half of the global->LDS copies for the stage NS-1 steps
+    // ahead; each SIMD's matrix unit thus alternates between the two groups'
+    // MFMA blocks.  Every phase ends with a barrier of all 8 waves; group 1
+    // starts one barrier late and group 0 ends with one extra barrier.
+    //
+    // Copy completion: stage s is first read by group 0 in its memory phase
+    // of step s, after the barrier that ends group 0's compute phase and
+    // group 1's memory phase of step s-1.  Each group therefore waits for
+    // its copies of stage s at the end of that phase, leaving the two
+    // younger stages (NS-2 of them) in flight.
     constexpr int LPS = (A_KC ? DmaLoader<ES, BM, LW, RB>::PER_WAVE : DmaTrLoader<ES, BM, LW, BK>::PER_WAVE) +
                         (B_KC ? DmaLoader<ES, BN, LW, RB>::PER_WAVE : DmaTrLoader<ES, BN, LW, BK>::PER_WAVE);
-    const bool loader = wave < LW;
+    const bool g0 = wave < NW / 2;
     static_assert(KK % PSUB == 0, "whole phases per K step");
-    if (loader) {
 #pragma unroll
-      for (int st = 0; st < NS - 1; ++st) fetch(kbeg + st * BK, st);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
-    }
+    for (int st = 0; st < NS - 1; ++st) fetch(kbeg + st * BK, st);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));
     barrier_only();
-    if (!loader) barrier_only();
+    if (!g0) barrier_only();
     for (int kt = 0; kt < nk; ++kt) {
       const char* a_s = smem + (kt % NS) * STAGE;
 #pragma unroll
@@ -386,7 +391,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
         // start of a step, the copies for the stage NS-1 steps ahead)
 #pragma unroll
         for (int u = 0; u < PSUB; ++u) read_frags(a_s, ph * PSUB + u, u);
-        if (ph == 0 && loader) fetch(kbeg + (kt + NS - 1) * BK, (kt + NS - 1) % NS);
+        if (ph == 0) fetch(kbeg + (kt + NS - 1) * BK, (kt + NS - 1) % NS);
+        if (ph == KK / PSUB - 1 && !g0)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));   // group 1's copies of the next stage
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): fragments are in registers
         barrier_only();
         // compute phase
@@ -394,12 +401,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
 #pragma unroll
         for (int u = 0; u < PSUB; ++u) mma_step(u);
         __builtin_amdgcn_sched_barrier(0);
-        if (ph == KK / PSUB - 1 && loader)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));   // the next stage has landed
+        if (ph == KK / PSUB - 1 && g0)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * LPS));   // group 0's copies of the next stage
         barrier_only();
       }
     }
-    if (loader) barrier_only();
+    if (g0) barrier_only();
     __builtin_amdgcn_s_waitcnt(0x0070);
   } else if constexpr (NS == 2) {
     // Two stages: the next tile is requested at the top of a step and must
