@@ -194,6 +194,35 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   return g;
 }
 
+// Wave quantisation of long-K bf16 products whose 256x256 tiles fill a whole
+// number of rounds of the 256 CUs only partly (e.g. 16384 x 1536: 384 tiles,
+// 1.5 rounds run as 2).  The first n1 tile columns form whole rounds and run
+// as usual; the remaining columns are split along K into `splits` parts that
+// together fill one round, and their fp32 partials are summed (in split
+// order) into C.  Only plain fp32 stores and fp32 accumulation qualify.
+struct TailPlan {
+  int n1;       // tile columns of the whole-round part (0: no tail split)
+  int splits;
+};
+TailPlan plan_tail(int dtype, int layout, int epi, int M, int N, int K) {
+  TailPlan t{0, 1};
+  if (dtype != DT_BF16 || layout == LAYOUT_MN || K < 4096) return t;
+  if (epi != EPI_STORE_F32 && epi != EPI_ACCUM_F32) return t;
+  if (plan_gemm(dtype, layout, M, N, K).tile != TILE_256x256_PP4) return t;
+  const long tm = (M + 255) / 256, tn = (N + 255) / 256;
+  if ((tm * tn) % 256 == 0) return t;
+  for (long n1 = tn - 1; n1 >= 1; --n1) {
+    if ((tm * n1) % 256) continue;
+    const long r = tm * (tn - n1);
+    const long sp = std::min<long>(4, 256 / r);
+    if (sp < 2 || (N - n1 * 256) % 4) return t;
+    t.n1 = (int)n1;
+    t.splits = (int)sp;
+    return t;
+  }
+  return t;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ model
@@ -298,6 +327,8 @@ int build_layout(gpt_model& m) {
   auto consider = [&](int layout, int M, int N, int K) {
     GemmPlan g = plan_gemm(s.dtype, layout, M, N, K);
     if (g.splits > 1) need = std::max(need, (size_t)g.splits * M * N);
+    const TailPlan tp = plan_tail(s.dtype, layout, EPI_STORE_F32, M, N, K);
+    if (tp.n1 > 0) need = std::max(need, (size_t)tp.splits * M * (N - tp.n1 * 256));
   };
   consider(LAYOUT_KN, s.BT, s.d, s.V);
   consider(LAYOUT_MN, s.V, s.d, s.BT);
@@ -309,6 +340,8 @@ int build_layout(gpt_model& m) {
   consider(LAYOUT_MN, s.d, s.d, s.BT);
   consider(LAYOUT_KN, s.BT, s.d, 3 * s.d);
   consider(LAYOUT_MN, 3 * s.d, s.d, s.BT);
+  consider(LAYOUT_KK, s.BT, s.d, s.F);
+  consider(LAYOUT_KK, s.BT, s.d, s.d);
   if (s.fp8) {
     for (int dty : {DT_FP8_A4B4, DT_FP8_A5B4}) {
       for (int K : {s.d, s.F, 3 * s.d}) {
@@ -435,6 +468,36 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   }
   a.k_split = K;
   char label[128];
+  const TailPlan tp = plan_tail(dty, layout, epi, M, N, K);
+  if (tp.n1 > 0) {
+    // whole rounds: the first n1 tile columns
+    const int N1 = tp.n1 * 256, N2 = N - N1;
+    a.N = N1;
+    gemm_kernel_label(dty, layout, epi, g.tile, label, sizeof label);
+    prof_begin(m, site, flops * N1 / N, 0, label);
+    if (gemm_launch(a, dty, layout, epi, g.tile, 1, m.st)) return fail(GPT_EINVAL, "gemm variant not instantiated");
+    prof_end(m);
+    // the remaining columns, split along K
+    GemmArgs t = a;
+    const size_t es = 2;   // bf16 operands (plan_tail admits no other type)
+    t.B = (const char*)B + (layout == LAYOUT_KK ? (size_t)N1 * ldb : (size_t)N1) * es;
+    t.N = N2;
+    int ks = (K + tp.splits - 1) / tp.splits;
+    ks = (ks + 63) / 64 * 64;
+    const int sp = (K + ks - 1) / ks;
+    t.k_split = ks;
+    t.part = at<float>(m, m.splitk);
+    gemm_kernel_label(dty, layout, EPI_PARTIAL, g.tile, label, sizeof label);
+    prof_begin(m, site, flops * N2 / N, 0, label);
+    if (gemm_launch(t, dty, layout, EPI_PARTIAL, g.tile, sp, m.st))
+      return fail(GPT_EINVAL, "gemm variant not instantiated (partial)");
+    prof_end(m);
+    prof_begin(m, "splitk_reduce", (sp + 1.0 + (epi == EPI_ACCUM_F32)) * M * (double)N2 * 4.0, 1,
+               "splitk_reduce_strided_kernel");
+    splitk_reduce_strided(t.part, sp, M, N2, (float*)C + N1, ldc, epi == EPI_ACCUM_F32, m.st);
+    prof_end(m);
+    return GPT_OK;
+  }
   gemm_kernel_label(dty, layout, epi, g.tile, label, sizeof label);
   prof_begin(m, site, flops, 0, label);
   if (gemm_launch(a, dty, layout, epi, g.tile, 1, m.st))

@@ -594,6 +594,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *(floatx4*)(out + i) = s;
 }
 
+// The same reduction into an M x N block of a matrix with row stride ldc.
+__global__ __launch_bounds__(256) void splitk_reduce_strided_kernel(const float* __restrict__ part, int splits, int M,
+                                                                    int N, float* __restrict__ out, long ldc,
+                                                                    int accumulate) {
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  const long mn = (long)M * N;
+  if (i >= mn) return;
+  const long m = i / N, n = i % N;
+  float* o = out + m * ldc + n;
+  floatx4 s = accumulate ? *(const floatx4*)o : floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < splits; ++z) s += *(const floatx4*)(part + (long)z * mn + i);
+  *(floatx4*)o = s;
+}
+
 // ------------------------------------------------------------------ dispatch
 
 // Tile table: id -> (BM, BN, waves M x N, bytes per K step per row, stages).
@@ -674,6 +688,7 @@ static int launch_epi(const GemmArgs& a, int layout, int epi, int tile, int spli
   GK_CASE(LAYOUT_KK, true, true, EPI_XENT_FWD)
   GK_CASE(LAYOUT_KK, true, true, EPI_XENT_BWD)
   GK_CASE(LAYOUT_KK, true, true, EPI_STORE_F32)
+  GK_CASE(LAYOUT_KK, true, true, EPI_PARTIAL)
   // input gradients: grad [M][K] x weight [K][N]
   GK_CASE(LAYOUT_KN, true, false, EPI_STORE)
   GK_CASE(LAYOUT_KN, true, false, EPI_STORE_F32)
@@ -719,6 +734,13 @@ void splitk_reduce(const float* part, int splits, long mn, float* out, int accum
   const long n4 = (mn + 3) / 4;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, splits, mn,
                      out, accumulate);
+}
+
+void splitk_reduce_strided(const float* part, int splits, int M, int N, float* out, long ldc, int accumulate,
+                           hipStream_t st) {
+  const long n4 = ((long)M * N + 3) / 4;
+  hipLaunchKernelGGL(splitk_reduce_strided_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, splits,
+                     M, N, out, ldc, accumulate);
 }
 
 }  // namespace gk

@@ -76,6 +76,10 @@ int gemm_launch(const GemmArgs& a, int dtype, int layout, int epi, int tile, int
                 hipStream_t st);
 void splitk_reduce(const float* part, int splits, long mn, float* out, int accumulate,
                    hipStream_t st);
+// out[m * ldc + n] (+)= sum over z of part[z][m][n] for an M x N block of a
+// wider fp32 matrix (N a multiple of 4, out and ldc 16-byte aligned).
+void splitk_reduce_strided(const float* part, int splits, int M, int N, float* out, long ldc, int accumulate,
+                           hipStream_t st);
 
 // ---------------------------------------------------------------- elementwise
 // Also checks that every token and target id is in [0, vocab) (sets *flag).
