@@ -367,13 +367,28 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
           if constexpr (DO_DK) dp[qb] = MF::mma(row_frag<T, RROW>(qs + OFF_DO, qb * 32 + l32, k, g), vf[k], dp[qb]);
         }
       const bool need_mask = (i0 < jw0 + 31) || (i0 + BQ - 1 - jw0 >= W) || (i0 + BQ > Tn) || (jw0 + 31 >= Tn);
+      // invisible pairs get a -inf exponent (exp2 -> 0); the exponentials
+      // themselves are unconditional so the loop stays branch-free
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int il = qb * 32 + acc_row(r, g);
+            const float x = __builtin_fmaf(sc[qb][r], c, -lse_c[qb][r >> 2][r & 3]);
+            sc[qb][r] = visible(i0 + il, j, W, Tn) ? x : -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], c, -lse_c[qb][r >> 2][r & 3]);
+      }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int il = qb * 32 + acc_row(r, g);
-          const float p0 = fast_exp2(__builtin_fmaf(sc[qb][r], c, -lse_c[qb][r >> 2][r & 3]));
-          const float p = (!need_mask || visible(i0 + il, j, W, Tn)) ? p0 : 0.f;
+          const float p = fast_exp2(sc[qb][r]);
           sc[qb][r] = p;
           if constexpr (DO_DK) dp[qb][r] = p * (dp[qb][r] - D_c[qb][r >> 2][r & 3]);
         }
@@ -507,12 +522,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a) {
         dp[0] = MF::mma(row_frag<T, RROW>(vs, l32, k, g), df[k], dp[0]);
       }
       const bool need_mask = (j0 + BKV - 1 > iw0) || (iw0 + 31 - j0 >= W) || (j0 + BKV > Tn) || (iw0 + 31 >= Tn);
+      // invisible pairs get a -inf exponent (exp2 -> 0), branch-free
+      if (need_mask) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p0 = fast_exp2(__builtin_fmaf(sc[0][r], c, -lse_i));
-        const float p = (!need_mask || visible(i, j0 + acc_row(r, g), W, Tn)) ? p0 : 0.f;
-        dp[0][r] = p * (dp[0][r] - D_i);
+        for (int r = 0; r < 16; ++r) {
+          const float x = __builtin_fmaf(sc[0][r], c, -lse_i);
+          sc[0][r] = visible(i, j0 + acc_row(r, g), W, Tn) ? x : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[0][r] = __builtin_fmaf(sc[0][r], c, -lse_i);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[0][r] = fast_exp2(sc[0][r]) * (dp[0][r] - D_i);
 #pragma unroll
       for (int k = 0; k < PS; ++k) {
         const typename MF::frag sf = acc_frag<T, 1>(dp, k);

@@ -111,6 +111,19 @@ __device__ __forceinline__ void lds_read(const char* base, int row, int byte, vo
   }
 }
 
+// Raw buffer resource for `nbytes` bytes at `base`.  Both are uniform across
+// the wave by construction; taking them through readfirstlane lets the
+// compiler prove it and keep the descriptor in scalar registers (a
+// descriptor it cannot prove uniform is wrapped in a per-load loop over
+// lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int nbytes) {
+  const unsigned long long bp = (unsigned long long)base;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)bp);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(bp >> 32));
+  const int nb = __builtin_amdgcn_readfirstlane(nbytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((unsigned long long)hi << 32) | lo), 0, nb, 0x00020000);
+}
+
 // Rows of a global matrix copied straight into a swizzled LDS tile by buffer
 // loads with the LDS bit (no registers).  One wave instruction writes 64
 // lanes x 16 bytes = RPI consecutive LDS rows of RB bytes; the lane owning
@@ -134,7 +147,7 @@ struct RowDma {
   __device__ __forceinline__ void init(const void* base, int stride, long nbytes, int wave, int lane) {
     if (nbytes > 0x7FFFFFF0L) nbytes = 0x7FFFFFF0L;
     if (nbytes < 0) nbytes = 0;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)nbytes, 0x00020000);
+    rsrc = uniform_rsrc(base, (int)nbytes);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int r = (wave * PER_WAVE + i) * RPI + lane / CPR;

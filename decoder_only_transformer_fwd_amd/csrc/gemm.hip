@@ -30,7 +30,6 @@
 
 namespace gk {
 
-constexpr uint32_t BUF_DWORD3 = 0x00020000u;   // raw buffer, 32-bit data format
 
 // M/N-contiguous operand: blocks of 16 bytes (EPC elements) along the rows
 // x EPC K-rows, transposed in registers, then stored K-contiguous in LDS.
@@ -116,7 +115,7 @@ struct DmaLoader {
     const long rows_left = nrows > r0 ? (long)(nrows - r0) : 0;
     long bytes = rows_left * ld * ES;
     if (bytes > 0x7FFFFFF0L) bytes = 0x7FFFFFF0L;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(base + (long)r0 * ld * ES), 0, (int)bytes, BUF_DWORD3);
+    rsrc = uniform_rsrc(base + (long)r0 * ld * ES, (int)bytes);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int r = wave * RPW + i * RPI + lane / CPR;
@@ -173,8 +172,7 @@ struct DmaTrLoader {
     long bytes = (long)(kend - k0 - 1) * ldb + col_bytes_left;
     if (bytes < 0) bytes = 0;
     if (bytes > 0x7FFFFFF0L) bytes = 0x7FFFFFF0L;
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (long)k0 * ldb), 0, (int)bytes, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t r = uniform_rsrc(base + (long)k0 * ldb, (int)bytes);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i)
       dma16(r, lds + (wave * PER_WAVE + i) * 1024, k0 + krow[i] < kend ? voff[i] : (int)0x80000000);
