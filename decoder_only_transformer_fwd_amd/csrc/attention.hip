@@ -7,8 +7,10 @@
 //
 // MFMA formulation.  The forward computes S^T = K Q^T so that each lane owns
 // one query (its column) and reduces over keys in-lane plus one swap with the
-// other half-wave; the output is accumulated transposed, O^T = V^T P^T, so the
-// online-softmax rescale is a per-lane scalar.  The accumulator registers of S
+// other half-wave; the output is accumulated transposed, O^T = V^T P^T, and
+// normalised per lane at the end.  The softmax needs no running maximum: the
+// heads are QK-normalised, so the scores are bounded and a fixed exponent
+// offset keeps every exponential in range.  The accumulator registers of S
 // are fed directly as the B operand of the next MFMA: the K index of that
 // operand runs over the keys in the accumulator's register order, and the
 // matching A operand (V^T) is read from LDS in the same order.  Operands that
@@ -150,8 +152,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   for (int x = 0; x < DB; ++x)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
-  float m = -1e30f, l = 0.f;   // running max of raw scores, running sum (this lane's keys)
+  // Softmax with a fixed exponent offset instead of a running maximum.  The
+  // heads are QK-normalised (|q^|, |k^| <= sqrt(Dh), up to bf16 rounding), so
+  // every scaled score s * c lies within +-c * Dh; with the offset
+  // M = 1.01 * c * Dh every exponent is <= 0 and >= -2M (2^-33 at Dh = 128),
+  // well inside fp32 and bf16 range.  No running max, no rescaling of the
+  // accumulators, and the same probabilities as the online form.
   const float c = a.scale_log2;
+  const float M = 1.01f * c * DH;
+  float l = 0.f;   // sum of this lane's exponentials
 
   if (nt > 0) {
     lk.issue(smem, jb0 * (int)(row3 * ES), wave);
@@ -184,32 +193,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!visible(i, j0 + jb * 32 + acc_row(r, g), W, Tn)) sc[jb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const float x = __builtin_fmaf(sc[jb][r], c, -M);
+            sc[jb][r] = visible(i, j0 + jb * 32 + acc_row(r, g), W, Tn) ? x : -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[jb][r] = __builtin_fmaf(sc[jb][r], c, -M);
       }
-      float mloc = m;
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[jb][r]);
-      const float mnew = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float alpha = fast_exp2((m - mnew) * c);
-      m = mnew;
-      const float mc = mnew * c;
-      float ps = 0.f;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(sc[jb][r], c, -mc));
+          const float p = fast_exp2(sc[jb][r]);
           sc[jb][r] = p;
-          ps += p;
+          l += p;
         }
-      l = l * alpha + ps;
-#pragma unroll
-      for (int x = 0; x < DB; ++x)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[x][r] *= alpha;
 #pragma unroll
       for (int k = 0; k < PS; ++k) {
         const typename MF::frag pf = acc_frag<T, 2>(sc, k);
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     block_amax<4>(a.amax_o, om, (float*)smem);
   }
   // log-sum-exp of the scaled scores, base 2
-  if (g == 0 && i < a.Tp) a.lse2[((long)b * a.H + h) * a.Tp + i] = i < Tn ? m * c + fast_log2(lt) : 0.f;
+  if (g == 0 && i < a.Tp) a.lse2[((long)b * a.H + h) * a.Tp + i] = i < Tn ? M + fast_log2(lt) : 0.f;
 }
 
 // ------------------------------------------------------------------ backward: dK, dV
