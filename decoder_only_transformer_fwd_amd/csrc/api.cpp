@@ -524,6 +524,11 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   const double es_d = (double)es;
   const std::string tname = dt == DT_BF16 ? "bf16" : "float";
   auto KL = [&](const char* k) { return std::string(k) + "<" + tname + ">"; };
+  auto norm_label = [&](const char* k) {
+    const int nch = norm_chunks(d);
+    return nch ? std::string(k) + "_reg_kernel<" + tname + ", " + std::to_string(nch) + ">"
+               : std::string(k) + "_kernel<" + tname + ">";
+  };
   auto KLD = [&](const char* k, const char* extra = "") {
     return std::string(k) + "<" + tname + ", " + std::to_string(Dh) + extra + ">";
   };
@@ -572,7 +577,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   for (int l = 0; l < s.L; ++l) {
     auto& Ly = m.lay[l];
     const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
-    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
+    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, norm_label("rmsnorm_fwd"));
     rmsnorm_fwd(dt, h, m.ws + Ly.n1, at<float>(m, Ly.rstd1), BT, d, s.eps, st, amx(l, SL_N1));
     prof_end(m);
     if (f8) {
@@ -607,7 +612,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
       rc = gemm(m, "gemm_o", LAYOUT_KK, EPI_ACCUM_F32, BT, d, d, m.ws + Ly.o, d, wp(P.Wo[l]), d, h, d);
     }
     if (rc) return rc;
-    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
+    prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, norm_label("rmsnorm_fwd"));
     rmsnorm_fwd(dt, h, m.ws + Ly.n2, at<float>(m, Ly.rstd2), BT, d, s.eps, st, amx(l, SL_N2));
     prof_end(m);
     GemmArgs ex{};
@@ -629,7 +634,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     }
     if (rc) return rc;
   }
-  prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, KL("rmsnorm_fwd_kernel"));
+  prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, norm_label("rmsnorm_fwd"));
   rmsnorm_fwd(dt, h, m.ws + m.nL, at<float>(m, m.rstdL), BT, d, s.eps, st);
   prof_end(m);
   {
@@ -661,7 +666,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   if ((rc = gemm(m, "wgrad_lm_head", LAYOUT_MN, EPI_STORE_F32, V, d, BT, m.ws + m.dz, V, m.ws + m.nL, d, grads + P.U,
                  d)))
     return rc;
-  prof_begin(m, "rmsnorm_bwd", (double)BT * d * (8.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
+  prof_begin(m, "rmsnorm_bwd", (double)BT * d * (8.0 + 2.0 * es_d), 1, norm_label("rmsnorm_bwd"));
   rmsnorm_bwd(dt, dm, m.ws + m.nL, at<float>(m, m.rstdL), dh, dhA, BT, d, 0, st, amx(s.L - 1, SL_DH2));
   prof_end(m);
   for (int l = s.L - 1; l >= 0; --l) {
@@ -697,7 +702,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                      grads + P.W1[l], d)))
         return rc;
     }
-    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
+    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, norm_label("rmsnorm_bwd"));
     rmsnorm_bwd(dt, dm, m.ws + Ly.n2, at<float>(m, Ly.rstd2), dh, dhA, BT, d, 1, st, amx(l, SL_DH1));
     prof_end(m);
     if (f8) {
@@ -758,7 +763,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                      grads + P.Wqkv[l], d)))
         return rc;
     }
-    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, KL("rmsnorm_bwd_kernel"));
+    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, norm_label("rmsnorm_bwd"));
     rmsnorm_bwd(dt, dm, m.ws + Ly.n1, at<float>(m, Ly.rstd1), dh, dhA, BT, d, 1, st, amx(l - 1, SL_DH2));
     prof_end(m);
   }

@@ -57,6 +57,113 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float* __restric
   if (amax) block_amax<4>(amax, m, red);
 }
 
+// Register-resident variants for d <= 512 * NCH, d % 8 == 0: one wave per
+// row, each lane holding NCH chunks of 8 consecutive elements (32-byte fp32
+// and 16-byte bf16 accesses), so every input byte is read exactly once.
+__device__ __forceinline__ void load8(const float* p, floatx4& lo, floatx4& hi) {
+  lo = *(const floatx4*)p;
+  hi = *(const floatx4*)(p + 4);
+}
+__device__ __forceinline__ void load8(const bf16* p, floatx4& lo, floatx4& hi) {
+  const bf16x8 v = *(const bf16x8*)p;
+  lo = __builtin_convertvector(__builtin_shufflevector(v, v, 0, 1, 2, 3), floatx4);
+  hi = __builtin_convertvector(__builtin_shufflevector(v, v, 4, 5, 6, 7), floatx4);
+}
+__device__ __forceinline__ void store8(float* p, floatx4 lo, floatx4 hi) {
+  *(floatx4*)p = lo;
+  *(floatx4*)(p + 4) = hi;
+}
+__device__ __forceinline__ void store8(bf16* p, floatx4 lo, floatx4 hi) {
+  const bf16x4 a = __builtin_convertvector(lo, bf16x4), b = __builtin_convertvector(hi, bf16x4);
+  *(bf16x8*)p = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_reg_kernel(const float* __restrict__ x, T* __restrict__ y,
+                                                              float* __restrict__ rstd, int rows, int d, float eps,
+                                                              unsigned* __restrict__ amax) {
+  __shared__ float red[4];
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  float m = 0.f;
+  if (row < rows) {
+    const float* xr = x + (long)row * d;
+    floatx4 v[NCH][2];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c = (k * 64 + lane) * 8;
+      if (c < d) {
+        load8(xr + c, v[k][0], v[k][1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(v[k][h][e], v[k][h][e], ss);
+      }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c = (k * 64 + lane) * 8;
+      if (c < d) {
+        const floatx4 lo = v[k][0] * r, hi = v[k][1] * r;
+        store8(y + (long)row * d + c, lo, hi);
+        if (amax) m = fmaxf(m, fmaxf(abs_max4<T>(lo), abs_max4<T>(hi)));
+      }
+    }
+    if (lane == 0) rstd[row] = r;
+  }
+  if (amax) block_amax<4>(amax, m, red);
+}
+
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const float* __restrict__ dy, const T* __restrict__ y,
+                                                              const float* __restrict__ rstd, float* __restrict__ dx,
+                                                              T* __restrict__ dxa, int rows, int d, int accumulate,
+                                                              unsigned* __restrict__ amax) {
+  __shared__ float red[4];
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  float m = 0.f;
+  if (row < rows) {
+    const long base = (long)row * d;
+    floatx4 a[NCH][2], b[NCH][2], acc[NCH][2];
+    float dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c = (k * 64 + lane) * 8;
+      if (c < d) {
+        load8(dy + base + c, a[k][0], a[k][1]);
+        load8(y + base + c, b[k][0], b[k][1]);
+        if (accumulate) load8(dx + base + c, acc[k][0], acc[k][1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(a[k][h][e], b[k][h][e], dot);
+      }
+    }
+    dot = wave_sum(dot) / (float)d;
+    const float r = rstd[row];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c = (k * 64 + lane) * 8;
+      if (c < d) {
+        floatx4 g[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          g[h] = (a[k][h] - b[k][h] * dot) * r;
+          if (accumulate) g[h] += acc[k][h];
+        }
+        store8(dx + base + c, g[0], g[1]);
+        store8(dxa + base + c, g[0], g[1]);
+        if (amax) m = fmaxf(m, fmaxf(abs_max4<T>(g[0]), abs_max4<T>(g[1])));
+      }
+    }
+  }
+  if (amax) block_amax<4>(amax, m, red);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __restrict__ y,
                                                           const float* __restrict__ rstd, float* __restrict__ dx,
@@ -466,9 +573,36 @@ void embed_fwd(int dtype, const int32_t* tokens, const int32_t* targets, const v
                        vocab, flag);
 }
 
+template <typename T>
+static void rmsnorm_fwd_reg(const float* x, T* y, float* rstd, int rows, int d, float eps, hipStream_t st,
+                            unsigned* amax) {
+  dim3 g((rows + 3) / 4);
+  switch (norm_chunks(d)) {
+    case 1: hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<T, 1>), g, dim3(256), 0, st, x, y, rstd, rows, d, eps, amax); break;
+    case 2: hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<T, 2>), g, dim3(256), 0, st, x, y, rstd, rows, d, eps, amax); break;
+    default: hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<T, 4>), g, dim3(256), 0, st, x, y, rstd, rows, d, eps, amax);
+  }
+}
+
+template <typename T>
+static void rmsnorm_bwd_reg(const float* dy, const T* y, const float* rstd, float* dx, T* dxa, int rows, int d,
+                            int accumulate, hipStream_t st, unsigned* amax) {
+  dim3 g((rows + 3) / 4);
+  switch (norm_chunks(d)) {
+    case 1: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 1>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax); break;
+    case 2: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 2>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax); break;
+    default: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 4>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax);
+  }
+}
+
 void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps, hipStream_t st,
                  unsigned* amax) {
   dim3 g((rows + 3) / 4);
+  if (norm_chunks(d)) {
+    if (dtype == DT_BF16) rmsnorm_fwd_reg(x, (bf16*)y, rstd, rows, d, eps, st, amax);
+    else rmsnorm_fwd_reg(x, (float*)y, rstd, rows, d, eps, st, amax);
+    return;
+  }
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(rmsnorm_fwd_kernel<bf16>, g, dim3(256), 0, st, x, (bf16*)y, rstd, rows, d, eps, amax);
   else
@@ -478,6 +612,11 @@ void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int 
 void rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* rstd, float* dx, void* dxa, int rows,
                  int d, int accumulate, hipStream_t st, unsigned* amax) {
   dim3 g((rows + 3) / 4);
+  if (norm_chunks(d)) {
+    if (dtype == DT_BF16) rmsnorm_bwd_reg(dy, (const bf16*)y, rstd, dx, (bf16*)dxa, rows, d, accumulate, st, amax);
+    else rmsnorm_bwd_reg(dy, (const float*)y, rstd, dx, (float*)dxa, rows, d, accumulate, st, amax);
+    return;
+  }
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, g, dim3(256), 0, st, dy, (const bf16*)y, rstd, dx, (bf16*)dxa,
                        rows, d, accumulate, amax);

@@ -86,6 +86,12 @@ void splitk_reduce_strided(const float* part, int splits, int M, int N, float* o
 void embed_fwd(int dtype, const int32_t* tokens, const int32_t* targets, const void* E, float* h, int rows, int d,
                int vocab, int* flag, hipStream_t st);
 // amax (optional): max |stored value| folded in as float bits (for fp8 scaling)
+// Chunks of 8 elements per lane for the register-resident norm kernels (0:
+// the row does not fit, the looping kernels run instead).
+inline int norm_chunks(int d) {
+  if (d % 8) return 0;
+  return d <= 512 ? 1 : d <= 1024 ? 2 : d <= 2048 ? 4 : 0;
+}
 void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps,
                  hipStream_t st, unsigned* amax = nullptr);
 // dx (+)= r * (dy - y * mean(dy*y)); also writes dx in the activation type.
