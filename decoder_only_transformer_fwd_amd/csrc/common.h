@@ -132,8 +132,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
 // base read as zero.
 // One wave instruction: 64 lanes x 16 bytes from the buffer into LDS at
 // lds + 16 * lane.  Bytes at or past the buffer's size read as zero.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int off, int soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, soff, 0, 0);
 }
 
 template <int ROWS, int RB, int NW>
@@ -155,10 +155,13 @@ struct RowDma {
       voff[i] = r * stride + c * 16;
     }
   }
+  // row_off is uniform and goes in the scalar offset, so the per-lane offset
+  // registers are never rewritten: no later register write has to wait for a
+  // copy still reading them.
   __device__ __forceinline__ void issue(char* lds, int row_off, int wave) const {
+    const int so = __builtin_amdgcn_readfirstlane(row_off);
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i)
-      dma16(rsrc, lds + (wave * PER_WAVE + i) * RPI * RB, voff[i] + row_off);
+    for (int i = 0; i < PER_WAVE; ++i) dma16(rsrc, lds + (wave * PER_WAVE + i) * RPI * RB, voff[i], so);
   }
 };
 
@@ -169,6 +172,20 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ shortx4 lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) shortx4*)p);
 }
+
+// Work-group barrier without the release/acquire fences of __syncthreads.
+// Those fences make every wave wait for all of its outstanding global->LDS
+// copies (vmcnt 0) at each barrier, which would drain a multi-stage pipeline;
+// callers wait for exactly the copies and LDS reads they depend on.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {

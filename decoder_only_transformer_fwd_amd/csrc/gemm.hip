@@ -195,20 +195,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int rb, int kbase, i
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Work-group barrier without the release/acquire fences of __syncthreads.
-// Those fences make every wave wait for all of its outstanding global->LDS
-// copies (vmcnt 0) at each barrier, which would drain a multi-stage pipeline;
-// callers wait for exactly the copies and LDS reads they depend on.
-__device__ __forceinline__ void barrier_only() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left unconstrained).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
 // Tiles are taken in groups of GROUP_M rows of tiles (about 1024 rows of A,
 // measured best at the step's shapes) across all tile columns.
 template <int GROUP_M>

@@ -25,8 +25,10 @@ import sys
 from collections import defaultdict
 
 _GARBLED = re.compile(r"gemm_kernel<[^>]*?>?, (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (true|false), (true|false), (\d+)")
-# tiles with the ping-pong schedule, by (BM, BN, waves M, waves N, row bytes, stages)
-_PP = {(256, 256, 2, 4, 64, 5), (256, 128, 4, 2, 128, 3)}
+# tiles with the ping-pong schedule, by (BM, BN, waves M, waves N, row bytes,
+# stages); the library's bf16 plan launches the 8-wave, 64-byte, 4-stage tile
+# only with the ping-pong schedule
+_PP = {(256, 256, 2, 4, 64, 4), (256, 256, 2, 4, 64, 5), (256, 128, 4, 2, 128, 3)}
 
 
 def _demangle(names):
@@ -65,7 +67,7 @@ def decode(name: str, demangled: str = None) -> str:
             bm, bn, wgm, wgn, rb, ns, akc, bkc, epi = g.groups()
             ty = "bf16"
             key = tuple(int(x) for x in (bm, bn, wgm, wgn, rb, ns))
-            pp = key in _PP or (key == (256, 256, 2, 4, 64, 4) and not (akc == "true" and bkc == "true"))
+            pp = key in _PP
         return (f"gemm_kernel<{ty}, {bm}, {bn}, {wgm}, {wgn}, {rb}, {ns}, {akc}, {bkc}, {epi}"
                 f"{', ping-pong' if pp else ''}>")
     return dm
