@@ -241,7 +241,7 @@ struct gpt_model {
     size_t n1T, oT, n2T, gT, wq[4], wqT[4];
   };
   std::vector<Layer> lay;
-  size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, dz, zlog, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
+  size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
       cosb, sinb, keys, total;
   size_t splitk_floats;
   size_t q8row, q8T, amax, scales;   // fp8: transient codes, per-tensor amax / scale slots
@@ -314,7 +314,6 @@ int build_layout(gpt_model& m) {
   m.lossdev = take(64);
   m.flag = take(64);
   m.dz = take(BT * s.V * A);
-  m.zlog = take(BT * s.V * 4);   // fp32 logits of the forward, read by the backward
   m.dm = take(BT * s.d * 4);
   m.dh = take(BT * s.d * 4);
   m.dhA = take(BT * s.d * A);
@@ -644,9 +643,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     ex.part = at<float>(m, m.part);
     ex.tgt = at<float>(m, m.tgt);
     ex.nblk = m.xent_nblk;
-    if ((rc = gemm(m, "gemm_lm_head_xent_fwd", LAYOUT_KK, EPI_XENT_FWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d,
-                   m.ws + m.zlog, V, ex)))
-      return rc;
+    if ((rc = gemm(m, "gemm_lm_head_xent_fwd", LAYOUT_KK, EPI_XENT_FWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, nullptr, V, ex))) return rc;
   }
   prof_begin(m, "xent_reduce", (double)BT * m.xent_nblk * 8.0 + BT * 12.0, 1, "xent_reduce_kernel + mean_reduce_kernel");
   xent_reduce(at<float>(m, m.part), at<float>(m, m.tgt), BT, m.xent_nblk, at<float>(m, m.lse),
@@ -655,10 +652,13 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   prof_end(m);
 
   // ---------------------------------------------------------------- backward
-  // logit gradient from the logits the forward kept (no second lm_head product)
-  prof_begin(m, "xent_dz", (double)BT * V * (4.0 + es_d) + BT * 8.0, 1, KL("xent_dz_kernel"));
-  xent_dz(dt, at<float>(m, m.zlog), at<float>(m, m.lse), targets, m.ws + m.dz, BT, V, 1.0f / (float)BT, st);
-  prof_end(m);
+  {
+    GemmArgs ex{};
+    ex.aux = targets;
+    ex.auxf = at<float>(m, m.lse);
+    ex.beta = 1.0f / (float)BT;
+    if ((rc = gemm(m, "gemm_lm_head_xent_bwd", LAYOUT_KK, EPI_XENT_BWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, m.ws + m.dz, V, ex))) return rc;
+  }
   float* dm = at<float>(m, m.dm);
   float* dh = at<float>(m, m.dh);
   void* dhA = m.ws + m.dhA;

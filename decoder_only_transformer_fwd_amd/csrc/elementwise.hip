@@ -57,7 +57,9 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float* __restric
   if (amax) block_amax<4>(amax, m, red);
 }
 
-// Eight consecutive elements as fp32: 32-byte fp32 and 16-byte bf16 accesses.
+// Register-resident variants for d <= 512 * NCH, d % 8 == 0: one wave per
+// row, each lane holding NCH chunks of 8 consecutive elements (32-byte fp32
+// and 16-byte bf16 accesses), so every input byte is read exactly once.
 __device__ __forceinline__ void load8(const float* p, floatx4& lo, floatx4& hi) {
   lo = *(const floatx4*)p;
   hi = *(const floatx4*)(p + 4);
@@ -76,40 +78,6 @@ __device__ __forceinline__ void store8(bf16* p, floatx4 lo, floatx4 hi) {
   *(bf16x8*)p = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// ------------------------------------------------------------------ cross-entropy backward
-// Eight consecutive logits per thread: 32-byte fp32 reads, 16-byte bf16 writes.
-template <typename T>
-__global__ __launch_bounds__(256) void xent_dz_kernel(const float* __restrict__ z, const float* __restrict__ lse,
-                                                      const int32_t* __restrict__ targets, T* __restrict__ dz,
-                                                      int rows, int V, float beta) {
-  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (i >= (long)rows * V) return;
-  const int m = (int)(i / V), n = (int)(i % V);
-  const float L2E = 1.4426950408889634f;
-  const float l = lse[m];
-  const int y = targets[m];
-  floatx4 v[2];
-  load8(z + i, v[0], v[1]);
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[h][e] = (fast_exp2((v[h][e] - l) * L2E) - (n + 4 * h + e == y ? 1.f : 0.f)) * beta;
-  store8(dz + i, v[0], v[1]);
-}
-
-void xent_dz(int dtype, const float* z, const float* lse, const int32_t* targets, void* dz, int rows, int V,
-             float beta, hipStream_t st) {
-  const long n8 = (long)rows * V / 8;
-  dim3 g((unsigned)((n8 + 255) / 256));
-  if (dtype == DT_F32)
-    hipLaunchKernelGGL(xent_dz_kernel<float>, g, dim3(256), 0, st, z, lse, targets, (float*)dz, rows, V, beta);
-  else
-    hipLaunchKernelGGL(xent_dz_kernel<bf16>, g, dim3(256), 0, st, z, lse, targets, (bf16*)dz, rows, V, beta);
-}
-
-// Register-resident RMSNorm for d <= 512 * NCH, d % 8 == 0: one wave per
-// row, each lane holding NCH chunks of 8 consecutive elements, so every input
-// byte is read exactly once.
 template <typename T, int NCH>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_reg_kernel(const float* __restrict__ x, T* __restrict__ y,
                                                               float* __restrict__ rstd, int rows, int d, float eps,

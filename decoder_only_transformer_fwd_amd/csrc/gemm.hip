@@ -462,18 +462,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
           if (n == y) p.tgt[m] = v;
         }
       se += __shfl_xor(se, 32, 64);
-      if (p.C != nullptr && mok) {   // the fp32 logits, kept for the backward
-        float* zrow = (float*)p.C + (long)m * p.ldc;
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = ncol0 + j * 32 + 8 * q + 4 * g;   // N is a multiple of 8
-            if (n < p.N)
-              store4(zrow + n, floatx4{acc[i][j][4 * q] * alpha, acc[i][j][4 * q + 1] * alpha,
-                                       acc[i][j][4 * q + 2] * alpha, acc[i][j][4 * q + 3] * alpha});
-          }
-      }
       const int blk = ncol0 / WN;
       if (mok && g == 0 && ncol0 < p.N) {
         p.part[((long)m * p.nblk + blk) * 2 + 0] = mx;
@@ -555,6 +543,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
             for (int e = 0; e < 4; ++e) rr[e] = v[e] * 2.f * fmaxf(u[e], 0.f);
             store4((TC*)p.C + off, rr);
             if (p.amax) amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
+          } else if constexpr (EPI == EPI_XENT_BWD) {
+            const float L2E = 1.4426950408889634f;
+            const float lse = p.auxf[m];
+            const int y = ((const int*)p.aux)[m];
+            floatx4 rr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[e] = (fast_exp2((v[e] - lse) * L2E) - (n + e == y ? 1.f : 0.f)) * p.beta;
+            store4((TC*)p.C + off, rr);
           } else if constexpr (EPI == EPI_PARTIAL) {
             store4(p.part + (long)blockIdx.z * p.M * p.N + (long)m * p.N + n, v);
           }
@@ -674,6 +670,7 @@ static int launch_epi(const GemmArgs& a, int layout, int epi, int tile, int spli
   GK_CASE(LAYOUT_KK, true, true, EPI_ACCUM_F32)
   GK_CASE(LAYOUT_KK, true, true, EPI_RELU2)
   GK_CASE(LAYOUT_KK, true, true, EPI_XENT_FWD)
+  GK_CASE(LAYOUT_KK, true, true, EPI_XENT_BWD)
   GK_CASE(LAYOUT_KK, true, true, EPI_STORE_F32)
   GK_CASE(LAYOUT_KK, true, true, EPI_PARTIAL)
   // input gradients: grad [M][K] x weight [K][N]

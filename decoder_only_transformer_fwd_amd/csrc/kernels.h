@@ -28,7 +28,7 @@ enum Epi {
   EPI_RELU2 = 3,      // C = acc (u), C2 = relu(acc)^2 (g)
   EPI_DRELU2 = 4,     // C = acc * 2 * relu(aux)
   EPI_XENT_FWD = 5,   // per-row partial (max, sum exp) + target logit
-  // 6: unused (the logit gradient is computed from the kept logits, see xent_dz)
+  EPI_XENT_BWD = 6,   // C = (exp(acc - lse) - onehot(target)) * beta
   EPI_PARTIAL = 7,    // part[split][M][N] = acc (split-K)
 };
 
@@ -60,11 +60,13 @@ struct GemmArgs {
   long ldc;
   void* C2;        // EPI_RELU2: g
   const void* aux; // EPI_DRELU2: u; EPI_XENT_*: int32 targets
+  const float* auxf; // EPI_XENT_BWD: per-row logsumexp
   float* part;     // EPI_XENT_FWD: [M][nblk][2]; EPI_PARTIAL: [splits][M][N]
   float* tgt;      // EPI_XENT_FWD: target logit per row
   float alpha;     // scales the accumulator before the epilogue
   const float* scale_a;  // fp8 products: quantisation scales of A and B (device);
   const float* scale_b;  // the accumulator is multiplied by alpha / (scale_a * scale_b)
+  float beta;      // EPI_XENT_BWD: 1 / rows
   int k_split;     // K elements handled per blockIdx.z
   int nblk;        // EPI_XENT_FWD: number of column blocks of width BN/2
   unsigned* amax;  // EPI_RELU2 / EPI_DRELU2: if set, max |stored g / du| is folded in (float bits)
@@ -90,12 +92,6 @@ inline int norm_chunks(int d) {
   if (d % 8) return 0;
   return d <= 512 ? 1 : d <= 1024 ? 2 : d <= 2048 ? 4 : 0;
 }
-// Logit gradient of the mean cross-entropy from the fp32 logits z [rows][V]
-// that the lm_head forward kept: dz = (exp(z - lse[row]) - [col ==
-// target[row]]) * beta, written as the activation type (V a multiple of 8).
-// The same values the lm_head product would give if recomputed.
-void xent_dz(int dtype, const float* z, const float* lse, const int32_t* targets, void* dz, int rows, int V,
-             float beta, hipStream_t st);
 void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps,
                  hipStream_t st, unsigned* amax = nullptr);
 // dx (+)= r * (dy - y * mean(dy*y)); also writes dx in the activation type.
