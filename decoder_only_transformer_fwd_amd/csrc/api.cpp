@@ -170,10 +170,15 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
       // one K step of one tile, seconds (the ping-pong tile steps 32 deep)
       const double t_step = dtype == DT_F32 ? 4e-6 : f8 ? 1.5e-6 : pp ? 0.95e-6 : 1.34e-6;
       const int step = pp ? 32 : bk;
-      const int cand[9] = {1, 2, 3, 4, 6, 8, 12, 16, 24};
-      const int ncand = pp ? 4 : 9;   // deeper splits lose to the reduction at 256x256
+      // split counts: up to 24 for 128x128; for the 256x256 tile up to 4, or
+      // up to 8 for small outputs (a few tiles must fill the CUs, and the
+      // fp32 partials stay small).  Measured: more splits of the 10-40 MB
+      // outputs cost more in the reduction than they gain.
+      const int cand_pp[8] = {1, 2, 3, 4, 5, 6, 7, 8};
+      const int cand_128[9] = {1, 2, 3, 4, 6, 8, 12, 16, 24};
+      const int ncand = pp ? ((double)M * N <= 2.5e6 ? 8 : 4) : 9;
       for (int c = 0; c < ncand; ++c) {
-        const int sp = cand[c];
+        const int sp = pp ? cand_pp[c] : cand_128[c];
         int ks = (K + sp - 1) / sp;
         ks = (ks + bk - 1) / bk * bk;
         const int real = (K + ks - 1) / ks;
