@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libgpt_mi355x.so")
 GPT_OK, GPT_EINVAL, GPT_ENULL, GPT_ETOKEN, GPT_EHIP, GPT_ENONFINITE, GPT_ESPACE, GPT_EALIGN = 0, -1, -2, -3, -4, -5, -6, -7
 GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 
-EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_destroy",
+EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_destroy",
             "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
             "gpt_profile_sites", "gpt_profile_get", "gpt_strerror", "gpt_last_error"]
 
@@ -55,6 +55,7 @@ def _load():
     lib.gpt_workspace_bytes.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(ctypes.c_size_t)]
     lib.gpt_create.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(P)]
     lib.gpt_step.argtypes = [P, P, P, P, ctypes.POINTER(F)]
+    lib.gpt_step_accum.argtypes = [P, P, P, P, F, I, ctypes.POINTER(F)]
     lib.gpt_destroy.argtypes = [P]
     lib.gpt_destroy.restype = None
     lib.gpt_debug_tensor.argtypes = [P, I, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I64),
@@ -71,7 +72,7 @@ def _load():
     lib.gpt_strerror.restype = ctypes.c_char_p
     lib.gpt_last_error.argtypes = []
     lib.gpt_last_error.restype = ctypes.c_char_p
-    for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step",
+    for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum",
                  "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
                  "gpt_profile_sites", "gpt_profile_get"):
         getattr(lib, name).restype = I
@@ -146,6 +147,14 @@ def gpt_step_rc(model: int, tokens: int, targets: int, grads: int) -> Tuple[int,
     loss = ctypes.c_float()
     rc = _lib.gpt_step(model, tokens, targets, grads, ctypes.byref(loss))
     return rc, loss.value
+
+
+def gpt_step_accum(model: int, tokens: int, targets: int, grads: int, grad_scale: float, accumulate: bool) -> float:
+    """grads <- (grads if accumulate else 0) + grad_scale * d(mean loss)/d(weights)."""
+    loss = ctypes.c_float()
+    _check(_lib.gpt_step_accum(model, tokens, targets, grads, float(grad_scale), int(bool(accumulate)),
+                               ctypes.byref(loss)), "gpt_step_accum")
+    return loss.value
 
 
 def gpt_destroy(model: int) -> None:
@@ -255,6 +264,10 @@ class Session:
 
     def step(self) -> float:
         return gpt_step(self.handle, self.tokens.data_ptr(), self.targets.data_ptr(), self.grads.data_ptr())
+
+    def step_accum(self, grad_scale: float, accumulate: bool) -> float:
+        return gpt_step_accum(self.handle, self.tokens.data_ptr(), self.targets.data_ptr(), self.grads.data_ptr(),
+                              grad_scale, accumulate)
 
     def step_rc(self) -> Tuple[int, float]:
         return gpt_step_rc(self.handle, self.tokens.data_ptr(), self.targets.data_ptr(), self.grads.data_ptr())

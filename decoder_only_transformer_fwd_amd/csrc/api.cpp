@@ -445,9 +445,12 @@ double visible_pairs(long T, long W) {
 }
 
 // One product with the planned tiling; splits go through the partial buffer
-// and an ordered reduction into C (fp32).
+// and an ordered reduction into C (fp32).  Weight gradients (wgrad) keep the
+// split plan of the storing form when they accumulate into C: the reduction
+// then adds the partial sums to what C holds.
 int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int K, const void* A, long lda,
-         const void* B, long ldb, void* C, long ldc, GemmArgs extra = GemmArgs{}, int dtype = -1) {
+         const void* B, long ldb, void* C, long ldc, GemmArgs extra = GemmArgs{}, int dtype = -1,
+         bool wgrad = false) {
   const double flops = 2.0 * M * N * (double)K;
   const int dty = dtype < 0 ? m.s.dtype : dtype;
   GemmArgs a = extra;
@@ -455,7 +458,7 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   if (a.alpha == 0.f) a.alpha = 1.f;
   GemmPlan g = plan_gemm(dty, layout, M, N, K);
   if (epi == EPI_XENT_FWD) g = GemmPlan{m.xent_tile, 1, K};
-  if (epi != EPI_STORE_F32) g.splits = 1, g.k_split = K;
+  if (epi != EPI_STORE_F32 && !(wgrad && epi == EPI_ACCUM_F32)) g.splits = 1, g.k_split = K;
   if (g.splits > 1 && ldc != N) g.splits = 1, g.k_split = K;
   if (g.splits > 1) {
     a.part = at<float>(m, m.splitk);
@@ -466,8 +469,9 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
     if (gemm_launch(a, dty, layout, EPI_PARTIAL, g.tile, g.splits, m.st))
       return fail(GPT_EINVAL, "gemm variant not instantiated (partial)");
     prof_end(m);
-    prof_begin(m, "splitk_reduce", (g.splits + 1.0) * M * N * 4.0, 1, "splitk_reduce_kernel");
-    splitk_reduce(a.part, g.splits, (long)M * N, (float*)C, 0, m.st);
+    const int acc = epi == EPI_ACCUM_F32;
+    prof_begin(m, "splitk_reduce", (g.splits + 1.0 + acc) * M * N * 4.0, 1, "splitk_reduce_kernel");
+    splitk_reduce(a.part, g.splits, (long)M * N, (float*)C, acc, m.st);
     prof_end(m);
     return GPT_OK;
   }
@@ -511,7 +515,12 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   return GPT_OK;
 }
 
-int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float* grads) {
+// One forward+backward pass.  Every gradient is linear in the logit gradient,
+// so grad_scale is applied there (once); with accumulate set, the weight
+// gradient products and the embedding scatter add to grads instead of
+// overwriting it.
+int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float* grads, float grad_scale,
+             int accumulate) {
   const Shape& s = m.s;
   const ParamOffsets& P = m.po;
   const int dt = s.dtype;
@@ -563,6 +572,19 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     ex.scale_a = sc8 + sa;
     ex.scale_b = sc8 + sb;
     return gemm(m, site, LAYOUT_KK, epi, M, N, K, A, K, B, K, C, ldc, ex, dty);
+  };
+  // weight-gradient products: store or accumulate into grads
+  const int wepi = accumulate ? EPI_ACCUM_F32 : EPI_STORE_F32;
+  auto wgrad = [&](const char* site, int M, int N, int K, const void* A, long lda, const void* B, long ldb,
+                   float* C, long ldc) {
+    return gemm(m, site, LAYOUT_MN, wepi, M, N, K, A, lda, B, ldb, C, ldc, GemmArgs{}, -1, true);
+  };
+  auto wgrad8 = [&](const char* site, int M, int N, int K, const void* A, const void* B, float* C, long ldc, int sa,
+                    int sb) {
+    GemmArgs ex{};
+    ex.scale_a = sc8 + sa;
+    ex.scale_b = sc8 + sb;
+    return gemm(m, site, LAYOUT_KK, wepi, M, N, K, A, K, B, K, C, ldc, ex, DT_FP8_A5B4, true);
   };
 
   fill_f32((float*)flag, 1, 0.f, st);
@@ -661,16 +683,14 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     GemmArgs ex{};
     ex.aux = targets;
     ex.auxf = at<float>(m, m.lse);
-    ex.beta = 1.0f / (float)BT;
+    ex.beta = grad_scale / (float)BT;
     if ((rc = gemm(m, "gemm_lm_head_xent_bwd", LAYOUT_KK, EPI_XENT_BWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, m.ws + m.dz, V, ex))) return rc;
   }
   float* dm = at<float>(m, m.dm);
   float* dh = at<float>(m, m.dh);
   void* dhA = m.ws + m.dhA;
   if ((rc = gemm(m, "dgrad_lm_head", LAYOUT_KN, EPI_STORE_F32, BT, d, V, m.ws + m.dz, V, wp(P.U), d, dm, d))) return rc;
-  if ((rc = gemm(m, "wgrad_lm_head", LAYOUT_MN, EPI_STORE_F32, V, d, BT, m.ws + m.dz, V, m.ws + m.nL, d, grads + P.U,
-                 d)))
-    return rc;
+  if ((rc = wgrad("wgrad_lm_head", V, d, BT, m.ws + m.dz, V, m.ws + m.nL, d, grads + P.U, d))) return rc;
   prof_begin(m, "rmsnorm_bwd", (double)BT * d * (8.0 + 2.0 * es_d), 1, norm_label("rmsnorm_bwd"));
   rmsnorm_bwd(dt, dm, m.ws + m.nL, at<float>(m, m.rstdL), dh, dhA, BT, d, 0, st, amx(s.L - 1, SL_DH2));
   prof_end(m);
@@ -685,26 +705,25 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
       if ((rc = gemm8("dgrad_w2_drelu2", DT_FP8_A5B4, EPI_DRELU2, BT, F, d, q8row, m.ws + Ly.wqT[3], m.ws + m.du, F,
                       slot(l, SL_DH2), slot(l, SL_W2), ex)))
         return rc;
-      if ((rc = gemm8("wgrad_w2", DT_FP8_A5B4, EPI_STORE_F32, d, F, BT, q8T, m.ws + Ly.gT, grads + P.W2[l], F,
-                      slot(l, SL_DH2), slot(l, SL_G))))
+      if ((rc = wgrad8("wgrad_w2", d, F, BT, q8T, m.ws + Ly.gT, grads + P.W2[l], F, slot(l, SL_DH2),
+                       slot(l, SL_G))))
         return rc;
       quant("fp8_quant_grad", FP8_E5M2, m.ws + m.du, BT, F, slot(l, SL_DU), q8row, q8T);
       if ((rc = gemm8("dgrad_w1", DT_FP8_A5B4, EPI_STORE_F32, BT, d, F, q8row, m.ws + Ly.wqT[2], dm, d,
                       slot(l, SL_DU), slot(l, SL_W1))))
         return rc;
-      if ((rc = gemm8("wgrad_w1", DT_FP8_A5B4, EPI_STORE_F32, F, d, BT, q8T, m.ws + Ly.n2T, grads + P.W1[l], d,
-                      slot(l, SL_DU), slot(l, SL_N2))))
+      if ((rc = wgrad8("wgrad_w1", F, d, BT, q8T, m.ws + Ly.n2T, grads + P.W1[l], d, slot(l, SL_DU),
+                       slot(l, SL_N2))))
         return rc;
     } else {
       if ((rc = gemm(m, "dgrad_w2_drelu2", LAYOUT_KN, EPI_DRELU2, BT, F, d, dhA, d, wp(P.W2[l]), F, m.ws + m.du, F,
                      ex)))
         return rc;
-      if ((rc = gemm(m, "wgrad_w2", LAYOUT_MN, EPI_STORE_F32, d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F)))
+      if ((rc = wgrad("wgrad_w2", d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F)))
         return rc;
       if ((rc = gemm(m, "dgrad_w1", LAYOUT_KN, EPI_STORE_F32, BT, d, F, m.ws + m.du, F, wp(P.W1[l]), d, dm, d)))
         return rc;
-      if ((rc = gemm(m, "wgrad_w1", LAYOUT_MN, EPI_STORE_F32, F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d,
-                     grads + P.W1[l], d)))
+      if ((rc = wgrad("wgrad_w1", F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d, grads + P.W1[l], d)))
         return rc;
     }
     prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, norm_label("rmsnorm_bwd"));
@@ -715,13 +734,13 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
       if ((rc = gemm8("dgrad_o", DT_FP8_A5B4, EPI_STORE, BT, d, d, q8row, m.ws + Ly.wqT[1], m.ws + m.dO, d,
                       slot(l, SL_DH1), slot(l, SL_WO))))
         return rc;
-      if ((rc = gemm8("wgrad_o", DT_FP8_A5B4, EPI_STORE_F32, d, d, BT, q8T, m.ws + Ly.oT, grads + P.Wo[l], d,
-                      slot(l, SL_DH1), slot(l, SL_O))))
+      if ((rc = wgrad8("wgrad_o", d, d, BT, q8T, m.ws + Ly.oT, grads + P.Wo[l], d, slot(l, SL_DH1),
+                       slot(l, SL_O))))
         return rc;
     } else {
       if ((rc = gemm(m, "dgrad_o", LAYOUT_KN, EPI_STORE, BT, d, d, dhA, d, wp(P.Wo[l]), d, m.ws + m.dO, d)))
         return rc;
-      if ((rc = gemm(m, "wgrad_o", LAYOUT_MN, EPI_STORE_F32, d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d)))
+      if ((rc = wgrad("wgrad_o", d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d)))
         return rc;
     }
     prof_begin(m, "attn_bwd_pre", (double)BT * d * 3.0 * es_d + (double)s.B * H * s.Tp * 4.0, 1, KLD("attn_bwd_pre_kernel"));
@@ -757,23 +776,23 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
       if ((rc = gemm8("dgrad_qkv", DT_FP8_A5B4, EPI_STORE_F32, BT, d, 3 * d, q8row, m.ws + Ly.wqT[0], dm, d,
                       slot(l, SL_DQKV), slot(l, SL_WQKV))))
         return rc;
-      if ((rc = gemm8("wgrad_qkv", DT_FP8_A5B4, EPI_STORE_F32, 3 * d, d, BT, q8T, m.ws + Ly.n1T, grads + P.Wqkv[l], d,
-                      slot(l, SL_DQKV), slot(l, SL_N1))))
+      if ((rc = wgrad8("wgrad_qkv", 3 * d, d, BT, q8T, m.ws + Ly.n1T, grads + P.Wqkv[l], d, slot(l, SL_DQKV),
+                       slot(l, SL_N1))))
         return rc;
     } else {
       if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, EPI_STORE_F32, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d,
                      dm, d)))
         return rc;
-      if ((rc = gemm(m, "wgrad_qkv", LAYOUT_MN, EPI_STORE_F32, 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d,
-                     grads + P.Wqkv[l], d)))
+      if ((rc = wgrad("wgrad_qkv", 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d, grads + P.Wqkv[l], d)))
         return rc;
     }
     prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, norm_label("rmsnorm_bwd"));
     rmsnorm_bwd(dt, dm, m.ws + Ly.n1, at<float>(m, Ly.rstd1), dh, dhA, BT, d, 1, st, amx(l - 1, SL_DH2));
     prof_end(m);
   }
-  prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * 4.0 + BT * 8.0, 1, "sort_keys_kernel + embed_bwd_runs_kernel");
-  embed_bwd(tokens, dh, grads + P.E, BT, d, V, at<uint32_t>(m, m.keys), nullptr, nullptr, st);
+  prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * (accumulate ? 8.0 : 4.0) + BT * 8.0, 1,
+             "sort_keys_kernel + embed_bwd_runs_kernel");
+  embed_bwd(tokens, dh, grads + P.E, BT, d, V, at<uint32_t>(m, m.keys), accumulate, st);
   prof_end(m);
   HIP_TRY(hipGetLastError());
   return GPT_OK;
@@ -855,9 +874,16 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
 }
 
 int gpt_step(gpt_model* m, const int32_t* tokens, const int32_t* targets, float* grads, float* loss) {
+  return gpt_step_accum(m, tokens, targets, grads, 1.0f, 0, loss);
+}
+
+int gpt_step_accum(gpt_model* m, const int32_t* tokens, const int32_t* targets, float* grads, float grad_scale,
+                   int accumulate, float* loss) {
   if (!m || !tokens || !targets || !grads || !loss) return fail(GPT_ENULL, "gpt_step: NULL argument");
   if ((uintptr_t)grads & (ALIGN - 1)) return fail(GPT_EALIGN, "grads must be 256-byte aligned");
-  int rc = run_step(*m, tokens, targets, grads);
+  if (!std::isfinite(grad_scale)) return fail(GPT_EINVAL, "grad_scale must be finite");
+  if (accumulate != 0 && accumulate != 1) return fail(GPT_EINVAL, "accumulate must be 0 or 1");
+  int rc = run_step(*m, tokens, targets, grads, grad_scale, accumulate);
   if (rc) return rc;
   float lossv = 0.f;
   int flag = 0;

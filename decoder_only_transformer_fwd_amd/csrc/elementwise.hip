@@ -513,7 +513,8 @@ __global__ __launch_bounds__(1024) void sort_keys_kernel(const int32_t* __restri
 // added in wave order, so the result does not depend on timing.
 __global__ __launch_bounds__(256) void embed_bwd_runs_kernel(const uint32_t* __restrict__ keys,
                                                              const float* __restrict__ dh, float* __restrict__ dE,
-                                                             int rows, int d, int pbits, int vocab) {
+                                                             int rows, int d, int pbits, int vocab,
+                                                             int accumulate) {
   __shared__ floatx4 part[3][64];
   const int i = blockIdx.x;
   const uint32_t id = keys[i] >> pbits;
@@ -552,6 +553,8 @@ __global__ __launch_bounds__(256) void embed_bwd_runs_kernel(const uint32_t* __r
     s += part[0][threadIdx.x];
     s += part[1][threadIdx.x];
     s += part[2][threadIdx.x];
+    // one work-group owns each id's row: the read-modify-write is race-free
+    if (accumulate) s += load4(dE + (long)id * d + c);
     store4(dE + (long)id * d + c, s);
   }
 }
@@ -691,14 +694,12 @@ void mean_reduce(const float* x, int n, float* out, hipStream_t st) {
 }
 
 void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab, uint32_t* keys,
-               int32_t* runs, int* nruns, hipStream_t st) {
-  (void)runs;
-  (void)nruns;
+               int accumulate, hipStream_t st) {
   int pbits = 0;
   while ((1 << pbits) < rows) ++pbits;
   int n2 = 1;
   while (n2 < rows) n2 <<= 1;
-  fill_f32(dE, (long)vocab * d, 0.f, st);
+  if (!accumulate) fill_f32(dE, (long)vocab * d, 0.f, st);
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)sort_keys_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
@@ -707,7 +708,7 @@ void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int 
   hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), n2 * sizeof(uint32_t), st, tokens, rows, pbits, n2,
                      vocab, keys);
   hipLaunchKernelGGL(embed_bwd_runs_kernel, dim3(rows, (d + 255) / 256), dim3(256), 0, st, keys, dh, dE, rows, d,
-                     pbits, vocab);
+                     pbits, vocab, accumulate);
 }
 
 void fill_f32(float* p, long n, float v, hipStream_t st) {

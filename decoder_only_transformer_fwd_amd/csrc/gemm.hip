@@ -573,8 +573,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             float* __restrict__ out, int accumulate) {
   const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= mn) return;
-  floatx4 s = accumulate ? *(const floatx4*)(out + i) : floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
   for (int z = 0; z < splits; ++z) s += *(const floatx4*)(part + (long)z * mn + i);
+  // accumulate: the product's value (as a storing call would write it) is
+  // added to out with one rounding
+  if (accumulate) s = *(const floatx4*)(out + i) + s;
   *(floatx4*)(out + i) = s;
 }
 
@@ -587,8 +590,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_strided_kernel(const float*
   if (i >= mn) return;
   const long m = i / N, n = i % N;
   float* o = out + m * ldc + n;
-  floatx4 s = accumulate ? *(const floatx4*)o : floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
   for (int z = 0; z < splits; ++z) s += *(const floatx4*)(part + (long)z * mn + i);
+  if (accumulate) s = *(const floatx4*)o + s;
   *(floatx4*)o = s;
 }
 
@@ -680,6 +684,7 @@ static int launch_epi(const GemmArgs& a, int layout, int epi, int tile, int spli
   GK_CASE(LAYOUT_KN, true, false, EPI_PARTIAL)
   // weight gradients: grad [K][M] x activation [K][N]
   GK_CASE(LAYOUT_MN, false, false, EPI_STORE_F32)
+  GK_CASE(LAYOUT_MN, false, false, EPI_ACCUM_F32)
   GK_CASE(LAYOUT_MN, false, false, EPI_PARTIAL)
 #undef GK_CASE
   return -1;

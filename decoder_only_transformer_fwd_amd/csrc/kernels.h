@@ -107,8 +107,9 @@ void attn_bwd_pre(int dtype, const void* dO, const void* O, float* Dv, void* dOT
 void xent_reduce(const float* part, const float* tgt, int rows, int nblk, float* lse, float* row_loss,
                  hipStream_t st);
 void mean_reduce(const float* x, int n, float* out, hipStream_t st);
+// dE[id] = (accumulate ? dE[id] : 0) + sum of dh rows whose token is id
 void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab,
-               uint32_t* keys, int32_t* runs, int* nruns, hipStream_t st);
+               uint32_t* keys, int accumulate, hipStream_t st);
 void fill_f32(float* p, long n, float v, hipStream_t st);
 
 // ---------------------------------------------------------------- fp8

@@ -119,6 +119,26 @@ int gpt_create(const gpt_config* cfg, gpt_model** out_model);
  * out-of-range id and GPT_ENONFINITE for a NaN/inf loss. */
 int gpt_step(gpt_model* model, const int32_t* tokens, const int32_t* targets, float* grads, float* loss);
 
+/* Gradient accumulation over micro-batches: a batch too large for one step
+ * is split into k micro-batches of B rows each, and the gradient of the
+ * mean loss over the whole batch is the mean of the micro-batch gradients
+ * (nanochat's training loop, gradient accumulation over micro-steps).
+ * Same as gpt_step, except that
+ *   grads <- grad_scale * g               (accumulate == 0)
+ *   grads <- grads + grad_scale * g       (accumulate == 1)
+ * where g is the gradient of this micro-batch's mean loss; *loss receives
+ * that (unscaled) mean.  grad_scale = 1/k with accumulate = 0 for the first
+ * micro-batch and 1 for the rest gives the full batch's gradient.  The scale
+ * multiplies the logit gradient, so every gradient carries it exactly once;
+ * each accumulated element is the fp32 sum, rounded once, of its previous
+ * value and the value a non-accumulating call would have stored.
+ * grad_scale must be finite (GPT_EINVAL otherwise); accumulate must be 0 or
+ * 1.  On GPT_ETOKEN / GPT_ENONFINITE the contents of grads are undefined
+ * (an accumulation in progress is lost).  gpt_step(...) is
+ * gpt_step_accum(..., 1.0f, 0, loss). */
+int gpt_step_accum(gpt_model* model, const int32_t* tokens, const int32_t* targets, float* grads,
+                   float grad_scale, int accumulate, float* loss);
+
 /* Release the handle (host memory only). */
 void gpt_destroy(gpt_model* model);
 

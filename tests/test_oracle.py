@@ -328,6 +328,20 @@ def test_unseen_embedding_rows_have_zero_gradient():
     assert np.all(np.any(G["E"][seen] != 0, axis=1))
 
 
+def test_batch_gradient_is_mean_of_sequence_gradients():
+    """The loss is the mean over all B*T positions and sequences do not
+    interact, so a batch's loss and gradient are the means of its sequences'
+    (the identity that gradient accumulation over micro-batches rests on)."""
+    s = small_shape(batch=3)
+    W, X, Y = load(s)
+    loss, G = O.forward_backward(s, W, X, Y)
+    s1 = s.replace(batch=1)
+    parts = [O.forward_backward(s1, W, X[b:b + 1], Y[b:b + 1]) for b in range(3)]
+    assert abs(loss - np.mean([p[0] for p in parts])) < 1e-12
+    for n, g in G.items():
+        np.testing.assert_allclose(g, sum(p[1][n] for p in parts) / 3, rtol=1e-9, atol=1e-15)
+
+
 # ---------------------------------------------------------------- inputs
 
 def test_zipf_head_probability():
