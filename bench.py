@@ -1,11 +1,14 @@
 """Benchmark: tokens/s and MFU of one GPT forward+backward training step on
 one MI355X, through the C ABI (``gpt_step``).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d24]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d24] [--grad-accum N]
 
 A step is one ``gpt_step`` call on one batch of seeded synthetic tokens with
 seeded random weights (inputs resident in HBM before the timed region); the
-timed region is K steps bracketed by device synchronisation.  The JSON line
+timed region is K steps bracketed by device synchronisation.  With
+``--grad-accum N`` a step is N ``gpt_step_accum`` calls over N different
+micro-batches of the workload's batch size, accumulating the gradient of
+their mean loss (N times the tokens per step).  The JSON line
 also carries the roofline of the dominant kernel (HIP-event timing of every
 launch site inside the timed region) and the CPU oracle's throughput on a
 bounded sample of the same workload.
@@ -59,6 +62,8 @@ def main() -> int:
     ap.add_argument("--config", default="d24", choices=sorted(gi.PRESETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sites", action="store_true", help="print per-site timings to stderr")
+    ap.add_argument("--grad-accum", type=int, default=1,
+                    help="micro-batches accumulated per step (gpt_step_accum)")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)")
@@ -69,26 +74,46 @@ def main() -> int:
     from decoder_only_transformer_fwd_amd import metrics as Mx
 
     s = gi.preset(args.config)
-    log(f"bench: {s}")
+    n_acc = args.grad_accum
+    if n_acc < 1:
+        log("--grad-accum must be at least 1")
+        return 2
+    log(f"bench: {s}" + (f", {n_acc} micro-batches per step" if n_acc > 1 else ""))
     W8 = gi.make_weights(s)
-    X, Y = gi.make_tokens(s)
     sess = G.Session(s, W8)
-    sess.set_tokens(X, Y)
     del W8
+    if n_acc == 1:
+        X, Y = gi.make_tokens(s)
+        sess.set_tokens(X, Y)
+
+        def step():
+            return sess.step()
+    else:
+        # N micro-batches drawn as one batch of N*B rows, all resident on the
+        # device before timing
+        X, Y = gi.make_tokens(s.replace(batch=s.batch * n_acc))
+        micro = [(torch.from_numpy(np.ascontiguousarray(X[i * s.batch:(i + 1) * s.batch])).to(sess.device),
+                  torch.from_numpy(np.ascontiguousarray(Y[i * s.batch:(i + 1) * s.batch])).to(sess.device))
+                 for i in range(n_acc)]
+
+        def step():
+            losses = [G.gpt_step_accum(sess.handle, x.data_ptr(), y.data_ptr(), sess.grads.data_ptr(),
+                                       1.0 / n_acc, i > 0) for i, (x, y) in enumerate(micro)]
+            return float(np.mean(losses))
     for _ in range(args.warmup):
-        sess.step()
+        step()
     sess.profile(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     loss = 0.0
     for _ in range(args.steps):
-        loss = sess.step()
+        loss = step()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     sites = sess.profile_sites()
     sess.profile(False)
 
-    tok_s = s.bt * args.steps / dt
+    tok_s = s.bt * n_acc * args.steps / dt
     peak = Mx.PEAK_FP32_MFMA if s.precision == "fp32" else Mx.PEAK_BF16
     mfu = tok_s * Mx.flops_per_token(s) / peak
     total_site_ms = sum(x["total_ms"] for x in sites)
@@ -165,7 +190,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,0.02) weights, seeded token ids)",
         "config": {"workload": s.name, "depth": s.depth, "d_model": s.d_model, "n_head": s.n_head,
                    "head_dim": s.head_dim, "mlp_hidden": s.mlp_hidden, "vocab": s.vocab,
-                   "seq_len": s.seq_len, "batch": s.batch, "tokens_per_step": s.bt,
+                   "seq_len": s.seq_len, "batch": s.batch, "grad_accum": n_acc, "tokens_per_step": s.bt * n_acc,
                    "window": s.window, "window_pattern": s.window_pattern, "token_dist": s.token_dist,
                    "precision": s.precision},
         "mfu": mfu,
