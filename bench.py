@@ -8,7 +8,8 @@ seeded random weights (inputs resident in HBM before the timed region); the
 timed region is K steps bracketed by device synchronisation.  With
 ``--grad-accum N`` a step is N ``gpt_step_accum`` calls over N different
 micro-batches of the workload's batch size, accumulating the gradient of
-their mean loss (N times the tokens per step).  The JSON line
+their mean loss (N times the tokens per step); with ``--optimizer`` each step
+ends with a Muon + AdamW update of the weights (``gpt_optim_step``).  The JSON line
 also carries the roofline of the dominant kernel (HIP-event timing of every
 launch site inside the timed region) and the CPU oracle's throughput on a
 bounded sample of the same workload.
@@ -64,6 +65,8 @@ def main() -> int:
     ap.add_argument("--sites", action="store_true", help="print per-site timings to stderr")
     ap.add_argument("--grad-accum", type=int, default=1,
                     help="micro-batches accumulated per step (gpt_step_accum)")
+    ap.add_argument("--optimizer", action="store_true",
+                    help="end every step with a Muon + AdamW update (gpt_optim_step)")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)")
@@ -100,6 +103,20 @@ def main() -> int:
             losses = [G.gpt_step_accum(sess.handle, x.data_ptr(), y.data_ptr(), sess.grads.data_ptr(),
                                        1.0 / n_acc, i > 0) for i, (x, y) in enumerate(micro)]
             return float(np.mean(losses))
+    if args.optimizer:
+        # the report card's learning rates, AdamW's scaled by 1/sqrt(d/768)
+        sc = (s.d_model / 768) ** -0.5
+        hp = G.optim_params(matrix_lr=0.02, momentum=0.95, nesterov=1, ns_steps=5, embedding_lr=0.2 * sc,
+                            unembedding_lr=0.004 * sc, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+                            grad_clip=1.0, step=1)
+        sess.optim_init()
+        fwd_bwd = step
+
+        def step():
+            loss = fwd_bwd()
+            sess.optim_step(hp)
+            hp.step += 1
+            return loss
     for _ in range(args.warmup):
         step()
     sess.profile(True)
@@ -191,6 +208,7 @@ def main() -> int:
         "config": {"workload": s.name, "depth": s.depth, "d_model": s.d_model, "n_head": s.n_head,
                    "head_dim": s.head_dim, "mlp_hidden": s.mlp_hidden, "vocab": s.vocab,
                    "seq_len": s.seq_len, "batch": s.batch, "grad_accum": n_acc, "tokens_per_step": s.bt * n_acc,
+                   "optimizer": "muon+adamw" if args.optimizer else None,
                    "window": s.window, "window_pattern": s.window_pattern, "token_dist": s.token_dist,
                    "precision": s.precision},
         "mfu": mfu,

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libgpt_mi355x.so")
 GPT_OK, GPT_EINVAL, GPT_ENULL, GPT_ETOKEN, GPT_EHIP, GPT_ENONFINITE, GPT_ESPACE, GPT_EALIGN = 0, -1, -2, -3, -4, -5, -6, -7
 GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 
-EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_destroy",
+EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum",
+            "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master", "gpt_destroy",
             "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
             "gpt_profile_sites", "gpt_profile_get", "gpt_strerror", "gpt_last_error"]
 
@@ -33,6 +34,26 @@ class gpt_config(ctypes.Structure):
         ("precision", ctypes.c_int32), ("weights", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
     ]
+
+
+class gpt_optim_params(ctypes.Structure):
+    _fields_ = [
+        ("matrix_lr", ctypes.c_float), ("momentum", ctypes.c_float), ("nesterov", ctypes.c_int32),
+        ("ns_steps", ctypes.c_int32), ("embedding_lr", ctypes.c_float), ("unembedding_lr", ctypes.c_float),
+        ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+        ("weight_decay", ctypes.c_float), ("grad_clip", ctypes.c_float), ("step", ctypes.c_int32),
+    ]
+
+
+def optim_params(**kw) -> gpt_optim_params:
+    """Optimizer parameters; every field must be given (no defaults are
+    implied by the library)."""
+    names = [f[0] for f in gpt_optim_params._fields_]
+    missing = [n for n in names if n not in kw]
+    extra = [n for n in kw if n not in names]
+    if missing or extra:
+        raise ValueError(f"optim_params: missing {missing}, unknown {extra}")
+    return gpt_optim_params(**{n: kw[n] for n in names})
 
 
 class gpt_tensor_desc(ctypes.Structure):
@@ -56,6 +77,10 @@ def _load():
     lib.gpt_create.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(P)]
     lib.gpt_step.argtypes = [P, P, P, P, ctypes.POINTER(F)]
     lib.gpt_step_accum.argtypes = [P, P, P, P, F, I, ctypes.POINTER(F)]
+    lib.gpt_optim_state_bytes.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(ctypes.c_size_t)]
+    lib.gpt_optim_init.argtypes = [P, P, ctypes.c_size_t]
+    lib.gpt_optim_step.argtypes = [P, P, P, ctypes.POINTER(gpt_optim_params), ctypes.POINTER(F)]
+    lib.gpt_optim_master.argtypes = [P, ctypes.POINTER(P)]
     lib.gpt_destroy.argtypes = [P]
     lib.gpt_destroy.restype = None
     lib.gpt_debug_tensor.argtypes = [P, I, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I64),
@@ -73,6 +98,7 @@ def _load():
     lib.gpt_last_error.argtypes = []
     lib.gpt_last_error.restype = ctypes.c_char_p
     for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum",
+                 "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
                  "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
                  "gpt_profile_sites", "gpt_profile_get"):
         getattr(lib, name).restype = I
@@ -155,6 +181,33 @@ def gpt_step_accum(model: int, tokens: int, targets: int, grads: int, grad_scale
     _check(_lib.gpt_step_accum(model, tokens, targets, grads, float(grad_scale), int(bool(accumulate)),
                                ctypes.byref(loss)), "gpt_step_accum")
     return loss.value
+
+
+def gpt_optim_state_bytes(cfg: gpt_config) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.gpt_optim_state_bytes(ctypes.byref(cfg), ctypes.byref(b)), "gpt_optim_state_bytes")
+    return b.value
+
+
+def gpt_optim_init(model: int, state: int, nbytes: int) -> None:
+    _check(_lib.gpt_optim_init(model, state, nbytes), "gpt_optim_init")
+
+
+def gpt_optim_step(model: int, state: int, grads: int, hp: gpt_optim_params, want_norm: bool = False):
+    """Enqueue one optimizer step; returns the gradient norm when asked
+    (which waits for the stream), else None."""
+    if want_norm:
+        n = ctypes.c_float()
+        _check(_lib.gpt_optim_step(model, state, grads, ctypes.byref(hp), ctypes.byref(n)), "gpt_optim_step")
+        return n.value
+    _check(_lib.gpt_optim_step(model, state, grads, ctypes.byref(hp), None), "gpt_optim_step")
+    return None
+
+
+def gpt_optim_master(model: int) -> int:
+    p = ctypes.c_void_p()
+    _check(_lib.gpt_optim_master(model, ctypes.byref(p)), "gpt_optim_master")
+    return p.value
 
 
 def gpt_destroy(model: int) -> None:
@@ -268,6 +321,29 @@ class Session:
     def step_accum(self, grad_scale: float, accumulate: bool) -> float:
         return gpt_step_accum(self.handle, self.tokens.data_ptr(), self.targets.data_ptr(), self.grads.data_ptr(),
                               grad_scale, accumulate)
+
+    def optim_init(self) -> None:
+        """Allocate (torch) and prepare the optimizer state of this model."""
+        t = self.torch
+        self.optim_bytes = gpt_optim_state_bytes(self.cfg)
+        self.optim_state = t.empty(self.optim_bytes, dtype=t.uint8, device=self.device)
+        gpt_optim_init(self.handle, self.optim_state.data_ptr(), self.optim_bytes)
+
+    def optim_step(self, hp: gpt_optim_params, want_norm: bool = False):
+        return gpt_optim_step(self.handle, self.optim_state.data_ptr(), self.grads.data_ptr(), hp, want_norm)
+
+    def master_numpy(self) -> Dict[str, np.ndarray]:
+        """fp32 master weights (copied to the host), per tensor."""
+        t = self.torch
+        ptr = gpt_optim_master(self.handle)
+        n = self.total
+        buf = t.empty(n, dtype=t.float32, device=self.device)
+        self.stream.synchronize()
+        rc = _hip().hipMemcpy(ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(ptr), ctypes.c_size_t(n * 4), 3)
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpy failed: {rc}")
+        g = buf.cpu().numpy()
+        return {name: g[off:off + r * c].reshape(r, c).copy() for name, off, r, c in self.layout}
 
     def step_rc(self) -> Tuple[int, float]:
         return gpt_step_rc(self.handle, self.tokens.data_ptr(), self.targets.data_ptr(), self.grads.data_ptr())

@@ -214,10 +214,18 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 }
 
 template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, int RB, int NS, bool A_KC, bool B_KC, int EPI,
-          typename TC, bool PP>
+          typename TC, bool PP, bool BATCHED>
 // Two waves per SIMD except for the 4-wave tiles whose accumulators need the
 // whole register file.
 __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 * 128) ? 1 : 2) void gemm_kernel(GemmArgs p) {
+  // batched products: this work-group's member of the batch
+  if constexpr (BATCHED) {
+    const long bz = blockIdx.y;
+    p.A = (const char*)p.A + bz * p.bsA * (long)sizeof(TA);
+    p.B = (const char*)p.B + bz * p.bsB * (long)sizeof(TA);
+    p.C = (char*)p.C + bz * p.bsC * (long)sizeof(TC);
+    p.aux = (const char*)p.aux + bz * p.bsC * (long)sizeof(TC);
+  }
   constexpr int THREADS = 64 * WGM * WGN;
   constexpr int NW = WGM * WGN;
   constexpr int ES = sizeof(TA);
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
     // Epilogues that read C (accumulate) or the saved pre-activation
     // (dReLU^2) load those values for a whole 32-row block up front: the
     // compiler cannot move a load above an earlier store that may alias it.
-    constexpr bool PRELOAD = EPI == EPI_ACCUM_F32 || EPI == EPI_DRELU2;
+    constexpr bool PRELOAD = EPI == EPI_ACCUM_F32 || EPI == EPI_DRELU2 || EPI == EPI_AXPBY;
     float amax_acc = 0.f;   // RELU2 / DRELU2: largest |stored activation|
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
@@ -553,6 +561,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
             store4((TC*)p.C + off, rr);
           } else if constexpr (EPI == EPI_PARTIAL) {
             store4(p.part + (long)blockIdx.z * p.M * p.N + (long)m * p.N + n, v);
+          } else if constexpr (EPI == EPI_AXPBY) {
+            floatx4 rr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[e] = fmaf(p.beta, pre[st][e], v[e]);
+            store4((TC*)p.C + off, rr);
           }
         }
       }
@@ -635,7 +648,7 @@ template <typename TA, typename MF, int T, bool AK, bool BK_, int EPI, typename 
 static void launch_cfg(const GemmArgs& a, int splits, hipStream_t st) {
   constexpr TileCfg c = TILES[T];
   dim3 grid(((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn), 1, splits);
-  hipLaunchKernelGGL((gemm_kernel<TA, MF, c.bm, c.bn, c.wgm, c.wgn, c.rb, c.ns, AK, BK_, EPI, TC, c.pp>), grid,
+  hipLaunchKernelGGL((gemm_kernel<TA, MF, c.bm, c.bn, c.wgm, c.wgn, c.rb, c.ns, AK, BK_, EPI, TC, c.pp, false>), grid,
                      dim3(64 * c.wgm * c.wgn), 0, st, a);
 }
 
@@ -708,6 +721,34 @@ static int launch_fp8(const GemmArgs& a, int layout, int epi, int tile, int spli
   GK_F8(EPI_DRELU2)
   GK_F8(EPI_PARTIAL)
 #undef GK_F8
+  return -1;
+}
+
+template <typename TA, typename MF, typename TC, int T, bool AK, bool BK_, int EPI>
+static void launch_batched_cfg(const GemmArgs& a, int batch, hipStream_t st) {
+  constexpr TileCfg c = TILES[T];
+  dim3 grid(((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn), batch, 1);
+  hipLaunchKernelGGL((gemm_kernel<TA, MF, c.bm, c.bn, c.wgm, c.wgn, c.rb, c.ns, AK, BK_, EPI, TC, c.pp, true>), grid,
+                     dim3(64 * c.wgm * c.wgn), 0, st, a);
+}
+
+template <bool AK, bool BK_, int EPI>
+static int launch_batched_tile(const GemmArgs& a, int tile, int batch, hipStream_t st) {
+  if (tile == TILE_256x256_PP4)
+    launch_batched_cfg<bf16, Mfma<bf16>, bf16, TILE_256x256_PP4, AK, BK_, EPI>(a, batch, st);
+  else if (tile == TILE_128x128)
+    launch_batched_cfg<bf16, Mfma<bf16>, bf16, TILE_128x128, AK, BK_, EPI>(a, batch, st);
+  else
+    return -1;
+  return 0;
+}
+
+int gemm_launch_batched(const GemmArgs& a, int layout, int epi, int tile, int batch, hipStream_t st) {
+  if (batch < 1 || batch > 65535) return -1;
+  if (layout == LAYOUT_KK && epi == EPI_STORE) return launch_batched_tile<true, true, EPI_STORE>(a, tile, batch, st);
+  if (layout == LAYOUT_KK && epi == EPI_AXPBY) return launch_batched_tile<true, true, EPI_AXPBY>(a, tile, batch, st);
+  if (layout == LAYOUT_KN && epi == EPI_AXPBY) return launch_batched_tile<true, false, EPI_AXPBY>(a, tile, batch, st);
+  if (layout == LAYOUT_MN && epi == EPI_STORE) return launch_batched_tile<false, false, EPI_STORE>(a, tile, batch, st);
   return -1;
 }
 

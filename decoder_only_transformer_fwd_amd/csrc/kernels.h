@@ -30,6 +30,7 @@ enum Epi {
   EPI_XENT_FWD = 5,   // per-row partial (max, sum exp) + target logit
   EPI_XENT_BWD = 6,   // C = (exp(acc - lse) - onehot(target)) * beta
   EPI_PARTIAL = 7,    // part[split][M][N] = acc (split-K)
+  EPI_AXPBY = 8,      // C (activation type) = alpha * acc + beta * aux (aux laid out as C)
 };
 
 // Work-group tiles (M x N); _W8 variants use 8 waves (2 x 4) instead of 4 (2 x 2).
@@ -70,10 +71,16 @@ struct GemmArgs {
   int k_split;     // K elements handled per blockIdx.z
   int nblk;        // EPI_XENT_FWD: number of column blocks of width BN/2
   unsigned* amax;  // EPI_RELU2 / EPI_DRELU2: if set, max |stored g / du| is folded in (float bits)
+  // Batched products (grid y = batch index): element strides between the
+  // batch's A, B and C (aux shares C's); zero for a single product.
+  long bsA, bsB, bsC;
 };
 
 int gemm_launch(const GemmArgs& a, int dtype, int layout, int epi, int tile, int splits,
                 hipStream_t st);
+// `batch` independent bf16 products of one shape (strides in a.bsA/bsB/bsC),
+// one grid; no split-K.
+int gemm_launch_batched(const GemmArgs& a, int layout, int epi, int tile, int batch, hipStream_t st);
 void splitk_reduce(const float* part, int splits, long mn, float* out, int accumulate,
                    hipStream_t st);
 // out[m * ldc + n] (+)= sum over z of part[z][m][n] for an M x N block of a
@@ -111,6 +118,37 @@ void mean_reduce(const float* x, int n, float* out, hipStream_t st);
 void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab,
                uint32_t* keys, int accumulate, hipStream_t st);
 void fill_f32(float* p, long n, float v, hipStream_t st);
+
+// ---------------------------------------------------------------- optimizer
+// One tensor of a pass list.  Passes walk their list in chunks of OPT_CHUNK
+// elements; blk0 is the tensor's first chunk index within the list, and every
+// list ends with a sentinel entry whose blk0 is the list's chunk count.
+constexpr int OPT_CHUNK = 4096;
+struct OptSeg {
+  long off;    // element offset in the parameter / gradient / master buffers
+  long soff;   // element offset of its state (Muon: momentum; AdamW: m, then v at soff + n)
+  long n;      // elements (a multiple of 4)
+  long xoff;   // Muon: element offset of its matrix in the Newton-Schulz buffer
+  int blk0;
+  int which;   // AdamW: 0 takes AdamArgs::lr0, 1 takes lr1
+};
+struct AdamArgs {
+  float b1, b2, eps, wd;
+  float ibc1, ibc2;   // 1 / (1 - b1^t), 1 / (1 - b2^t)
+  float lr0, lr1;
+};
+void opt_sumsq(const float* x, const OptSeg* seg, int nseg, int nblk, float* part, hipStream_t st);
+void opt_norm(const float* part, int nblk, float clip, float* hdr, hipStream_t st);
+void opt_adamw(float* master, float* state, const float* g, void* w16, const OptSeg* seg, int nseg, int nblk,
+               const float* hdr, const AdamArgs& a, hipStream_t st);
+void opt_muon_momentum(const float* g, float* state, const OptSeg* seg, int nseg, int nblk, const float* hdr,
+                       float mu, int nesterov, float* part, hipStream_t st);
+void opt_muon_normalise(const float* g, const float* state, const OptSeg* seg, int nseg, int nblk,
+                        const float* hdr, float mu, int nesterov, const float* part, void* X, hipStream_t st);
+// p <- p (1 - lr wd) - lr * scale * O
+void opt_muon_update(float* master, const void* X, void* w16, const OptSeg* seg, int nseg, int nblk, float lr,
+                     float scale, float wd, hipStream_t st);
+void opt_widen(const void* w16, float* master, const OptSeg* seg, int nseg, int nblk, hipStream_t st);
 
 // ---------------------------------------------------------------- fp8
 void zero_u32(unsigned* p, int n, hipStream_t st);

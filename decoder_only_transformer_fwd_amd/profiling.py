@@ -53,9 +53,11 @@ def decode(name: str, demangled: str = None) -> str:
     dm = re.sub(r"\((GemmArgs|AttnArgs|[^()]*)\)$", "", dm)
     if "gemm_kernel<" in dm:
         m = re.match(r"gemm_kernel<(bf16|float|u8), (Mfma<\w+>|MfmaF8<(\d), (\d)>), (\d+), (\d+), (\d+), (\d+), "
-                     r"(\d+), (\d+), (true|false), (true|false), (\d+), \w+, (true|false)>$", dm)
+                     r"(\d+), (\d+), (true|false), (true|false), (\d+), \w+, (true|false), (true|false)>$", dm)
+        batched = False
         if m:
-            ty, _, fb, fa, bm, bn, wgm, wgn, rb, ns, akc, bkc, epi, pp = m.groups()
+            ty, _, fb, fa, bm, bn, wgm, wgn, rb, ns, akc, bkc, epi, pp, bt = m.groups()
+            batched = bt == "true"
             if ty == "u8":
                 fmt = {"0": "e4m3", "1": "e5m2"}
                 ty = f"fp8 {fmt[fa]} x {fmt[fb]}"   # the MFMA takes the B operand first
@@ -69,7 +71,7 @@ def decode(name: str, demangled: str = None) -> str:
             key = tuple(int(x) for x in (bm, bn, wgm, wgn, rb, ns))
             pp = key in _PP
         return (f"gemm_kernel<{ty}, {bm}, {bn}, {wgm}, {wgn}, {rb}, {ns}, {akc}, {bkc}, {epi}"
-                f"{', ping-pong' if pp else ''}>")
+                f"{', ping-pong' if pp else ''}{', batched' if batched else ''}>")
     return dm
 
 

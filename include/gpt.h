@@ -139,6 +139,65 @@ int gpt_step(gpt_model* model, const int32_t* tokens, const int32_t* targets, fl
 int gpt_step_accum(gpt_model* model, const int32_t* tokens, const int32_t* targets, float* grads,
                    float grad_scale, int accumulate, float* loss);
 
+/* ------------------------------------------------------------ optimizer
+ * One optimizer step over every parameter, after the gradients of the step
+ * (or of accumulated micro-batches) are complete: Muon on the projection
+ * matrices (Wq, Wk, Wv, Wo, W1, W2, each matrix on its own) and AdamW on the
+ * embedding E and the lm_head U ("Introducing nanochat", the pretraining log
+ * and the paragraph after it; learning rates, weight decay and the gradient
+ * clip of its report card's base-model section).  The pages name Muon
+ * without its algorithm; it follows the published description (K. Jordan et
+ * al., 2024): Nesterov momentum, then the update is orthogonalised by the
+ * quintic Newton-Schulz iteration X <- a X + (b A + c A^2) X, A = X X^T,
+ * (a, b, c) = (3.4445, -4.7750, 2.0315), on the Frobenius-normalised update
+ * in bf16, and scaled by sqrt(max(1, rows/cols)).  AdamW has bias-corrected
+ * moments and decoupled weight decay.  Muon momentum is kept as
+ *   buf <- mu buf + (1 - mu) g,   u = (1 - mu) g + mu buf   (nesterov)
+ *   or u = buf,
+ * which differs from mu buf + g only by a factor the normalisation removes.
+ * Every gradient is first scaled by min(1, grad_clip / (||g|| + 1e-6)),
+ * ||g|| the 2-norm over all parameters (grad_clip <= 0: no clipping). */
+typedef struct {
+  float matrix_lr;       /* Muon learning rate */
+  float momentum;        /* Muon momentum mu, in [0, 1) */
+  int32_t nesterov;      /* 1: Nesterov look-ahead, 0: plain momentum */
+  int32_t ns_steps;      /* Newton-Schulz iterations, 1..32 (5) */
+  float embedding_lr;    /* AdamW learning rate of E */
+  float unembedding_lr;  /* AdamW learning rate of U */
+  float beta1, beta2;    /* AdamW moment decays, in [0, 1) */
+  float eps;             /* AdamW denominator epsilon, > 0 */
+  float weight_decay;    /* decoupled: p <- p (1 - lr wd) for every parameter */
+  float grad_clip;       /* global-norm clip; <= 0 disables */
+  int32_t step;          /* AdamW step count t >= 1 (bias correction) */
+} gpt_optim_params;
+
+/* Bytes of device state the optimizer needs for this config: fp32 master
+ * weights (bf16 parameters only), Muon momenta, AdamW moments, pass tables
+ * and the Newton-Schulz work buffers. */
+int gpt_optim_state_bytes(const gpt_config* cfg, size_t* bytes);
+
+/* Prepare `state` (device, 256-byte aligned, at least gpt_optim_state_bytes)
+ * for this model: master weights from the model's weight buffer, zero
+ * moments.  Synchronises the model's stream.  The model remembers the state;
+ * a later gpt_optim_init (any state) replaces it. */
+int gpt_optim_init(gpt_model* model, void* state, size_t state_bytes);
+
+/* One optimizer step with device fp32 gradients `grads` (parameter layout):
+ * updates the master weights and moments in `state` and rewrites the
+ * model's weight buffer (cfg->weights) with the new weights (bf16: rounded
+ * to nearest even from the fp32 masters).  Enqueued on the model's stream;
+ * returns without waiting unless grad_norm (host, optional) is given, which
+ * then receives the gradient norm before clipping.  Errors: GPT_EINVAL for
+ * a state not prepared for this model or out-of-range parameters (nothing
+ * is enqueued then). */
+int gpt_optim_step(gpt_model* model, void* state, const float* grads, const gpt_optim_params* hp,
+                   float* grad_norm);
+
+/* Device pointer to the fp32 master weights in the parameter layout (inside
+ * the state gpt_optim_init prepared; for GPT_FP32 models, the weight buffer
+ * itself), e.g. to checkpoint them. */
+int gpt_optim_master(gpt_model* model, float** master);
+
 /* Release the handle (host memory only). */
 void gpt_destroy(gpt_model* model);
 

@@ -30,3 +30,12 @@ def test_algorithmic_flops_count_visible_pairs():
     attn_conv = M.flops_per_token(t) - 6 * M.scaling_params(t)
     attn_alg = M.algorithmic_flops_per_token(t) - 6 * M.scaling_params(t)
     assert abs(attn_alg / attn_conv - (t.seq_len + 1) / (2 * t.seq_len)) < 1e-12
+
+
+def test_profiler_kernel_names_decode_to_step_labels():
+    from decoder_only_transformer_fwd_amd import profiling as Pf
+    base = "void gk::gemm_kernel<__bf16, gk::Mfma<__bf16>, 256, 256, 2, 4, 64, 4, true, false, 8, __bf16, true, {}>" \
+           "(gk::GemmArgs)"
+    assert Pf.decode("k", base.format("false")) == "gemm_kernel<bf16, 256, 256, 2, 4, 64, 4, true, false, 8, ping-pong>"
+    assert Pf.decode("k", base.format("true")) == \
+        "gemm_kernel<bf16, 256, 256, 2, 4, 64, 4, true, false, 8, ping-pong, batched>"
