@@ -62,14 +62,22 @@ __global__ __launch_bounds__(256) void opt_sumsq_kernel(const float* __restrict_
 // hdr[0] = sqrt(sum part), hdr[1] = clip coefficient min(1, clip / (norm +
 // 1e-6)) (1 when clip <= 0).  One work-group; the partials are added in a
 // fixed order in double.
-__global__ __launch_bounds__(256) void opt_norm_kernel(const float* __restrict__ part, int nb, float clip,
-                                                       float* __restrict__ hdr) {
-  __shared__ double red[256];
-  double acc = 0.0;
-  for (int i = threadIdx.x; i < nb; i += 256) acc += (double)part[i];
-  red[threadIdx.x] = acc;
+__global__ __launch_bounds__(1024) void opt_norm_kernel(const float* __restrict__ part, int nb, float clip,
+                                                        float* __restrict__ hdr) {
+  __shared__ double red[1024];
+  // four independent running sums per thread keep four loads in flight
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int i = threadIdx.x;
+  for (; i + 3 * 1024 < nb; i += 4 * 1024) {
+    a0 += (double)part[i];
+    a1 += (double)part[i + 1024];
+    a2 += (double)part[i + 2 * 1024];
+    a3 += (double)part[i + 3 * 1024];
+  }
+  for (; i < nb; i += 1024) a0 += (double)part[i];
+  red[threadIdx.x] = (a0 + a1) + (a2 + a3);
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
+  for (int o = 512; o > 0; o >>= 1) {
     if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
@@ -225,7 +233,7 @@ void opt_sumsq(const float* x, const OptSeg* seg, int nseg, int nblk, float* par
   hipLaunchKernelGGL(opt_sumsq_kernel, dim3(nblk), dim3(256), 0, st, x, seg, nseg, part);
 }
 void opt_norm(const float* part, int nblk, float clip, float* hdr, hipStream_t st) {
-  hipLaunchKernelGGL(opt_norm_kernel, dim3(1), dim3(256), 0, st, part, nblk, clip, hdr);
+  hipLaunchKernelGGL(opt_norm_kernel, dim3(1), dim3(1024), 0, st, part, nblk, clip, hdr);
 }
 void opt_adamw(float* master, float* state, const float* g, void* w16, const OptSeg* seg, int nseg, int nblk,
                const float* hdr, const AdamArgs& a, hipStream_t st) {

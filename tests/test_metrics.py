@@ -39,3 +39,9 @@ def test_profiler_kernel_names_decode_to_step_labels():
     assert Pf.decode("k", base.format("false")) == "gemm_kernel<bf16, 256, 256, 2, 4, 64, 4, true, false, 8, ping-pong>"
     assert Pf.decode("k", base.format("true")) == \
         "gemm_kernel<bf16, 256, 256, 2, 4, 64, 4, true, false, 8, ping-pong, batched>"
+    garbled = "void gk::gemm_kernel<bool _Accum, gk, Mfma<bool _Accum>, 256, 256, 2, 4, 64, 4, true, true, 8, " \
+              "bool _Accum, bool, E, {}>(gk::GemmArgs)"
+    assert Pf.decode("k", garbled.format("false")) == \
+        "gemm_kernel<bf16, 256, 256, 2, 4, 64, 4, true, true, 8, ping-pong>"
+    assert Pf.decode("k", garbled.format("true")) == \
+        "gemm_kernel<bf16, 256, 256, 2, 4, 64, 4, true, true, 8, ping-pong, batched>"
