@@ -55,6 +55,94 @@ def cpu_baseline(s, budget_rows: int = 1) -> dict:
                       f"rows ({sample.bt} tokens), fp64 numpy, {dt:.1f} s"}
 
 
+def decode_bytes(s, pos: int) -> float:
+    """HBM bytes one decode step must move at position pos: every weight
+    matrix and the lm_head once (bf16), the batch's embedding rows, and each
+    layer's visible cached keys and values plus the new ones."""
+    d, f = s.d_model, s.mlp_hidden
+    weights = 2.0 * (s.depth * (4 * d * d + 2 * d * f) + s.vocab * d) + 2.0 * s.batch * d
+    kv = 0.0
+    for w in gi.layer_windows(s):
+        vis = min(pos + 1, w)
+        kv += 2.0 * 2.0 * s.batch * s.n_head * s.head_dim * (vis + 1)
+    logits = 4.0 * s.batch * s.vocab
+    return weights + kv + logits
+
+
+def bench_decode(args, s) -> int:
+    import torch
+    import decoder_only_transformer_fwd_amd as G
+    from decoder_only_transformer_fwd_amd import metrics as Mx
+    P, K, Wm = args.prompt, args.steps, args.warmup
+    if P + Wm + K > s.seq_len:
+        log(f"--prompt + --warmup + --steps must be <= seq_len ({s.seq_len})")
+        return 2
+    log(f"bench decode: {s}, prompt {P}, {K} timed steps")
+    W8 = gi.make_weights(s)
+    sess = G.Session(s, W8)
+    del W8
+    sess.infer_init()
+    X, _ = gi.make_tokens(s)
+    prompt = torch.from_numpy(np.ascontiguousarray(X[:, :P])).to(sess.device)
+    toks = [torch.from_numpy(np.ascontiguousarray(X[:, p])).to(sess.device) for p in range(P, P + Wm + K)]
+    sess.prefill(prompt)   # warm-up of the prefill path
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sess.prefill(prompt)
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    # timed: each step replays the captured graph of the decoding step
+    for i in range(Wm):
+        sess.decode(toks[i], P + i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(Wm, Wm + K):
+        sess.decode(toks[i], P + i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt / K * 1e3
+    byts = sum(decode_bytes(s, P + i) for i in range(Wm, Wm + K)) / K
+    # per-launch timing: the same steps again, run eagerly with HIP events
+    sess.prefill(prompt)
+    for i in range(Wm):
+        sess.decode(toks[i], P + i)
+    sess.profile(True)
+    for i in range(Wm, Wm + K):
+        sess.decode(toks[i], P + i)
+    sites = sess.profile_sites()
+    sess.profile(False)
+    kernel_ms = sum(x["total_ms"] for x in sites) / K
+    if args.sites:
+        for x in sorted(sites, key=lambda x: -x["total_ms"]):
+            log(f"  {x['name']:28s} {x['launches']:6d} launches {x['total_ms'] / K:9.4f} ms/step")
+    out = {
+        "metric": "decode tokens/s (KV-cache, one token per row per step)",
+        "value": s.batch * K / dt,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, seeded token ids)",
+        "config": {"workload": s.name, "depth": s.depth, "d_model": s.d_model, "n_head": s.n_head,
+                   "head_dim": s.head_dim, "mlp_hidden": s.mlp_hidden, "vocab": s.vocab, "batch": s.batch,
+                   "prompt": P, "window": s.window, "window_pattern": s.window_pattern},
+        "prefill": {"tokens_per_s": s.batch * P / t_prefill, "ms": t_prefill * 1e3},
+        "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9, "peak": Mx.PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": byts / (ms * 1e-3) / Mx.PEAK_HBM, "traffic": None,
+                     "kernel": "whole decode step (graph replay, wall time)", "bytes_per_step": byts,
+                     "kernel_ms_per_step_eager": kernel_ms},
+        "cpu_baseline": None,
+    }
+    sess.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -67,6 +155,10 @@ def main() -> int:
                     help="micro-batches accumulated per step (gpt_step_accum)")
     ap.add_argument("--optimizer", action="store_true",
                     help="end every step with a Muon + AdamW update (gpt_optim_step)")
+    ap.add_argument("--decode", action="store_true",
+                    help="KV-cache inference instead of training: prefill --prompt tokens per row, "
+                         "then time --steps decode steps (one token per row each)")
+    ap.add_argument("--prompt", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)")
@@ -77,6 +169,8 @@ def main() -> int:
     from decoder_only_transformer_fwd_amd import metrics as Mx
 
     s = gi.preset(args.config)
+    if args.decode:
+        return bench_decode(args, s)
     n_acc = args.grad_accum
     if n_acc < 1:
         log("--grad-accum must be at least 1")

@@ -20,7 +20,8 @@ GPT_OK, GPT_EINVAL, GPT_ENULL, GPT_ETOKEN, GPT_EHIP, GPT_ENONFINITE, GPT_ESPACE,
 GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 
 EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum",
-            "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master", "gpt_destroy",
+            "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
+            "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_destroy",
             "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
             "gpt_profile_sites", "gpt_profile_get", "gpt_strerror", "gpt_last_error"]
 
@@ -81,6 +82,9 @@ def _load():
     lib.gpt_optim_init.argtypes = [P, P, ctypes.c_size_t]
     lib.gpt_optim_step.argtypes = [P, P, P, ctypes.POINTER(gpt_optim_params), ctypes.POINTER(F)]
     lib.gpt_optim_master.argtypes = [P, ctypes.POINTER(P)]
+    lib.gpt_kv_cache_bytes.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(ctypes.c_size_t)]
+    lib.gpt_prefill.argtypes = [P, P, I, P, P]
+    lib.gpt_decode.argtypes = [P, P, I, P, P]
     lib.gpt_destroy.argtypes = [P]
     lib.gpt_destroy.restype = None
     lib.gpt_debug_tensor.argtypes = [P, I, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I64),
@@ -99,6 +103,7 @@ def _load():
     lib.gpt_last_error.restype = ctypes.c_char_p
     for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum",
                  "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
+                 "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode",
                  "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
                  "gpt_profile_sites", "gpt_profile_get"):
         getattr(lib, name).restype = I
@@ -208,6 +213,20 @@ def gpt_optim_master(model: int) -> int:
     p = ctypes.c_void_p()
     _check(_lib.gpt_optim_master(model, ctypes.byref(p)), "gpt_optim_master")
     return p.value
+
+
+def gpt_kv_cache_bytes(cfg: gpt_config) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.gpt_kv_cache_bytes(ctypes.byref(cfg), ctypes.byref(b)), "gpt_kv_cache_bytes")
+    return b.value
+
+
+def gpt_prefill(model: int, tokens: int, n_tokens: int, kv_cache: int, logits: int) -> None:
+    _check(_lib.gpt_prefill(model, tokens, n_tokens, kv_cache, logits), "gpt_prefill")
+
+
+def gpt_decode(model: int, tokens: int, pos: int, kv_cache: int, logits: int) -> None:
+    _check(_lib.gpt_decode(model, tokens, pos, kv_cache, logits), "gpt_decode")
 
 
 def gpt_destroy(model: int) -> None:
@@ -344,6 +363,30 @@ class Session:
             raise RuntimeError(f"hipMemcpy failed: {rc}")
         g = buf.cpu().numpy()
         return {name: g[off:off + r * c].reshape(r, c).copy() for name, off, r, c in self.layout}
+
+    def infer_init(self) -> None:
+        """Allocate (torch) the KV cache and a logits buffer."""
+        t = self.torch
+        self.kv_bytes = gpt_kv_cache_bytes(self.cfg)
+        self.kv = t.empty(self.kv_bytes, dtype=t.uint8, device=self.device)
+        self.logits = t.empty((self.shape.batch, self.shape.vocab), dtype=t.float32, device=self.device)
+
+    def prefill(self, prompt) -> "np.ndarray":
+        """prompt: int32 [B, n] (host array or device tensor); returns the
+        next-token logits [B, V] as a device tensor."""
+        t = self.torch
+        x = prompt if isinstance(prompt, t.Tensor) else t.from_numpy(np.ascontiguousarray(prompt, np.int32))
+        x = x.to(self.device).contiguous()
+        gpt_prefill(self.handle, x.data_ptr(), x.shape[1], self.kv.data_ptr(), self.logits.data_ptr())
+        return self.logits
+
+    def decode(self, tokens, pos: int):
+        """tokens: int32 [B] at position pos; returns logits [B, V] (device)."""
+        t = self.torch
+        x = tokens if isinstance(tokens, t.Tensor) else t.from_numpy(np.ascontiguousarray(tokens, np.int32))
+        x = x.to(self.device).contiguous()
+        gpt_decode(self.handle, x.data_ptr(), pos, self.kv.data_ptr(), self.logits.data_ptr())
+        return self.logits
 
     def step_rc(self) -> Tuple[int, float]:
         return gpt_step_rc(self.handle, self.tokens.data_ptr(), self.targets.data_ptr(), self.grads.data_ptr())

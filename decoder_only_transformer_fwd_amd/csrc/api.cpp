@@ -33,6 +33,10 @@ int fail(int code, const std::string& msg) {
   } while (0)
 
 constexpr size_t ALIGN = 256;
+// decoding: K splits of the products whose few weight rows would leave most
+// CUs idle (output projection, W2); their partials go through the next norm
+constexpr int DEC_KSPLIT = 8;
+static_assert(DEC_KSPLIT <= 8, "the decoder's add + norm kernel adds at most 8 partials");
 size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 
 struct Shape {
@@ -266,7 +270,7 @@ struct gpt_model {
     size_t n1T, oT, n2T, gT, wq[4], wqT[4];
   };
   std::vector<Layer> lay;
-  size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
+  size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, dpart, dtok, dpos, dsplit, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
       cosb, sinb, keys, total;
   size_t splitk_floats;
   size_t q8row, q8T, amax, scales;   // fp8: transient codes, per-tensor amax / scale slots
@@ -287,6 +291,17 @@ struct gpt_model {
   };
   OptPlan opt;
   void* opt_state = nullptr;   // the state buffer gpt_optim_init prepared
+  // decoding: one step captured as a HIP graph (for the cache and logits
+  // buffers it was captured with), replayed on a stream of its own that is
+  // ordered after the model's stream by events
+  struct DecodeGraph {
+    hipStream_t cs = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t before = nullptr, after = nullptr;
+    const void* kv = nullptr;
+    const void* logits = nullptr;
+  } dg;
   bool prof_on = false;
   std::vector<Site> sites;
   std::vector<hipEvent_t> ev_pool;
@@ -296,6 +311,11 @@ struct gpt_model {
   double cur_work = 0.0;
   ~gpt_model() {
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+    if (dg.exec) (void)hipGraphExecDestroy(dg.exec);
+    if (dg.graph) (void)hipGraphDestroy(dg.graph);
+    if (dg.before) (void)hipEventDestroy(dg.before);
+    if (dg.after) (void)hipEventDestroy(dg.after);
+    if (dg.cs) (void)hipStreamDestroy(dg.cs);
   }
 };
 
@@ -340,6 +360,12 @@ int build_layout(gpt_model& m) {
   m.rowloss = take(BT * 4);
   m.lossdev = take(64);
   m.flag = take(64);
+  // decoding: attention split partials (128 keys per split), the step's
+  // token ids and position
+  m.dpart = take((size_t)s.B * s.H * ((s.T + 127) / 128) * (s.Dh + 1) * 4);
+  m.dtok = take((size_t)s.B * 4);
+  m.dsplit = take((size_t)DEC_KSPLIT * s.B * std::max(s.d, s.F) * 4);
+  m.dpos = take(64);
   m.dz = take(BT * s.V * A);
   m.dm = take(BT * s.d * 4);
   m.dh = take(BT * s.d * 4);
@@ -540,10 +566,11 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
 // One forward+backward pass.  Every gradient is linear in the logit gradient,
 // so grad_scale is applied there (once); with accumulate set, the weight
 // gradient products and the embedding scatter add to grads instead of
-// overwriting it.
+// overwriting it.  `shape` (default: the model's) may describe fewer tokens
+// per row; forward_only stops after the final norm (prefill).
 int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float* grads, float grad_scale,
-             int accumulate) {
-  const Shape& s = m.s;
+             int accumulate, const Shape* shape = nullptr, bool forward_only = false) {
+  const Shape& s = shape ? *shape : m.s;
   const ParamOffsets& P = m.po;
   const int dt = s.dtype;
   const size_t es = s.es;
@@ -686,6 +713,10 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   prof_begin(m, "rmsnorm_fwd", (double)BT * d * (4.0 + es_d) + BT * 4.0, 1, norm_label("rmsnorm_fwd"));
   rmsnorm_fwd(dt, h, m.ws + m.nL, at<float>(m, m.rstdL), BT, d, s.eps, st);
   prof_end(m);
+  if (forward_only) {
+    HIP_TRY(hipGetLastError());
+    return GPT_OK;
+  }
   {
     GemmArgs ex{};
     ex.aux = targets;
@@ -1029,6 +1060,161 @@ int run_optim(gpt_model& m, char* state, const float* grads, const gpt_optim_par
   return GPT_OK;
 }
 
+// ------------------------------------------------------------------ inference
+size_t kv_layer_elems(const Shape& s) { return (size_t)s.B * s.H * s.T * s.Dh; }
+
+int check_infer(gpt_model& m) {
+  if (m.s.dtype != DT_BF16) return fail(GPT_EINVAL, "inference runs on bf16 parameters (GPT_BF16 or GPT_FP8 models)");
+  if (m.s.B > 32) return fail(GPT_EINVAL, "inference supports batch <= 32");
+  if (m.s.Dh != 64 && m.s.Dh != 128) return fail(GPT_EINVAL, "inference supports head_dim 64 or 128");
+  return GPT_OK;
+}
+
+// One skinny product of decoding, timed as a site like the step's products.
+int dec_gemm(gpt_model& m, const char* site, int epi, const void* x, long ldx, int K, const void* Wt, int N, void* C,
+             int ldc, void* C2 = nullptr, int ksplit = 1) {
+  const int B = m.s.B;
+  prof_begin(m, site, 2.0 * B * (double)N * K, 0, std::string("skinny_gemm_kernel<") + std::to_string(epi) + ">");
+  if (skinny_gemm(epi, x, ldx, B, K, Wt, N, C, ldc, C2, ksplit, m.st)) return fail(GPT_EINVAL, "skinny gemm shape");
+  prof_end(m);
+  return GPT_OK;
+}
+
+// Prefill: the forward over n tokens per row (positions 0..n-1), the keys and
+// values of every layer into the cache, and the next-token logits of the
+// last position.
+int run_prefill(gpt_model& m, const int32_t* tokens, int n, char* kv, float* logits) {
+  Shape sp = m.s;
+  sp.T = n;
+  sp.BT = sp.B * n;
+  sp.Tp = (n + 63) / 64 * 64;
+  sp.fp8 = false;   // fp8 models decode with their bf16 weights
+  for (auto& w : sp.win) w = std::min(w, n);
+  int rc = run_step(m, tokens, tokens, nullptr, 1.f, 0, &sp, true);
+  if (rc) return rc;
+  const Shape& s = m.s;
+  const size_t kvl = kv_layer_elems(s);
+  prof_begin(m, "prefill_kv_fill", (double)sp.BT * 2.0 * s.d * 2.0 * 2.0, 1, "kv_fill_kernel");
+  for (int l = 0; l < s.L; ++l) {
+    uint16_t* kc = (uint16_t*)kv + (size_t)2 * l * kvl;
+    kv_fill(m.ws + m.lay[l].qkv, kc, kc + kvl, s.B, n, s.H, s.Dh, s.T, m.st);
+  }
+  prof_end(m);
+  // rows b*n + n - 1 of the final normalised activations
+  return dec_gemm(m, "prefill_lm_head", EPI_STORE_F32, m.ws + m.nL + (size_t)(n - 1) * s.d * 2, (long)n * s.d, s.d,
+                  m.W + (size_t)m.po.U * 2, s.V, logits, s.V);
+}
+
+// One decoding step on the model's stream: token ids and position come from
+// the decoder's device buffers (decode_stage fills them), so the launch
+// sequence does not depend on them and can be captured once.  `pos` (host)
+// only sizes the profiler's work accounting.
+int run_decode(gpt_model& m, int pos, char* kv, float* logits) {
+  const Shape& s = m.s;
+  const ParamOffsets& P = m.po;
+  const int B = s.B, d = s.d, F = s.F, V = s.V, H = s.H, Dh = s.Dh;
+  hipStream_t st = m.st;
+  auto wp = [&](long off) { return (const void*)(m.W + off * 2); };
+  float* h = at<float>(m, m.h);
+  int* flag = at<int>(m, m.flag);
+  char* n1 = m.ws + m.lay[0].n1;
+  char* qkv = m.ws + m.lay[0].qkv;
+  char* o = m.ws + m.lay[0].o;
+  char* u = m.ws + m.lay[0].u;
+  char* g = m.ws + m.lay[0].g;
+  float* dpart = at<float>(m, m.dpart);
+  const int32_t* tokens = at<int32_t>(m, m.dtok);
+  const int* posp = at<int>(m, m.dpos);
+  const size_t kvl = kv_layer_elems(s);
+  int rc;
+  float* split = at<float>(m, m.dsplit);
+  prof_begin(m, "decode_embed", (double)B * d * 6.0, 1, "embed_fwd_kernel<bf16>");
+  embed_fwd(DT_BF16, tokens, tokens, wp(P.E), h, B, d, V, flag, st);
+  prof_end(m);
+  int pending = 0;   // K-split partials of the last product, added by the next norm
+  auto addnorm = [&](void* y) {
+    prof_begin(m, "decode_add_rmsnorm", (double)B * d * (4.0 * pending + 10.0), 1, "decode_add_rmsnorm_kernel");
+    decode_add_rmsnorm(h, split, pending, B, d, y, s.eps, st);
+    prof_end(m);
+    pending = 0;
+  };
+  for (int l = 0; l < s.L; ++l) {
+    uint16_t* kc = (uint16_t*)kv + (size_t)2 * l * kvl;
+    uint16_t* vc = kc + kvl;
+    addnorm(n1);
+    if ((rc = dec_gemm(m, "decode_qkv", EPI_STORE, n1, d, d, wp(P.Wqkv[l]), 3 * d, qkv, 3 * d))) return rc;
+    prof_begin(m, "decode_rope_qknorm", (double)B * d * 10.0, 1, "rope_qknorm_decode_kernel");
+    if (rope_qknorm_decode(qkv, kc, vc, at<float>(m, m.cosb), at<float>(m, m.sinb), B, H, Dh, s.T, posp, s.eps, st))
+      return fail(GPT_EINVAL, "decode rope head_dim");
+    prof_end(m);
+    const int lo = std::max(0, pos - s.win[l] + 1);
+    prof_begin(m, "decode_attention", (double)B * H * (pos - lo + 1) * Dh * 4.0, 1,
+               "attn_decode_split_kernel + attn_decode_combine_kernel");
+    if (attn_decode(qkv, kc, vc, dpart, o, B, H, Dh, s.T, posp, s.win[l], st))
+      return fail(GPT_EINVAL, "decode attention head_dim");
+    prof_end(m);
+    if ((rc = dec_gemm(m, "decode_o", EPI_PARTIAL, o, d, d, wp(P.Wo[l]), d, split, d, nullptr, DEC_KSPLIT))) return rc;
+    pending = DEC_KSPLIT;
+    addnorm(n1);
+    if ((rc = dec_gemm(m, "decode_w1_relu2", EPI_RELU2, n1, d, d, wp(P.W1[l]), F, u, F, g))) return rc;
+    if ((rc = dec_gemm(m, "decode_w2", EPI_PARTIAL, g, F, F, wp(P.W2[l]), d, split, d, nullptr, DEC_KSPLIT))) return rc;
+    pending = DEC_KSPLIT;
+  }
+  addnorm(m.ws + m.nL);
+  if ((rc = dec_gemm(m, "decode_lm_head", EPI_STORE_F32, m.ws + m.nL, d, d, wp(P.U), V, logits, V))) return rc;
+  HIP_TRY(hipGetLastError());
+  return GPT_OK;
+}
+
+// Replays the captured decoding step (capturing it first, or again when the
+// cache or logits buffer differs from the captured one).
+int decode_graph_launch(gpt_model& m, int pos, void* kv, float* logits) {
+  auto& g = m.dg;
+  if (!g.cs) {
+    HIP_TRY(hipStreamCreateWithFlags(&g.cs, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreateWithFlags(&g.before, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&g.after, hipEventDisableTiming));
+  }
+  if (!g.exec || g.kv != kv || g.logits != logits) {
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    if (g.graph) (void)hipGraphDestroy(g.graph);
+    g.exec = nullptr;
+    g.graph = nullptr;
+    HIP_TRY(hipStreamBeginCapture(g.cs, hipStreamCaptureModeThreadLocal));
+    hipStream_t saved = m.st;
+    m.st = g.cs;
+    const int rc = run_decode(m, pos, (char*)kv, logits);
+    m.st = saved;
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(g.cs, &graph);
+    if (rc) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(GPT_EHIP, std::string("decode graph capture: ") + hipGetErrorString(e));
+    g.graph = graph;
+    HIP_TRY(hipGraphInstantiate(&g.exec, g.graph, nullptr, nullptr, 0));
+    g.kv = kv;
+    g.logits = logits;
+  }
+  HIP_TRY(hipEventRecord(g.before, m.st));
+  HIP_TRY(hipStreamWaitEvent(g.cs, g.before, 0));
+  HIP_TRY(hipGraphLaunch(g.exec, g.cs));
+  HIP_TRY(hipEventRecord(g.after, g.cs));
+  HIP_TRY(hipStreamWaitEvent(m.st, g.after, 0));
+  return GPT_OK;
+}
+
+// Waits for the stream, then reports an out-of-range id.
+int finish_infer(gpt_model& m) {
+  int flag = 0;
+  HIP_TRY(hipMemcpyAsync(&flag, m.ws + m.flag, 4, hipMemcpyDeviceToHost, m.st));
+  HIP_TRY(hipStreamSynchronize(m.st));
+  if (m.prof_on) prof_collect(m);
+  if (flag) return fail(GPT_ETOKEN, "a token id is outside [0, vocab)");
+  return GPT_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ C ABI
@@ -1129,6 +1315,41 @@ int gpt_step_accum(gpt_model* m, const int32_t* tokens, const int32_t* targets, 
 }
 
 void gpt_destroy(gpt_model* m) { delete m; }
+
+int gpt_kv_cache_bytes(const gpt_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(GPT_ENULL, "bytes is NULL");
+  Shape s;
+  int rc = check_config(cfg, s);
+  if (rc) return rc;
+  *bytes = (size_t)2 * s.L * kv_layer_elems(s) * 2;
+  return GPT_OK;
+}
+
+int gpt_prefill(gpt_model* m, const int32_t* tokens, int n_tokens, void* kv_cache, float* logits) {
+  if (!m || !tokens || !kv_cache || !logits) return fail(GPT_ENULL, "gpt_prefill: NULL argument");
+  int rc = check_infer(*m);
+  if (rc) return rc;
+  if (n_tokens < 1 || n_tokens > m->s.T) return fail(GPT_EINVAL, "n_tokens must be in [1, seq_len]");
+  if (((uintptr_t)kv_cache | (uintptr_t)logits) & 15) return fail(GPT_EALIGN, "kv_cache and logits must be 16-byte aligned");
+  if ((rc = run_prefill(*m, tokens, n_tokens, (char*)kv_cache, logits))) return rc;
+  return finish_infer(*m);
+}
+
+int gpt_decode(gpt_model* m, const int32_t* tokens, int pos, void* kv_cache, float* logits) {
+  if (!m || !tokens || !kv_cache || !logits) return fail(GPT_ENULL, "gpt_decode: NULL argument");
+  int rc = check_infer(*m);
+  if (rc) return rc;
+  if (pos < 1 || pos >= m->s.T) return fail(GPT_EINVAL, "pos must be in [1, seq_len)");
+  if (((uintptr_t)kv_cache | (uintptr_t)logits) & 15) return fail(GPT_EALIGN, "kv_cache and logits must be 16-byte aligned");
+  decode_stage(tokens, m->s.B, pos, at<int32_t>(*m, m->dtok), at<int>(*m, m->dpos), at<int>(*m, m->flag), m->st);
+  if (m->prof_on) {
+    // profiled steps run eagerly, so that every launch is timed
+    if ((rc = run_decode(*m, pos, (char*)kv_cache, logits))) return rc;
+  } else {
+    if ((rc = decode_graph_launch(*m, pos, kv_cache, logits))) return rc;
+  }
+  return finish_infer(*m);
+}
 
 int gpt_optim_state_bytes(const gpt_config* cfg, size_t* bytes) {
   if (!bytes) return fail(GPT_ENULL, "bytes is NULL");

@@ -150,6 +150,31 @@ void opt_muon_update(float* master, const void* X, void* w16, const OptSeg* seg,
                      float scale, float wd, hipStream_t st);
 void opt_widen(const void* w16, float* master, const OptSeg* seg, int nseg, int nblk, hipStream_t st);
 
+// ---------------------------------------------------------------- decoding
+// out[b][n] = sum_k x[b][k] W[n][k] (bf16 x with row stride ldx, W [N][K];
+// B <= 32, K % 16 == 0) with epilogue EPI_STORE (bf16), EPI_STORE_F32 or
+// EPI_RELU2 (C = u, C2 = relu(u)^2), C and C2 with row stride ldc; or, with
+// ksplit > 1, EPI_PARTIAL: K in ksplit runs, C[y][b][n] (row stride ldc)
+// the y-th run's sum.
+int skinny_gemm(int epi, const void* x, long ldx, int B, int K, const void* W, int N, void* C, int ldc, void* C2,
+                int ksplit, hipStream_t st);
+// h [B][d] fp32 += sum of nsplit (<= 8) partials part[s][B][d] (in order),
+// then y = bf16 RMSNorm(h)
+void decode_add_rmsnorm(float* h, const float* part, int nsplit, int B, int d, void* y, float eps, hipStream_t st);
+// rotary + QK norm of the new token at position *posp (device; qkv
+// [B][3d]); k^ and v go to the caches [B][H][Tmax][Dh] at that position.
+int rope_qknorm_decode(void* qkv, void* kc, void* vc, const float* cosb, const float* sinb, int B, int H, int Dh,
+                       int Tmax, const int* posp, float eps, hipStream_t st);
+// caches[b][h][t] = k^ / v of qkv row (b, t) for t < T (qkv [B*T][3d])
+void kv_fill(const void* qkv, void* kc, void* vc, int B, int T, int H, int Dh, int Tmax, hipStream_t st);
+// o [B][d] = attention of the new token's q^ (qkv [B][3d]) over cached keys
+// max(0, pos - window + 1) .. pos, pos = *posp (device);
+// part: B * H * ceil(min(window, Tmax) / 128) * (Dh + 1) floats
+int attn_decode(const void* qkv, const void* kc, const void* vc, float* part, void* o, int B, int H, int Dh, int Tmax,
+                const int* posp, int window, hipStream_t st);
+// tok[0..B) = tokens[0..B), *posp = pos, *flag = 0 (one small kernel)
+void decode_stage(const int32_t* tokens, int B, int pos, int32_t* tok, int* posp, int* flag, hipStream_t st);
+
 // ---------------------------------------------------------------- fp8
 void zero_u32(unsigned* p, int n, hipStream_t st);
 // Per-tensor amax: AMAX_SLOT words per tensor (see wave_amax), zeroed before

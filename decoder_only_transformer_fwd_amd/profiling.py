@@ -137,8 +137,9 @@ def traffic_md(fetch: str, write: str, copy_fetch: str, copy_write: str, copy_mi
     return "\n".join(out) + "\n"
 
 
-# sources of the optimizer's own kernels, which the training step does not run
-_NOT_STEP = {"optim.hip"}
+# sources of the optimizer's and the decoder's own kernels, which the training
+# step does not run
+_NOT_STEP = {"optim.hip", "infer.hip"}
 
 
 def source_digest() -> str:

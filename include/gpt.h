@@ -198,6 +198,36 @@ int gpt_optim_step(gpt_model* model, void* state, const float* grads, const gpt_
  * itself), e.g. to checkpoint them. */
 int gpt_optim_master(gpt_model* model, float** master);
 
+/* ------------------------------------------------------------ inference
+ * Forward-only generation with a KV cache ("Introducing nanochat": the
+ * model is served by an inference engine with a KV cache, prefill then
+ * token-by-token decoding).  Every row of the batch advances together: a
+ * prompt of n tokens per row is prefilled, then one token per row is decoded
+ * per call.  Runs on bf16 parameters (GPT_BF16; GPT_FP8 models decode with
+ * their bf16 weights); batch <= 32, head_dim 64 or 128; positions up to
+ * seq_len - 1 (the RoPE table's length).  The model's workspace is reused, so
+ * these calls must not overlap gpt_step on the same handle.
+ *
+ * KV cache: caller-owned device memory of gpt_kv_cache_bytes, bf16, layer l
+ * at K = base + 2l * S, V = base + (2l + 1) * S, each [batch][n_head]
+ * [seq_len][head_dim] (S = batch * n_head * seq_len * head_dim elements);
+ * it holds the QK-normalised, rotated keys and the raw values. */
+int gpt_kv_cache_bytes(const gpt_config* cfg, size_t* bytes);
+
+/* tokens: device int32 [batch, n_tokens] (row-major), 1 <= n_tokens <=
+ * seq_len.  Runs the forward over positions 0..n_tokens-1, writes their keys
+ * and values into the cache, and writes logits: device fp32 [batch, vocab],
+ * the next-token logits after each row's last token.  Waits for the stream.
+ * GPT_ETOKEN for an id outside [0, vocab). */
+int gpt_prefill(gpt_model* model, const int32_t* tokens, int n_tokens, void* kv_cache, float* logits);
+
+/* tokens: device int32 [batch], the token at position pos of each row,
+ * 1 <= pos < seq_len, with positions 0..pos-1 already in the cache (from
+ * gpt_prefill and earlier gpt_decode calls).  Appends its key and value at
+ * pos and writes logits [batch, vocab] fp32 (device) for position pos + 1.
+ * Waits for the stream.  GPT_ETOKEN for an id outside [0, vocab). */
+int gpt_decode(gpt_model* model, const int32_t* tokens, int pos, void* kv_cache, float* logits);
+
 /* Release the handle (host memory only). */
 void gpt_destroy(gpt_model* model);
 
