@@ -114,8 +114,15 @@ def _copy_factor(path: str, counter: str, nbytes: float) -> float:
     return nbytes / max(vals)
 
 
+def _avg_ns(stats: str):
+    """{raw kernel name: average duration in ns} from a --stats CSV."""
+    if not stats:
+        return {}
+    return {r["Name"]: float(r["AverageNs"]) for r in csv.DictReader(open(stats))}
+
+
 def traffic_md(fetch: str, write: str, copy_fetch: str, copy_write: str, copy_mib: float, command: str,
-               top: int = 25) -> str:
+               top: int = 25, stats: str = None) -> str:
     nbytes = copy_mib * 2 ** 20
     ff = _copy_factor(copy_fetch, "FETCH_SIZE", nbytes)
     fw = _copy_factor(copy_write, "WRITE_SIZE", nbytes)
@@ -129,11 +136,53 @@ def traffic_md(fetch: str, write: str, copy_fetch: str, copy_write: str, copy_mi
            "Commands (from the repository root, on one MI355X), one counter per pass:", "", "```", command, "```", "",
            f"Calibration: a plain {copy_mib:.0f} MiB device copy reads and writes {nbytes:.0f} bytes; "
            f"bytes per counter unit: FETCH_SIZE x {ff:.1f}, WRITE_SIZE x {fw:.1f}.", "",
-           "| kernel | dispatches | read MB / dispatch | written MB / dispatch |", "|---|---:|---:|---:|"]
+           "| kernel | dispatches | read MB / dispatch | written MB / dispatch | HBM GB/s |",
+           "|---|---:|---:|---:|---:|"]
+    if stats:
+        out[-3:-3] = ["", "HBM GB/s: the measured bytes per dispatch over the kernel's average duration in a "
+                          "kernel trace of the same command (`--kernel-trace --stats`, its own run)."]
     labels = _decode_all(list(agg))
+    dur = _avg_ns(stats)
     for name, (n, rd, wr) in sorted(agg.items(), key=lambda kv: -(kv[1][1] + kv[1][2]))[:top]:
-        out.append(f"| {labels[name]} | {n} | {rd / n / 1e6:.2f} | {wr / max(n, 1) / 1e6:.2f} |")
+        rate = f"{(rd + wr) / n / dur[name]:.0f}" if name in dur else "-"
+        out.append(f"| {labels[name]} | {n} | {rd / n / 1e6:.2f} | {wr / max(n, 1) / 1e6:.2f} | {rate} |")
     out += ["", f"Kernel sources: {source_digest()}"]
+    return "\n".join(out) + "\n"
+
+
+N_SIMD = 1024    # 256 CUs x 4 SIMDs
+N_XCD = 8
+
+
+def mfma_md(pmc: str, stats: str, command: str, note: str = "", top: int = 30) -> str:
+    """Per-kernel MFMA utilisation from GRBM_GUI_ACTIVE and
+    SQ_VALU_MFMA_BUSY_CYCLES: busy = MFMA-busy SIMD cycles / (1024 SIMDs x
+    GRBM_GUI_ACTIVE / 8 XCDs)."""
+    gui = _per_dispatch(pmc, "GRBM_GUI_ACTIVE")
+    busy = _per_dispatch(pmc, "SQ_VALU_MFMA_BUSY_CYCLES")
+    agg = defaultdict(lambda: [0, 0.0, 0.0])
+    for d, (name, g) in gui.items():
+        agg[name][0] += 1
+        agg[name][1] += g / N_XCD
+        agg[name][2] += busy.get(d, (name, 0.0))[1]
+    dur = _avg_ns(stats)
+    out = ["# MFMA utilisation per kernel (rocprofv3 GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES)", "",
+           "Command (from the repository root, on one MI355X):", "", "```", command, "```", ""]
+    if note:
+        out += [note, ""]
+    out += ["MFMA busy: MFMA-busy SIMD cycles divided by (1024 SIMDs x GRBM_GUI_ACTIVE / 8), the "
+            "graphics engine's active cycles per XCD during the dispatch.  GRBM_GUI_ACTIVE also counts "
+            "each dispatch's start-up and drain (for the short kernels of this run it exceeds duration x "
+            "2.4 GHz), so the fraction is a lower bound, loosest for short dispatches.  The profiler "
+            "serialises dispatches in a counter run, so clocks and durations there differ from the "
+            "back-to-back step.", "",
+            "| kernel | dispatches | avg duration (us) | GRBM_GUI_ACTIVE / 8 per dispatch | MFMA busy |",
+            "|---|---:|---:|---:|---:|"]
+    labels = _decode_all(list(agg))
+    for name, (n, cyc, b) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:top]:
+        c = cyc / n
+        du = f"{dur[name] / 1e3:.1f}" if name in dur else "-"
+        out.append(f"| {labels[name]} | {n} | {du} | {c:.3g} | {100 * b / n / N_SIMD / c:.0f} % |")
     return "\n".join(out) + "\n"
 
 
@@ -170,7 +219,7 @@ def traffic_lookup(md_path: str, label: str):
         return None
     for line in text.splitlines():
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) == 4 and cells[0] == label:
+        if len(cells) in (4, 5) and cells[0] == label:
             return float(cells[2]) * 1e6, float(cells[3]) * 1e6
     return None
 
@@ -201,13 +250,21 @@ def main(argv=None) -> int:
     for k in ("fetch", "write", "copy-fetch", "copy-write", "command"):
         t.add_argument("--" + k, required=True)
     t.add_argument("--copy-mib", type=float, default=1024)
+    t.add_argument("--stats", default=None)
+    u = sub.add_parser("mfma")
+    for k in ("pmc", "stats", "command"):
+        u.add_argument("--" + k, required=True)
+    u.add_argument("--note", default="")
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         _copy(a.mib)
     elif a.cmd == "stats":
         sys.stdout.write(stats_md(a.csv, a.title, a.command, a.note))
+    elif a.cmd == "mfma":
+        sys.stdout.write(mfma_md(a.pmc, a.stats, a.command, a.note))
     else:
-        sys.stdout.write(traffic_md(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.command))
+        sys.stdout.write(traffic_md(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.command,
+                                    stats=a.stats))
     return 0
 
 

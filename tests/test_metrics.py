@@ -45,3 +45,15 @@ def test_profiler_kernel_names_decode_to_step_labels():
         "gemm_kernel<bf16, 256, 256, 2, 4, 64, 4, true, true, 8, ping-pong>"
     assert Pf.decode("k", garbled.format("true")) == \
         "gemm_kernel<bf16, 256, 256, 2, 4, 64, 4, true, true, 8, ping-pong, batched>"
+
+
+def test_traffic_summary_lookup(tmp_path):
+    from decoder_only_transformer_fwd_amd import profiling as Pf
+    p = tmp_path / "t.md"
+    row = "| gemm_kernel<bf16, 1> | 4 | 1.50 | 0.25 | 900 |"
+    p.write_text(f"| kernel | dispatches | read | written | GB/s |\n|---|---:|---:|---:|---:|\n{row}\n\n"
+                 f"Kernel sources: {Pf.source_digest()}\n")
+    assert Pf.traffic_lookup(str(p), "gemm_kernel<bf16, 1>") == (1.5e6, 0.25e6)
+    assert Pf.traffic_lookup(str(p), "other") is None
+    p.write_text(p.read_text().replace(Pf.source_digest(), "0" * 16))   # other kernel sources: stale
+    assert Pf.traffic_lookup(str(p), "gemm_kernel<bf16, 1>") is None
