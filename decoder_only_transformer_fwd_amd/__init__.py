@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libgpt_mi355x.so")
 GPT_OK, GPT_EINVAL, GPT_ENULL, GPT_ETOKEN, GPT_EHIP, GPT_ENONFINITE, GPT_ESPACE, GPT_EALIGN = 0, -1, -2, -3, -4, -5, -6, -7
 GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 
-EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum",
+EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_step_micro",
             "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
             "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_destroy",
             "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
@@ -78,6 +78,7 @@ def _load():
     lib.gpt_create.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(P)]
     lib.gpt_step.argtypes = [P, P, P, P, ctypes.POINTER(F)]
     lib.gpt_step_accum.argtypes = [P, P, P, P, F, I, ctypes.POINTER(F)]
+    lib.gpt_step_micro.argtypes = [P, P, P, I, P, F, I, ctypes.POINTER(F)]
     lib.gpt_optim_state_bytes.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(ctypes.c_size_t)]
     lib.gpt_optim_init.argtypes = [P, P, ctypes.c_size_t]
     lib.gpt_optim_step.argtypes = [P, P, P, ctypes.POINTER(gpt_optim_params), ctypes.POINTER(F)]
@@ -101,7 +102,7 @@ def _load():
     lib.gpt_strerror.restype = ctypes.c_char_p
     lib.gpt_last_error.argtypes = []
     lib.gpt_last_error.restype = ctypes.c_char_p
-    for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum",
+    for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_step_micro",
                  "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
                  "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode",
                  "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
@@ -229,6 +230,16 @@ def gpt_decode(model: int, tokens: int, pos: int, kv_cache: int, logits: int) ->
     _check(_lib.gpt_decode(model, tokens, pos, kv_cache, logits), "gpt_decode")
 
 
+def gpt_step_micro(model: int, tokens: int, targets: int, n_micro: int, grads: int, grad_scale: float,
+                   accumulate: bool) -> List[float]:
+    """n_micro micro-batches ([n_micro, B, T] device token buffers) in one
+    graph replay; returns the micro-batch losses."""
+    losses = (ctypes.c_float * n_micro)()
+    _check(_lib.gpt_step_micro(model, tokens, targets, n_micro, grads, float(grad_scale), int(bool(accumulate)),
+                               losses), "gpt_step_micro")
+    return list(losses)
+
+
 def gpt_destroy(model: int) -> None:
     _lib.gpt_destroy(model)
 
@@ -339,6 +350,17 @@ class Session:
 
     def step_accum(self, grad_scale: float, accumulate: bool) -> float:
         return gpt_step_accum(self.handle, self.tokens.data_ptr(), self.targets.data_ptr(), self.grads.data_ptr(),
+                              grad_scale, accumulate)
+
+    def step_micro(self, X: np.ndarray, Y: np.ndarray, grad_scale: float, accumulate: bool) -> List[float]:
+        """X, Y: int32 [n, B, T] (host arrays or device tensors)."""
+        t = self.torch
+        xs = X if isinstance(X, t.Tensor) else t.from_numpy(np.ascontiguousarray(X, np.int32))
+        ys = Y if isinstance(Y, t.Tensor) else t.from_numpy(np.ascontiguousarray(Y, np.int32))
+        xs = xs.to(self.device).contiguous()
+        ys = ys.to(self.device).contiguous()
+        self._micro = (xs, ys)   # keep the buffers the captured graph reads alive
+        return gpt_step_micro(self.handle, xs.data_ptr(), ys.data_ptr(), xs.shape[0], self.grads.data_ptr(),
                               grad_scale, accumulate)
 
     def optim_init(self) -> None:

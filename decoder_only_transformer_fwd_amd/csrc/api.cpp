@@ -37,6 +37,8 @@ constexpr size_t ALIGN = 256;
 // CUs idle (output projection, W2); their partials go through the next norm
 constexpr int DEC_KSPLIT = 8;
 static_assert(DEC_KSPLIT <= 8, "the decoder's add + norm kernel adds at most 8 partials");
+// micro-batches per gpt_step_micro call
+constexpr int MAX_MICRO = 1024;
 size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 
 struct Shape {
@@ -270,7 +272,7 @@ struct gpt_model {
     size_t n1T, oT, n2T, gT, wq[4], wqT[4];
   };
   std::vector<Layer> lay;
-  size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, dpart, dtok, dpos, dsplit, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
+  size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, mloss, dpart, dtok, dpos, dsplit, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
       cosb, sinb, keys, total;
   size_t splitk_floats;
   size_t q8row, q8T, amax, scales;   // fp8: transient codes, per-tensor amax / scale slots
@@ -302,6 +304,17 @@ struct gpt_model {
     const void* kv = nullptr;
     const void* logits = nullptr;
   } dg;
+  // gpt_step_micro: the n micro-batch steps captured as one graph, for the
+  // buffers and arguments it was captured with (replayed on dg.cs)
+  struct MicroGraph {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    const void* tokens = nullptr;
+    const void* targets = nullptr;
+    const void* grads = nullptr;
+    int n = 0, accumulate = 0;
+    float scale = 0.f;
+  } mg;
   bool prof_on = false;
   std::vector<Site> sites;
   std::vector<hipEvent_t> ev_pool;
@@ -311,6 +324,8 @@ struct gpt_model {
   double cur_work = 0.0;
   ~gpt_model() {
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+    if (mg.exec) (void)hipGraphExecDestroy(mg.exec);
+    if (mg.graph) (void)hipGraphDestroy(mg.graph);
     if (dg.exec) (void)hipGraphExecDestroy(dg.exec);
     if (dg.graph) (void)hipGraphDestroy(dg.graph);
     if (dg.before) (void)hipEventDestroy(dg.before);
@@ -360,6 +375,7 @@ int build_layout(gpt_model& m) {
   m.rowloss = take(BT * 4);
   m.lossdev = take(64);
   m.flag = take(64);
+  m.mloss = take((size_t)MAX_MICRO * 4);   // per-micro-batch losses of gpt_step_micro
   // decoding: attention split partials (128 keys per split), the step's
   // token ids and position
   m.dpart = take((size_t)s.B * s.H * ((s.T + 127) / 128) * (s.Dh + 1) * 4);
@@ -569,7 +585,8 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
 // overwriting it.  `shape` (default: the model's) may describe fewer tokens
 // per row; forward_only stops after the final norm (prefill).
 int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float* grads, float grad_scale,
-             int accumulate, const Shape* shape = nullptr, bool forward_only = false) {
+             int accumulate, const Shape* shape = nullptr, bool forward_only = false, float* loss_out = nullptr,
+             bool clear_flag = true) {
   const Shape& s = shape ? *shape : m.s;
   const ParamOffsets& P = m.po;
   const int dt = s.dtype;
@@ -636,7 +653,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     return gemm(m, site, LAYOUT_KK, wepi, M, N, K, A, K, B, K, C, ldc, ex, DT_FP8_A5B4, true);
   };
 
-  fill_f32((float*)flag, 1, 0.f, st);
+  if (clear_flag) fill_f32((float*)flag, 1, 0.f, st);
   if (f8) {
     zero_u32(amax8, m.n_slots * AMAX_SLOT, st);
     for (int l = 0; l < s.L; ++l) {
@@ -728,7 +745,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   prof_begin(m, "xent_reduce", (double)BT * m.xent_nblk * 8.0 + BT * 12.0, 1, "xent_reduce_kernel + mean_reduce_kernel");
   xent_reduce(at<float>(m, m.part), at<float>(m, m.tgt), BT, m.xent_nblk, at<float>(m, m.lse),
               at<float>(m, m.rowloss), st);
-  mean_reduce(at<float>(m, m.rowloss), BT, at<float>(m, m.lossdev), st);
+  mean_reduce(at<float>(m, m.rowloss), BT, loss_out ? loss_out : at<float>(m, m.lossdev), st);
   prof_end(m);
 
   // ---------------------------------------------------------------- backward
@@ -1166,15 +1183,23 @@ int run_decode(gpt_model& m, int pos, char* kv, float* logits) {
   return GPT_OK;
 }
 
-// Replays the captured decoding step (capturing it first, or again when the
-// cache or logits buffer differs from the captured one).
-int decode_graph_launch(gpt_model& m, int pos, void* kv, float* logits) {
+// Graph-replay stream and events of the handle (created on first use).
+int graph_stream(gpt_model& m) {
   auto& g = m.dg;
   if (!g.cs) {
     HIP_TRY(hipStreamCreateWithFlags(&g.cs, hipStreamNonBlocking));
     HIP_TRY(hipEventCreateWithFlags(&g.before, hipEventDisableTiming));
     HIP_TRY(hipEventCreateWithFlags(&g.after, hipEventDisableTiming));
   }
+  return GPT_OK;
+}
+
+// Replays the captured decoding step (capturing it first, or again when the
+// cache or logits buffer differs from the captured one).
+int decode_graph_launch(gpt_model& m, int pos, void* kv, float* logits) {
+  const int rc0 = graph_stream(m);
+  if (rc0) return rc0;
+  auto& g = m.dg;
   if (!g.exec || g.kv != kv || g.logits != logits) {
     if (g.exec) (void)hipGraphExecDestroy(g.exec);
     if (g.graph) (void)hipGraphDestroy(g.graph);
@@ -1202,6 +1227,64 @@ int decode_graph_launch(gpt_model& m, int pos, void* kv, float* logits) {
   HIP_TRY(hipGraphLaunch(g.exec, g.cs));
   HIP_TRY(hipEventRecord(g.after, g.cs));
   HIP_TRY(hipStreamWaitEvent(m.st, g.after, 0));
+  return GPT_OK;
+}
+
+// The n micro-batch steps of gpt_step_micro, enqueued on m.st: the first
+// stores or accumulates as asked, the rest accumulate; each writes its mean
+// loss to mloss[i]; the token-range flag is cleared once and collects all.
+int run_micro(gpt_model& m, const int32_t* tokens, const int32_t* targets, int n, float* grads, float scale,
+              int accumulate) {
+  fill_f32(at<float>(m, m.flag), 1, 0.f, m.st);
+  const long bt = m.s.BT;
+  for (int i = 0; i < n; ++i) {
+    const int rc = run_step(m, tokens + i * bt, targets + i * bt, grads, scale, i ? 1 : accumulate, nullptr, false,
+                            at<float>(m, m.mloss) + i, false);
+    if (rc) return rc;
+  }
+  return GPT_OK;
+}
+
+// Replays the captured micro-batch sequence (capturing it first, or again
+// when any argument differs from the captured one).
+int micro_graph_launch(gpt_model& m, const int32_t* tokens, const int32_t* targets, int n, float* grads, float scale,
+                       int accumulate) {
+  int rc = graph_stream(m);
+  if (rc) return rc;
+  auto& g = m.mg;
+  auto& d = m.dg;
+  if (!g.exec || g.tokens != tokens || g.targets != targets || g.grads != grads || g.n != n ||
+      g.accumulate != accumulate || g.scale != scale) {
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    if (g.graph) (void)hipGraphDestroy(g.graph);
+    g.exec = nullptr;
+    g.graph = nullptr;
+    HIP_TRY(hipStreamBeginCapture(d.cs, hipStreamCaptureModeThreadLocal));
+    hipStream_t saved = m.st;
+    m.st = d.cs;
+    rc = run_micro(m, tokens, targets, n, grads, scale, accumulate);
+    m.st = saved;
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(d.cs, &graph);
+    if (rc) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(GPT_EHIP, std::string("step graph capture: ") + hipGetErrorString(e));
+    g.graph = graph;
+    HIP_TRY(hipGraphInstantiate(&g.exec, g.graph, nullptr, nullptr, 0));
+    g.tokens = tokens;
+    g.targets = targets;
+    g.grads = grads;
+    g.n = n;
+    g.accumulate = accumulate;
+    g.scale = scale;
+  }
+  HIP_TRY(hipEventRecord(d.before, m.st));
+  HIP_TRY(hipStreamWaitEvent(d.cs, d.before, 0));
+  HIP_TRY(hipGraphLaunch(g.exec, d.cs));
+  HIP_TRY(hipEventRecord(d.after, d.cs));
+  HIP_TRY(hipStreamWaitEvent(m.st, d.after, 0));
   return GPT_OK;
 }
 
@@ -1311,6 +1394,27 @@ int gpt_step_accum(gpt_model* m, const int32_t* tokens, const int32_t* targets, 
   *loss = lossv;
   if (flag) return fail(GPT_ETOKEN, "a token or target id is outside [0, vocab)");
   if (!std::isfinite(lossv)) return fail(GPT_ENONFINITE, "loss is not finite");
+  return GPT_OK;
+}
+
+int gpt_step_micro(gpt_model* m, const int32_t* tokens, const int32_t* targets, int n_micro, float* grads,
+                   float grad_scale, int accumulate, float* losses) {
+  if (!m || !tokens || !targets || !grads || !losses) return fail(GPT_ENULL, "gpt_step_micro: NULL argument");
+  if (n_micro < 1 || n_micro > MAX_MICRO) return fail(GPT_EINVAL, "n_micro must be in [1, 1024]");
+  if ((uintptr_t)grads & (ALIGN - 1)) return fail(GPT_EALIGN, "grads must be 256-byte aligned");
+  if (!std::isfinite(grad_scale)) return fail(GPT_EINVAL, "grad_scale must be finite");
+  if (accumulate != 0 && accumulate != 1) return fail(GPT_EINVAL, "accumulate must be 0 or 1");
+  int rc = m->prof_on ? run_micro(*m, tokens, targets, n_micro, grads, grad_scale, accumulate)
+                      : micro_graph_launch(*m, tokens, targets, n_micro, grads, grad_scale, accumulate);
+  if (rc) return rc;
+  int flag = 0;
+  HIP_TRY(hipMemcpyAsync(losses, m->ws + m->mloss, (size_t)n_micro * 4, hipMemcpyDeviceToHost, m->st));
+  HIP_TRY(hipMemcpyAsync(&flag, m->ws + m->flag, 4, hipMemcpyDeviceToHost, m->st));
+  HIP_TRY(hipStreamSynchronize(m->st));
+  if (m->prof_on) prof_collect(*m);
+  if (flag) return fail(GPT_ETOKEN, "a token or target id is outside [0, vocab)");
+  for (int i = 0; i < n_micro; ++i)
+    if (!std::isfinite(losses[i])) return fail(GPT_ENONFINITE, "a micro-batch loss is not finite");
   return GPT_OK;
 }
 

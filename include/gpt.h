@@ -139,6 +139,20 @@ int gpt_step(gpt_model* model, const int32_t* tokens, const int32_t* targets, fl
 int gpt_step_accum(gpt_model* model, const int32_t* tokens, const int32_t* targets, float* grads,
                    float grad_scale, int accumulate, float* loss);
 
+/* n_micro micro-batches in one call, replayed as one captured HIP graph:
+ * tokens and targets are device int32 [n_micro, batch, seq_len] (all
+ * resident), grads as in gpt_step_accum: the first micro-batch stores
+ * (accumulate == 0) or adds (accumulate == 1), every later one adds, each
+ * scaled by grad_scale.  losses: host float[n_micro], each micro-batch's mean
+ * loss.  1 <= n_micro <= 1024.  The graph is captured on the first call and
+ * again whenever a pointer or argument differs from the captured call's; it
+ * runs on a stream of the handle ordered after cfg->stream by events, and
+ * the call waits for it.  With profiling on, the steps run eagerly.
+ * GPT_ETOKEN if any id is out of range, GPT_ENONFINITE if any loss is not
+ * finite (grads undefined then). */
+int gpt_step_micro(gpt_model* model, const int32_t* tokens, const int32_t* targets, int n_micro, float* grads,
+                   float grad_scale, int accumulate, float* losses);
+
 /* ------------------------------------------------------------ optimizer
  * One optimizer step over every parameter, after the gradients of the step
  * (or of accumulated micro-batches) are complete: Muon on the projection

@@ -154,3 +154,56 @@ def test_bad_accumulation_arguments_are_rejected():
     # nothing was enqueued: the gradients are untouched
     assert bool((sess.grads == g1).all())
     sess.close()
+
+
+def test_micro_batch_graph_matches_eager_steps():
+    """gpt_step_micro (n micro-batches replayed as one captured graph) gives
+    the gradients and losses of n gpt_step_accum calls bit for bit, on every
+    replay, with eager work and synchronisation between replays; with
+    profiling on it runs eagerly and agrees too."""
+    import decoder_only_transformer_fwd_amd as G
+    s6 = SMALL["bf16_mid"].replace(batch=6)
+    s = s6.replace(batch=2)
+    n = 3
+    W8 = gi.make_weights(s6)
+    X, Y = gi.make_tokens(s6)
+    Xm = X.reshape(n, s.batch, s.seq_len)
+    Ym = Y.reshape(n, s.batch, s.seq_len)
+    log("micro-batch graph vs eager: bf16_mid, 3 x 2 rows")
+    sess = G.Session(s, W8)
+    t = sess.torch
+    ref_losses = []
+    for i in range(n):
+        sess.set_tokens(Xm[i], Ym[i])
+        ref_losses.append(sess.step_accum(1.0 / n, accumulate=i > 0))
+    ref = sess.grads.clone()
+    Xd = t.from_numpy(np.ascontiguousarray(Xm)).to(sess.device)
+    Yd = t.from_numpy(np.ascontiguousarray(Ym)).to(sess.device)
+    for rep in range(3):
+        sess.grads.fill_(float("nan"))
+        losses = sess.step_micro(Xd, Yd, 1.0 / n, accumulate=False)
+        assert losses == ref_losses, (rep, losses, ref_losses)
+        assert bool((sess.grads == ref).all()), rep
+        junk = t.randn(4096, device=sess.device).cumsum(0)   # eager work between replays
+        t.cuda.synchronize()
+        del junk
+    # accumulating onto what the buffer holds: the same bits as the eager
+    # accumulating steps
+    for i in range(n):
+        sess.set_tokens(Xm[i], Ym[i])
+        sess.step_accum(1.0 / n, accumulate=True)
+    ref2 = sess.grads.clone()
+    sess.grads.copy_(ref)
+    sess.step_micro(Xd, Yd, 1.0 / n, accumulate=True)
+    assert bool((sess.grads == ref2).all())
+    sess.profile(True)
+    losses = sess.step_micro(Xd, Yd, 1.0 / n, accumulate=False)
+    sess.profile(False)
+    assert losses == ref_losses and bool((sess.grads == ref).all())
+    # an out-of-range id in the last micro-batch is reported
+    Yb = Yd.clone()
+    Yb[n - 1, 0, 3] = s.vocab
+    rc = G._lib.gpt_step_micro(sess.handle, Xd.data_ptr(), Yb.data_ptr(), n, sess.grads.data_ptr(), 1.0 / n, 0,
+                               (ctypes.c_float * n)())
+    assert rc == G.GPT_ETOKEN
+    sess.close()
