@@ -1160,14 +1160,11 @@ int run_decode(gpt_model& m, int pos, char* kv, float* logits) {
     uint16_t* vc = kc + kvl;
     addnorm(n1);
     if ((rc = dec_gemm(m, "decode_qkv", EPI_STORE, n1, d, d, wp(P.Wqkv[l]), 3 * d, qkv, 3 * d))) return rc;
-    prof_begin(m, "decode_rope_qknorm", (double)B * d * 10.0, 1, "rope_qknorm_decode_kernel");
-    if (rope_qknorm_decode(qkv, kc, vc, at<float>(m, m.cosb), at<float>(m, m.sinb), B, H, Dh, s.T, posp, s.eps, st))
-      return fail(GPT_EINVAL, "decode rope head_dim");
-    prof_end(m);
     const int lo = std::max(0, pos - s.win[l] + 1);
     prof_begin(m, "decode_attention", (double)B * H * (pos - lo + 1) * Dh * 4.0, 1,
                "attn_decode_split_kernel + attn_decode_combine_kernel");
-    if (attn_decode(qkv, kc, vc, dpart, o, B, H, Dh, s.T, posp, s.win[l], st))
+    if (attn_decode(qkv, kc, vc, at<float>(m, m.cosb), at<float>(m, m.sinb), dpart, o, B, H, Dh, s.T, posp,
+                    s.win[l], s.eps, st))
       return fail(GPT_EINVAL, "decode attention head_dim");
     prof_end(m);
     if ((rc = dec_gemm(m, "decode_o", EPI_PARTIAL, o, d, d, wp(P.Wo[l]), d, split, d, nullptr, DEC_KSPLIT))) return rc;

@@ -153,66 +153,6 @@ void decode_add_rmsnorm(float* h, const float* part, int nsplit, int B, int d, v
                      eps);
 }
 
-// ------------------------------------------------------------------ rotary + QK norm at one position
-// One wave per (head, sequence): rotate q and k of the new token by
-// +pos*theta_i over half-split pairs, normalise each to unit RMS over the
-// head, write q^ back into qkv and k^, v into the cache at `pos`.
-template <int DH>
-__global__ __launch_bounds__(64) void rope_qknorm_decode_kernel(bf16* __restrict__ qkv, bf16* __restrict__ kc,
-                                                                bf16* __restrict__ vc, const float* __restrict__ cosb,
-                                                                const float* __restrict__ sinb, int H, int Tmax,
-                                                                const int* __restrict__ posp, float eps) {
-  constexpr int HALF = DH / 2;
-  const int h = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
-  const int pos = *posp;
-  const int d = H * DH;
-  bf16* row = qkv + (long)b * 3 * d;
-  const long crow = (((long)b * H + h) * Tmax + pos) * DH;
-  const bool act = j < HALF;
-  const float c = act ? cosb[(long)pos * HALF + j] : 0.f;
-  const float sn = act ? sinb[(long)pos * HALF + j] : 0.f;
-#pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    bf16* x = row + part * d + h * DH;
-    const float x1 = act ? (float)x[j] : 0.f;
-    const float x2 = act ? (float)x[j + HALF] : 0.f;
-    float y1 = x1 * c - x2 * sn;
-    float y2 = x1 * sn + x2 * c;
-    const float ss = wave_sum(y1 * y1 + y2 * y2);
-    const float r = 1.0f / sqrtf(ss / (float)DH + eps);
-    y1 *= r;
-    y2 *= r;
-    if (act) {
-      if (part == 0) {
-        x[j] = (bf16)y1;
-        x[j + HALF] = (bf16)y2;
-      } else {
-        kc[crow + j] = (bf16)y1;
-        kc[crow + j + HALF] = (bf16)y2;
-      }
-    }
-  }
-  const bf16* v = row + 2 * d + h * DH;
-  if (act) {
-    vc[crow + j] = v[j];
-    vc[crow + j + HALF] = v[j + HALF];
-  }
-}
-
-int rope_qknorm_decode(void* qkv, void* kc, void* vc, const float* cosb, const float* sinb, int B, int H, int Dh,
-                       int Tmax, const int* posp, float eps, hipStream_t st) {
-  const dim3 grid(H, B);
-  if (Dh == 128)
-    hipLaunchKernelGGL(rope_qknorm_decode_kernel<128>, grid, dim3(64), 0, st, (bf16*)qkv, (bf16*)kc, (bf16*)vc, cosb,
-                       sinb, H, Tmax, posp, eps);
-  else if (Dh == 64)
-    hipLaunchKernelGGL(rope_qknorm_decode_kernel<64>, grid, dim3(64), 0, st, (bf16*)qkv, (bf16*)kc, (bf16*)vc, cosb,
-                       sinb, H, Tmax, posp, eps);
-  else
-    return -1;
-  return 0;
-}
-
 // ------------------------------------------------------------------ prefill: cache fill
 // kc/vc[b][h][t][:] = k^ / v of row (b, t) of qkv [B*T][3d], t < T.
 __global__ __launch_bounds__(256) void kv_fill_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ kc,
@@ -237,8 +177,12 @@ void kv_fill(const void* qkv, void* kc, void* vc, int B, int T, int H, int Dh, i
 // Split pass: work-group (split, h, b) takes keys [lo + split*128, +128)
 // of the visible range [lo, pos], lo = max(0, pos - window + 1); 16 (Dh 128)
 // or 8 (Dh 64) lanes share one key row, so a wave covers 4 or 8 keys per
-// load.  QK-normalised queries and keys bound every score by sqrt(Dh), so
-// the softmax uses a fixed exponent offset M = 1.01 sqrt(Dh) log2(e) and the
+// load.  The new token's rotary embedding and QK norm are done here: every
+// work-group forms q^ from the raw q of qkv [B][3d]; the one whose split
+// holds pos also forms k^ of the new token, writes k^ and v into the cache
+// at pos for later steps, and uses them from registers for key pos.
+// QK-normalised queries and keys bound every score by sqrt(Dh), so the
+// softmax uses a fixed exponent offset M = 1.01 sqrt(Dh) log2(e) and the
 // splits only add their (sum p, sum p v) partials: part[b][h][split] =
 // {o[Dh], l}.  The grid covers the most splits the window can need, so it
 // does not depend on pos (read from device memory); splits past pos write
@@ -247,13 +191,38 @@ void kv_fill(const void* qkv, void* kc, void* vc, int B, int T, int H, int Dh, i
 // flight at once)
 constexpr int ATT_SPLIT = 128;
 
+// Rotary embedding by +pos*theta_i over half-split pairs, then unit RMS over
+// the head, for the 8 values this lane holds (lane li of an LPK-lane group
+// holds elements 8li..8li+7; its pair partner is lane li ^ LPK/2); the
+// result is rounded to bf16, as a stored q^ / k^ is.
+template <int LPK>
+__device__ __forceinline__ void rope_norm8(const bf16x8 xv, const float* cs, const float* sn, bool first, float eps,
+                                           float* out) {
+  constexpr int DH = LPK * 8;
+  float y[8];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = (float)xv[e];
+    const float pr = __shfl_xor(x, LPK / 2, 64);
+    y[e] = first ? x * cs[e] - pr * sn[e] : pr * sn[e] + x * cs[e];
+    ss += y[e] * y[e];
+  }
+#pragma unroll
+  for (int o = LPK / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float r = 1.0f / sqrtf(ss / (float)DH + eps);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (float)(bf16)(y[e] * r);
+}
+
 template <int DH>
-__global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16* __restrict__ qkv,
-                                                                const bf16* __restrict__ kc,
-                                                                const bf16* __restrict__ vc, float* __restrict__ part,
-                                                                int H, int Tmax, const int* __restrict__ posp,
-                                                                int window, float scale_log2) {
-  constexpr int LPK = DH / 8, KPI = 64 / LPK;
+__global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ kc,
+                                                                bf16* __restrict__ vc, float* __restrict__ part,
+                                                                const float* __restrict__ cosb,
+                                                                const float* __restrict__ sinb, int H, int Tmax,
+                                                                const int* __restrict__ posp, int window,
+                                                                float scale_log2, float eps) {
+  constexpr int LPK = DH / 8, KPI = 64 / LPK, HALF = DH / 2;
   __shared__ float red[4][DH + 1];
   const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nsplit = gridDim.x;
@@ -264,14 +233,37 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16* __re
     for (int i = threadIdx.x; i <= DH; i += 256) out[i] = 0.f;
     return;
   }
+  const bool has_pos = pos < lo + (sp + 1) * ATT_SPLIT;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kg = lane / LPK, li = lane % LPK;
+  const bool first = li < LPK / 2;
   const int d = H * DH;
-  const bf16x8 qv = *(const bf16x8*)(qkv + (long)b * 3 * d + h * DH + li * 8);
-  float q[8];
+  const bf16* row = qkv + (long)b * 3 * d + h * DH + li * 8;
+  float cs[8], sn[8];
+  {
+    const float* c = cosb + (long)pos * HALF + (li % (LPK / 2)) * 8;
+    const float* s = sinb + (long)pos * HALF + (li % (LPK / 2)) * 8;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) q[e] = (float)qv[e];
+    for (int e = 0; e < 8; ++e) {
+      cs[e] = c[e];
+      sn[e] = s[e];
+    }
+  }
+  float q[8];
+  rope_norm8<LPK>(*(const bf16x8*)row, cs, sn, first, eps, q);
   const long base = ((long)b * H + h) * Tmax * DH;
+  bf16x8 knew = bf16x8{}, vnew = bf16x8{};
+  if (has_pos) {   // uniform over the work-group
+    float k[8];
+    rope_norm8<LPK>(*(const bf16x8*)(row + d), cs, sn, first, eps, k);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) knew[e] = (bf16)k[e];
+    vnew = *(const bf16x8*)(row + 2 * d);
+    if (wave == 0 && kg == 0) {
+      *(bf16x8*)(kc + base + (long)pos * DH + li * 8) = knew;
+      *(bf16x8*)(vc + base + (long)pos * DH + li * 8) = vnew;
+    }
+  }
   const float M = 1.01f * scale_log2 * (float)DH;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float l = 0.f;
@@ -281,8 +273,12 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16* __re
     const int j = k0 + it * KPI + kg;
     const bool ok = j <= pos;
     const int jj = ok ? j : pos;   // a valid row; its weight is zero
-    const bf16x8 kv = *(const bf16x8*)(kc + base + (long)jj * DH + li * 8);
-    const bf16x8 vv = *(const bf16x8*)(vc + base + (long)jj * DH + li * 8);
+    bf16x8 kv = *(const bf16x8*)(kc + base + (long)jj * DH + li * 8);
+    bf16x8 vv = *(const bf16x8*)(vc + base + (long)jj * DH + li * 8);
+    if (jj == pos) {   // the new token: its key and value come from registers
+      kv = knew;
+      vv = vnew;
+    }
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) s += q[e] * (float)kv[e];
@@ -324,18 +320,18 @@ __global__ __launch_bounds__(DH) void attn_decode_combine_kernel(const float* __
   o[(long)b * H * DH + h * DH + i] = (bf16)(num / den);
 }
 
-int attn_decode(const void* qkv, const void* kc, const void* vc, float* part, void* o, int B, int H, int Dh, int Tmax,
-                const int* posp, int window, hipStream_t st) {
+int attn_decode(const void* qkv, void* kc, void* vc, const float* cosb, const float* sinb, float* part, void* o,
+                int B, int H, int Dh, int Tmax, const int* posp, int window, float eps, hipStream_t st) {
   const int nsplit = (std::min(window, Tmax) + ATT_SPLIT - 1) / ATT_SPLIT;
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)Dh));
   const dim3 g1(nsplit, H, B), g2(H, B);
   if (Dh == 128) {
-    hipLaunchKernelGGL(attn_decode_split_kernel<128>, g1, dim3(256), 0, st, (const bf16*)qkv, (const bf16*)kc,
-                       (const bf16*)vc, part, H, Tmax, posp, window, sl2);
+    hipLaunchKernelGGL(attn_decode_split_kernel<128>, g1, dim3(256), 0, st, (const bf16*)qkv, (bf16*)kc, (bf16*)vc,
+                       part, cosb, sinb, H, Tmax, posp, window, sl2, eps);
     hipLaunchKernelGGL(attn_decode_combine_kernel<128>, g2, dim3(128), 0, st, part, (bf16*)o, H, nsplit);
   } else if (Dh == 64) {
-    hipLaunchKernelGGL(attn_decode_split_kernel<64>, g1, dim3(256), 0, st, (const bf16*)qkv, (const bf16*)kc,
-                       (const bf16*)vc, part, H, Tmax, posp, window, sl2);
+    hipLaunchKernelGGL(attn_decode_split_kernel<64>, g1, dim3(256), 0, st, (const bf16*)qkv, (bf16*)kc, (bf16*)vc,
+                       part, cosb, sinb, H, Tmax, posp, window, sl2, eps);
     hipLaunchKernelGGL(attn_decode_combine_kernel<64>, g2, dim3(64), 0, st, part, (bf16*)o, H, nsplit);
   } else {
     return -1;

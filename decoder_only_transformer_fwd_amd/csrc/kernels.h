@@ -161,17 +161,15 @@ int skinny_gemm(int epi, const void* x, long ldx, int B, int K, const void* W, i
 // h [B][d] fp32 += sum of nsplit (<= 8) partials part[s][B][d] (in order),
 // then y = bf16 RMSNorm(h)
 void decode_add_rmsnorm(float* h, const float* part, int nsplit, int B, int d, void* y, float eps, hipStream_t st);
-// rotary + QK norm of the new token at position *posp (device; qkv
-// [B][3d]); k^ and v go to the caches [B][H][Tmax][Dh] at that position.
-int rope_qknorm_decode(void* qkv, void* kc, void* vc, const float* cosb, const float* sinb, int B, int H, int Dh,
-                       int Tmax, const int* posp, float eps, hipStream_t st);
 // caches[b][h][t] = k^ / v of qkv row (b, t) for t < T (qkv [B*T][3d])
 void kv_fill(const void* qkv, void* kc, void* vc, int B, int T, int H, int Dh, int Tmax, hipStream_t st);
-// o [B][d] = attention of the new token's q^ (qkv [B][3d]) over cached keys
-// max(0, pos - window + 1) .. pos, pos = *posp (device);
+// o [B][d] = attention of the new token over cached keys max(0, pos -
+// window + 1) .. pos, pos = *posp (device).  qkv [B][3d] holds the new
+// token's raw q, k, v: its rotary embedding and QK norm are applied here, and
+// k^ and v are written into the caches [B][H][Tmax][Dh] at pos.
 // part: B * H * ceil(min(window, Tmax) / 128) * (Dh + 1) floats
-int attn_decode(const void* qkv, const void* kc, const void* vc, float* part, void* o, int B, int H, int Dh, int Tmax,
-                const int* posp, int window, hipStream_t st);
+int attn_decode(const void* qkv, void* kc, void* vc, const float* cosb, const float* sinb, float* part, void* o,
+                int B, int H, int Dh, int Tmax, const int* posp, int window, float eps, hipStream_t st);
 // tok[0..B) = tokens[0..B), *posp = pos, *flag = 0 (one small kernel)
 void decode_stage(const int32_t* tokens, int B, int pos, int32_t* tok, int* posp, int* flag, hipStream_t st);
 
