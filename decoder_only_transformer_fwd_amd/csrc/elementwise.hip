@@ -700,10 +700,14 @@ void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int 
   int n2 = 1;
   while (n2 < rows) n2 <<= 1;
   if (!accumulate) fill_f32(dE, (long)vocab * d, 0.f, st);
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the sort holds up to 32768 keys in LDS: raise the kernel's dynamic LDS
+  // limit once per device (a function attribute is per device)
+  static bool attr_set[64] = {};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
     (void)hipFuncSetAttribute((const void*)sort_keys_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
-    attr_set = true;
+    if (dev >= 0 && dev < 64) attr_set[dev] = true;
   }
   hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), n2 * sizeof(uint32_t), st, tokens, rows, pbits, n2,
                      vocab, keys);
