@@ -586,7 +586,7 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
 // per row; forward_only stops after the final norm (prefill).
 int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float* grads, float grad_scale,
              int accumulate, const Shape* shape = nullptr, bool forward_only = false, float* loss_out = nullptr,
-             bool clear_flag = true) {
+             bool clear_flag = true, bool quant_weights = true) {
   const Shape& s = shape ? *shape : m.s;
   const ParamOffsets& P = m.po;
   const int dt = s.dtype;
@@ -654,9 +654,11 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   };
 
   if (clear_flag) fill_f32((float*)flag, 1, 0.f, st);
+  // fp8: the weights' codes and scales are made here, unless the caller
+  // knows they are those of the previous step (unchanged weights)
   if (f8) {
     zero_u32(amax8, m.n_slots * AMAX_SLOT, st);
-    for (int l = 0; l < s.L; ++l) {
+    for (int l = 0; l < s.L && quant_weights; ++l) {
       auto& Ly = m.lay[l];
       quant("fp8_quant_weights", FP8_E4M3, wp(P.Wqkv[l]), 3 * d, d, slot(l, SL_WQKV), m.ws + Ly.wq[0], m.ws + Ly.wqT[0], false);
       quant("fp8_quant_weights", FP8_E4M3, wp(P.Wo[l]), d, d, slot(l, SL_WO), m.ws + Ly.wq[1], m.ws + Ly.wqT[1], false);
@@ -1230,13 +1232,15 @@ int decode_graph_launch(gpt_model& m, int pos, void* kv, float* logits) {
 // The n micro-batch steps of gpt_step_micro, enqueued on m.st: the first
 // stores or accumulates as asked, the rest accumulate; each writes its mean
 // loss to mloss[i]; the token-range flag is cleared once and collects all.
+// The weights cannot change within the call, so an fp8 model quantises them
+// once, in the first step.
 int run_micro(gpt_model& m, const int32_t* tokens, const int32_t* targets, int n, float* grads, float scale,
               int accumulate) {
   fill_f32(at<float>(m, m.flag), 1, 0.f, m.st);
   const long bt = m.s.BT;
   for (int i = 0; i < n; ++i) {
     const int rc = run_step(m, tokens + i * bt, targets + i * bt, grads, scale, i ? 1 : accumulate, nullptr, false,
-                            at<float>(m, m.mloss) + i, false);
+                            at<float>(m, m.mloss) + i, false, i == 0);
     if (rc) return rc;
   }
   return GPT_OK;

@@ -156,20 +156,23 @@ def test_bad_accumulation_arguments_are_rejected():
     sess.close()
 
 
-def test_micro_batch_graph_matches_eager_steps():
+@pytest.mark.parametrize("name", ["bf16_mid", "fp8_mid"])
+def test_micro_batch_graph_matches_eager_steps(name):
     """gpt_step_micro (n micro-batches replayed as one captured graph) gives
     the gradients and losses of n gpt_step_accum calls bit for bit, on every
     replay, with eager work and synchronisation between replays; with
-    profiling on it runs eagerly and agrees too."""
+    profiling on it runs eagerly and agrees too.  (fp8: the call quantises
+    the unchanged weights once, the separate calls once each, to the same
+    codes.)"""
     import decoder_only_transformer_fwd_amd as G
-    s6 = SMALL["bf16_mid"].replace(batch=6)
+    s6 = SMALL[name].replace(batch=6)
     s = s6.replace(batch=2)
     n = 3
     W8 = gi.make_weights(s6)
     X, Y = gi.make_tokens(s6)
     Xm = X.reshape(n, s.batch, s.seq_len)
     Ym = Y.reshape(n, s.batch, s.seq_len)
-    log("micro-batch graph vs eager: bf16_mid, 3 x 2 rows")
+    log(f"micro-batch graph vs eager: {name}, 3 x 2 rows")
     sess = G.Session(s, W8)
     t = sess.torch
     ref_losses = []
