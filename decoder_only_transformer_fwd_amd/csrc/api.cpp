@@ -987,7 +987,10 @@ int ns_gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, i
   gemm_kernel_label(DT_BF16, layout, epi, tile, label, sizeof label);
   std::string lab(label);
   lab.insert(lab.size() - 1, ", batched");
-  prof_begin(m, site, 2.0 * M * N * (double)K * batch, 0, lab);
+  // a symmetric product computes the tiles on and above the diagonal only
+  const double t = (M + tile_bm(tile) - 1) / tile_bm(tile);
+  const double frac = (epi == EPI_STORE_SYM || epi == EPI_AXPBY_SYM) ? (t + 1) / (2 * t) : 1.0;
+  prof_begin(m, site, 2.0 * M * N * (double)K * batch * frac, 0, lab);
   if (gemm_launch_batched(a, layout, epi, tile, batch, m.st)) return fail(GPT_EINVAL, "batched gemm variant");
   prof_end(m);
   return GPT_OK;
@@ -1049,17 +1052,17 @@ int run_optim(gpt_model& m, char* state, const float* grads, const gpt_optim_par
     prof_end(m);
     for (int it = 0; it < hp.ns_steps; ++it) {
       int rc2;
-      // A = X X^T (wide) or X^T X (tall): [mm, mm]
+      // A = X X^T (wide) or X^T X (tall): [mm, mm], symmetric
       if (!tall)
-        rc2 = ns_gemm(m, "ns_gram", LAYOUT_KK, EPI_STORE, mm, mm, kk, X, c, rc, X, c, rc, Am, m2, nullptr, 1.f, 0.f,
-                      cnt);
+        rc2 = ns_gemm(m, "ns_gram", LAYOUT_KK, EPI_STORE_SYM, mm, mm, kk, X, c, rc, X, c, rc, Am, m2, nullptr, 1.f,
+                      0.f, cnt);
       else
-        rc2 = ns_gemm(m, "ns_gram", LAYOUT_MN, EPI_STORE, mm, mm, kk, X, c, rc, X, c, rc, Am, m2, nullptr, 1.f, 0.f,
-                      cnt);
+        rc2 = ns_gemm(m, "ns_gram", LAYOUT_MN, EPI_STORE_SYM, mm, mm, kk, X, c, rc, X, c, rc, Am, m2, nullptr, 1.f,
+                      0.f, cnt);
       if (rc2) return rc2;
-      // B = b A + c A A (A symmetric, so A A = A A^T)
-      if ((rc2 = ns_gemm(m, "ns_poly", LAYOUT_KK, EPI_AXPBY, mm, mm, mm, Am, mm, m2, Am, mm, m2, Bm, m2, Am, c_ns,
-                         b_ns, cnt)))
+      // B = b A + c A A (A symmetric, so A A = A A^T, and B is symmetric)
+      if ((rc2 = ns_gemm(m, "ns_poly", LAYOUT_KK, EPI_AXPBY_SYM, mm, mm, mm, Am, mm, m2, Am, mm, m2, Bm, m2, Am,
+                         c_ns, b_ns, cnt)))
         return rc2;
       // X' = a X + B X (wide) or a X + X B (tall; B symmetric)
       if (!tall)

@@ -218,6 +218,10 @@ template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, int RB, in
 // Two waves per SIMD except for the 4-wave tiles whose accumulators need the
 // whole register file.
 __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 * 128) ? 1 : 2) void gemm_kernel(GemmArgs p) {
+  // symmetric variants: the base epilogue E, upper-triangle tiles, mirrored stores
+  constexpr bool SYM = EPI == EPI_STORE_SYM || EPI == EPI_AXPBY_SYM;
+  constexpr int E = EPI == EPI_STORE_SYM ? EPI_STORE : EPI == EPI_AXPBY_SYM ? EPI_AXPBY : EPI;
+  static_assert(!SYM || BATCHED, "symmetric products are batched launches");
   // batched products: this work-group's member of the batch
   if constexpr (BATCHED) {
     const long bz = blockIdx.y;
@@ -259,7 +263,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
   int tm, tn;
-  tile_coords<(BM >= 1024 ? 1 : 1024 / BM)>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  if constexpr (SYM) {
+    // tiles on or above the diagonal, row by row
+    int idx = blockIdx.x;
+    tm = 0;
+    while (idx >= tiles_n - tm) idx -= tiles_n - tm++;
+    tn = tm + idx;
+  } else {
+    tile_coords<(BM >= 1024 ? 1 : 1024 / BM)>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int kbeg = blockIdx.z * p.k_split;
@@ -490,7 +502,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
     // Epilogues that read C (accumulate) or the saved pre-activation
     // (dReLU^2) load those values for a whole 32-row block up front: the
     // compiler cannot move a load above an earlier store that may alias it.
-    constexpr bool PRELOAD = EPI == EPI_ACCUM_F32 || EPI == EPI_DRELU2 || EPI == EPI_AXPBY;
+    constexpr bool PRELOAD = E == EPI_ACCUM_F32 || E == EPI_DRELU2 || E == EPI_AXPBY;
     float amax_acc = 0.f;   // RELU2 / DRELU2: largest |stored activation|
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
@@ -504,7 +516,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
           const int m = min(m0 + wm * WM + i * 32 + st * RPS + lane / LPR, p.M - 1);
           const int n = min(n0 + wn * WN + (lane % LPR) * 4, p.N - 4);
           const long off = (long)m * p.ldc + n;
-          if constexpr (EPI == EPI_ACCUM_F32) pre[st] = load4((const float*)p.C + off);
+          if constexpr (E == EPI_ACCUM_F32) pre[st] = load4((const float*)p.C + off);
           else pre[st] = load4((const TC*)p.aux + off);
         }
       }
@@ -528,13 +540,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
         const int n = n0 + wn * WN + c4 * 4;
         if (m < p.M && n < p.N) {
           const long off = (long)m * p.ldc + n;
-          if constexpr (EPI == EPI_STORE) {
+          if constexpr (E == EPI_STORE) {
             store4((TC*)p.C + off, v);
-          } else if constexpr (EPI == EPI_STORE_F32) {
+            if constexpr (SYM)
+              if (tm != tn)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ((TC*)p.C)[(long)(n + e) * p.ldc + m] = from_f32<TC>(v[e]);
+          } else if constexpr (E == EPI_STORE_F32) {
             store4((float*)p.C + off, v);
-          } else if constexpr (EPI == EPI_ACCUM_F32) {
+          } else if constexpr (E == EPI_ACCUM_F32) {
             store4((float*)p.C + off, pre[st] + v);
-          } else if constexpr (EPI == EPI_RELU2) {
+          } else if constexpr (E == EPI_RELU2) {
             store4((TC*)p.C + off, v);
             floatx4 rr;
 #pragma unroll
@@ -544,14 +560,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
             }
             store4((TC*)p.C2 + off, rr);
             if (p.amax) amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
-          } else if constexpr (EPI == EPI_DRELU2) {
+          } else if constexpr (E == EPI_DRELU2) {
             const floatx4 u = pre[st];
             floatx4 rr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) rr[e] = v[e] * 2.f * fmaxf(u[e], 0.f);
             store4((TC*)p.C + off, rr);
             if (p.amax) amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
-          } else if constexpr (EPI == EPI_XENT_BWD) {
+          } else if constexpr (E == EPI_XENT_BWD) {
             const float L2E = 1.4426950408889634f;
             const float lse = p.auxf[m];
             const int y = ((const int*)p.aux)[m];
@@ -559,20 +575,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
 #pragma unroll
             for (int e = 0; e < 4; ++e) rr[e] = (fast_exp2((v[e] - lse) * L2E) - (n + e == y ? 1.f : 0.f)) * p.beta;
             store4((TC*)p.C + off, rr);
-          } else if constexpr (EPI == EPI_PARTIAL) {
+          } else if constexpr (E == EPI_PARTIAL) {
             store4(p.part + (long)blockIdx.z * p.M * p.N + (long)m * p.N + n, v);
-          } else if constexpr (EPI == EPI_AXPBY) {
+          } else if constexpr (E == EPI_AXPBY) {
             floatx4 rr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) rr[e] = fmaf(p.beta, pre[st][e], v[e]);
             store4((TC*)p.C + off, rr);
+            if constexpr (SYM)
+              if (tm != tn)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ((TC*)p.C)[(long)(n + e) * p.ldc + m] = from_f32<TC>(rr[e]);
           }
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // staging reads done before the region is rewritten
       __builtin_amdgcn_wave_barrier();
     }
-    if constexpr (EPI == EPI_RELU2 || EPI == EPI_DRELU2) {
+    if constexpr (E == EPI_RELU2 || E == EPI_DRELU2) {
       if (p.amax) {
         __syncthreads();   // every wave is done with its staging region
         block_amax<NW>(p.amax, amax_acc, (float*)smem);
@@ -727,7 +747,9 @@ static int launch_fp8(const GemmArgs& a, int layout, int epi, int tile, int spli
 template <typename TA, typename MF, typename TC, int T, bool AK, bool BK_, int EPI>
 static void launch_batched_cfg(const GemmArgs& a, int batch, hipStream_t st) {
   constexpr TileCfg c = TILES[T];
-  dim3 grid(((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn), batch, 1);
+  const int tm = (a.M + c.bm - 1) / c.bm, tn = (a.N + c.bn - 1) / c.bn;
+  constexpr bool sym = EPI == EPI_STORE_SYM || EPI == EPI_AXPBY_SYM;
+  dim3 grid(sym ? tn * (tn + 1) / 2 : tm * tn, batch, 1);
   hipLaunchKernelGGL((gemm_kernel<TA, MF, c.bm, c.bn, c.wgm, c.wgn, c.rb, c.ns, AK, BK_, EPI, TC, c.pp, true>), grid,
                      dim3(64 * c.wgm * c.wgn), 0, st, a);
 }
@@ -745,6 +767,17 @@ static int launch_batched_tile(const GemmArgs& a, int tile, int batch, hipStream
 
 int gemm_launch_batched(const GemmArgs& a, int layout, int epi, int tile, int batch, hipStream_t st) {
   if (batch < 1 || batch > 65535) return -1;
+  if (epi == EPI_STORE_SYM || epi == EPI_AXPBY_SYM) {
+    // square output, square tiles
+    if (a.M != a.N || tile_bm(tile) != tile_bn(tile)) return -1;
+    if (layout == LAYOUT_KK && epi == EPI_STORE_SYM)
+      return launch_batched_tile<true, true, EPI_STORE_SYM>(a, tile, batch, st);
+    if (layout == LAYOUT_MN && epi == EPI_STORE_SYM)
+      return launch_batched_tile<false, false, EPI_STORE_SYM>(a, tile, batch, st);
+    if (layout == LAYOUT_KK && epi == EPI_AXPBY_SYM)
+      return launch_batched_tile<true, true, EPI_AXPBY_SYM>(a, tile, batch, st);
+    return -1;
+  }
   if (layout == LAYOUT_KK && epi == EPI_STORE) return launch_batched_tile<true, true, EPI_STORE>(a, tile, batch, st);
   if (layout == LAYOUT_KK && epi == EPI_AXPBY) return launch_batched_tile<true, true, EPI_AXPBY>(a, tile, batch, st);
   if (layout == LAYOUT_KN && epi == EPI_AXPBY) return launch_batched_tile<true, false, EPI_AXPBY>(a, tile, batch, st);

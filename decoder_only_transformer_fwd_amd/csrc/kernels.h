@@ -31,6 +31,11 @@ enum Epi {
   EPI_XENT_BWD = 6,   // C = (exp(acc - lse) - onehot(target)) * beta
   EPI_PARTIAL = 7,    // part[split][M][N] = acc (split-K)
   EPI_AXPBY = 8,      // C (activation type) = alpha * acc + beta * aux (aux laid out as C)
+  // EPI_STORE / EPI_AXPBY for a product known to be symmetric (M == N, and a
+  // symmetric aux): only the tiles on or above the diagonal are computed,
+  // each stored also transposed (batched launches only)
+  EPI_STORE_SYM = 9,
+  EPI_AXPBY_SYM = 10,
 };
 
 // Work-group tiles (M x N); _W8 variants use 8 waves (2 x 4) instead of 4 (2 x 2).
