@@ -161,7 +161,7 @@ def main() -> int:
     ap.add_argument("--prompt", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1:
-        log("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)")
+        log("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)")
         return 2
 
     import torch
