@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgpt_mi355x.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 
-SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "fp8.hip", "optim.hip", "infer.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "fp8.hip", "optim.hip", "infer.hip", "api.cpp", "optim_host.cpp", "infer_host.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

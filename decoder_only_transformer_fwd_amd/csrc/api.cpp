@@ -11,12 +11,12 @@
 #include <string>
 #include <vector>
 
-#include "../../include/gpt.h"
-#include "kernels.h"
+#include "model.h"
 
 using namespace gk;
+using namespace gm;
 
-namespace {
+namespace gm __attribute__((visibility("hidden"))) {
 
 thread_local std::string g_last_error;
 
@@ -25,28 +25,6 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
-#define HIP_TRY(expr)                                                              \
-  do {                                                                             \
-    hipError_t e_ = (expr);                                                        \
-    if (e_ != hipSuccess)                                                          \
-      return fail(GPT_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_));    \
-  } while (0)
-
-constexpr size_t ALIGN = 256;
-// decoding: K splits of the products whose few weight rows would leave most
-// CUs idle (output projection, W2); their partials go through the next norm
-constexpr int DEC_KSPLIT = 8;
-static_assert(DEC_KSPLIT <= 8, "the decoder's add + norm kernel adds at most 8 partials");
-// micro-batches per gpt_step_micro call
-constexpr int MAX_MICRO = 1024;
-size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
-
-struct Shape {
-  int L, d, H, Dh, F, V, T, B, BT, Tp, dtype, es;
-  bool fp8;   // linear layers (QKV, O, W1, W2) in fp8; everything else as bf16
-  float eps, base;
-  std::vector<int> win;   // keys visible per layer
-};
 
 int check_config(const gpt_config* c, Shape& s) {
   if (!c) return fail(GPT_ENULL, "cfg is NULL");
@@ -88,13 +66,6 @@ int check_config(const gpt_config* c, Shape& s) {
   }
   return GPT_OK;
 }
-
-struct ParamOffsets {
-  long E, U;
-  std::vector<long> Wqkv, Wo, W1, W2;
-  long total;
-  std::vector<gpt_tensor_desc> descs;
-};
 
 void param_offsets(const Shape& s, ParamOffsets& p) {
   long off = 0;
@@ -235,106 +206,9 @@ TailPlan plan_tail(int dtype, int layout, int epi, int M, int N, int K) {
   return t;
 }
 
-}  // namespace
+}  // namespace gm
 
-// ------------------------------------------------------------------ model
-// Optimizer state plan: byte offsets into the caller's state buffer and the
-// pass lists (each list ends with a sentinel entry).
-struct OptPlan {
-  struct List {
-    int seg0 = 0, n = 0, nblk = 0;
-  };
-  struct Group {   // Muon matrices of one shape, orthogonalised as one batch
-    List list;
-    int rows = 0, cols = 0, count = 0;
-  };
-  size_t hdr = 0, table = 0, part = 0, master = 0, mom = 0, ns = 0, total = 0;
-  size_t xa = 0, xb = 0, ab = 0, bb = 0;   // Newton-Schulz buffers (offsets from ns)
-  bool has_master = false;
-  List all, adam;
-  std::vector<Group> groups;
-  std::vector<OptSeg> table_host;
-  int max_part = 0;
-};
-
-struct gpt_model {
-  gpt_config cfg;
-  Shape s;
-  ParamOffsets po;
-  hipStream_t st;
-  char* ws;
-  const char* W;
-  // workspace offsets (bytes)
-  struct Layer {
-    size_t n1, rstd1, qkv, rqk, qT, kT, vT, o, lse2, n2, rstd2, u, g;
-    // fp8: transposed activation codes kept for the weight gradients, and the
-    // step's weight codes (row-major and transposed) for QKV, O, W1, W2
-    size_t n1T, oT, n2T, gT, wq[4], wqT[4];
-  };
-  std::vector<Layer> lay;
-  size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, mloss, dpart, dtok, dpos, dsplit, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
-      cosb, sinb, keys, total;
-  size_t splitk_floats;
-  size_t q8row, q8T, amax, scales;   // fp8: transient codes, per-tensor amax / scale slots
-  int n_slots;
-  int xent_tile, xent_nblk;
-  // optional per-launch-site timing with HIP events on the step's stream
-  struct Site {
-    std::string name;
-    std::string kernel;   // template signature of the launched kernel
-    long launches = 0;
-    double ms = 0.0, work = 0.0;
-    int work_kind = 0;  // 0 = flops, 1 = bytes
-  };
-  struct Pending {
-    int site;
-    double work;
-    hipEvent_t a, b;
-  };
-  OptPlan opt;
-  void* opt_state = nullptr;   // the state buffer gpt_optim_init prepared
-  // decoding: one step captured as a HIP graph (for the cache and logits
-  // buffers it was captured with), replayed on a stream of its own that is
-  // ordered after the model's stream by events
-  struct DecodeGraph {
-    hipStream_t cs = nullptr;
-    hipGraph_t graph = nullptr;
-    hipGraphExec_t exec = nullptr;
-    hipEvent_t before = nullptr, after = nullptr;
-    const void* kv = nullptr;
-    const void* logits = nullptr;
-  } dg;
-  // gpt_step_micro: the n micro-batch steps captured as one graph, for the
-  // buffers and arguments it was captured with (replayed on dg.cs)
-  struct MicroGraph {
-    hipGraph_t graph = nullptr;
-    hipGraphExec_t exec = nullptr;
-    const void* tokens = nullptr;
-    const void* targets = nullptr;
-    const void* grads = nullptr;
-    int n = 0, accumulate = 0;
-    float scale = 0.f;
-  } mg;
-  bool prof_on = false;
-  std::vector<Site> sites;
-  std::vector<hipEvent_t> ev_pool;
-  size_t ev_used = 0;
-  std::vector<Pending> pend;
-  int cur_site = -1;
-  double cur_work = 0.0;
-  ~gpt_model() {
-    for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
-    if (mg.exec) (void)hipGraphExecDestroy(mg.exec);
-    if (mg.graph) (void)hipGraphDestroy(mg.graph);
-    if (dg.exec) (void)hipGraphExecDestroy(dg.exec);
-    if (dg.graph) (void)hipGraphDestroy(dg.graph);
-    if (dg.before) (void)hipEventDestroy(dg.before);
-    if (dg.after) (void)hipEventDestroy(dg.after);
-    if (dg.cs) (void)hipStreamDestroy(dg.cs);
-  }
-};
-
-namespace {
+namespace gm __attribute__((visibility("hidden"))) {
 
 int build_layout(gpt_model& m) {
   const Shape& s = m.s;
@@ -450,9 +324,6 @@ int build_layout(gpt_model& m) {
   m.total = off;
   return GPT_OK;
 }
-
-template <typename P>
-P* at(gpt_model& m, size_t off) { return (P*)(m.ws + off); }
 
 // Site timing: prof_begin records an event before a launch, prof_end after
 // it; gpt_step resolves the pairs once the stream has been synchronised.
@@ -585,8 +456,8 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
 // overwriting it.  `shape` (default: the model's) may describe fewer tokens
 // per row; forward_only stops after the final norm (prefill).
 int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float* grads, float grad_scale,
-             int accumulate, const Shape* shape = nullptr, bool forward_only = false, float* loss_out = nullptr,
-             bool clear_flag = true, bool quant_weights = true) {
+             int accumulate, const Shape* shape, bool forward_only, float* loss_out, bool clear_flag,
+             bool quant_weights) {
   const Shape& s = shape ? *shape : m.s;
   const ParamOffsets& P = m.po;
   const int dt = s.dtype;
@@ -870,321 +741,6 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   return GPT_OK;
 }
 
-// ------------------------------------------------------------------ optimizer
-// Muon on every projection matrix, AdamW on E and U (the state holds fp32
-// master weights for bf16 parameters, Muon momenta, AdamW moments, the pass
-// lists and the Newton-Schulz buffers).
-void optim_plan(const Shape& s, const ParamOffsets& P, OptPlan& o) {
-  o = OptPlan{};
-  std::vector<OptSeg> tab;
-  long mom = 0;   // floats of momentum / moment state so far
-  auto close_list = [&](OptPlan::List& l, std::vector<OptSeg> entries) {
-    l.seg0 = (int)tab.size();
-    l.n = (int)entries.size();
-    int blk = 0;
-    for (auto& e : entries) {
-      e.blk0 = blk;
-      blk += (int)((e.n + OPT_CHUNK - 1) / OPT_CHUNK);
-      tab.push_back(e);
-    }
-    OptSeg sentinel{};
-    sentinel.blk0 = blk;
-    tab.push_back(sentinel);
-    l.nblk = blk;
-    o.max_part = std::max(o.max_part, blk);
-  };
-  auto seg_of = [](const gpt_tensor_desc& t) {
-    OptSeg e{};
-    e.off = t.offset;
-    e.n = (long)t.rows * t.cols;
-    return e;
-  };
-  // every tensor: the global gradient norm
-  {
-    std::vector<OptSeg> v;
-    for (auto& t : P.descs) v.push_back(seg_of(t));
-    close_list(o.all, v);
-  }
-  // Muon groups by shape, in layout order
-  std::vector<std::pair<int, int>> shapes;
-  for (auto& t : P.descs) {
-    const bool mat = strcmp(t.name, "E") != 0 && strcmp(t.name, "U") != 0;
-    if (mat && std::find(shapes.begin(), shapes.end(), std::make_pair(t.rows, t.cols)) == shapes.end())
-      shapes.push_back({t.rows, t.cols});
-  }
-  size_t ns_need = 0;
-  for (auto& sh : shapes) {
-    OptPlan::Group g;
-    g.rows = sh.first;
-    g.cols = sh.second;
-    std::vector<OptSeg> v;
-    for (auto& t : P.descs) {
-      if (!strcmp(t.name, "E") || !strcmp(t.name, "U") || t.rows != g.rows || t.cols != g.cols) continue;
-      OptSeg e = seg_of(t);
-      e.soff = mom;
-      mom += e.n;
-      e.xoff = (long)g.count * g.rows * g.cols;
-      g.count++;
-      v.push_back(e);
-    }
-    close_list(g.list, v);
-    const long m = std::min(g.rows, g.cols);
-    const size_t xbytes = align_up((size_t)g.count * g.rows * g.cols * 2);
-    const size_t abytes = align_up((size_t)g.count * m * m * 2);
-    ns_need = std::max(ns_need, 2 * xbytes + 2 * abytes);
-    o.groups.push_back(g);
-  }
-  // AdamW: E (lr0), U (lr1)
-  {
-    std::vector<OptSeg> v;
-    for (auto& t : P.descs) {
-      if (strcmp(t.name, "E") && strcmp(t.name, "U")) continue;
-      OptSeg e = seg_of(t);
-      e.soff = mom;
-      mom += 2 * e.n;
-      e.which = strcmp(t.name, "U") == 0;
-      v.push_back(e);
-    }
-    close_list(o.adam, v);
-  }
-  o.table_host = tab;
-  o.has_master = s.dtype != DT_F32;
-  size_t off = 0;
-  o.hdr = off; off += ALIGN;
-  o.table = off; off += align_up(tab.size() * sizeof(OptSeg));
-  o.part = off; off += align_up((size_t)o.max_part * 4);
-  o.master = off; off += o.has_master ? align_up((size_t)P.total * 4) : 0;
-  o.mom = off; off += align_up((size_t)mom * 4);
-  o.ns = off; off += ns_need;
-  o.total = off;
-}
-
-// Newton-Schulz buffers of one group (byte offsets from the state base).
-void ns_buffers(const OptPlan& o, const OptPlan::Group& g, size_t& xa, size_t& xb, size_t& ab, size_t& bb) {
-  const long m = std::min(g.rows, g.cols);
-  const size_t xbytes = align_up((size_t)g.count * g.rows * g.cols * 2);
-  const size_t abytes = align_up((size_t)g.count * m * m * 2);
-  xa = o.ns;
-  xb = xa + xbytes;
-  ab = xb + xbytes;
-  bb = ab + abytes;
-}
-
-int ns_tile(int M, int N) { return M >= 256 && N >= 256 ? TILE_256x256_PP4 : TILE_128x128; }
-
-// One batched bf16 product of the orthogonalisation: C = alpha * op(A, B)
-// (+ beta * aux, aux laid out as C), `batch` members at element strides.
-int ns_gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int K, const void* A, long lda,
-            long bsA, const void* B, long ldb, long bsB, void* C, long bsC, const void* aux, float alpha,
-            float beta, int batch) {
-  GemmArgs a{};
-  a.A = A; a.B = B; a.C = C; a.aux = aux;
-  a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = ldb; a.ldc = N;
-  a.alpha = alpha; a.beta = beta; a.k_split = K;
-  a.bsA = bsA; a.bsB = bsB; a.bsC = bsC;
-  const int tile = ns_tile(M, N);
-  char label[128];
-  gemm_kernel_label(DT_BF16, layout, epi, tile, label, sizeof label);
-  std::string lab(label);
-  lab.insert(lab.size() - 1, ", batched");
-  // a symmetric product computes the tiles on and above the diagonal only
-  const double t = (M + tile_bm(tile) - 1) / tile_bm(tile);
-  const double frac = (epi == EPI_STORE_SYM || epi == EPI_AXPBY_SYM) ? (t + 1) / (2 * t) : 1.0;
-  prof_begin(m, site, 2.0 * M * N * (double)K * batch * frac, 0, lab);
-  if (gemm_launch_batched(a, layout, epi, tile, batch, m.st)) return fail(GPT_EINVAL, "batched gemm variant");
-  prof_end(m);
-  return GPT_OK;
-}
-
-// One optimizer step (enqueued on the model's stream).
-int run_optim(gpt_model& m, char* state, const float* grads, const gpt_optim_params& hp, bool want_norm) {
-  const OptPlan& o = m.opt;
-  hipStream_t st = m.st;
-  float* hdr = (float*)(state + o.hdr);
-  const OptSeg* tab = (const OptSeg*)(state + o.table);
-  float* part = (float*)(state + o.part);
-  float* mom = (float*)(state + o.mom);
-  // fp32 parameters are their own master copy; bf16 ones get a refreshed copy
-  float* master = o.has_master ? (float*)(state + o.master) : (float*)m.W;
-  void* w16 = o.has_master ? (void*)m.W : nullptr;
-  const double n_all = (double)m.po.total;
-
-  if (hp.grad_clip > 0.f || want_norm) {
-    prof_begin(m, "optim_grad_norm", n_all * 4.0, 1, "opt_sumsq_kernel + opt_norm_kernel");
-    opt_sumsq(grads, tab + o.all.seg0, o.all.n, o.all.nblk, part, st);
-    opt_norm(part, o.all.nblk, hp.grad_clip, hdr, st);
-    prof_end(m);
-  } else {
-    fill_f32(hdr + 1, 1, 1.f, st);   // clip coefficient 1
-  }
-  {
-    AdamArgs a{};
-    a.b1 = hp.beta1; a.b2 = hp.beta2; a.eps = hp.eps; a.wd = hp.weight_decay;
-    a.ibc1 = (float)(1.0 / (1.0 - std::pow((double)hp.beta1, (double)hp.step)));
-    a.ibc2 = (float)(1.0 / (1.0 - std::pow((double)hp.beta2, (double)hp.step)));
-    a.lr0 = hp.embedding_lr;
-    a.lr1 = hp.unembedding_lr;
-    double n = 0;
-    for (int i = 0; i < o.adam.n; ++i) n += (double)o.table_host[o.adam.seg0 + i].n;
-    prof_begin(m, "optim_adamw", n * (o.has_master ? 30.0 : 28.0), 1, "opt_adamw_kernel");
-    opt_adamw(master, mom, grads, w16, tab + o.adam.seg0, o.adam.n, o.adam.nblk, hdr, a, st);
-    prof_end(m);
-  }
-  const float a_ns = 3.4445f, b_ns = -4.7750f, c_ns = 2.0315f;
-  for (const auto& g : o.groups) {
-    const int r = g.rows, c = g.cols, cnt = g.count;
-    const bool tall = r > c;
-    const int mm = tall ? c : r, kk = tall ? r : c;
-    const long rc = (long)r * c, m2 = (long)mm * mm;
-    size_t xa, xb, ab, bb;
-    ns_buffers(o, g, xa, xb, ab, bb);
-    char* X = state + xa;
-    char* Y = state + xb;
-    char* Am = state + ab;
-    char* Bm = state + bb;
-    const double n = (double)rc * cnt;
-    prof_begin(m, "optim_muon_momentum", n * 12.0, 1, "opt_muon_momentum_kernel");
-    opt_muon_momentum(grads, mom, tab + g.list.seg0, g.list.n, g.list.nblk, hdr, hp.momentum, hp.nesterov, part, st);
-    prof_end(m);
-    prof_begin(m, "optim_muon_normalise", n * 10.0, 1, "opt_muon_normalise_kernel");
-    opt_muon_normalise(grads, mom, tab + g.list.seg0, g.list.n, g.list.nblk, hdr, hp.momentum, hp.nesterov, part, X,
-                       st);
-    prof_end(m);
-    for (int it = 0; it < hp.ns_steps; ++it) {
-      int rc2;
-      // A = X X^T (wide) or X^T X (tall): [mm, mm], symmetric
-      if (!tall)
-        rc2 = ns_gemm(m, "ns_gram", LAYOUT_KK, EPI_STORE_SYM, mm, mm, kk, X, c, rc, X, c, rc, Am, m2, nullptr, 1.f,
-                      0.f, cnt);
-      else
-        rc2 = ns_gemm(m, "ns_gram", LAYOUT_MN, EPI_STORE_SYM, mm, mm, kk, X, c, rc, X, c, rc, Am, m2, nullptr, 1.f,
-                      0.f, cnt);
-      if (rc2) return rc2;
-      // B = b A + c A A (A symmetric, so A A = A A^T, and B is symmetric)
-      if ((rc2 = ns_gemm(m, "ns_poly", LAYOUT_KK, EPI_AXPBY_SYM, mm, mm, mm, Am, mm, m2, Am, mm, m2, Bm, m2, Am,
-                         c_ns, b_ns, cnt)))
-        return rc2;
-      // X' = a X + B X (wide) or a X + X B (tall; B symmetric)
-      if (!tall)
-        rc2 = ns_gemm(m, "ns_apply", LAYOUT_KN, EPI_AXPBY, r, c, r, Bm, mm, m2, X, c, rc, Y, rc, X, 1.f, a_ns, cnt);
-      else
-        rc2 = ns_gemm(m, "ns_apply", LAYOUT_KK, EPI_AXPBY, r, c, c, X, c, rc, Bm, mm, m2, Y, rc, X, 1.f, a_ns, cnt);
-      if (rc2) return rc2;
-      std::swap(X, Y);
-    }
-    const float scale = std::sqrt(std::max(1.0f, (float)r / (float)c));
-    prof_begin(m, "optim_muon_update", n * (o.has_master ? 12.0 : 10.0), 1, "opt_muon_update_kernel");
-    opt_muon_update(master, X, w16, tab + g.list.seg0, g.list.n, g.list.nblk, hp.matrix_lr, scale, hp.weight_decay,
-                    st);
-    prof_end(m);
-  }
-  HIP_TRY(hipGetLastError());
-  return GPT_OK;
-}
-
-// ------------------------------------------------------------------ inference
-size_t kv_layer_elems(const Shape& s) { return (size_t)s.B * s.H * s.T * s.Dh; }
-
-int check_infer(gpt_model& m) {
-  if (m.s.dtype != DT_BF16) return fail(GPT_EINVAL, "inference runs on bf16 parameters (GPT_BF16 or GPT_FP8 models)");
-  if (m.s.B > 32) return fail(GPT_EINVAL, "inference supports batch <= 32");
-  if (m.s.Dh != 64 && m.s.Dh != 128) return fail(GPT_EINVAL, "inference supports head_dim 64 or 128");
-  return GPT_OK;
-}
-
-// One skinny product of decoding, timed as a site like the step's products.
-int dec_gemm(gpt_model& m, const char* site, int epi, const void* x, long ldx, int K, const void* Wt, int N, void* C,
-             int ldc, void* C2 = nullptr, int ksplit = 1) {
-  const int B = m.s.B;
-  prof_begin(m, site, 2.0 * B * (double)N * K, 0, std::string("skinny_gemm_kernel<") + std::to_string(epi) + ">");
-  if (skinny_gemm(epi, x, ldx, B, K, Wt, N, C, ldc, C2, ksplit, m.st)) return fail(GPT_EINVAL, "skinny gemm shape");
-  prof_end(m);
-  return GPT_OK;
-}
-
-// Prefill: the forward over n tokens per row (positions 0..n-1), the keys and
-// values of every layer into the cache, and the next-token logits of the
-// last position.
-int run_prefill(gpt_model& m, const int32_t* tokens, int n, char* kv, float* logits) {
-  Shape sp = m.s;
-  sp.T = n;
-  sp.BT = sp.B * n;
-  sp.Tp = (n + 63) / 64 * 64;
-  sp.fp8 = false;   // fp8 models decode with their bf16 weights
-  for (auto& w : sp.win) w = std::min(w, n);
-  int rc = run_step(m, tokens, tokens, nullptr, 1.f, 0, &sp, true);
-  if (rc) return rc;
-  const Shape& s = m.s;
-  const size_t kvl = kv_layer_elems(s);
-  prof_begin(m, "prefill_kv_fill", (double)sp.BT * 2.0 * s.d * 2.0 * 2.0, 1, "kv_fill_kernel");
-  for (int l = 0; l < s.L; ++l) {
-    uint16_t* kc = (uint16_t*)kv + (size_t)2 * l * kvl;
-    kv_fill(m.ws + m.lay[l].qkv, kc, kc + kvl, s.B, n, s.H, s.Dh, s.T, m.st);
-  }
-  prof_end(m);
-  // rows b*n + n - 1 of the final normalised activations
-  return dec_gemm(m, "prefill_lm_head", EPI_STORE_F32, m.ws + m.nL + (size_t)(n - 1) * s.d * 2, (long)n * s.d, s.d,
-                  m.W + (size_t)m.po.U * 2, s.V, logits, s.V);
-}
-
-// One decoding step on the model's stream: token ids and position come from
-// the decoder's device buffers (decode_stage fills them), so the launch
-// sequence does not depend on them and can be captured once.  `pos` (host)
-// only sizes the profiler's work accounting.
-int run_decode(gpt_model& m, int pos, char* kv, float* logits) {
-  const Shape& s = m.s;
-  const ParamOffsets& P = m.po;
-  const int B = s.B, d = s.d, F = s.F, V = s.V, H = s.H, Dh = s.Dh;
-  hipStream_t st = m.st;
-  auto wp = [&](long off) { return (const void*)(m.W + off * 2); };
-  float* h = at<float>(m, m.h);
-  int* flag = at<int>(m, m.flag);
-  char* n1 = m.ws + m.lay[0].n1;
-  char* qkv = m.ws + m.lay[0].qkv;
-  char* o = m.ws + m.lay[0].o;
-  char* u = m.ws + m.lay[0].u;
-  char* g = m.ws + m.lay[0].g;
-  float* dpart = at<float>(m, m.dpart);
-  const int32_t* tokens = at<int32_t>(m, m.dtok);
-  const int* posp = at<int>(m, m.dpos);
-  const size_t kvl = kv_layer_elems(s);
-  int rc;
-  float* split = at<float>(m, m.dsplit);
-  prof_begin(m, "decode_embed", (double)B * d * 6.0, 1, "embed_fwd_kernel<bf16>");
-  embed_fwd(DT_BF16, tokens, tokens, wp(P.E), h, B, d, V, flag, st);
-  prof_end(m);
-  int pending = 0;   // K-split partials of the last product, added by the next norm
-  auto addnorm = [&](void* y) {
-    prof_begin(m, "decode_add_rmsnorm", (double)B * d * (4.0 * pending + 10.0), 1, "decode_add_rmsnorm_kernel");
-    decode_add_rmsnorm(h, split, pending, B, d, y, s.eps, st);
-    prof_end(m);
-    pending = 0;
-  };
-  for (int l = 0; l < s.L; ++l) {
-    uint16_t* kc = (uint16_t*)kv + (size_t)2 * l * kvl;
-    uint16_t* vc = kc + kvl;
-    addnorm(n1);
-    if ((rc = dec_gemm(m, "decode_qkv", EPI_STORE, n1, d, d, wp(P.Wqkv[l]), 3 * d, qkv, 3 * d))) return rc;
-    const int lo = std::max(0, pos - s.win[l] + 1);
-    prof_begin(m, "decode_attention", (double)B * H * (pos - lo + 1) * Dh * 4.0, 1,
-               "attn_decode_split_kernel + attn_decode_combine_kernel");
-    if (attn_decode(qkv, kc, vc, at<float>(m, m.cosb), at<float>(m, m.sinb), dpart, o, B, H, Dh, s.T, posp,
-                    s.win[l], s.eps, st))
-      return fail(GPT_EINVAL, "decode attention head_dim");
-    prof_end(m);
-    if ((rc = dec_gemm(m, "decode_o", EPI_PARTIAL, o, d, d, wp(P.Wo[l]), d, split, d, nullptr, DEC_KSPLIT))) return rc;
-    pending = DEC_KSPLIT;
-    addnorm(n1);
-    if ((rc = dec_gemm(m, "decode_w1_relu2", EPI_RELU2, n1, d, d, wp(P.W1[l]), F, u, F, g))) return rc;
-    if ((rc = dec_gemm(m, "decode_w2", EPI_PARTIAL, g, F, F, wp(P.W2[l]), d, split, d, nullptr, DEC_KSPLIT))) return rc;
-    pending = DEC_KSPLIT;
-  }
-  addnorm(m.ws + m.nL);
-  if ((rc = dec_gemm(m, "decode_lm_head", EPI_STORE_F32, m.ws + m.nL, d, d, wp(P.U), V, logits, V))) return rc;
-  HIP_TRY(hipGetLastError());
-  return GPT_OK;
-}
-
 // Graph-replay stream and events of the handle (created on first use).
 int graph_stream(gpt_model& m) {
   auto& g = m.dg;
@@ -1193,42 +749,6 @@ int graph_stream(gpt_model& m) {
     HIP_TRY(hipEventCreateWithFlags(&g.before, hipEventDisableTiming));
     HIP_TRY(hipEventCreateWithFlags(&g.after, hipEventDisableTiming));
   }
-  return GPT_OK;
-}
-
-// Replays the captured decoding step (capturing it first, or again when the
-// cache or logits buffer differs from the captured one).
-int decode_graph_launch(gpt_model& m, int pos, void* kv, float* logits) {
-  const int rc0 = graph_stream(m);
-  if (rc0) return rc0;
-  auto& g = m.dg;
-  if (!g.exec || g.kv != kv || g.logits != logits) {
-    if (g.exec) (void)hipGraphExecDestroy(g.exec);
-    if (g.graph) (void)hipGraphDestroy(g.graph);
-    g.exec = nullptr;
-    g.graph = nullptr;
-    HIP_TRY(hipStreamBeginCapture(g.cs, hipStreamCaptureModeThreadLocal));
-    hipStream_t saved = m.st;
-    m.st = g.cs;
-    const int rc = run_decode(m, pos, (char*)kv, logits);
-    m.st = saved;
-    hipGraph_t graph = nullptr;
-    const hipError_t e = hipStreamEndCapture(g.cs, &graph);
-    if (rc) {
-      if (graph) (void)hipGraphDestroy(graph);
-      return rc;
-    }
-    if (e != hipSuccess) return fail(GPT_EHIP, std::string("decode graph capture: ") + hipGetErrorString(e));
-    g.graph = graph;
-    HIP_TRY(hipGraphInstantiate(&g.exec, g.graph, nullptr, nullptr, 0));
-    g.kv = kv;
-    g.logits = logits;
-  }
-  HIP_TRY(hipEventRecord(g.before, m.st));
-  HIP_TRY(hipStreamWaitEvent(g.cs, g.before, 0));
-  HIP_TRY(hipGraphLaunch(g.exec, g.cs));
-  HIP_TRY(hipEventRecord(g.after, g.cs));
-  HIP_TRY(hipStreamWaitEvent(m.st, g.after, 0));
   return GPT_OK;
 }
 
@@ -1292,17 +812,7 @@ int micro_graph_launch(gpt_model& m, const int32_t* tokens, const int32_t* targe
   return GPT_OK;
 }
 
-// Waits for the stream, then reports an out-of-range id.
-int finish_infer(gpt_model& m) {
-  int flag = 0;
-  HIP_TRY(hipMemcpyAsync(&flag, m.ws + m.flag, 4, hipMemcpyDeviceToHost, m.st));
-  HIP_TRY(hipStreamSynchronize(m.st));
-  if (m.prof_on) prof_collect(m);
-  if (flag) return fail(GPT_ETOKEN, "a token id is outside [0, vocab)");
-  return GPT_OK;
-}
-
-}  // namespace
+}  // namespace gm
 
 // ------------------------------------------------------------------ C ABI
 extern "C" {
@@ -1423,116 +933,6 @@ int gpt_step_micro(gpt_model* m, const int32_t* tokens, const int32_t* targets, 
 }
 
 void gpt_destroy(gpt_model* m) { delete m; }
-
-int gpt_kv_cache_bytes(const gpt_config* cfg, size_t* bytes) {
-  if (!bytes) return fail(GPT_ENULL, "bytes is NULL");
-  Shape s;
-  int rc = check_config(cfg, s);
-  if (rc) return rc;
-  *bytes = (size_t)2 * s.L * kv_layer_elems(s) * 2;
-  return GPT_OK;
-}
-
-int gpt_prefill(gpt_model* m, const int32_t* tokens, int n_tokens, void* kv_cache, float* logits) {
-  if (!m || !tokens || !kv_cache || !logits) return fail(GPT_ENULL, "gpt_prefill: NULL argument");
-  int rc = check_infer(*m);
-  if (rc) return rc;
-  if (n_tokens < 1 || n_tokens > m->s.T) return fail(GPT_EINVAL, "n_tokens must be in [1, seq_len]");
-  if (((uintptr_t)kv_cache | (uintptr_t)logits) & 15) return fail(GPT_EALIGN, "kv_cache and logits must be 16-byte aligned");
-  if ((rc = run_prefill(*m, tokens, n_tokens, (char*)kv_cache, logits))) return rc;
-  return finish_infer(*m);
-}
-
-int gpt_decode(gpt_model* m, const int32_t* tokens, int pos, void* kv_cache, float* logits) {
-  if (!m || !tokens || !kv_cache || !logits) return fail(GPT_ENULL, "gpt_decode: NULL argument");
-  int rc = check_infer(*m);
-  if (rc) return rc;
-  if (pos < 1 || pos >= m->s.T) return fail(GPT_EINVAL, "pos must be in [1, seq_len)");
-  if (((uintptr_t)kv_cache | (uintptr_t)logits) & 15) return fail(GPT_EALIGN, "kv_cache and logits must be 16-byte aligned");
-  decode_stage(tokens, m->s.B, pos, at<int32_t>(*m, m->dtok), at<int>(*m, m->dpos), at<int>(*m, m->flag), m->st);
-  if (m->prof_on) {
-    // profiled steps run eagerly, so that every launch is timed
-    if ((rc = run_decode(*m, pos, (char*)kv_cache, logits))) return rc;
-  } else {
-    if ((rc = decode_graph_launch(*m, pos, kv_cache, logits))) return rc;
-  }
-  return finish_infer(*m);
-}
-
-int gpt_optim_state_bytes(const gpt_config* cfg, size_t* bytes) {
-  if (!bytes) return fail(GPT_ENULL, "bytes is NULL");
-  Shape s;
-  int rc = check_config(cfg, s);
-  if (rc) return rc;
-  ParamOffsets p;
-  param_offsets(s, p);
-  OptPlan o;
-  optim_plan(s, p, o);
-  *bytes = o.total;
-  return GPT_OK;
-}
-
-int gpt_optim_init(gpt_model* m, void* state, size_t state_bytes) {
-  if (!m || !state) return fail(GPT_ENULL, "gpt_optim_init: NULL argument");
-  if ((uintptr_t)state & (ALIGN - 1)) return fail(GPT_EALIGN, "state must be 256-byte aligned");
-  OptPlan o;
-  optim_plan(m->s, m->po, o);
-  if (state_bytes < o.total)
-    return fail(GPT_ESPACE, "optimizer state too small: need " + std::to_string(o.total) + " bytes");
-  char* st = (char*)state;
-  m->opt_state = nullptr;
-  HIP_TRY(hipMemcpyAsync(st + o.table, o.table_host.data(), o.table_host.size() * sizeof(OptSeg),
-                         hipMemcpyHostToDevice, m->st));
-  long nmom = 0;
-  for (const auto& g : o.groups) nmom += (long)g.rows * g.cols * g.count;
-  for (int i = 0; i < o.adam.n; ++i) nmom += 2 * o.table_host[o.adam.seg0 + i].n;
-  fill_f32((float*)(st + o.mom), nmom, 0.f, m->st);
-  fill_f32((float*)(st + o.hdr), ALIGN / 4, 0.f, m->st);
-  if (o.has_master)
-    opt_widen(m->W, (float*)(st + o.master), (const OptSeg*)(st + o.table) + o.all.seg0, o.all.n, o.all.nblk, m->st);
-  HIP_TRY(hipGetLastError());
-  HIP_TRY(hipStreamSynchronize(m->st));   // the table's host copy must outlive the transfer
-  m->opt = o;
-  m->opt_state = state;
-  return GPT_OK;
-}
-
-int gpt_optim_master(gpt_model* m, float** master) {
-  if (!m || !master) return fail(GPT_ENULL, "gpt_optim_master: NULL argument");
-  if (!m->opt_state) return fail(GPT_EINVAL, "no optimizer state: call gpt_optim_init first");
-  *master = m->opt.has_master ? (float*)((char*)m->opt_state + m->opt.master) : (float*)m->W;
-  return GPT_OK;
-}
-
-int gpt_optim_step(gpt_model* m, void* state, const float* grads, const gpt_optim_params* hp, float* grad_norm) {
-  if (!m || !state || !grads || !hp) return fail(GPT_ENULL, "gpt_optim_step: NULL argument");
-  if (state != m->opt_state) return fail(GPT_EINVAL, "state was not prepared by gpt_optim_init for this model");
-  if ((uintptr_t)grads & (ALIGN - 1)) return fail(GPT_EALIGN, "grads must be 256-byte aligned");
-  const float f[] = {hp->matrix_lr, hp->momentum, hp->embedding_lr, hp->unembedding_lr, hp->beta1,
-                     hp->beta2,     hp->eps,      hp->weight_decay, hp->grad_clip};
-  for (float x : f)
-    if (!std::isfinite(x)) return fail(GPT_EINVAL, "optimizer parameters must be finite");
-  if (hp->momentum < 0.f || hp->momentum >= 1.f) return fail(GPT_EINVAL, "momentum must be in [0, 1)");
-  if (hp->beta1 < 0.f || hp->beta1 >= 1.f || hp->beta2 < 0.f || hp->beta2 >= 1.f)
-    return fail(GPT_EINVAL, "beta1 and beta2 must be in [0, 1)");
-  if (!(hp->eps > 0.f)) return fail(GPT_EINVAL, "eps must be positive");
-  if (hp->ns_steps < 1 || hp->ns_steps > 32) return fail(GPT_EINVAL, "ns_steps must be in [1, 32]");
-  if (hp->nesterov != 0 && hp->nesterov != 1) return fail(GPT_EINVAL, "nesterov must be 0 or 1");
-  if (hp->step < 1) return fail(GPT_EINVAL, "step must be >= 1");
-  int rc = run_optim(*m, (char*)state, grads, *hp, grad_norm != nullptr);
-  if (rc) return rc;
-  if (grad_norm) {
-    float v = 0.f;
-    HIP_TRY(hipMemcpyAsync(&v, (char*)state + m->opt.hdr, 4, hipMemcpyDeviceToHost, m->st));
-    HIP_TRY(hipStreamSynchronize(m->st));
-    *grad_norm = v;
-  }
-  if (m->prof_on) {
-    HIP_TRY(hipStreamSynchronize(m->st));
-    prof_collect(*m);
-  }
-  return GPT_OK;
-}
 
 int gpt_debug_tensor(gpt_model* m, int which, int layer, void** ptr, int64_t* rows, int64_t* cols,
                      int* elem_bytes) {

@@ -186,9 +186,9 @@ def mfma_md(pmc: str, stats: str, command: str, note: str = "", top: int = 30) -
     return "\n".join(out) + "\n"
 
 
-# sources of the optimizer's and the decoder's own kernels, which the training
-# step does not run
-_NOT_STEP = {"optim.hip", "infer.hip"}
+# sources of the optimizer's and the decoder's own kernels and launch code,
+# which the training step does not run
+_NOT_STEP = {"optim.hip", "infer.hip", "optim_host.cpp", "infer_host.cpp"}
 
 
 def source_digest() -> str:
