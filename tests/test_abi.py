@@ -138,3 +138,39 @@ def test_fp8_workspace_holds_the_codes(M):
 def test_strerror(M):
     assert M.gpt_strerror(M.GPT_ETOKEN) == "token id out of range"
     assert M.gpt_strerror(12345) == "unknown error"
+
+
+@pytest.mark.parametrize("name", ["tiny", "d24"])
+def test_kv_cache_and_optimizer_state_sizes(M, name):
+    """The KV cache is K and V of every layer, bf16 [B, H, T, Dh]; the
+    optimizer state holds at least the fp32 masters (bf16 parameters), one
+    fp32 momentum per matrix entry and two AdamW moments per E / U entry."""
+    s = gi.preset(name)
+    cfg = M.make_config(s)
+    assert M.gpt_kv_cache_bytes(cfg) == 2 * s.depth * s.batch * s.n_head * s.seq_len * s.head_dim * 2
+    layout, total = M.gpt_param_layout(cfg)
+    n_mat = sum(r * c for n, _, r, c in layout if n not in ("E", "U"))
+    n_emb = sum(r * c for n, _, r, c in layout if n in ("E", "U"))
+    need = 4 * (n_mat + 2 * n_emb) + (4 * total if s.precision != "fp32" else 0)
+    got = M.gpt_optim_state_bytes(cfg)
+    assert got >= need
+    # plus the Newton-Schulz buffers of the largest shape group (bf16: two
+    # copies of the group's matrices and two of its Gram matrices)
+    d, f = s.d_model, s.mlp_hidden
+    groups = [(4 * s.depth, d, d), (s.depth, f, d), (s.depth, d, f)]
+    ns = max(2 * 2 * n * r * c + 2 * 2 * n * min(r, c) ** 2 for n, r, c in groups)
+    assert got >= need + ns
+    assert got <= need + ns + 64 * 2 ** 20   # tables, partials and padding are small
+
+
+def test_optimizer_and_inference_argument_errors(M):
+    lib = M._lib
+    assert lib.gpt_optim_init(None, None, 0) == M.GPT_ENULL
+    assert lib.gpt_optim_step(None, None, None, None, None) == M.GPT_ENULL
+    assert lib.gpt_prefill(None, None, 1, None, None) == M.GPT_ENULL
+    assert lib.gpt_decode(None, None, 1, None, None) == M.GPT_ENULL
+    losses = (ctypes.c_float * 1)()
+    assert lib.gpt_step_micro(None, None, None, 1, None, 1.0, 0, losses) == M.GPT_ENULL
+    b = ctypes.c_size_t()
+    assert lib.gpt_kv_cache_bytes(None, ctypes.byref(b)) == M.GPT_ENULL
+    assert lib.gpt_optim_state_bytes(M.make_config(gi.preset("tiny")), None) == M.GPT_ENULL
