@@ -161,3 +161,26 @@ def test_graph_replays_match_eager_steps():
         t.cuda.synchronize()
         del junk
     sess.close()
+
+
+def test_fp8_model_serves_with_its_bf16_weights():
+    """An FP8-configured model prefills and decodes with bf16 products on its
+    bf16 weights: the same logits, bit for bit, as the bf16-configured model
+    with the same weights."""
+    import decoder_only_transformer_fwd_amd as G
+    s8 = SMALL["fp8_mid"]
+    sb = s8.replace(precision="bf16")
+    W8 = gi.make_weights(s8)
+    X, _ = gi.make_tokens(s8)
+    log("fp8 model inference vs bf16 model: fp8_mid")
+    out = []
+    for s in (s8, sb):
+        sess = G.Session(s, W8)
+        sess.infer_init()
+        zs = [sess.prefill(X[:, :100]).clone()]
+        for p in range(100, 104):
+            zs.append(sess.decode(X[:, p], p).clone())
+        out.append(zs)
+        sess.close()
+    for a, b in zip(*out):
+        assert bool((a == b).all())
