@@ -483,6 +483,8 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   auto KLD = [&](const char* k, const char* extra = "") {
     return std::string(k) + "<" + tname + ", " + std::to_string(Dh) + extra + ">";
   };
+  // kernels with a separate bf16, head-128 form
+  auto KLV = [&](const char* k, const char* k128) { return dt == DT_BF16 && Dh == 128 ? std::string(k128) : KLD(k); };
   // fp8 linear layers: per-tensor scale slots (12 per layer), transient codes
   enum { SL_N1, SL_O, SL_N2, SL_G, SL_WQKV, SL_WO, SL_W1, SL_W2, SL_DH2, SL_DU, SL_DH1, SL_DQKV };
   const bool f8 = s.fp8;
@@ -555,7 +557,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                 3 * d);
     }
     if (rc) return rc;
-    prof_begin(m, "rope_qknorm_fwd", (double)BT * d * 8.0 * es_d + BT * 2.0 * H * 4.0, 1, KLD("rope_qknorm_fwd_kernel"));
+    prof_begin(m, "rope_qknorm_fwd", (double)BT * d * 8.0 * es_d + BT * 2.0 * H * 4.0, 1, KLV("rope_qknorm_fwd_kernel", "rope_qknorm_fwd128_kernel"));
     rope_qknorm_fwd(dt, m.ws + Ly.qkv, at<float>(m, Ly.rqk), m.ws + Ly.qT, m.ws + Ly.kT, m.ws + Ly.vT, cosb, sinb,
                     s.B, s.T, s.Tp, H, Dh, s.eps, st);
     AttnArgs aa{};
@@ -686,7 +688,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
       if ((rc = wgrad("wgrad_o", d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d)))
         return rc;
     }
-    prof_begin(m, "attn_bwd_pre", (double)BT * d * 3.0 * es_d + (double)s.B * H * s.Tp * 4.0, 1, KLD("attn_bwd_pre_kernel"));
+    prof_begin(m, "attn_bwd_pre", (double)BT * d * 3.0 * es_d + (double)s.B * H * s.Tp * 4.0, 1, KLV("attn_bwd_pre_kernel", "attn_bwd_pre128_kernel"));
     attn_bwd_pre(dt, m.ws + m.dO, m.ws + Ly.o, at<float>(m, m.Dv), m.ws + m.dOT, s.B, s.T, s.Tp, H, Dh, st);
     prof_end(m);
     AttnArgs aa{};
@@ -710,7 +712,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                KLD("attn_bwd_dq_kernel"));
     if (attn_bwd(dt, Dh, aa, 2, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
     prof_end(m);
-    prof_begin(m, "rope_qknorm_bwd", (double)BT * d * 6.0 * es_d + BT * 2.0 * H * 4.0, 1, KLD("rope_qknorm_bwd_kernel"));
+    prof_begin(m, "rope_qknorm_bwd", (double)BT * d * 6.0 * es_d + BT * 2.0 * H * 4.0, 1, KLV("rope_qknorm_bwd_kernel", "rope_qknorm_bwd128_kernel"));
     rope_qknorm_bwd(dt, m.ws + m.dqkv, m.ws + Ly.qkv, at<float>(m, Ly.rqk), cosb, sinb, s.B, s.T, H, Dh, st,
                     amx(l, SL_DQKV));
     prof_end(m);

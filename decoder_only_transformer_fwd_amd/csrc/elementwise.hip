@@ -261,60 +261,64 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qk
   }
 }
 
-// The same for bf16 heads of 128: grid (ceil(T/64), H, B), 256 threads.
-// Thread (p, c) = (tid / 8, tid % 8) owns tokens 2p and 2p+1 of the tile and
-// the 16-byte chunks c and c+8 of each head vector (elements 8c.. and
-// 64+8c.., the rotation pairs).  The head's sum of squares is a reduction over
-// the 8 lanes sharing p.  The transposed copies go through LDS as 4-byte words
+// The same for bf16 heads of 128: grid (ceil(T/128), H, B), 512 threads.
+// Thread (p, c) = (tid / 8, tid % 8) owns tokens 2p and 2p+1 of the 128-token
+// tile and the 16-byte chunks c and c+8 of each head vector (elements 8c..
+// and 64+8c.., the rotation pairs).  The head's sum of squares is a reduction
+// over the 8 lanes sharing p.  All twelve 16-byte loads of q, k and v (and
+// the rotation table) are issued before any arithmetic, so a thread has them
+// in flight together.  The transposed copies go through LDS as 4-byte words
 // holding one dimension of two consecutive tokens; the word stride per
-// dimension is odd (33), so both the writes and the row reads are free of
-// bank conflicts.
-__global__ __launch_bounds__(256) void rope_qknorm_fwd128_kernel(bf16* __restrict__ qkv, float* __restrict__ rstd_qk,
+// dimension is odd (65), so the word writes are free of bank conflicts.  Each
+// dimension then leaves as one 256-byte run of the transposed row (chunks at
+// or past Tp, a multiple of 64, are not stored).
+__global__ __launch_bounds__(512) void rope_qknorm_fwd128_kernel(bf16* __restrict__ qkv, float* __restrict__ rstd_qk,
                                                                  bf16* __restrict__ qT, bf16* __restrict__ kT,
                                                                  bf16* __restrict__ vT, const float* __restrict__ cosb,
                                                                  const float* __restrict__ sinb, int Tn, int Tp,
                                                                  int H, float eps) {
-  constexpr int DH = 128, HALF = 64, S = 33;
+  constexpr int DH = 128, HALF = 64, TT = 128, S = TT / 2 + 1;
   __shared__ uint32_t tile[DH * S];
-  const int t0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const int t0 = blockIdx.x * TT, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, p = tid >> 3, c = tid & 7;
   const int d = H * DH;
   const long row3 = 3L * d;
+  bf16x8 raw[3][2][2];
+  floatx4 cs[2][2], sn[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = t0 + 2 * p + u;
+    const bool ok = t < Tn;
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+      const bf16* px = qkv + ((long)b * Tn + t) * row3 + part * d + h * DH;
+      raw[part][u][0] = ok ? *(const bf16x8*)(px + 8 * c) : bf16x8{};
+      raw[part][u][1] = ok ? *(const bf16x8*)(px + HALF + 8 * c) : bf16x8{};
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      cs[u][q] = ok ? *(const floatx4*)(cosb + (long)t * HALF + 8 * c + 4 * q) : floatx4{};
+      sn[u][q] = ok ? *(const floatx4*)(sinb + (long)t * HALF + 8 * c + 4 * q) : floatx4{};
+    }
+  }
+#pragma unroll
   for (int part = 0; part < 3; ++part) {
-    const int col = part * d + h * DH;
     float x[2][16];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int t = t0 + 2 * p + u;
-      bf16* px = qkv + ((long)b * Tn + t) * row3 + col;
-      bf16x8 lo, hi;
-      if (t < Tn) {
-        lo = *(const bf16x8*)(px + 8 * c);
-        hi = *(const bf16x8*)(px + HALF + 8 * c);
-      } else {
-        lo = hi = bf16x8{};
-      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        x[u][e] = (float)lo[e];
-        x[u][8 + e] = (float)hi[e];
+        x[u][e] = (float)raw[part][u][0][e];
+        x[u][8 + e] = (float)raw[part][u][1][e];
       }
       if (part < 2) {
-        float cs[8], sn[8];
-        if (t < Tn) {
-          *(floatx4*)&cs[0] = *(const floatx4*)(cosb + (long)t * HALF + 8 * c);
-          *(floatx4*)&cs[4] = *(const floatx4*)(cosb + (long)t * HALF + 8 * c + 4);
-          *(floatx4*)&sn[0] = *(const floatx4*)(sinb + (long)t * HALF + 8 * c);
-          *(floatx4*)&sn[4] = *(const floatx4*)(sinb + (long)t * HALF + 8 * c + 4);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) cs[e] = sn[e] = 0.f;
-        }
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float r1 = x[u][e] * cs[e] - x[u][8 + e] * sn[e];
-          const float r2 = x[u][e] * sn[e] + x[u][8 + e] * cs[e];
+          const float ce = cs[u][e >> 2][e & 3], se = sn[u][e >> 2][e & 3];
+          const float r1 = x[u][e] * ce - x[u][8 + e] * se;
+          const float r2 = x[u][e] * se + x[u][8 + e] * ce;
           x[u][e] = r1;
           x[u][8 + e] = r2;
           ss += r1 * r1 + r2 * r2;
@@ -324,6 +328,7 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd128_kernel(bf16* __restric
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[u][e] *= r;
         if (t < Tn) {
+          bf16* px = qkv + ((long)b * Tn + t) * row3 + part * d + h * DH;
           bf16x8 ylo, yhi;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -344,14 +349,69 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd128_kernel(bf16* __restric
       tile[dim * S + p] = w;
     }
     __syncthreads();
+    // 16-byte stores: thread (dim, q) writes tokens 8q .. 8q+7 of one dimension
     bf16* dst = (part == 0 ? qT : (part == 1 ? kT : vT)) + ((long)b * H + h) * DH * Tp + t0;
 #pragma unroll
-    for (int k = 0; k < DH / 8; ++k) {
-      const int dim = (tid >> 5) + 8 * k, wd = tid & 31;
-      *(uint32_t*)(dst + (long)dim * Tp + 2 * wd) = tile[dim * S + wd];
+    for (int k = 0; k < DH * (TT / 8) / 512; ++k) {
+      const int idx = tid + 512 * k, dim = idx / (TT / 8), q = idx % (TT / 8);
+      const uint32_t* w = tile + dim * S + 4 * q;
+      if (t0 + 8 * q < Tp) *(u32x4*)(dst + (long)dim * Tp + 8 * q) = u32x4{w[0], w[1], w[2], w[3]};
     }
     __syncthreads();
   }
+}
+
+// Backward of the rotation + QK norm for bf16 heads of 128, in place on the q
+// and k columns of dqkv.  A group of 8 lanes takes one head vector (q or k of
+// one head of one token, numbered row * 2H + v, which is also its rstd index);
+// lane c holds elements 8c.. and 64+8c.. (the rotation pairs) of the gradient
+// and of the normalised output, each as one 16-byte load.
+__global__ __launch_bounds__(256) void rope_qknorm_bwd128_kernel(bf16* __restrict__ dqkv, const bf16* __restrict__ qkv,
+                                                                 const float* __restrict__ rstd_qk,
+                                                                 const float* __restrict__ cosb,
+                                                                 const float* __restrict__ sinb, long nvec, int Tn,
+                                                                 int H, unsigned* __restrict__ amax) {
+  constexpr int DH = 128, HALF = 64;
+  __shared__ float red[4];
+  const long vec = (long)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int c = threadIdx.x & 7;
+  const bool ok = vec < nvec;
+  const long row = ok ? vec / (2 * H) : 0;
+  const int v = (int)(vec - row * 2 * H);
+  const int t = (int)(row % Tn);
+  const long off = row * 3L * H * DH + (long)v * DH;   // q heads at h*DH, k heads at d + h*DH
+  bf16x8 g[2], y[2];
+  floatx4 cs[2], sn[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    g[hf] = ok ? *(const bf16x8*)(dqkv + off + hf * HALF + 8 * c) : bf16x8{};
+    y[hf] = ok ? *(const bf16x8*)(qkv + off + hf * HALF + 8 * c) : bf16x8{};
+    cs[hf] = ok ? *(const floatx4*)(cosb + (long)t * HALF + 8 * c + 4 * hf) : floatx4{};
+    sn[hf] = ok ? *(const floatx4*)(sinb + (long)t * HALF + 8 * c + 4 * hf) : floatx4{};
+  }
+  const float r = ok ? rstd_qk[vec] : 0.f;
+  float dot = 0.f;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = __builtin_fmaf((float)g[hf][e], (float)y[hf][e], dot);
+  dot = group_sum<8>(dot) / (float)DH;
+  bf16x8 o[2];
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float ce = cs[e >> 2][e & 3], se = sn[e >> 2][e & 3];
+    const float d1 = r * ((float)g[0][e] - (float)y[0][e] * dot);
+    const float d2 = r * ((float)g[1][e] - (float)y[1][e] * dot);
+    o[0][e] = (bf16)(d1 * ce + d2 * se);
+    o[1][e] = (bf16)(-d1 * se + d2 * ce);
+    m = fmaxf(m, fmaxf(fabsf((float)o[0][e]), fabsf((float)o[1][e])));
+  }
+  if (ok) {
+    *(bf16x8*)(dqkv + off + 8 * c) = o[0];
+    *(bf16x8*)(dqkv + off + HALF + 8 * c) = o[1];
+  }
+  if (amax) block_amax<4>(amax, m, red);
 }
 
 // dq' = r * (g - y * mean(g*y)), then the inverse rotation; in place on the
@@ -428,6 +488,62 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const T* __restrict__
     if (t0 + cc * EPC < Tp)
       *(u32x4*)(dOT + (((long)b * H + h) * DH + r) * Tp + t0 + cc * EPC) =
           *(const u32x4*)(tile + r * LDW + cc * EPC);
+  }
+}
+
+// The same for bf16 heads of 128: grid (ceil(T/128), H, B), 512 threads.
+// Thread (p, j) = (tid / 16, tid % 16) owns the 16-byte chunk j (dimensions
+// 8j .. 8j+7) of tokens 2p, 2p+1 and 64+2p, 65+2p of the 128-token tile; all
+// eight 16-byte loads go out together.  D is a sum over the 16 lanes sharing
+// a token.  dO^T goes through LDS as 4-byte words holding one dimension of two
+// consecutive tokens (odd word stride 65), then out in 16-byte stores, one
+// 256-byte run per dimension (chunks at or past Tp are not stored).
+__global__ __launch_bounds__(512) void attn_bwd_pre128_kernel(const bf16* __restrict__ dO, const bf16* __restrict__ O,
+                                                              float* __restrict__ Dv, bf16* __restrict__ dOT, int Tn,
+                                                              int Tp, int H) {
+  constexpr int DH = 128, TT = 128, S = TT / 2 + 1;
+  __shared__ uint32_t tile[DH * S];
+  const int t0 = blockIdx.x * TT, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, p = tid >> 4, j = tid & 15;
+  const int d = H * DH;
+  bf16x8 g[2][2], o[2][2];   // [half of the tile][token of the pair]
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = t0 + 64 * hf + 2 * p + u;
+      const long off = ((long)b * Tn + t) * d + h * DH + 8 * j;
+      g[hf][u] = t < Tn ? *(const bf16x8*)(dO + off) : bf16x8{};
+      o[hf][u] = t < Tn ? *(const bf16x8*)(O + off) : bf16x8{};
+    }
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)g[hf][u][e], (float)o[hf][u][e], s);
+      s = group_sum<16>(s);
+      const int t = t0 + 64 * hf + 2 * p + u;
+      if (j == 0 && t < Tp) Dv[((long)b * H + h) * Tp + t] = s;   // zero past Tn: the loads were zero
+    }
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // (a vector element is copied out before the bit cast: taking the cast
+      // of the element expression itself read element 0)
+      const bf16 lo = g[hf][0][e], hi = g[hf][1][e];
+      tile[(8 * j + e) * S + 32 * hf + p] =
+          (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+  __syncthreads();
+  bf16* dst = dOT + ((long)b * H + h) * DH * Tp + t0;
+#pragma unroll
+  for (int k = 0; k < DH * (TT / 8) / 512; ++k) {
+    const int idx = tid + 512 * k, dim = idx / (TT / 8), q = idx % (TT / 8);
+    const uint32_t* w = tile + dim * S + 4 * q;
+    if (t0 + 8 * q < Tp) *(u32x4*)(dst + (long)dim * Tp + 8 * q) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -633,7 +749,7 @@ static void rope_fwd_t(void* qkv, float* rq, void* qT, void* kT, void* vT, const
                        int T_, int Tp, int H, float eps, hipStream_t st) {
   dim3 g((T_ + 63) / 64, H, B);
   if constexpr (sizeof(T) == 2 && DH == 128) {
-    hipLaunchKernelGGL(rope_qknorm_fwd128_kernel, g, dim3(256), 0, st, (bf16*)qkv, rq, (bf16*)qT, (bf16*)kT,
+    hipLaunchKernelGGL(rope_qknorm_fwd128_kernel, dim3((T_ + 127) / 128, H, B), dim3(512), 0, st, (bf16*)qkv, rq, (bf16*)qT, (bf16*)kT,
                        (bf16*)vT, c, s, T_, Tp, H, eps);
     return;
   }
@@ -654,6 +770,12 @@ template <typename T, int DH>
 static void rope_bwd_t(void* dqkv, const void* qkv, const float* rq, const float* c, const float* s, int B, int T_,
                        int H, hipStream_t st, unsigned* amax) {
   const int rows = B * T_;
+  if constexpr (sizeof(T) == 2 && DH == 128) {
+    const long nvec = (long)rows * 2 * H;
+    hipLaunchKernelGGL(rope_qknorm_bwd128_kernel, dim3((unsigned)((nvec + 31) / 32)), dim3(256), 0, st, (bf16*)dqkv,
+                       (const bf16*)qkv, rq, c, s, nvec, T_, H, amax);
+    return;
+  }
   hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, DH>), dim3((rows + 3) / 4), dim3(256), 0, st, (T*)dqkv,
                      (const T*)qkv, rq, c, s, rows, T_, H, amax);
 }
@@ -670,6 +792,11 @@ void rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const float* rq, co
 template <typename T, int DH>
 static void pre_t(const void* dO, const void* O, float* Dv, void* dOT, int B, int T_, int Tp, int H, hipStream_t st) {
   dim3 g((T_ + 63) / 64, H, B);
+  if constexpr (sizeof(T) == 2 && DH == 128) {
+    hipLaunchKernelGGL(attn_bwd_pre128_kernel, dim3((T_ + 127) / 128, H, B), dim3(512), 0, st, (const bf16*)dO, (const bf16*)O, Dv, (bf16*)dOT,
+                       T_, Tp, H);
+    return;
+  }
   hipLaunchKernelGGL((attn_bwd_pre_kernel<T, DH>), g, dim3(256), 0, st, (const T*)dO, (const T*)O, Dv, (T*)dOT, T_,
                      Tp, H);
 }
