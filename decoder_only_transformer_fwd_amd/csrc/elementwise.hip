@@ -699,6 +699,7 @@ static void rmsnorm_fwd_reg(const float* x, T* y, float* rstd, int rows, int d, 
   switch (norm_chunks(d)) {
     case 1: hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<T, 1>), g, dim3(256), 0, st, x, y, rstd, rows, d, eps, amax); break;
     case 2: hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<T, 2>), g, dim3(256), 0, st, x, y, rstd, rows, d, eps, amax); break;
+    case 3: hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<T, 3>), g, dim3(256), 0, st, x, y, rstd, rows, d, eps, amax); break;
     default: hipLaunchKernelGGL((rmsnorm_fwd_reg_kernel<T, 4>), g, dim3(256), 0, st, x, y, rstd, rows, d, eps, amax);
   }
 }
@@ -710,6 +711,7 @@ static void rmsnorm_bwd_reg(const float* dy, const T* y, const float* rstd, floa
   switch (norm_chunks(d)) {
     case 1: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 1>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax); break;
     case 2: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 2>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax); break;
+    case 3: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 3>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax); break;
     default: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 4>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax);
   }
 }

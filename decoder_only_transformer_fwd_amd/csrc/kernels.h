@@ -102,7 +102,7 @@ void embed_fwd(int dtype, const int32_t* tokens, const int32_t* targets, const v
 // the row does not fit, the looping kernels run instead).
 inline int norm_chunks(int d) {
   if (d % 8) return 0;
-  return d <= 512 ? 1 : d <= 1024 ? 2 : d <= 2048 ? 4 : 0;
+  return d <= 512 ? 1 : d <= 1024 ? 2 : d <= 1536 ? 3 : d <= 2048 ? 4 : 0;
 }
 void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps,
                  hipStream_t st, unsigned* amax = nullptr);
