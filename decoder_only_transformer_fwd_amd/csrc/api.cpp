@@ -182,7 +182,7 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
 // 1.5 rounds run as 2).  The first n1 tile columns form whole rounds and run
 // as usual; the remaining columns are split along K into `splits` parts that
 // together fill one round, and their fp32 partials are summed (in split
-// order) into C.  Only plain fp32 stores and fp32 accumulation qualify.
+// order) into C.  Plain stores (fp32 or bf16) and fp32 accumulation qualify.
 struct TailPlan {
   int n1;       // tile columns of the whole-round part (0: no tail split)
   int splits;
@@ -190,7 +190,7 @@ struct TailPlan {
 TailPlan plan_tail(int dtype, int layout, int epi, int M, int N, int K) {
   TailPlan t{0, 1};
   if (dtype != DT_BF16 || layout == LAYOUT_MN || K < 4096) return t;
-  if (epi != EPI_STORE_F32 && epi != EPI_ACCUM_F32) return t;
+  if (epi != EPI_STORE_F32 && epi != EPI_ACCUM_F32 && epi != EPI_STORE) return t;
   if (plan_gemm(dtype, layout, M, N, K).tile != TILE_256x256_PP4) return t;
   const long tm = (M + 255) / 256, tn = (N + 255) / 256;
   if ((tm * tn) % 256 == 0) return t;
@@ -436,9 +436,11 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
     if (gemm_launch(t, dty, layout, EPI_PARTIAL, g.tile, sp, m.st))
       return fail(GPT_EINVAL, "gemm variant not instantiated (partial)");
     prof_end(m);
-    prof_begin(m, "splitk_reduce", (sp + 1.0 + (epi == EPI_ACCUM_F32)) * M * (double)N2 * 4.0, 1,
+    const bool c16 = epi == EPI_STORE;   // bf16 C
+    prof_begin(m, "splitk_reduce", (sp + (c16 ? 0.5 : 1.0 + (epi == EPI_ACCUM_F32))) * M * (double)N2 * 4.0, 1,
                "splitk_reduce_strided_kernel");
-    splitk_reduce_strided(t.part, sp, M, N2, (float*)C + N1, ldc, epi == EPI_ACCUM_F32, m.st);
+    splitk_reduce_strided(t.part, sp, M, N2, (char*)C + (size_t)N1 * (c16 ? 2 : 4), ldc, epi == EPI_ACCUM_F32, c16,
+                          m.st);
     prof_end(m);
     return GPT_OK;
   }
@@ -631,14 +633,25 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     ex.beta = grad_scale / (float)BT;
     if ((rc = gemm(m, "gemm_lm_head_xent_bwd", LAYOUT_KK, EPI_XENT_BWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, m.ws + m.dz, V, ex))) return rc;
   }
-  float* dm = at<float>(m, m.dm);
+  // The input gradients of the products that feed a norm backward (lm_head,
+  // W1, Wqkv) are stored bf16 in the bf16 configuration, as the other
+  // activation gradients are; the residual gradient dh stays fp32.
+  void* dm = m.ws + m.dm;
+  const bool dn_act = dt == DT_BF16 && !f8 && norm_chunks(d) != 0;
+  const int epi_dn = dn_act ? EPI_STORE : EPI_STORE_F32;
+  const double dn_b = dn_act ? 2.0 : 4.0;   // bytes per dy element read by the norm backward
+  auto norm_bwd = [&](const void* y, const float* rstd, int accumulate, unsigned* amax) {
+    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (dn_b + 4.0 + 4.0 * accumulate + 2.0 * es_d), 1,
+               norm_label("rmsnorm_bwd"));
+    const int r = rmsnorm_bwd(dt, dm, dn_act, y, rstd, at<float>(m, m.dh), m.ws + m.dhA, BT, d, accumulate, st, amax);
+    prof_end(m);
+    return r ? fail(GPT_EINVAL, "rmsnorm_bwd variant not built") : GPT_OK;
+  };
   float* dh = at<float>(m, m.dh);
   void* dhA = m.ws + m.dhA;
-  if ((rc = gemm(m, "dgrad_lm_head", LAYOUT_KN, EPI_STORE_F32, BT, d, V, m.ws + m.dz, V, wp(P.U), d, dm, d))) return rc;
+  if ((rc = gemm(m, "dgrad_lm_head", LAYOUT_KN, epi_dn, BT, d, V, m.ws + m.dz, V, wp(P.U), d, dm, d))) return rc;
   if ((rc = wgrad("wgrad_lm_head", V, d, BT, m.ws + m.dz, V, m.ws + m.nL, d, grads + P.U, d))) return rc;
-  prof_begin(m, "rmsnorm_bwd", (double)BT * d * (8.0 + 2.0 * es_d), 1, norm_label("rmsnorm_bwd"));
-  rmsnorm_bwd(dt, dm, m.ws + m.nL, at<float>(m, m.rstdL), dh, dhA, BT, d, 0, st, amx(s.L - 1, SL_DH2));
-  prof_end(m);
+  if ((rc = norm_bwd(m.ws + m.nL, at<float>(m, m.rstdL), 0, amx(s.L - 1, SL_DH2)))) return rc;
   for (int l = s.L - 1; l >= 0; --l) {
     auto& Ly = m.lay[l];
     GemmArgs ex{};
@@ -666,14 +679,12 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
         return rc;
       if ((rc = wgrad("wgrad_w2", d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F)))
         return rc;
-      if ((rc = gemm(m, "dgrad_w1", LAYOUT_KN, EPI_STORE_F32, BT, d, F, m.ws + m.du, F, wp(P.W1[l]), d, dm, d)))
+      if ((rc = gemm(m, "dgrad_w1", LAYOUT_KN, epi_dn, BT, d, F, m.ws + m.du, F, wp(P.W1[l]), d, dm, d)))
         return rc;
       if ((rc = wgrad("wgrad_w1", F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d, grads + P.W1[l], d)))
         return rc;
     }
-    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, norm_label("rmsnorm_bwd"));
-    rmsnorm_bwd(dt, dm, m.ws + Ly.n2, at<float>(m, Ly.rstd2), dh, dhA, BT, d, 1, st, amx(l, SL_DH1));
-    prof_end(m);
+    if ((rc = norm_bwd(m.ws + Ly.n2, at<float>(m, Ly.rstd2), 1, amx(l, SL_DH1)))) return rc;
     if (f8) {
       quant("fp8_quant_grad", FP8_E5M2, dhA, BT, d, slot(l, SL_DH1), q8row, q8T);
       if ((rc = gemm8("dgrad_o", DT_FP8_A5B4, EPI_STORE, BT, d, d, q8row, m.ws + Ly.wqT[1], m.ws + m.dO, d,
@@ -725,15 +736,13 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                        slot(l, SL_N1))))
         return rc;
     } else {
-      if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, EPI_STORE_F32, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d,
-                     dm, d)))
+      if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, epi_dn, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d, dm,
+                     d)))
         return rc;
       if ((rc = wgrad("wgrad_qkv", 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d, grads + P.Wqkv[l], d)))
         return rc;
     }
-    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (12.0 + 2.0 * es_d), 1, norm_label("rmsnorm_bwd"));
-    rmsnorm_bwd(dt, dm, m.ws + Ly.n1, at<float>(m, Ly.rstd1), dh, dhA, BT, d, 1, st, amx(l - 1, SL_DH2));
-    prof_end(m);
+    if ((rc = norm_bwd(m.ws + Ly.n1, at<float>(m, Ly.rstd1), 1, amx(l - 1, SL_DH2)))) return rc;
   }
   prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * (accumulate ? 8.0 : 4.0) + BT * 8.0, 1,
              "sort_keys_kernel + embed_bwd_runs_kernel");

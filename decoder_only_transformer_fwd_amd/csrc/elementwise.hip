@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_reg_kernel(const float* __res
 }
 
 template <typename T, int NCH>
-__global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const float* __restrict__ dy, const T* __restrict__ y,
+__global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const void* __restrict__ dy, int dy_act,
+                                                              const T* __restrict__ y,
                                                               const float* __restrict__ rstd, float* __restrict__ dx,
                                                               T* __restrict__ dxa, int rows, int d, int accumulate,
                                                               unsigned* __restrict__ amax) {
@@ -134,7 +135,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const float* __res
     for (int k = 0; k < NCH; ++k) {
       const int c = (k * 64 + lane) * 8;
       if (c < d) {
-        load8(dy + base + c, a[k][0], a[k][1]);
+        if (dy_act) load8((const T*)dy + base + c, a[k][0], a[k][1]);   // dy in the activation type
+        else load8((const float*)dy + base + c, a[k][0], a[k][1]);
         load8(y + base + c, b[k][0], b[k][1]);
         if (accumulate) load8(dx + base + c, acc[k][0], acc[k][1]);
 #pragma unroll
@@ -705,15 +707,16 @@ static void rmsnorm_fwd_reg(const float* x, T* y, float* rstd, int rows, int d, 
 }
 
 template <typename T>
-static void rmsnorm_bwd_reg(const float* dy, const T* y, const float* rstd, float* dx, T* dxa, int rows, int d,
-                            int accumulate, hipStream_t st, unsigned* amax) {
+static void rmsnorm_bwd_reg(const void* dy, int dy_act, const T* y, const float* rstd, float* dx, T* dxa, int rows,
+                            int d, int accumulate, hipStream_t st, unsigned* amax) {
   dim3 g((rows + 3) / 4);
-  switch (norm_chunks(d)) {
-    case 1: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 1>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax); break;
-    case 2: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 2>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax); break;
-    case 3: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 3>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax); break;
-    default: hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, 4>), g, dim3(256), 0, st, dy, y, rstd, dx, dxa, rows, d, accumulate, amax);
-  }
+#define RBR(N)                                                                                                 \
+  case N:                                                                                                      \
+    hipLaunchKernelGGL((rmsnorm_bwd_reg_kernel<T, N>), g, dim3(256), 0, st, dy, dy_act, y, rstd, dx, dxa, rows, d, \
+                       accumulate, amax);                                                                      \
+    break;
+  switch (norm_chunks(d)) { RBR(1) RBR(2) RBR(3) default: RBR(4) }
+#undef RBR
 }
 
 void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps, hipStream_t st,
@@ -730,20 +733,22 @@ void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int 
     hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, g, dim3(256), 0, st, x, (float*)y, rstd, rows, d, eps, amax);
 }
 
-void rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* rstd, float* dx, void* dxa, int rows,
-                 int d, int accumulate, hipStream_t st, unsigned* amax) {
+int rmsnorm_bwd(int dtype, const void* dy, int dy_act, const void* y, const float* rstd, float* dx, void* dxa,
+                int rows, int d, int accumulate, hipStream_t st, unsigned* amax) {
   dim3 g((rows + 3) / 4);
   if (norm_chunks(d)) {
-    if (dtype == DT_BF16) rmsnorm_bwd_reg(dy, (const bf16*)y, rstd, dx, (bf16*)dxa, rows, d, accumulate, st, amax);
-    else rmsnorm_bwd_reg(dy, (const float*)y, rstd, dx, (float*)dxa, rows, d, accumulate, st, amax);
-    return;
+    if (dtype == DT_BF16) rmsnorm_bwd_reg(dy, dy_act, (const bf16*)y, rstd, dx, (bf16*)dxa, rows, d, accumulate, st, amax);
+    else rmsnorm_bwd_reg(dy, dy_act, (const float*)y, rstd, dx, (float*)dxa, rows, d, accumulate, st, amax);
+    return 0;
   }
+  if (dy_act && dtype != DT_F32) return -1;   // the row-loop form reads fp32 dy only
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, g, dim3(256), 0, st, dy, (const bf16*)y, rstd, dx, (bf16*)dxa,
-                       rows, d, accumulate, amax);
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, g, dim3(256), 0, st, (const float*)dy, (const bf16*)y, rstd, dx,
+                       (bf16*)dxa, rows, d, accumulate, amax);
   else
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, g, dim3(256), 0, st, dy, (const float*)y, rstd, dx,
+    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, g, dim3(256), 0, st, (const float*)dy, (const float*)y, rstd, dx,
                        (float*)dxa, rows, d, accumulate, amax);
+  return 0;
 }
 
 template <typename T, int DH>

@@ -615,16 +615,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // The same reduction into an M x N block of a matrix with row stride ldc.
+// out_bf16: C holds bf16 (no accumulation), else fp32.
 __global__ __launch_bounds__(256) void splitk_reduce_strided_kernel(const float* __restrict__ part, int splits, int M,
-                                                                    int N, float* __restrict__ out, long ldc,
-                                                                    int accumulate) {
+                                                                    int N, void* __restrict__ out, long ldc,
+                                                                    int accumulate, int out_bf16) {
   const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
   const long mn = (long)M * N;
   if (i >= mn) return;
   const long m = i / N, n = i % N;
-  float* o = out + m * ldc + n;
   floatx4 s = {0.f, 0.f, 0.f, 0.f};
   for (int z = 0; z < splits; ++z) s += *(const floatx4*)(part + (long)z * mn + i);
+  if (out_bf16) {
+    *(bf16x4*)((bf16*)out + m * ldc + n) = __builtin_convertvector(s, bf16x4);
+    return;
+  }
+  float* o = (float*)out + m * ldc + n;
   if (accumulate) s = *(const floatx4*)o + s;
   *(floatx4*)o = s;
 }
@@ -799,11 +804,11 @@ void splitk_reduce(const float* part, int splits, long mn, float* out, int accum
                      out, accumulate);
 }
 
-void splitk_reduce_strided(const float* part, int splits, int M, int N, float* out, long ldc, int accumulate,
-                           hipStream_t st) {
+void splitk_reduce_strided(const float* part, int splits, int M, int N, void* out, long ldc, int accumulate,
+                           int out_bf16, hipStream_t st) {
   const long n4 = ((long)M * N + 3) / 4;
   hipLaunchKernelGGL(splitk_reduce_strided_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, splits,
-                     M, N, out, ldc, accumulate);
+                     M, N, out, ldc, accumulate, out_bf16);
 }
 
 }  // namespace gk

@@ -89,9 +89,10 @@ int gemm_launch_batched(const GemmArgs& a, int layout, int epi, int tile, int ba
 void splitk_reduce(const float* part, int splits, long mn, float* out, int accumulate,
                    hipStream_t st);
 // out[m * ldc + n] (+)= sum over z of part[z][m][n] for an M x N block of a
-// wider fp32 matrix (N a multiple of 4, out and ldc 16-byte aligned).
-void splitk_reduce_strided(const float* part, int splits, int M, int N, float* out, long ldc, int accumulate,
-                           hipStream_t st);
+// wider fp32 matrix (N a multiple of 4, out and ldc 16-byte aligned), or, when
+// out_bf16, out = the sum rounded to a bf16 matrix (8-byte aligned).
+void splitk_reduce_strided(const float* part, int splits, int M, int N, void* out, long ldc, int accumulate,
+                           int out_bf16, hipStream_t st);
 
 // ---------------------------------------------------------------- elementwise
 // Also checks that every token and target id is in [0, vocab) (sets *flag).
@@ -107,8 +108,10 @@ inline int norm_chunks(int d) {
 void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int d, float eps,
                  hipStream_t st, unsigned* amax = nullptr);
 // dx (+)= r * (dy - y * mean(dy*y)); also writes dx in the activation type.
-void rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* rstd, float* dx,
-                 void* dx_act, int rows, int d, int accumulate, hipStream_t st, unsigned* amax = nullptr);
+// dy is fp32, or in the activation type when dy_act (register-chunk widths
+// only: norm_chunks(d) != 0); returns -1 for a combination not built.
+int rmsnorm_bwd(int dtype, const void* dy, int dy_act, const void* y, const float* rstd, float* dx,
+                void* dx_act, int rows, int d, int accumulate, hipStream_t st, unsigned* amax = nullptr);
 void rope_qknorm_fwd(int dtype, void* qkv, float* rstd_qk, void* qT, void* kT, void* vT,
                      const float* cosb, const float* sinb, int B, int T, int Tp, int H, int Dh,
                      float eps, hipStream_t st);
