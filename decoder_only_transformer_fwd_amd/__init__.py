@@ -21,7 +21,7 @@ GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 
 EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_step_micro",
             "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
-            "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_destroy",
+            "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_rope_table", "gpt_destroy",
             "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
             "gpt_profile_sites", "gpt_profile_get", "gpt_strerror", "gpt_last_error"]
 
@@ -86,6 +86,7 @@ def _load():
     lib.gpt_kv_cache_bytes.argtypes = [ctypes.POINTER(gpt_config), ctypes.POINTER(ctypes.c_size_t)]
     lib.gpt_prefill.argtypes = [P, P, I, P, P]
     lib.gpt_decode.argtypes = [P, P, I, P, P]
+    lib.gpt_rope_table.argtypes = [ctypes.POINTER(gpt_config), P, P]
     lib.gpt_destroy.argtypes = [P]
     lib.gpt_destroy.restype = None
     lib.gpt_debug_tensor.argtypes = [P, I, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I64),
@@ -104,7 +105,7 @@ def _load():
     lib.gpt_last_error.restype = ctypes.c_char_p
     for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_step_micro",
                  "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
-                 "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode",
+                 "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_rope_table",
                  "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
                  "gpt_profile_sites", "gpt_profile_get"):
         getattr(lib, name).restype = I
@@ -238,6 +239,15 @@ def gpt_step_micro(model: int, tokens: int, targets: int, n_micro: int, grads: i
     _check(_lib.gpt_step_micro(model, tokens, targets, n_micro, grads, float(grad_scale), int(bool(accumulate)),
                                losses), "gpt_step_micro")
     return list(losses)
+
+
+def gpt_rope_table(cfg: gpt_config) -> Tuple[np.ndarray, np.ndarray]:
+    """The library's RoPE table (host computation): cos, sin as fp32 [T, Dh/2]."""
+    half = cfg.head_dim // 2
+    c = np.zeros((cfg.seq_len, half), dtype=np.float32)
+    s = np.zeros((cfg.seq_len, half), dtype=np.float32)
+    _check(_lib.gpt_rope_table(ctypes.byref(cfg), c.ctypes.data, s.ctypes.data), "gpt_rope_table")
+    return c, s
 
 
 def gpt_destroy(model: int) -> None:

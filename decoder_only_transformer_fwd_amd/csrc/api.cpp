@@ -44,7 +44,10 @@ int check_config(const gpt_config* c, Shape& s) {
   if (s.d % 64 || s.F % 64) return fail(GPT_EINVAL, "d_model and mlp_hidden must be multiples of 64");
   if (s.V % 8 || s.V > 65536) return fail(GPT_EINVAL, "vocab must be a multiple of 8 and <= 65536");
   if ((long)s.B * s.T > 32768) return fail(GPT_EINVAL, "batch * seq_len must be <= 32768");
-  if (!(c->norm_eps >= 0.f) || !(c->rope_base > 0.f)) return fail(GPT_EINVAL, "bad norm_eps or rope_base");
+  // eps > 0: the norms divide by sqrt(mean(x^2) + eps), and the attention
+  // kernels' padded query/key positions are all-zero vectors
+  if (!(c->norm_eps > 0.f) || !std::isfinite(c->norm_eps) || !(c->rope_base > 0.f) || !std::isfinite(c->rope_base))
+    return fail(GPT_EINVAL, "norm_eps and rope_base must be positive and finite");
   s.BT = s.B * s.T;
   s.Tp = (s.T + 63) / 64 * 64;
   if (s.fp8 && s.BT % 64) return fail(GPT_EINVAL, "GPT_FP8 needs batch * seq_len to be a multiple of 64");
@@ -204,6 +207,20 @@ TailPlan plan_tail(int dtype, int layout, int epi, int M, int N, int K) {
     return t;
   }
   return t;
+}
+
+// RoPE table (nanochat User Guide, section 10, rotary embeddings): the pair
+// (x[i], x[i + Dh/2]) of position t rotates by t * theta_i with
+// theta_i = base^(-2i/Dh), i < Dh/2.  Evaluated in double, stored as fp32,
+// [T][Dh/2] each for cos and sin.
+void rope_table(const Shape& s, float* cosv, float* sinv) {
+  const int half = s.Dh / 2;
+  for (int t = 0; t < s.T; ++t)
+    for (int i = 0; i < half; ++i) {
+      const double th = std::pow((double)s.base, -2.0 * i / s.Dh);
+      cosv[(size_t)t * half + i] = (float)std::cos(t * th);
+      sinv[(size_t)t * half + i] = (float)std::sin(t * th);
+    }
 }
 
 }  // namespace gm
@@ -877,15 +894,9 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   m->st = (hipStream_t)cfg->stream;
   m->ws = (char*)cfg->workspace;
   m->W = (const char*)cfg->weights;
-  // RoPE table: t * base^(-2i/Dh) evaluated in double, stored as fp32.
   const int half = m->s.Dh / 2;
   std::vector<float> c((size_t)m->s.T * half), sn((size_t)m->s.T * half);
-  for (int t = 0; t < m->s.T; ++t)
-    for (int i = 0; i < half; ++i) {
-      const double th = std::pow((double)m->s.base, -2.0 * i / m->s.Dh);
-      c[(size_t)t * half + i] = (float)std::cos(t * th);
-      sn[(size_t)t * half + i] = (float)std::sin(t * th);
-    }
+  rope_table(m->s, c.data(), sn.data());
   hipError_t e1 = hipMemcpyAsync(m->ws + m->cosb, c.data(), c.size() * 4, hipMemcpyHostToDevice, m->st);
   hipError_t e2 = hipMemcpyAsync(m->ws + m->sinb, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, m->st);
   hipError_t e3 = hipStreamSynchronize(m->st);
@@ -895,6 +906,15 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
                               hipGetErrorString(e2) + " / " + hipGetErrorString(e3));
   }
   *out = m;
+  return GPT_OK;
+}
+
+int gpt_rope_table(const gpt_config* cfg, float* cos_out, float* sin_out) {
+  if (!cos_out || !sin_out) return fail(GPT_ENULL, "gpt_rope_table: NULL output");
+  Shape s;
+  const int rc = check_config(cfg, s);
+  if (rc) return rc;
+  rope_table(s, cos_out, sin_out);
   return GPT_OK;
 }
 

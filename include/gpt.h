@@ -60,7 +60,7 @@ typedef struct gpt_config {
   char window_pattern[8]; /* NUL-terminated, chars 'S'/'L', cycled over layers;
                              the last layer is always 'L' (full causal)       */
   float rope_base;      /* RoPE base (10000)                                  */
-  float norm_eps;       /* RMSNorm epsilon for every norm (1e-6)              */
+  float norm_eps;       /* RMSNorm epsilon for every norm (1e-6), > 0         */
   int32_t precision;    /* gpt_precision: storage/compute policy, see below   */
   const void* weights;  /* device, caller-owned parameter buffer: see layout  */
   void* workspace;      /* device, caller-owned, >= gpt_workspace_bytes()     */
@@ -241,6 +241,15 @@ int gpt_prefill(gpt_model* model, const int32_t* tokens, int n_tokens, void* kv_
  * pos and writes logits [batch, vocab] fp32 (device) for position pos + 1.
  * Waits for the stream.  GPT_ETOKEN for an id outside [0, vocab). */
 int gpt_decode(gpt_model* model, const int32_t* tokens, int pos, void* kv_cache, float* logits);
+
+/* The RoPE table the step uses, computed on the host (no GPU needed):
+ * cos_out[t][i] = cos(t * theta_i), sin_out[t][i] = sin(t * theta_i) with
+ * theta_i = rope_base^(-2i/head_dim), 0 <= t < seq_len, 0 <= i < head_dim/2
+ * (nanochat User Guide, section 10, rotary embeddings; the half-split pair
+ * convention is stated at the top of this header).  Evaluated in double and
+ * rounded to fp32.  cos_out, sin_out: host float[seq_len * head_dim / 2],
+ * caller-owned.  GPT_EINVAL for a bad config, GPT_ENULL for a NULL output. */
+int gpt_rope_table(const gpt_config* cfg, float* cos_out, float* sin_out);
 
 /* Release the handle (host memory only). */
 void gpt_destroy(gpt_model* model);

@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI: the library loads, exports every declared
 entry point, and validates configurations without touching a GPU."""
 import ctypes
+import math
 import os
 import re
 
@@ -84,6 +85,9 @@ BAD = [
     dict(depth=0),
     dict(precision="fp8", seq_len=100, batch=1),  # fp8 needs B*T % 64 == 0
     dict(precision="fp8", head_dim=32, d_model=64, n_head=2),  # fp8 attention is bf16: Dh 64/128
+    dict(norm_eps=0.0),                          # the norms need eps > 0
+    dict(norm_eps=-1e-6),
+    dict(rope_base=0.0),
 ]
 
 
@@ -174,3 +178,15 @@ def test_optimizer_and_inference_argument_errors(M):
     b = ctypes.c_size_t()
     assert lib.gpt_kv_cache_bytes(None, ctypes.byref(b)) == M.GPT_ENULL
     assert lib.gpt_optim_state_bytes(M.make_config(gi.preset("tiny")), None) == M.GPT_ENULL
+
+
+def test_library_rope_table_matches_pinned_schedule(M):
+    """The table the library uploads (computed on the host) against the
+    hard-coded rotary angles of the oracle's pin."""
+    from tests.test_oracle import ROPE_PINS
+    s = gi.preset("d24").replace(seq_len=1001)
+    c, sn = M.gpt_rope_table(M.make_config(s))
+    assert c.shape == (1001, 64)
+    for i, t, ang in ROPE_PINS:
+        assert abs(float(c[t, i]) - math.cos(ang)) < 2e-7, (i, t)
+        assert abs(float(sn[t, i]) - math.sin(ang)) < 2e-7, (i, t)

@@ -215,6 +215,30 @@ def test_rope_invariants():
     np.testing.assert_allclose(O.rope_bwd(y, cos, sin), x, rtol=0, atol=1e-14)
 
 
+# Hard-coded values of the rotary schedule theta_i = base^(-2i/Dh) (nanochat
+# User Guide, section 10, rotary embeddings; half-split pairs, reading c4):
+# at Dh = 128 and base 10000, pair i = 16 turns by t * 10000^(-1/4) = 0.1 t
+# rad, pair i = 32 by 10000^(-1/2) t = 0.01 t and pair i = 48 by 0.001 t.  A
+# schedule with the exponent -i/Dh (or any other) gives other angles.
+ROPE_PINS = [  # (pair i, position t, angle in radians)
+    (0, 100, 100.0), (16, 100, 10.0), (32, 100, 1.0), (48, 100, 0.1),
+    (16, 7, 0.7), (32, 1000, 10.0), (48, 1000, 1.0),
+]
+
+
+def test_rope_frequency_schedule_pinned():
+    cos, sin = O.rope_tables(1001, 128, 10000.0)
+    for i, t, ang in ROPE_PINS:
+        assert abs(cos[t, i] - math.cos(ang)) < 1e-12, (i, t)
+        assert abs(sin[t, i] - math.sin(ang)) < 1e-12, (i, t)
+    # the rotation pairs dimension i with dimension i + Dh/2
+    x = np.zeros((1, 101, 1, 128))
+    x[0, 100, 0, 32] = 1.0
+    y = O.rope(x, cos[:101], sin[:101])[0, 100, 0]
+    assert abs(y[32] - math.cos(1.0)) < 1e-12 and abs(y[96] - math.sin(1.0)) < 1e-12
+    assert np.count_nonzero(np.abs(y) > 1e-15) == 2
+
+
 def test_rmsnorm_commutes_with_rope_and_has_rms_one():
     rng = np.random.default_rng(2)
     T, H, Dh, eps = 6, 3, 8, 1e-6
