@@ -209,6 +209,61 @@ TailPlan plan_tail(int dtype, int layout, int epi, int M, int N, int K) {
   return t;
 }
 
+// Argument checks shared by gpt_gemm and gpt_gemm_noalloc (no device calls).
+int gemm_check(int dtype, int layout, int M, int N, int K, const void* A, const void* B, const float* C, int splits,
+               int tile, const char* who) {
+  const std::string w(who);
+  if (!A || !B || !C) return fail(GPT_ENULL, w + ": NULL operand");
+  if (dtype != DT_F32 && dtype != DT_BF16) return fail(GPT_EINVAL, w + ": dtype");
+  if (layout < 0 || layout > 2) return fail(GPT_EINVAL, w + ": layout");
+  if (M < 1 || N < 1 || K < 1 || M % 8 || N % 8 || K % 8) return fail(GPT_EINVAL, w + ": sizes");
+  if (splits < 1 || (splits > 1 && layout == LAYOUT_KK)) return fail(GPT_EINVAL, w + ": splits");
+  if (tile < 0) tile = plan_gemm(dtype, layout, M, N, K).tile;
+  if (dtype == DT_F32 && tile != TILE_128x128 && tile != TILE_64x64) return fail(GPT_EINVAL, w + ": tile");
+  if (dtype == DT_BF16 && (tile == TILE_64x64 || tile >= TILE_COUNT || (tile_needs_kc(tile) && layout != LAYOUT_KK)))
+    return fail(GPT_EINVAL, w + ": tile");
+  return GPT_OK;
+}
+
+// K per split after rounding to whole K steps, and the number of splits
+// that leaves (the partial buffer holds that many M x N blocks).
+int gemm_real_splits(int dtype, int K, int splits, int* k_split) {
+  const int bk = dtype == DT_F32 ? 32 : 64;
+  int ks = (K + splits - 1) / splits;
+  ks = (ks + bk - 1) / bk * bk;
+  if (k_split) *k_split = ks;
+  return (K + ks - 1) / ks;
+}
+
+// One product C = A B^T (layouts as in gpt_gemm); splits > 1 sums K splits
+// through `workspace` (>= real splits * M * N floats) in split order.
+// Arguments were checked by gemm_check.
+int gemm_entry(int dtype, int layout, int M, int N, int K, const void* A, const void* B, float* C, float* workspace,
+               int splits, int tile, void* stream, const char* who) {
+  const std::string w(who);
+  if (tile < 0) tile = plan_gemm(dtype, layout, M, N, K).tile;
+  GemmArgs a{};
+  a.A = A; a.B = B; a.M = M; a.N = N; a.K = K;
+  a.lda = layout == LAYOUT_MN ? M : K;
+  a.ldb = layout == LAYOUT_KK ? K : N;
+  a.C = C; a.ldc = N; a.alpha = 1.f;
+  hipStream_t st = (hipStream_t)stream;
+  if (splits > 1) {
+    int ks = 0;
+    splits = gemm_real_splits(dtype, K, splits, &ks);
+    a.k_split = ks;
+    a.part = workspace;
+    if (gemm_launch(a, dtype, layout, EPI_PARTIAL, tile, splits, st)) return fail(GPT_EINVAL, w + ": variant");
+    splitk_reduce(workspace, splits, (long)M * N, C, 0, st);
+  } else {
+    a.k_split = K;
+    if (gemm_launch(a, dtype, layout, EPI_STORE_F32, tile, 1, st)) return fail(GPT_EINVAL, w + ": variant");
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPT_EHIP, w + ": launch: " + hipGetErrorString(e));
+  return GPT_OK;
+}
+
 // RoPE table (nanochat User Guide, section 10, rotary embeddings): the pair
 // (x[i], x[i + Dh/2]) of position t rotates by t * theta_i with
 // theta_i = base^(-2i/Dh), i < Dh/2.  Evaluated in double, stored as fp32,
@@ -987,38 +1042,10 @@ int gpt_debug_tensor(gpt_model* m, int which, int layer, void** ptr, int64_t* ro
 
 int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const void* B, float* C, float* workspace,
              int splits, int tile, void* stream) {
-  if (!A || !B || !C) return fail(GPT_ENULL, "gpt_gemm: NULL operand");
-  if (dtype != DT_F32 && dtype != DT_BF16) return fail(GPT_EINVAL, "gpt_gemm: dtype");
-  if (layout < 0 || layout > 2) return fail(GPT_EINVAL, "gpt_gemm: layout");
-  if (M < 1 || N < 1 || K < 1 || M % 8 || N % 8 || K % 8) return fail(GPT_EINVAL, "gpt_gemm: sizes");
-  if (splits < 1 || (splits > 1 && (!workspace || layout == LAYOUT_KK)))
-    return fail(GPT_EINVAL, "gpt_gemm: splits");
-  if (tile < 0) tile = plan_gemm(dtype, layout, M, N, K).tile;
-  if (dtype == DT_F32 && tile != TILE_128x128 && tile != TILE_64x64) return fail(GPT_EINVAL, "gpt_gemm: tile");
-  if (dtype == DT_BF16 && (tile == TILE_64x64 || tile >= TILE_COUNT || (tile_needs_kc(tile) && layout != LAYOUT_KK)))
-    return fail(GPT_EINVAL, "gpt_gemm: tile");
-  GemmArgs a{};
-  a.A = A; a.B = B; a.M = M; a.N = N; a.K = K;
-  a.lda = layout == LAYOUT_MN ? M : K;
-  a.ldb = layout == LAYOUT_KK ? K : N;
-  a.C = C; a.ldc = N; a.alpha = 1.f;
-  hipStream_t st = (hipStream_t)stream;
-  const int bk = dtype == DT_F32 ? 32 : 64;
-  if (splits > 1) {
-    int ks = (K + splits - 1) / splits;
-    ks = (ks + bk - 1) / bk * bk;
-    splits = (K + ks - 1) / ks;
-    a.k_split = ks;
-    a.part = workspace;
-    if (gemm_launch(a, dtype, layout, EPI_PARTIAL, tile, splits, st)) return fail(GPT_EINVAL, "gpt_gemm: variant");
-    splitk_reduce(workspace, splits, (long)M * N, C, 0, st);
-  } else {
-    a.k_split = K;
-    if (gemm_launch(a, dtype, layout, EPI_STORE_F32, tile, 1, st)) return fail(GPT_EINVAL, "gpt_gemm: variant");
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(GPT_EHIP, std::string("launch: ") + hipGetErrorString(e));
-  return GPT_OK;
+  int rc = gemm_check(dtype, layout, M, N, K, A, B, C, splits, tile, "gpt_gemm");
+  if (rc) return rc;
+  if (splits > 1 && !workspace) return fail(GPT_EINVAL, "gpt_gemm: splits > 1 needs a workspace");
+  return gemm_entry(dtype, layout, M, N, K, A, B, C, workspace, splits, tile, stream, "gpt_gemm");
 }
 
 int gpt_fp8_quantize(int fmt, const void* x, int rows, int cols, uint32_t* amax, float* scale, void* q, void* qT,

@@ -45,6 +45,14 @@ struct Shape {
 
 int check_config(const gpt_config* c, Shape& s);
 
+// Single products for gpt_gemm / gpt_gemm_noalloc: argument checks (host
+// only), the split count after rounding K to whole steps, and the launch.
+int gemm_check(int dtype, int layout, int M, int N, int K, const void* A, const void* B, const float* C, int splits,
+               int tile, const char* who);
+int gemm_real_splits(int dtype, int K, int splits, int* k_split);
+int gemm_entry(int dtype, int layout, int M, int N, int K, const void* A, const void* B, float* C, float* workspace,
+               int splits, int tile, void* stream, const char* who);
+
 struct ParamOffsets {
   long E, U;
   std::vector<long> Wqkv, Wo, W1, W2;
