@@ -22,7 +22,7 @@ GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_step_micro",
             "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
             "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_rope_table", "gpt_destroy",
-            "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
+            "gpt_debug_tensor", "gpt_gemm", "gpt_gemm_noalloc", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
             "gpt_profile_sites", "gpt_profile_get", "gpt_strerror", "gpt_last_error"]
 
 
@@ -92,6 +92,7 @@ def _load():
     lib.gpt_debug_tensor.argtypes = [P, I, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I64),
                                      ctypes.POINTER(I)]
     lib.gpt_gemm.argtypes = [I, I, I, I, I, P, P, P, P, I, I, P]
+    lib.gpt_gemm_noalloc.argtypes = [I, I, I, I, I, P, P, P, I, I, P]
     lib.gpt_fp8_quantize.argtypes = [I, P, I, I, P, P, P, P, P]
     lib.gpt_gemm_fp8.argtypes = [I, I, I, I, P, P, P, P, P, P, I, P]
     D = ctypes.c_double
@@ -106,7 +107,7 @@ def _load():
     for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_step_micro",
                  "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
                  "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_rope_table",
-                 "gpt_debug_tensor", "gpt_gemm", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
+                 "gpt_debug_tensor", "gpt_gemm", "gpt_gemm_noalloc", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
                  "gpt_profile_sites", "gpt_profile_get"):
         getattr(lib, name).restype = I
     return lib
@@ -266,6 +267,15 @@ def gpt_gemm(dtype: int, layout: int, M: int, N: int, K: int, A: int, B: int, C:
              workspace: int = 0, splits: int = 1, tile: int = -1, stream: int = 0) -> None:
     _check(_lib.gpt_gemm(dtype, layout, M, N, K, A, B, C, workspace or None, splits, tile, stream or None),
            "gpt_gemm")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gpt_gemm_noalloc(dtype: int, layout: int, M: int, N: int, K: int, A: int, B: int, C: int,
+                     splits: int = 1, tile: int = -1, stream: int = 0) -> None:
+    """gpt_gemm with the split-K partials in the library's own scratch array."""
+    _check(_lib.gpt_gemm_noalloc(dtype, layout, M, N, K, A, B, C, splits, tile, stream or None), "gpt_gemm_noalloc")
 
 
 def gpt_fp8_quantize(fmt: int, x: int, rows: int, cols: int, amax: int, scale: int, q: int, qT: int = 0,

@@ -272,6 +272,25 @@ int gpt_debug_tensor(gpt_model* model, int which, int layer, void** ptr, int64_t
 int gpt_gemm(int dtype, int layout, int M, int N, int K, const void* A, const void* B, float* C,
              float* workspace, int splits, int tile, void* stream);
 
+/* gpt_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same product, kernels and argument rules as gpt_gemm, with the split-K
+ * partial sums kept in a scratch array inside the library instead of a
+ * caller workspace.  The array is GPT_NOALLOC_SCRATCH_BYTES (64 MiB) of
+ * device memory per GPU, part of the library's code object, held until the
+ * process ends; its device address is looked up once per device (on the
+ * first call with that device current).  The call allocates nothing.
+ * splits * M * N must not exceed GPT_NOALLOC_SCRATCH_BYTES / 4 partial sums
+ * (splits counted after K is rounded to whole K steps): GPT_EINVAL
+ * otherwise, before anything is enqueued.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads)
+ * race on it, so order them.  Nothing in the array needs clearing between
+ * calls (each split writes its whole block before it is summed).  Enqueued
+ * on `stream`; does not synchronise. */
+#define GPT_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gpt_gemm_noalloc(int dtype, int layout, int M, int N, int K, const void* A, const void* B, float* C,
+                     int splits, int tile, void* stream);
+
 /* Per-tensor fp8 quantisation, as used by GPT_FP8 (current scaling):
  *   s = fmax / max|x| (fmax 448 for E4M3, 57344 for E5M2; s = 1 if x is all
  *   zero; s capped at 2^64), computed in fp32;

@@ -190,3 +190,18 @@ def test_library_rope_table_matches_pinned_schedule(M):
     for i, t, ang in ROPE_PINS:
         assert abs(float(c[t, i]) - math.cos(ang)) < 2e-7, (i, t)
         assert abs(float(sn[t, i]) - math.sin(ang)) < 2e-7, (i, t)
+
+
+def test_noalloc_rejects_partials_beyond_its_scratch(M):
+    """Host-side checks of gpt_gemm_noalloc: sizes past the scratch limit are
+    refused before anything reaches the GPU."""
+    lim = M.NOALLOC_SCRATCH_BYTES // 4
+    # 2048 x 2048 x 8 splits = 32 Mi partial sums > 16 Mi
+    with pytest.raises(M.GPTError) as e:
+        M.gpt_gemm_noalloc(1, 2, 2048, 2048, 16384, 256, 256, 256, splits=8)
+    assert e.value.code == M.GPT_EINVAL and "scratch" in str(e.value)
+    assert 2048 * 2048 * 8 > lim
+    with pytest.raises(M.GPTError):
+        M.gpt_gemm_noalloc(1, 0, 64, 64, 64, 256, 256, 256, splits=2)   # KK layout is not split
+    with pytest.raises(M.GPTError):
+        M.gpt_gemm_noalloc(1, 2, 64, 64, 64, 0, 256, 256, splits=2)     # NULL operand
