@@ -53,10 +53,18 @@ class GPTShape:
     init_std: float = 0.02
     weight_seed: int = 0
     token_seed: int = 1
+    n_kv_head: int = 0         # key/value heads (grouped-query attention); 0 = n_head
 
     @property
     def bt(self) -> int:
         return self.batch * self.seq_len
+
+    @property
+    def kv_heads(self) -> int:
+        """Key/value heads: n_kv_head, or n_head when it is 0 (plain
+        multi-head attention).  Query head h reads key/value head
+        h // (n_head // kv_heads)."""
+        return self.n_kv_head or self.n_head
 
     @property
     def param_dtype(self) -> str:
@@ -117,10 +125,11 @@ def layer_windows(s: GPTShape) -> List[int]:
 def param_shapes(s: GPTShape) -> List[Tuple[str, Tuple[int, int]]]:
     """(name, [rows, cols]) in parameter-layout order."""
     d, f, v = s.d_model, s.mlp_hidden, s.vocab
+    dkv = s.kv_heads * s.head_dim
     out = [("E", (v, d))]
     for l in range(s.depth):
-        out += [(f"L{l}.Wq", (d, d)), (f"L{l}.Wk", (d, d)),
-                (f"L{l}.Wv", (d, d)), (f"L{l}.Wo", (d, d)),
+        out += [(f"L{l}.Wq", (d, d)), (f"L{l}.Wk", (dkv, d)),
+                (f"L{l}.Wv", (dkv, d)), (f"L{l}.Wo", (d, d)),
                 (f"L{l}.W1", (f, d)), (f"L{l}.W2", (d, f))]
     out.append(("U", (v, d)))
     return out

@@ -20,6 +20,13 @@ describe, evaluated in float64 with hand-derived adjoints:
     PyTorch-style mean cross-entropy over the target positions; rows are
     drawn as T+1 ids and split into inputs and shifted targets.
 
+Grouped-query attention (nanochat User Guide, section 10, base model
+paragraph, lists Group-Query Attention among the architecture's features):
+with n_kv_head = Hkv < H, Wk and Wv are [Hkv*Dh, d], and query head h attends
+with the keys and values of head h // (H / Hkv).  The backward sums the key
+and value gradients of the H/Hkv query heads that share a key/value head.
+Hkv = H is plain multi-head attention.
+
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
   pre-norm blocks plus a final norm before lm_head, no norm after the
@@ -36,8 +43,8 @@ operands, so the oracle takes that encoding as a step of the method
 OCP E4M3 and gradient operands in E5M2, each tensor with its own current
 per-tensor scale (``fp8_codec.quantize_tensor``); the products of the decoded
 operands are then exact (fp64), and gradients pass the encoding unchanged
-(straight-through).  The fused QKV weight [3d, d] and its output gradient
-[BT, 3d] are one tensor each.  Everything else stays exact.
+(straight-through).  The fused QKV weight [d + 2 Hkv Dh, d] and its output
+gradient [BT, d + 2 Hkv Dh] are one tensor each.  Everything else stays exact.
 
 Memory plan: the residual stream h is checkpointed (fp64) at each layer input;
 the backward recomputes the layer's internals from it.  Attention is done one
@@ -146,6 +153,19 @@ def attention_bwd(do: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return dq, dk, dv
 
 
+def expand_kv(x: np.ndarray, n_head: int) -> np.ndarray:
+    """[Hkv, T, Dh] -> [H, T, Dh]: query head h reads key/value head
+    h // (H / Hkv) (grouped-query attention)."""
+    return np.repeat(x, n_head // x.shape[0], axis=0)
+
+
+def reduce_kv(dx: np.ndarray, kv_heads: int) -> np.ndarray:
+    """Adjoint of expand_kv: [H, T, Dh] -> [Hkv, T, Dh], the sum over the
+    query heads of each group."""
+    H, T, Dh = dx.shape
+    return dx.reshape(kv_heads, H // kv_heads, T, Dh).sum(axis=1)
+
+
 def logsumexp_rows(z: np.ndarray) -> np.ndarray:
     m = z.max(axis=-1, keepdims=True)
     return (m + np.log(np.sum(np.exp(z - m), axis=-1, keepdims=True)))[..., 0]
@@ -193,7 +213,8 @@ class Fp8Operands(LinearOperands):
         d = s.d_model
         for l in range(s.depth):
             qkv = fp8_value(np.concatenate([W[f"L{l}.Wq"], W[f"L{l}.Wk"], W[f"L{l}.Wv"]]), "e4m3")
-            out[f"L{l}.Wq"], out[f"L{l}.Wk"], out[f"L{l}.Wv"] = qkv[:d], qkv[d:2 * d], qkv[2 * d:]
+            dkv = W[f"L{l}.Wk"].shape[0]
+            out[f"L{l}.Wq"], out[f"L{l}.Wk"], out[f"L{l}.Wv"] = qkv[:d], qkv[d:d + dkv], qkv[d + dkv:]
             for w in ("Wo", "W1", "W2"):
                 out[f"L{l}.{w}"] = fp8_value(W[f"L{l}.{w}"], "e4m3")
         return out
@@ -222,20 +243,21 @@ class _Layer:
                  h: np.ndarray, cos: np.ndarray, sin: np.ndarray, window: int,
                  enc: LinearOperands):
         B, T, H, Dh, eps = s.batch, s.seq_len, s.n_head, s.head_dim, s.norm_eps
+        Hkv = s.kv_heads
         self.h_in = h
         self.a, self.r1 = rmsnorm(h, eps)                          # [BT, d]
         self.aq = enc.act(self.a)
         q = (self.aq @ W[f"L{l}.Wq"].T).reshape(B, T, H, Dh)
-        k = (self.aq @ W[f"L{l}.Wk"].T).reshape(B, T, H, Dh)
-        self.v = (self.aq @ W[f"L{l}.Wv"].T).reshape(B, T, H, Dh)
+        k = (self.aq @ W[f"L{l}.Wk"].T).reshape(B, T, Hkv, Dh)
+        self.v = (self.aq @ W[f"L{l}.Wv"].T).reshape(B, T, Hkv, Dh)
         self.qr, self.kr = rope(q, cos, sin), rope(k, cos, sin)
         self.qn, self.rq = rmsnorm(self.qr, eps)                   # QK-norm
         self.kn, self.rk = rmsnorm(self.kr, eps)
-        o = np.empty_like(self.v)
+        o = np.empty((B, T, H, Dh))
         for b in range(B):  # one batch row at a time: P is [H, T, T]
             qb = self.qn[b].transpose(1, 0, 2)
-            kb = self.kn[b].transpose(1, 0, 2)
-            vb = self.v[b].transpose(1, 0, 2)
+            kb = expand_kv(self.kn[b].transpose(1, 0, 2), H)
+            vb = expand_kv(self.v[b].transpose(1, 0, 2), H)
             o[b] = attention_fwd(qb, kb, vb, window).transpose(1, 0, 2)
         self.o = o.reshape(B * T, H * Dh)
         self.oq = enc.act(self.o)
@@ -365,20 +387,21 @@ def forward_backward(s: gi.GPTShape, W: Dict[str, np.ndarray], X: np.ndarray,
         dhq = enc.grad(dh)
         grads[f"L{l}.Wo"] = dhq.T @ L.oq
         do = (dhq @ Wl[f"L{l}.Wo"]).reshape(B, T, H, Dh)
+        Hkv = s.kv_heads
         dqn = np.empty_like(do)
-        dkn = np.empty_like(do)
-        dv = np.empty_like(do)
+        dkn = np.empty((B, T, Hkv, Dh))
+        dv = np.empty((B, T, Hkv, Dh))
         for b in range(B):
             qb = L.qn[b].transpose(1, 0, 2)
-            kb = L.kn[b].transpose(1, 0, 2)
-            vb = L.v[b].transpose(1, 0, 2)
+            kb = expand_kv(L.kn[b].transpose(1, 0, 2), H)
+            vb = expand_kv(L.v[b].transpose(1, 0, 2), H)
             dq_, dk_, dv_ = attention_bwd(do[b].transpose(1, 0, 2), qb, kb, vb, wins[l])
             dqn[b] = dq_.transpose(1, 0, 2)
-            dkn[b] = dk_.transpose(1, 0, 2)
-            dv[b] = dv_.transpose(1, 0, 2)
+            dkn[b] = reduce_kv(dk_, Hkv).transpose(1, 0, 2)
+            dv[b] = reduce_kv(dv_, Hkv).transpose(1, 0, 2)
         dq = rope_bwd(rmsnorm_bwd(dqn, L.qn, L.rq), cos, sin).reshape(B * T, d)
-        dk = rope_bwd(rmsnorm_bwd(dkn, L.kn, L.rk), cos, sin).reshape(B * T, d)
-        dv = dv.reshape(B * T, d)
+        dk = rope_bwd(rmsnorm_bwd(dkn, L.kn, L.rk), cos, sin).reshape(B * T, Hkv * Dh)
+        dv = dv.reshape(B * T, Hkv * Dh)
         dq, dk, dv = enc.grad_fused(dq, dk, dv)   # the fused projection's output gradient
         grads[f"L{l}.Wq"] = dq.T @ L.aq
         grads[f"L{l}.Wk"] = dk.T @ L.aq

@@ -342,6 +342,74 @@ def test_finite_differences_tiny_config():
     _fd_check(s, n_coords=6, seed=1)
 
 
+# ---------------------------------------------------------------- grouped-query attention
+
+def test_finite_differences_grouped_query_model():
+    """4 query heads sharing 2 key/value heads (and sharing 1): every tensor
+    against central differences."""
+    _fd_check(small_shape(n_head=4, head_dim=4, n_kv_head=2), n_coords=10, seed=3)
+    _fd_check(small_shape(n_head=4, head_dim=4, n_kv_head=1, window_pattern="L"), n_coords=6, seed=4)
+
+
+def _expanded_to_mha(s, W):
+    """The multi-head model whose key/value row blocks repeat the grouped
+    model's: query head h gets key/value block h // (H / Hkv)."""
+    G, Dh = s.n_head // s.kv_heads, s.head_dim
+    sm = s.replace(n_kv_head=0)
+    Wm = dict(W)
+    for l in range(s.depth):
+        for w in ("Wk", "Wv"):
+            blocks = W[f"L{l}.{w}"].reshape(s.kv_heads, Dh, -1)
+            Wm[f"L{l}.{w}"] = np.repeat(blocks, G, axis=0).reshape(s.n_head * Dh, -1)
+    return sm, Wm
+
+
+@pytest.mark.parametrize("kv", [1, 2])
+def test_grouped_query_equals_multi_head_with_shared_rows(kv):
+    """A grouped model is the multi-head model (an independent code path:
+    no head mapping at all) whose key/value rows are shared by the heads of
+    a group; its key/value gradients are the sums of the multi-head
+    gradients over each group's rows (the chain rule through the shared
+    parameters), and every other gradient is equal."""
+    s = small_shape(n_head=4, head_dim=4, n_kv_head=kv, seq_len=10)
+    W, X, Y = load(s)
+    loss, G = O.forward_backward(s, W, X, Y)
+    sm, Wm = _expanded_to_mha(s, W)
+    loss_m, Gm = O.forward_backward(sm, Wm, X, Y)
+    assert abs(loss - loss_m) < 1e-12
+    g, Dh = s.n_head // kv, s.head_dim
+    for n in G:
+        if n.endswith(".Wk") or n.endswith(".Wv"):
+            want = Gm[n].reshape(kv, g, Dh, -1).sum(axis=1).reshape(kv * Dh, -1)
+            np.testing.assert_allclose(G[n], want, rtol=0, atol=1e-13)
+        else:
+            np.testing.assert_allclose(G[n], Gm[n], rtol=0, atol=1e-13)
+
+
+def test_grouped_attention_matches_brute_force():
+    """Per-(h, i, j) loops in which head h reads key/value head h // 3."""
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((6, 8, 4))
+    k, v = rng.standard_normal((2, 8, 4)), rng.standard_normal((2, 8, 4))
+    o = O.attention_fwd(q, O.expand_kv(k, 6), O.expand_kv(v, 6), 5)
+    kk = np.stack([k[h // 3] for h in range(6)])
+    vv = np.stack([v[h // 3] for h in range(6)])
+    np.testing.assert_allclose(o, brute_attention(q, kk, vv, 5), rtol=0, atol=1e-12)
+    # the adjoint of the expansion sums each group
+    dx = rng.standard_normal((6, 8, 4))
+    r = O.reduce_kv(dx, 2)
+    np.testing.assert_allclose(r[0], dx[0] + dx[1] + dx[2], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r[1], dx[3] + dx[4] + dx[5], rtol=0, atol=1e-14)
+
+
+def test_kv_heads_equal_to_heads_is_multi_head():
+    s = small_shape()
+    W, X, Y = load(s)
+    l0, G0 = O.forward_backward(s, W, X, Y)
+    l1, G1 = O.forward_backward(s.replace(n_kv_head=s.n_head), W, X, Y)
+    assert l0 == l1 and all(np.array_equal(G0[n], G1[n]) for n in G0)
+
+
 def test_unseen_embedding_rows_have_zero_gradient():
     s = small_shape(vocab=200)
     W, X, Y = load(s)
