@@ -59,12 +59,12 @@ def decode_bytes(s, pos: int) -> float:
     """HBM bytes one decode step must move at position pos: every weight
     matrix and the lm_head once (bf16), the batch's embedding rows, and each
     layer's visible cached keys and values plus the new ones."""
-    d, f = s.d_model, s.mlp_hidden
-    weights = 2.0 * (s.depth * (4 * d * d + 2 * d * f) + s.vocab * d) + 2.0 * s.batch * d
+    d, f, dkv = s.d_model, s.mlp_hidden, s.kv_heads * s.head_dim
+    weights = 2.0 * (s.depth * (2 * d * d + 2 * dkv * d + 2 * d * f) + s.vocab * d) + 2.0 * s.batch * d
     kv = 0.0
     for w in gi.layer_windows(s):
         vis = min(pos + 1, w)
-        kv += 2.0 * 2.0 * s.batch * s.n_head * s.head_dim * (vis + 1)
+        kv += 2.0 * 2.0 * s.batch * s.kv_heads * s.head_dim * (vis + 1)
     logits = 4.0 * s.batch * s.vocab
     return weights + kv + logits
 
@@ -129,6 +129,7 @@ def bench_decode(args, s) -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, seeded token ids)",
         "config": {"workload": s.name, "depth": s.depth, "d_model": s.d_model, "n_head": s.n_head,
+                   "n_kv_head": s.kv_heads,
                    "head_dim": s.head_dim, "mlp_hidden": s.mlp_hidden, "vocab": s.vocab, "batch": s.batch,
                    "prompt": P, "window": s.window, "window_pattern": s.window_pattern},
         "prefill": {"tokens_per_s": s.batch * P / t_prefill, "ms": t_prefill * 1e3},
@@ -315,6 +316,7 @@ def main() -> int:
         "dtype": dtype,
         "data": "synthetic (seeded N(0,0.02) weights, seeded token ids)",
         "config": {"workload": s.name, "depth": s.depth, "d_model": s.d_model, "n_head": s.n_head,
+                   "n_kv_head": s.kv_heads,
                    "head_dim": s.head_dim, "mlp_hidden": s.mlp_hidden, "vocab": s.vocab,
                    "seq_len": s.seq_len, "batch": s.batch, "grad_accum": n_acc, "tokens_per_step": s.bt * n_acc,
                    "optimizer": "muon+adamw" if args.optimizer else None,

@@ -33,7 +33,7 @@ class gpt_config(ctypes.Structure):
         ("seq_len", ctypes.c_int32), ("batch", ctypes.c_int32), ("window", ctypes.c_int32),
         ("window_pattern", ctypes.c_char * 8), ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float),
         ("precision", ctypes.c_int32), ("weights", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-        ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p), ("n_kv_head", ctypes.c_int32),
     ]
 
 
@@ -143,6 +143,7 @@ def make_config(shape, weights: int = 0, workspace: int = 0, workspace_bytes: in
     c.window_pattern = shape.window_pattern.encode()
     c.rope_base, c.norm_eps = shape.rope_base, shape.norm_eps
     c.precision = _PREC[shape.precision]
+    c.n_kv_head = getattr(shape, "n_kv_head", 0)
     c.weights, c.workspace, c.workspace_bytes, c.stream = weights or None, workspace or None, workspace_bytes, stream or None
     return c
 

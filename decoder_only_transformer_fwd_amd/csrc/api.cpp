@@ -39,6 +39,10 @@ int check_config(const gpt_config* c, Shape& s) {
   if (s.L < 1 || s.d < 1 || s.H < 1 || s.F < 1 || s.V < 1 || s.T < 1 || s.B < 1)
     return fail(GPT_EINVAL, "all sizes must be positive");
   if ((long)s.H * s.Dh != s.d) return fail(GPT_EINVAL, "d_model must equal n_head * head_dim");
+  s.Hkv = c->n_kv_head ? c->n_kv_head : s.H;
+  if (s.Hkv < 1 || s.Hkv > s.H || s.H % s.Hkv) return fail(GPT_EINVAL, "n_kv_head must divide n_head");
+  s.dkv = s.Hkv * s.Dh;
+  s.Nqkv = s.d + 2 * s.dkv;
   const bool dh_ok = s.dtype == DT_F32 ? (s.Dh == 32 || s.Dh == 64) : (s.Dh == 64 || s.Dh == 128);
   if (!dh_ok) return fail(GPT_EINVAL, "unsupported head_dim for this precision");
   if (s.d % 64 || s.F % 64) return fail(GPT_EINVAL, "d_model and mlp_hidden must be multiples of 64");
@@ -91,8 +95,8 @@ void param_offsets(const Shape& s, ParamOffsets& p) {
   char nm[24];
   for (int l = 0; l < s.L; ++l) {
     snprintf(nm, sizeof nm, "L%d.Wq", l); p.Wqkv[l] = add(nm, s.d, s.d);
-    snprintf(nm, sizeof nm, "L%d.Wk", l); add(nm, s.d, s.d);
-    snprintf(nm, sizeof nm, "L%d.Wv", l); add(nm, s.d, s.d);
+    snprintf(nm, sizeof nm, "L%d.Wk", l); add(nm, s.dkv, s.d);
+    snprintf(nm, sizeof nm, "L%d.Wv", l); add(nm, s.dkv, s.d);
     snprintf(nm, sizeof nm, "L%d.Wo", l); p.Wo[l] = add(nm, s.d, s.d);
     snprintf(nm, sizeof nm, "L%d.W1", l); p.W1[l] = add(nm, s.F, s.d);
     snprintf(nm, sizeof nm, "L%d.W2", l); p.W2[l] = add(nm, s.d, s.F);
@@ -297,11 +301,11 @@ int build_layout(gpt_model& m) {
     auto& L = m.lay[l];
     L.n1 = take(BT * s.d * A);
     L.rstd1 = take(BT * 4);
-    L.qkv = take(BT * 3 * s.d * A);
-    L.rqk = take(BT * 2 * s.H * 4);
+    L.qkv = take(BT * s.Nqkv * A);
+    L.rqk = take(BT * (s.H + s.Hkv) * 4);
     L.qT = take((size_t)s.B * s.H * s.Dh * s.Tp * A);
-    L.kT = take((size_t)s.B * s.H * s.Dh * s.Tp * A);
-    L.vT = take((size_t)s.B * s.H * s.Dh * s.Tp * A);
+    L.kT = take((size_t)s.B * s.Hkv * s.Dh * s.Tp * A);
+    L.vT = take((size_t)s.B * s.Hkv * s.Dh * s.Tp * A);
     L.o = take(BT * s.d * A);
     L.lse2 = take((size_t)s.B * s.H * s.Tp * 4);
     L.n2 = take(BT * s.d * A);
@@ -336,7 +340,7 @@ int build_layout(gpt_model& m) {
   m.dO = take(BT * s.d * A);
   m.dOT = take((size_t)s.B * s.H * s.Dh * s.Tp * A);
   m.Dv = take((size_t)s.B * s.H * s.Tp * 4);
-  m.dqkv = take(BT * 3 * s.d * A);
+  m.dqkv = take(BT * s.Nqkv * A);
   // split-K partials: the largest need among the planned products
   size_t need = 0;
   auto consider = [&](int layout, int M, int N, int K) {
@@ -353,30 +357,30 @@ int build_layout(gpt_model& m) {
   consider(LAYOUT_MN, s.F, s.d, s.BT);
   consider(LAYOUT_KN, s.BT, s.d, s.d);
   consider(LAYOUT_MN, s.d, s.d, s.BT);
-  consider(LAYOUT_KN, s.BT, s.d, 3 * s.d);
-  consider(LAYOUT_MN, 3 * s.d, s.d, s.BT);
+  consider(LAYOUT_KN, s.BT, s.d, s.Nqkv);
+  consider(LAYOUT_MN, s.Nqkv, s.d, s.BT);
   consider(LAYOUT_KK, s.BT, s.d, s.F);
   consider(LAYOUT_KK, s.BT, s.d, s.d);
   if (s.fp8) {
     for (int dty : {DT_FP8_A4B4, DT_FP8_A5B4}) {
-      for (int K : {s.d, s.F, 3 * s.d}) {
+      for (int K : {s.d, s.F, s.Nqkv}) {
         GemmPlan g = plan_gemm(dty, LAYOUT_KK, s.BT, s.d, K);
         if (g.splits > 1) need = std::max(need, (size_t)g.splits * s.BT * s.d);
       }
-      const int MN[4][2] = {{3 * s.d, s.d}, {s.d, s.d}, {s.F, s.d}, {s.d, s.F}};
+      const int MN[4][2] = {{s.Nqkv, s.d}, {s.d, s.d}, {s.F, s.d}, {s.d, s.F}};
       for (auto& mn : MN) {
         GemmPlan g = plan_gemm(dty, LAYOUT_KK, mn[0], mn[1], s.BT);
         if (g.splits > 1) need = std::max(need, (size_t)g.splits * mn[0] * mn[1]);
       }
     }
-    const size_t wide = (size_t)std::max(s.F, 3 * s.d);
+    const size_t wide = (size_t)std::max(s.F, s.Nqkv);
     for (int l = 0; l < s.L; ++l) {
       auto& L = m.lay[l];
       L.n1T = take(BT * s.d);
       L.oT = take(BT * s.d);
       L.n2T = take(BT * s.d);
       L.gT = take(BT * s.F);
-      const size_t wsz[4] = {(size_t)3 * s.d * s.d, (size_t)s.d * s.d, (size_t)s.F * s.d, (size_t)s.d * s.F};
+      const size_t wsz[4] = {(size_t)s.Nqkv * s.d, (size_t)s.d * s.d, (size_t)s.F * s.d, (size_t)s.d * s.F};
       for (int k = 0; k < 4; ++k) {
         L.wq[k] = take(wsz[k]);
         L.wqT[k] = take(wsz[k]);
@@ -539,7 +543,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   const char* W = m.W;
   auto wp = [&](long off) { return (const void*)(W + off * es); };
   hipStream_t st = m.st;
-  const int BT = s.BT, d = s.d, F = s.F, V = s.V, H = s.H, Dh = s.Dh;
+  const int BT = s.BT, d = s.d, F = s.F, V = s.V, H = s.H, Dh = s.Dh, Hkv = s.Hkv, Nqkv = s.Nqkv;
   float* h = at<float>(m, m.h);
   int* flag = at<int>(m, m.flag);
   const float* cosb = at<float>(m, m.cosb);
@@ -607,7 +611,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     zero_u32(amax8, m.n_slots * AMAX_SLOT, st);
     for (int l = 0; l < s.L && quant_weights; ++l) {
       auto& Ly = m.lay[l];
-      quant("fp8_quant_weights", FP8_E4M3, wp(P.Wqkv[l]), 3 * d, d, slot(l, SL_WQKV), m.ws + Ly.wq[0], m.ws + Ly.wqT[0], false);
+      quant("fp8_quant_weights", FP8_E4M3, wp(P.Wqkv[l]), Nqkv, d, slot(l, SL_WQKV), m.ws + Ly.wq[0], m.ws + Ly.wqT[0], false);
       quant("fp8_quant_weights", FP8_E4M3, wp(P.Wo[l]), d, d, slot(l, SL_WO), m.ws + Ly.wq[1], m.ws + Ly.wqT[1], false);
       quant("fp8_quant_weights", FP8_E4M3, wp(P.W1[l]), F, d, slot(l, SL_W1), m.ws + Ly.wq[2], m.ws + Ly.wqT[2], false);
       quant("fp8_quant_weights", FP8_E4M3, wp(P.W2[l]), d, F, slot(l, SL_W2), m.ws + Ly.wq[3], m.ws + Ly.wqT[3], false);
@@ -624,20 +628,22 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     prof_end(m);
     if (f8) {
       quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.n1, BT, d, slot(l, SL_N1), q8row, m.ws + Ly.n1T);
-      rc = gemm8("gemm_qkv", DT_FP8_A4B4, EPI_STORE, BT, 3 * d, d, q8row, m.ws + Ly.wq[0], m.ws + Ly.qkv, 3 * d,
+      rc = gemm8("gemm_qkv", DT_FP8_A4B4, EPI_STORE, BT, Nqkv, d, q8row, m.ws + Ly.wq[0], m.ws + Ly.qkv, Nqkv,
                  slot(l, SL_N1), slot(l, SL_WQKV));
     } else {
-      rc = gemm(m, "gemm_qkv", LAYOUT_KK, EPI_STORE, BT, 3 * d, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d, m.ws + Ly.qkv,
-                3 * d);
+      rc = gemm(m, "gemm_qkv", LAYOUT_KK, EPI_STORE, BT, Nqkv, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d, m.ws + Ly.qkv,
+                Nqkv);
     }
     if (rc) return rc;
-    prof_begin(m, "rope_qknorm_fwd", (double)BT * d * 8.0 * es_d + BT * 2.0 * H * 4.0, 1, KLV("rope_qknorm_fwd_kernel", "rope_qknorm_fwd128_kernel"));
+    // reads q, k, v; writes q^, k^ in place and the transposed q^, k^, v
+    prof_begin(m, "rope_qknorm_fwd", (double)BT * (3.0 * d + 5.0 * s.dkv) * es_d + BT * (double)(H + Hkv) * 4.0, 1,
+               KLV("rope_qknorm_fwd_kernel", "rope_qknorm_fwd128_kernel"));
     rope_qknorm_fwd(dt, m.ws + Ly.qkv, at<float>(m, Ly.rqk), m.ws + Ly.qT, m.ws + Ly.kT, m.ws + Ly.vT, cosb, sinb,
-                    s.B, s.T, s.Tp, H, Dh, s.eps, st);
+                    s.B, s.T, s.Tp, H, Hkv, Dh, s.eps, st);
     AttnArgs aa{};
     aa.qkv = m.ws + Ly.qkv; aa.qT = m.ws + Ly.qT; aa.kT = m.ws + Ly.kT; aa.vT = m.ws + Ly.vT;
     aa.o = m.ws + Ly.o; aa.lse2 = at<float>(m, Ly.lse2);
-    aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.d = d; aa.window = s.win[l];
+    aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.Hkv = Hkv; aa.d = d; aa.ldqkv = Nqkv; aa.window = s.win[l];
     aa.scale = 1.0f / std::sqrt((float)Dh);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
     aa.amax_o = amx(l, SL_O);
@@ -779,7 +785,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     aa.o = m.ws + Ly.o; aa.lse2 = at<float>(m, Ly.lse2);
     aa.dO = m.ws + m.dO; aa.dOT = m.ws + m.dOT; aa.Dv = at<float>(m, m.Dv); aa.dqkv = m.ws + m.dqkv;
     aa.amax_dv = amx(l, SL_DQKV);
-    aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.d = d; aa.window = s.win[l];
+    aa.B = s.B; aa.T = s.T; aa.Tp = s.Tp; aa.H = H; aa.Hkv = Hkv; aa.d = d; aa.ldqkv = Nqkv; aa.window = s.win[l];
     aa.scale = 1.0f / std::sqrt((float)Dh);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
     const bool win = s.win[l] < s.T;
@@ -795,23 +801,24 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                KLD("attn_bwd_dq_kernel"));
     if (attn_bwd(dt, Dh, aa, 2, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
     prof_end(m);
-    prof_begin(m, "rope_qknorm_bwd", (double)BT * d * 6.0 * es_d + BT * 2.0 * H * 4.0, 1, KLV("rope_qknorm_bwd_kernel", "rope_qknorm_bwd128_kernel"));
-    rope_qknorm_bwd(dt, m.ws + m.dqkv, m.ws + Ly.qkv, at<float>(m, Ly.rqk), cosb, sinb, s.B, s.T, H, Dh, st,
+    prof_begin(m, "rope_qknorm_bwd", (double)BT * (d + s.dkv) * 3.0 * es_d + BT * (double)(H + Hkv) * 4.0, 1,
+               KLV("rope_qknorm_bwd_kernel", "rope_qknorm_bwd128_kernel"));
+    rope_qknorm_bwd(dt, m.ws + m.dqkv, m.ws + Ly.qkv, at<float>(m, Ly.rqk), cosb, sinb, s.B, s.T, H, Hkv, Dh, st,
                     amx(l, SL_DQKV));
     prof_end(m);
     if (f8) {
-      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.dqkv, BT, 3 * d, slot(l, SL_DQKV), q8row, q8T);
-      if ((rc = gemm8("dgrad_qkv", DT_FP8_A5B4, EPI_STORE_F32, BT, d, 3 * d, q8row, m.ws + Ly.wqT[0], dm, d,
+      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.dqkv, BT, Nqkv, slot(l, SL_DQKV), q8row, q8T);
+      if ((rc = gemm8("dgrad_qkv", DT_FP8_A5B4, EPI_STORE_F32, BT, d, Nqkv, q8row, m.ws + Ly.wqT[0], dm, d,
                       slot(l, SL_DQKV), slot(l, SL_WQKV))))
         return rc;
-      if ((rc = wgrad8("wgrad_qkv", 3 * d, d, BT, q8T, m.ws + Ly.n1T, grads + P.Wqkv[l], d, slot(l, SL_DQKV),
+      if ((rc = wgrad8("wgrad_qkv", Nqkv, d, BT, q8T, m.ws + Ly.n1T, grads + P.Wqkv[l], d, slot(l, SL_DQKV),
                        slot(l, SL_N1))))
         return rc;
     } else {
-      if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, epi_dn, BT, d, 3 * d, m.ws + m.dqkv, 3 * d, wp(P.Wqkv[l]), d, dm,
+      if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, epi_dn, BT, d, Nqkv, m.ws + m.dqkv, Nqkv, wp(P.Wqkv[l]), d, dm,
                      d)))
         return rc;
-      if ((rc = wgrad("wgrad_qkv", 3 * d, d, BT, m.ws + m.dqkv, 3 * d, m.ws + Ly.n1, d, grads + P.Wqkv[l], d)))
+      if ((rc = wgrad("wgrad_qkv", Nqkv, d, BT, m.ws + m.dqkv, Nqkv, m.ws + Ly.n1, d, grads + P.Wqkv[l], d)))
         return rc;
     }
     if ((rc = norm_bwd(m.ws + Ly.n1, at<float>(m, Ly.rstd1), 1, amx(l - 1, SL_DH2)))) return rc;
@@ -1030,7 +1037,7 @@ int gpt_debug_tensor(gpt_model* m, int which, int layer, void** ptr, int64_t* ro
   *elem_bytes = s.es;
   switch (which) {
     case 0: *ptr = m->ws + m->h; *cols = s.d; *elem_bytes = 4; break;
-    case 1: *ptr = m->ws + m->lay[layer].qkv; *cols = 3 * s.d; break;
+    case 1: *ptr = m->ws + m->lay[layer].qkv; *cols = s.Nqkv; break;
     case 2: *ptr = m->ws + m->lay[layer].o; *cols = s.d; break;
     case 3: *ptr = m->ws + m->rowloss; *cols = 1; *elem_bytes = 4; break;
     case 4: *ptr = m->ws + m->lse; *cols = 1; *elem_bytes = 4; break;

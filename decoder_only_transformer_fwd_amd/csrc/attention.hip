@@ -19,9 +19,10 @@
 // so every LDS read is one contiguous 8- or 16-byte access.
 //
 // Backward: D_i = rowsum(dO*O) comes from a separate pass; dV and dK are
-// produced by two passes over 128-key tiles iterating over query tiles, dQ by
-// one pass over 128-query tiles iterating over key tiles.  No atomics: the
-// result is bitwise reproducible.
+// produced by two passes over 128-key tiles iterating over query tiles (of
+// every query head that shares the key/value head, with grouped-query
+// attention), dQ by one pass over 128-query tiles iterating over key tiles.
+// No atomics: the result is bitwise reproducible.
 #include "common.h"
 #include "kernels.h"
 
@@ -118,7 +119,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   int qb, h, b;
   attn_coords(qb, h, b);
   const int Tn = a.T, W = a.window, d = a.d;
-  const long row3 = 3L * d;
+  const long row3 = a.ldqkv;
+  const int hk = h / (a.H / a.Hkv);   // key/value head of query head h
   const int i0 = qb * BQ, iw0 = i0 + wave * 32, i = iw0 + l32;
 
   const char* qkv = (const char*)a.qkv;
@@ -141,9 +143,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   RowDma<BKV, KROW, 4> lk;
   RowDma<DH, VROW, 4> lv;
   {
-    const char* kbase = qkv + (((long)b * Tn) * row3 + d + h * DH) * ES;
+    const char* kbase = qkv + (((long)b * Tn) * row3 + d + hk * DH) * ES;
     lk.init(kbase, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + KROW, wave, lane);
-    const char* vtbase = (const char*)a.vT + (((long)b * a.H + h) * DH) * (long)a.Tp * ES;
+    const char* vtbase = (const char*)a.vT + (((long)b * a.Hkv + hk) * DH) * (long)a.Tp * ES;
     lv.init(vtbase, a.Tp * ES, (long)DH * a.Tp * ES, wave, lane);
   }
 
@@ -271,18 +273,20 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
-  int kb, h, b;
-  attn_coords(kb, h, b);
+  int kb, hk, b;   // key tile, key/value head, batch row
+  attn_coords(kb, hk, b);
   const int Tn = a.T, W = a.window, d = a.d, Tp = a.Tp;
-  const long row3 = 3L * d;
+  const long row3 = a.ldqkv;
+  const int dkv = a.Hkv * DH;
+  const int G = a.H / a.Hkv;   // query heads per key/value head
   const int j0 = kb * BKV, jw0 = j0 + wave * 32, j = jw0 + l32;
   const float c = a.scale_log2;
 
   const char* qkv = (const char*)a.qkv;
   typename MF::frag kf[KS], vf[DO_DK ? KS : 1];
   {
-    const char* krow = qkv + (((long)b * Tn + j) * row3 + d + h * DH) * ES;
-    const char* vrow = krow + (long)d * ES;
+    const char* krow = qkv + (((long)b * Tn + j) * row3 + d + hk * DH) * ES;
+    const char* vrow = krow + (long)dkv * ES;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (j < Tn) {
@@ -298,21 +302,11 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
   const int ib = j0;
   const int iend = min(Tn, j0 + BKV - 1 + W);
   const int nq = iend > ib ? (iend - ib + BQ - 1) / BQ : 0;
-  const long hoff = ((long)b * a.H + h);
 
   RowDma<BQ, RROW, 4> lq, ldo;
   RowDma<DH, TROW, 4> lqt, ldot;
-  lq.init(qkv + (((long)b * Tn) * row3 + h * DH) * ES, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + RROW, wave,
-          lane);
-  if constexpr (DO_DK) {
-    ldo.init((const char*)a.dO + (((long)b * Tn) * d + h * DH) * ES, d * ES, (long)(Tn - 1) * d * ES + RROW, wave,
-             lane);
-    lqt.init((const char*)a.qT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
-  }
-  if constexpr (DO_DV) ldot.init((const char*)a.dOT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
-  // lse / D of the queries this lane's accumulator rows cover: i0 + 32qb + 8q + 4g + e
-  const float* lseb = a.lse2 + hoff * Tp + 4 * g;
-  const float* Db = a.Dv + hoff * Tp + 4 * g;
+  const float* lseb;
+  const float* Db;
 
   floatx16 dk[DO_DK ? DB : 1], dv[DO_DV ? DB : 1];
 #pragma unroll
@@ -333,6 +327,22 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
     if constexpr (DO_DV) ldot.issue(st + OFF_DOT, i0 * ES, wave);
   };
 
+  // the query heads that share this key/value head, one after another
+  for (int gq = 0; gq < G; ++gq) {
+  const int hq = hk * G + gq;
+  const long hoff = ((long)b * a.H + hq);
+  lq.init(qkv + (((long)b * Tn) * row3 + hq * DH) * ES, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + RROW, wave,
+          lane);
+  if constexpr (DO_DK) {
+    ldo.init((const char*)a.dO + (((long)b * Tn) * d + hq * DH) * ES, d * ES, (long)(Tn - 1) * d * ES + RROW, wave,
+             lane);
+    lqt.init((const char*)a.qT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
+  }
+  if constexpr (DO_DV) ldot.init((const char*)a.dOT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
+  // lse / D of the queries this lane's accumulator rows cover: i0 + 32qb + 8q + 4g + e
+  lseb = a.lse2 + hoff * Tp + 4 * g;
+  Db = a.Dv + hoff * Tp + 4 * g;
+  if (gq > 0) __syncthreads();   // every wave is done with the previous head's stages
   if (nq > 0) issue(ib, 0);
   for (int it = 0; it < nq; ++it) {
     const int i0 = ib + it * BQ;
@@ -405,10 +415,11 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
       }
     }
   }
+  }   // query heads of the group
 
   float vm = 0.f;
   if (j < Tn) {
-    T* base = (T*)a.dqkv + ((long)b * Tn + j) * row3 + h * DH;
+    T* base = (T*)a.dqkv + ((long)b * Tn + j) * row3 + hk * DH;
 #pragma unroll
     for (int x = 0; x < DB; ++x)
 #pragma unroll
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
         }
         if constexpr (DO_DV) {
           floatx4 vv = {dv[x][4 * q], dv[x][4 * q + 1], dv[x][4 * q + 2], dv[x][4 * q + 3]};
-          store4(base + 2 * d + cc, vv);
+          store4(base + d + dkv + cc, vv);
           if (a.amax_dv) vm = fmaxf(vm, abs_max4<T>(vv));
         }
       }
@@ -453,7 +464,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   int qb, h, b;
   attn_coords(qb, h, b);
   const int Tn = a.T, W = a.window, d = a.d, Tp = a.Tp;
-  const long row3 = 3L * d;
+  const long row3 = a.ldqkv;
+  const int hk = h / (a.H / a.Hkv);   // key/value head of query head h
   const int i0 = qb * BQ, iw0 = i0 + wave * 32, i = iw0 + l32;
   const long hoff = ((long)b * a.H + h);
   const float c = a.scale_log2;
@@ -484,10 +496,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a) {
   RowDma<BKV, RROW, 4> lk, lv;
   RowDma<DH, TROW, 4> lkt;
   {
-    const char* kbase = qkv + (((long)b * Tn) * row3 + d + h * DH) * ES;
+    const char* kbase = qkv + (((long)b * Tn) * row3 + d + hk * DH) * ES;
     lk.init(kbase, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + RROW, wave, lane);
-    lv.init(kbase + (long)d * ES, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + RROW, wave, lane);
-    lkt.init((const char*)a.kT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
+    lv.init(kbase + (long)a.Hkv * DH * ES, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + RROW, wave, lane);
+    lkt.init((const char*)a.kT + ((long)b * a.Hkv + hk) * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
   }
 
   floatx16 dq[DB];
@@ -566,8 +578,9 @@ static void fwd_t(const AttnArgs& a, hipStream_t st) {
 template <typename T, int DH>
 static void bwd_t(const AttnArgs& a, int part, hipStream_t st) {
   dim3 g((a.T + 127) / 128, a.H, a.B);
-  if (part == 0) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH, 32, 1>), g, dim3(256), 0, st, a);
-  else if (part == 1) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH, 32, 2>), g, dim3(256), 0, st, a);
+  dim3 gkv((a.T + 127) / 128, a.Hkv, a.B);   // dK / dV: one work-group per key/value head
+  if (part == 0) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH, 32, 1>), gkv, dim3(256), 0, st, a);
+  else if (part == 1) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH, 32, 2>), gkv, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DH>), g, dim3(256), 0, st, a);
 }
 

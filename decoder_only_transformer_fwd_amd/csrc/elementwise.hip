@@ -197,16 +197,23 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
 }
 
 // ------------------------------------------------------------------ rotary + QK norm
-// Grid (ceil(T/64), H, B); 256 threads.  For q and k of head h: rotate the
-// half-split pairs (x[i], x[i+Dh/2]) by t*theta_i, RMS-normalise the head
-// vector, write it back in place and into the transposed copy [B][H][Dh][Tp];
-// v is only transposed.  Tokens t >= T are written as zeros in the copies.
+// Column of head h's part (0 q, 1 k, 2 v) in a qkv row: q heads, then the Hkv
+// key heads, then the Hkv value heads.
+__device__ __forceinline__ int qkv_col(int part, int h, int H, int Hkv, int DH) {
+  return part == 0 ? h * DH : part == 1 ? (H + h) * DH : (H + Hkv + h) * DH;
+}
+
+// Grid (ceil(T/64), H, B); 256 threads.  For q of head h, and k of head h
+// when h < Hkv: rotate the half-split pairs (x[i], x[i+Dh/2]) by t*theta_i,
+// RMS-normalise the head vector, write it back in place and into the
+// transposed copy [B][heads][Dh][Tp]; v (h < Hkv) is only transposed.  Tokens
+// t >= T are written as zeros in the copies.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rstd_qk,
                                                               T* __restrict__ qT, T* __restrict__ kT,
                                                               T* __restrict__ vT, const float* __restrict__ cosb,
                                                               const float* __restrict__ sinb, int Tn, int Tp,
-                                                              int H, float eps) {
+                                                              int H, int Hkv, float eps) {
   constexpr int HALF = DH / 2;
   constexpr int TPP = 64 / HALF;      // tokens per wave pass
   constexpr int LDW = 64 + 16 / sizeof(T) * 2;  // padded tile row (elements), 16-byte multiple
@@ -214,10 +221,10 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qk
   const int t0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / HALF, i = lane % HALF;
-  const int d = H * DH;
-  const long row3 = 3L * d;
-  for (int part = 0; part < 3; ++part) {
-    const int col = part * d + h * DH;
+  const long row3 = (long)(H + 2 * Hkv) * DH;
+  const int nparts = h < Hkv ? 3 : 1;   // block-uniform
+  for (int part = 0; part < nparts; ++part) {
+    const int col = qkv_col(part, h, H, Hkv, DH);
     for (int tt = wave * 16; tt < wave * 16 + 16; tt += TPP) {
       const int tl = tt + sub;
       const int t = t0 + tl;
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qk
         if (ok) {
           px[i] = from_f32<T>(y1);
           px[i + HALF] = from_f32<T>(y2);
-          if (i == 0) rstd_qk[((long)b * Tn + t) * 2 * H + part * H + h] = r;
+          if (i == 0) rstd_qk[((long)b * Tn + t) * (H + Hkv) + part * H + h] = r;
         }
       }
       tile[i * LDW + tl] = from_f32<T>(ok ? y1 : 0.f);
@@ -251,12 +258,13 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qk
     }
     __syncthreads();
     T* dst = part == 0 ? qT : (part == 1 ? kT : vT);
+    const int nh = part == 0 ? H : Hkv;
     constexpr int EPC = 16 / sizeof(T);
     constexpr int CPR = 64 / EPC;    // chunks per row
     for (int c = threadIdx.x; c < DH * CPR; c += 256) {
       const int r = c / CPR, cc = c % CPR;
       if (t0 + cc * EPC < Tp)
-        *(u32x4*)(dst + (((long)b * H + h) * DH + r) * Tp + t0 + cc * EPC) =
+        *(u32x4*)(dst + (((long)b * nh + h) * DH + r) * Tp + t0 + cc * EPC) =
             *(const u32x4*)(tile + r * LDW + cc * EPC);
     }
     __syncthreads();
@@ -278,13 +286,13 @@ __global__ __launch_bounds__(512) void rope_qknorm_fwd128_kernel(bf16* __restric
                                                                  bf16* __restrict__ qT, bf16* __restrict__ kT,
                                                                  bf16* __restrict__ vT, const float* __restrict__ cosb,
                                                                  const float* __restrict__ sinb, int Tn, int Tp,
-                                                                 int H, float eps) {
+                                                                 int H, int Hkv, float eps) {
   constexpr int DH = 128, HALF = 64, TT = 128, S = TT / 2 + 1;
   __shared__ uint32_t tile[DH * S];
   const int t0 = blockIdx.x * TT, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, p = tid >> 3, c = tid & 7;
-  const int d = H * DH;
-  const long row3 = 3L * d;
+  const long row3 = (long)(H + 2 * Hkv) * DH;
+  const bool kv = h < Hkv;   // this block also owns key/value head h (block-uniform)
   bf16x8 raw[3][2][2];
   floatx4 cs[2][2], sn[2][2];
 #pragma unroll
@@ -293,9 +301,10 @@ __global__ __launch_bounds__(512) void rope_qknorm_fwd128_kernel(bf16* __restric
     const bool ok = t < Tn;
 #pragma unroll
     for (int part = 0; part < 3; ++part) {
-      const bf16* px = qkv + ((long)b * Tn + t) * row3 + part * d + h * DH;
-      raw[part][u][0] = ok ? *(const bf16x8*)(px + 8 * c) : bf16x8{};
-      raw[part][u][1] = ok ? *(const bf16x8*)(px + HALF + 8 * c) : bf16x8{};
+      const bool okp = ok && (part == 0 || kv);
+      const bf16* px = qkv + ((long)b * Tn + t) * row3 + qkv_col(part, h, H, Hkv, DH);
+      raw[part][u][0] = okp ? *(const bf16x8*)(px + 8 * c) : bf16x8{};
+      raw[part][u][1] = okp ? *(const bf16x8*)(px + HALF + 8 * c) : bf16x8{};
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -305,6 +314,7 @@ __global__ __launch_bounds__(512) void rope_qknorm_fwd128_kernel(bf16* __restric
   }
 #pragma unroll
   for (int part = 0; part < 3; ++part) {
+    if (part > 0 && !kv) break;   // block-uniform: every thread leaves together
     float x[2][16];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(512) void rope_qknorm_fwd128_kernel(bf16* __restric
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[u][e] *= r;
         if (t < Tn) {
-          bf16* px = qkv + ((long)b * Tn + t) * row3 + part * d + h * DH;
+          bf16* px = qkv + ((long)b * Tn + t) * row3 + qkv_col(part, h, H, Hkv, DH);
           bf16x8 ylo, yhi;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(512) void rope_qknorm_fwd128_kernel(bf16* __restric
           }
           *(bf16x8*)(px + 8 * c) = ylo;
           *(bf16x8*)(px + HALF + 8 * c) = yhi;
-          if (c == 0) rstd_qk[((long)b * Tn + t) * 2 * H + part * H + h] = r;
+          if (c == 0) rstd_qk[((long)b * Tn + t) * (H + Hkv) + part * H + h] = r;
         }
       }
     }
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(512) void rope_qknorm_fwd128_kernel(bf16* __restric
     }
     __syncthreads();
     // 16-byte stores: thread (dim, q) writes tokens 8q .. 8q+7 of one dimension
-    bf16* dst = (part == 0 ? qT : (part == 1 ? kT : vT)) + ((long)b * H + h) * DH * Tp + t0;
+    bf16* dst = (part == 0 ? qT : (part == 1 ? kT : vT)) + ((long)b * (part == 0 ? H : Hkv) + h) * DH * Tp + t0;
 #pragma unroll
     for (int k = 0; k < DH * (TT / 8) / 512; ++k) {
       const int idx = tid + 512 * k, dim = idx / (TT / 8), q = idx % (TT / 8);
@@ -365,23 +375,26 @@ __global__ __launch_bounds__(512) void rope_qknorm_fwd128_kernel(bf16* __restric
 
 // Backward of the rotation + QK norm for bf16 heads of 128, in place on the q
 // and k columns of dqkv.  A group of 8 lanes takes one head vector (q or k of
-// one head of one token, numbered row * 2H + v, which is also its rstd index);
-// lane c holds elements 8c.. and 64+8c.. (the rotation pairs) of the gradient
-// and of the normalised output, each as one 16-byte load.
+// one head of one token, numbered row * (H + Hkv) + v, which is also its rstd
+// index; v < H is q head v, v >= H k head v - H, and either sits at column
+// v * Dh of the row); lane c holds elements 8c.. and 64+8c.. (the rotation
+// pairs) of the gradient and of the normalised output, each as one 16-byte
+// load.
 __global__ __launch_bounds__(256) void rope_qknorm_bwd128_kernel(bf16* __restrict__ dqkv, const bf16* __restrict__ qkv,
                                                                  const float* __restrict__ rstd_qk,
                                                                  const float* __restrict__ cosb,
                                                                  const float* __restrict__ sinb, long nvec, int Tn,
-                                                                 int H, unsigned* __restrict__ amax) {
+                                                                 int H, int Hkv, unsigned* __restrict__ amax) {
   constexpr int DH = 128, HALF = 64;
   __shared__ float red[4];
   const long vec = (long)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int c = threadIdx.x & 7;
   const bool ok = vec < nvec;
-  const long row = ok ? vec / (2 * H) : 0;
-  const int v = (int)(vec - row * 2 * H);
+  const int nv = H + Hkv;
+  const long row = ok ? vec / nv : 0;
+  const int v = (int)(vec - row * nv);
   const int t = (int)(row % Tn);
-  const long off = row * 3L * H * DH + (long)v * DH;   // q heads at h*DH, k heads at d + h*DH
+  const long off = row * (long)(H + 2 * Hkv) * DH + (long)v * DH;
   bf16x8 g[2], y[2];
   floatx4 cs[2], sn[2];
 #pragma unroll
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(T* __restrict__ dq
                                                               const float* __restrict__ rstd_qk,
                                                               const float* __restrict__ cosb,
                                                               const float* __restrict__ sinb, int rows, int Tn,
-                                                              int H, unsigned* __restrict__ amax) {
+                                                              int H, int Hkv, unsigned* __restrict__ amax) {
   constexpr int HALF = DH / 2;
   constexpr int VPP = 64 / HALF;   // head vectors per pass
   __shared__ float red[4];
@@ -431,18 +444,18 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(T* __restrict__ dq
   const int lane = threadIdx.x & 63;
   const int t = row % Tn;
   const int sub = lane / HALF, i = lane % HALF;
-  const int d = H * DH;
+  const int nv = H + Hkv;
   const bool ok = row < rows;
   const float c = ok ? cosb[t * HALF + i] : 0.f, s = ok ? sinb[t * HALF + i] : 0.f;
   float m = 0.f;
-  for (int v0 = 0; ok && v0 < 2 * H; v0 += VPP) {
-    const int v = v0 + sub;       // 0..2H-1: q heads then k heads
-    if (v >= 2 * H) continue;
-    const long off = (long)row * 3 * d + (long)v * DH;  // q at h*DH, k at d + h*DH
+  for (int v0 = 0; ok && v0 < nv; v0 += VPP) {
+    const int v = v0 + sub;       // q heads then k heads, head v at column v * DH
+    if (v >= nv) continue;
+    const long off = (long)row * (H + 2 * Hkv) * DH + (long)v * DH;
     const float g1 = to_f32(dqkv[off + i]), g2 = to_f32(dqkv[off + i + HALF]);
     const float y1 = to_f32(qkv[off + i]), y2 = to_f32(qkv[off + i + HALF]);
     const float dot = group_sum<HALF>(g1 * y1 + g2 * y2) / (float)DH;
-    const float r = rstd_qk[(long)row * 2 * H + v];
+    const float r = rstd_qk[(long)row * nv + v];
     const float d1 = r * (g1 - y1 * dot), d2 = r * (g2 - y2 * dot);
     const T o1 = from_f32<T>(d1 * c + d2 * s), o2 = from_f32<T>(-d1 * s + d2 * c);
     dqkv[off + i] = o1;
@@ -753,21 +766,21 @@ int rmsnorm_bwd(int dtype, const void* dy, int dy_act, const void* y, const floa
 
 template <typename T, int DH>
 static void rope_fwd_t(void* qkv, float* rq, void* qT, void* kT, void* vT, const float* c, const float* s, int B,
-                       int T_, int Tp, int H, float eps, hipStream_t st) {
+                       int T_, int Tp, int H, int Hkv, float eps, hipStream_t st) {
   dim3 g((T_ + 63) / 64, H, B);
   if constexpr (sizeof(T) == 2 && DH == 128) {
-    hipLaunchKernelGGL(rope_qknorm_fwd128_kernel, dim3((T_ + 127) / 128, H, B), dim3(512), 0, st, (bf16*)qkv, rq, (bf16*)qT, (bf16*)kT,
-                       (bf16*)vT, c, s, T_, Tp, H, eps);
+    hipLaunchKernelGGL(rope_qknorm_fwd128_kernel, dim3((T_ + 127) / 128, H, B), dim3(512), 0, st, (bf16*)qkv, rq,
+                       (bf16*)qT, (bf16*)kT, (bf16*)vT, c, s, T_, Tp, H, Hkv, eps);
     return;
   }
   hipLaunchKernelGGL((rope_qknorm_fwd_kernel<T, DH>), g, dim3(256), 0, st, (T*)qkv, rq, (T*)qT, (T*)kT, (T*)vT, c,
-                     s, T_, Tp, H, eps);
+                     s, T_, Tp, H, Hkv, eps);
 }
 
 void rope_qknorm_fwd(int dtype, void* qkv, float* rq, void* qT, void* kT, void* vT, const float* c,
-                     const float* s, int B, int T_, int Tp, int H, int Dh, float eps, hipStream_t st) {
+                     const float* s, int B, int T_, int Tp, int H, int Hkv, int Dh, float eps, hipStream_t st) {
 #define RF(TT, D) \
-  if (Dh == D) return rope_fwd_t<TT, D>(qkv, rq, qT, kT, vT, c, s, B, T_, Tp, H, eps, st);
+  if (Dh == D) return rope_fwd_t<TT, D>(qkv, rq, qT, kT, vT, c, s, B, T_, Tp, H, Hkv, eps, st);
   if (dtype == DT_BF16) { RF(bf16, 32) RF(bf16, 64) RF(bf16, 128) }
   else { RF(float, 32) RF(float, 64) RF(float, 128) }
 #undef RF
@@ -775,22 +788,22 @@ void rope_qknorm_fwd(int dtype, void* qkv, float* rq, void* qT, void* kT, void* 
 
 template <typename T, int DH>
 static void rope_bwd_t(void* dqkv, const void* qkv, const float* rq, const float* c, const float* s, int B, int T_,
-                       int H, hipStream_t st, unsigned* amax) {
+                       int H, int Hkv, hipStream_t st, unsigned* amax) {
   const int rows = B * T_;
   if constexpr (sizeof(T) == 2 && DH == 128) {
-    const long nvec = (long)rows * 2 * H;
+    const long nvec = (long)rows * (H + Hkv);
     hipLaunchKernelGGL(rope_qknorm_bwd128_kernel, dim3((unsigned)((nvec + 31) / 32)), dim3(256), 0, st, (bf16*)dqkv,
-                       (const bf16*)qkv, rq, c, s, nvec, T_, H, amax);
+                       (const bf16*)qkv, rq, c, s, nvec, T_, H, Hkv, amax);
     return;
   }
   hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, DH>), dim3((rows + 3) / 4), dim3(256), 0, st, (T*)dqkv,
-                     (const T*)qkv, rq, c, s, rows, T_, H, amax);
+                     (const T*)qkv, rq, c, s, rows, T_, H, Hkv, amax);
 }
 
 void rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const float* rq, const float* c, const float* s,
-                     int B, int T_, int H, int Dh, hipStream_t st, unsigned* amax) {
+                     int B, int T_, int H, int Hkv, int Dh, hipStream_t st, unsigned* amax) {
 #define RB(TT, D) \
-  if (Dh == D) return rope_bwd_t<TT, D>(dqkv, qkv, rq, c, s, B, T_, H, st, amax);
+  if (Dh == D) return rope_bwd_t<TT, D>(dqkv, qkv, rq, c, s, B, T_, H, Hkv, st, amax);
   if (dtype == DT_BF16) { RB(bf16, 32) RB(bf16, 64) RB(bf16, 128) }
   else { RB(float, 32) RB(float, 64) RB(float, 128) }
 #undef RB

@@ -154,23 +154,25 @@ void decode_add_rmsnorm(float* h, const float* part, int nsplit, int B, int d, v
 }
 
 // ------------------------------------------------------------------ prefill: cache fill
-// kc/vc[b][h][t][:] = k^ / v of row (b, t) of qkv [B*T][3d], t < T.
+// kc/vc[b][g][t][:] = k^ / v of key/value head g of row (b, t) of qkv
+// [B*T][d + 2*Hkv*Dh], t < T.
 __global__ __launch_bounds__(256) void kv_fill_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ kc,
-                                                      bf16* __restrict__ vc, int T, int H, int Dh, int Tmax) {
+                                                      bf16* __restrict__ vc, int T, int H, int Hkv, int Dh,
+                                                      int Tmax) {
   const int t = blockIdx.x, b = blockIdx.y;
-  const int d = H * Dh;
-  const bf16* row = qkv + ((long)b * T + t) * 3 * d;
-  for (int i = threadIdx.x * 8; i < 2 * d; i += 256 * 8) {
-    const int part = i / d, c = i % d, h = c / Dh, e = c % Dh;
+  const int d = H * Dh, dkv = Hkv * Dh;
+  const bf16* row = qkv + ((long)b * T + t) * (d + 2 * dkv);
+  for (int i = threadIdx.x * 8; i < 2 * dkv; i += 256 * 8) {
+    const int part = i / dkv, c = i % dkv, g = c / Dh, e = c % Dh;
     const bf16x8 v = *(const bf16x8*)(row + d + i);
-    bf16* dst = (part == 0 ? kc : vc) + (((long)b * H + h) * Tmax + t) * Dh + e;
+    bf16* dst = (part == 0 ? kc : vc) + (((long)b * Hkv + g) * Tmax + t) * Dh + e;
     *(bf16x8*)dst = v;
   }
 }
 
-void kv_fill(const void* qkv, void* kc, void* vc, int B, int T, int H, int Dh, int Tmax, hipStream_t st) {
-  hipLaunchKernelGGL(kv_fill_kernel, dim3(T, B), dim3(256), 0, st, (const bf16*)qkv, (bf16*)kc, (bf16*)vc, T, H, Dh,
-                     Tmax);
+void kv_fill(const void* qkv, void* kc, void* vc, int B, int T, int H, int Hkv, int Dh, int Tmax, hipStream_t st) {
+  hipLaunchKernelGGL(kv_fill_kernel, dim3(T, B), dim3(256), 0, st, (const bf16*)qkv, (bf16*)kc, (bf16*)vc, T, H, Hkv,
+                     Dh, Tmax);
 }
 
 // ------------------------------------------------------------------ attention over the cache
@@ -219,8 +221,8 @@ template <int DH>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ kc,
                                                                 bf16* __restrict__ vc, float* __restrict__ part,
                                                                 const float* __restrict__ cosb,
-                                                                const float* __restrict__ sinb, int H, int Tmax,
-                                                                const int* __restrict__ posp, int window,
+                                                                const float* __restrict__ sinb, int H, int Hkv,
+                                                                int Tmax, const int* __restrict__ posp, int window,
                                                                 float scale_log2, float eps) {
   constexpr int LPK = DH / 8, KPI = 64 / LPK, HALF = DH / 2;
   __shared__ float red[4][DH + 1];
@@ -237,8 +239,10 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16* __re
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kg = lane / LPK, li = lane % LPK;
   const bool first = li < LPK / 2;
-  const int d = H * DH;
-  const bf16* row = qkv + (long)b * 3 * d + h * DH + li * 8;
+  const int d = H * DH, dkv = Hkv * DH;
+  const int G = H / Hkv, hk = h / G;   // key/value head of query head h
+  const bf16* row = qkv + (long)b * (d + 2 * dkv) + h * DH + li * 8;
+  const bf16* kvrow = qkv + (long)b * (d + 2 * dkv) + d + hk * DH + li * 8;
   float cs[8], sn[8];
   {
     const float* c = cosb + (long)pos * HALF + (li % (LPK / 2)) * 8;
@@ -251,15 +255,16 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const bf16* __re
   }
   float q[8];
   rope_norm8<LPK>(*(const bf16x8*)row, cs, sn, first, eps, q);
-  const long base = ((long)b * H + h) * Tmax * DH;
+  const long base = ((long)b * Hkv + hk) * Tmax * DH;
   bf16x8 knew = bf16x8{}, vnew = bf16x8{};
   if (has_pos) {   // uniform over the work-group
     float k[8];
-    rope_norm8<LPK>(*(const bf16x8*)(row + d), cs, sn, first, eps, k);
+    rope_norm8<LPK>(*(const bf16x8*)kvrow, cs, sn, first, eps, k);
 #pragma unroll
     for (int e = 0; e < 8; ++e) knew[e] = (bf16)k[e];
-    vnew = *(const bf16x8*)(row + 2 * d);
-    if (wave == 0 && kg == 0) {
+    vnew = *(const bf16x8*)(kvrow + dkv);
+    // the first query head of the group writes the shared key and value
+    if (wave == 0 && kg == 0 && h % G == 0) {
       *(bf16x8*)(kc + base + (long)pos * DH + li * 8) = knew;
       *(bf16x8*)(vc + base + (long)pos * DH + li * 8) = vnew;
     }
@@ -321,17 +326,17 @@ __global__ __launch_bounds__(DH) void attn_decode_combine_kernel(const float* __
 }
 
 int attn_decode(const void* qkv, void* kc, void* vc, const float* cosb, const float* sinb, float* part, void* o,
-                int B, int H, int Dh, int Tmax, const int* posp, int window, float eps, hipStream_t st) {
+                int B, int H, int Hkv, int Dh, int Tmax, const int* posp, int window, float eps, hipStream_t st) {
   const int nsplit = (std::min(window, Tmax) + ATT_SPLIT - 1) / ATT_SPLIT;
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)Dh));
   const dim3 g1(nsplit, H, B), g2(H, B);
   if (Dh == 128) {
     hipLaunchKernelGGL(attn_decode_split_kernel<128>, g1, dim3(256), 0, st, (const bf16*)qkv, (bf16*)kc, (bf16*)vc,
-                       part, cosb, sinb, H, Tmax, posp, window, sl2, eps);
+                       part, cosb, sinb, H, Hkv, Tmax, posp, window, sl2, eps);
     hipLaunchKernelGGL(attn_decode_combine_kernel<128>, g2, dim3(128), 0, st, part, (bf16*)o, H, nsplit);
   } else if (Dh == 64) {
     hipLaunchKernelGGL(attn_decode_split_kernel<64>, g1, dim3(256), 0, st, (const bf16*)qkv, (bf16*)kc, (bf16*)vc,
-                       part, cosb, sinb, H, Tmax, posp, window, sl2, eps);
+                       part, cosb, sinb, H, Hkv, Tmax, posp, window, sl2, eps);
     hipLaunchKernelGGL(attn_decode_combine_kernel<64>, g2, dim3(64), 0, st, part, (bf16*)o, H, nsplit);
   } else {
     return -1;

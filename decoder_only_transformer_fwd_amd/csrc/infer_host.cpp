@@ -14,7 +14,7 @@ using namespace gm;
 namespace gm __attribute__((visibility("hidden"))) {
 
 // ------------------------------------------------------------------ inference
-size_t kv_layer_elems(const Shape& s) { return (size_t)s.B * s.H * s.T * s.Dh; }
+size_t kv_layer_elems(const Shape& s) { return (size_t)s.B * s.Hkv * s.T * s.Dh; }
 
 int check_infer(gpt_model& m) {
   if (m.s.dtype != DT_BF16) return fail(GPT_EINVAL, "inference runs on bf16 parameters (GPT_BF16 or GPT_FP8 models)");
@@ -47,10 +47,10 @@ int run_prefill(gpt_model& m, const int32_t* tokens, int n, char* kv, float* log
   if (rc) return rc;
   const Shape& s = m.s;
   const size_t kvl = kv_layer_elems(s);
-  prof_begin(m, "prefill_kv_fill", (double)sp.BT * 2.0 * s.d * 2.0 * 2.0, 1, "kv_fill_kernel");
+  prof_begin(m, "prefill_kv_fill", (double)sp.BT * 2.0 * s.dkv * 2.0 * 2.0, 1, "kv_fill_kernel");
   for (int l = 0; l < s.L; ++l) {
     uint16_t* kc = (uint16_t*)kv + (size_t)2 * l * kvl;
-    kv_fill(m.ws + m.lay[l].qkv, kc, kc + kvl, s.B, n, s.H, s.Dh, s.T, m.st);
+    kv_fill(m.ws + m.lay[l].qkv, kc, kc + kvl, s.B, n, s.H, s.Hkv, s.Dh, s.T, m.st);
   }
   prof_end(m);
   // rows b*n + n - 1 of the final normalised activations
@@ -95,11 +95,11 @@ int run_decode(gpt_model& m, int pos, char* kv, float* logits) {
     uint16_t* kc = (uint16_t*)kv + (size_t)2 * l * kvl;
     uint16_t* vc = kc + kvl;
     addnorm(n1);
-    if ((rc = dec_gemm(m, "decode_qkv", EPI_STORE, n1, d, d, wp(P.Wqkv[l]), 3 * d, qkv, 3 * d))) return rc;
+    if ((rc = dec_gemm(m, "decode_qkv", EPI_STORE, n1, d, d, wp(P.Wqkv[l]), s.Nqkv, qkv, s.Nqkv))) return rc;
     const int lo = std::max(0, pos - s.win[l] + 1);
-    prof_begin(m, "decode_attention", (double)B * H * (pos - lo + 1) * Dh * 4.0, 1,
+    prof_begin(m, "decode_attention", (double)B * s.Hkv * (pos - lo + 1) * Dh * 4.0, 1,
                "attn_decode_split_kernel + attn_decode_combine_kernel");
-    if (attn_decode(qkv, kc, vc, at<float>(m, m.cosb), at<float>(m, m.sinb), dpart, o, B, H, Dh, s.T, posp,
+    if (attn_decode(qkv, kc, vc, at<float>(m, m.cosb), at<float>(m, m.sinb), dpart, o, B, H, s.Hkv, Dh, s.T, posp,
                     s.win[l], s.eps, st))
       return fail(GPT_EINVAL, "decode attention head_dim");
     prof_end(m);

@@ -112,11 +112,15 @@ void rmsnorm_fwd(int dtype, const float* x, void* y, float* rstd, int rows, int 
 // only: norm_chunks(d) != 0); returns -1 for a combination not built.
 int rmsnorm_bwd(int dtype, const void* dy, int dy_act, const void* y, const float* rstd, float* dx,
                 void* dx_act, int rows, int d, int accumulate, hipStream_t st, unsigned* amax = nullptr);
+// qkv [B*T][H*Dh + 2*Hkv*Dh]: q heads, then k heads, then v heads; rstd_qk
+// [B*T][H + Hkv] (q heads, then k heads); qT [B][H][Dh][Tp], kT, vT
+// [B][Hkv][Dh][Tp].
 void rope_qknorm_fwd(int dtype, void* qkv, float* rstd_qk, void* qT, void* kT, void* vT,
-                     const float* cosb, const float* sinb, int B, int T, int Tp, int H, int Dh,
+                     const float* cosb, const float* sinb, int B, int T, int Tp, int H, int Hkv, int Dh,
                      float eps, hipStream_t st);
 void rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const float* rstd_qk, const float* cosb,
-                     const float* sinb, int B, int T, int H, int Dh, hipStream_t st, unsigned* amax = nullptr);
+                     const float* sinb, int B, int T, int H, int Hkv, int Dh, hipStream_t st,
+                     unsigned* amax = nullptr);
 void attn_bwd_pre(int dtype, const void* dO, const void* O, float* Dv, void* dOT, int B, int T, int Tp,
                   int H, int Dh, hipStream_t st);
 void xent_reduce(const float* part, const float* tgt, int rows, int nblk, float* lse, float* row_loss,
@@ -169,15 +173,17 @@ int skinny_gemm(int epi, const void* x, long ldx, int B, int K, const void* W, i
 // h [B][d] fp32 += sum of nsplit (<= 8) partials part[s][B][d] (in order),
 // then y = bf16 RMSNorm(h)
 void decode_add_rmsnorm(float* h, const float* part, int nsplit, int B, int d, void* y, float eps, hipStream_t st);
-// caches[b][h][t] = k^ / v of qkv row (b, t) for t < T (qkv [B*T][3d])
-void kv_fill(const void* qkv, void* kc, void* vc, int B, int T, int H, int Dh, int Tmax, hipStream_t st);
+// caches[b][g][t] = k^ / v of key/value head g of qkv row (b, t) for t < T
+// (qkv [B*T][d + 2*Hkv*Dh])
+void kv_fill(const void* qkv, void* kc, void* vc, int B, int T, int H, int Hkv, int Dh, int Tmax, hipStream_t st);
 // o [B][d] = attention of the new token over cached keys max(0, pos -
-// window + 1) .. pos, pos = *posp (device).  qkv [B][3d] holds the new
-// token's raw q, k, v: its rotary embedding and QK norm are applied here, and
-// k^ and v are written into the caches [B][H][Tmax][Dh] at pos.
+// window + 1) .. pos, pos = *posp (device).  qkv [B][d + 2*Hkv*Dh] holds the
+// new token's raw q, k, v: its rotary embedding and QK norm are applied here,
+// and k^ and v are written into the caches [B][Hkv][Tmax][Dh] at pos; query
+// head h reads key/value head h / (H / Hkv).
 // part: B * H * ceil(min(window, Tmax) / 128) * (Dh + 1) floats
 int attn_decode(const void* qkv, void* kc, void* vc, const float* cosb, const float* sinb, float* part, void* o,
-                int B, int H, int Dh, int Tmax, const int* posp, int window, float eps, hipStream_t st);
+                int B, int H, int Hkv, int Dh, int Tmax, const int* posp, int window, float eps, hipStream_t st);
 // tok[0..B) = tokens[0..B), *posp = pos, *flag = 0 (one small kernel)
 void decode_stage(const int32_t* tokens, int B, int pos, int32_t* tok, int* posp, int* flag, hipStream_t st);
 
@@ -193,24 +199,28 @@ void fp8_quantize(int fmt, const void* x, int R, int C, const unsigned* amax, fl
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
-  const void* qkv;   // [B*T][3*d]: q^ at col h*Dh, k^ at d + h*Dh, v at 2d + h*Dh
+  // [B*T][ldqkv], ldqkv = d + 2*Hkv*Dh: q^ of head h at col h*Dh, k^ of
+  // key/value head g at d + g*Dh, v at d + Hkv*Dh + g*Dh; query head h uses
+  // key/value head h / (H / Hkv)
+  const void* qkv;
   const void* qT;    // [B][H][Dh][Tp]
-  const void* kT;
+  const void* kT;    // [B][Hkv][Dh][Tp]
   const void* vT;
   void* o;           // [B*T][d]
   float* lse2;       // [B][H][Tp], log2 domain
   const void* dO;    // [B*T][d]
   const void* dOT;   // [B][H][Dh][Tp]
   const float* Dv;   // [B][H][Tp] rowsum(dO * O)
-  void* dqkv;        // [B*T][3*d]
-  int B, T, Tp, H, d, window;
+  void* dqkv;        // [B*T][ldqkv]
+  int B, T, Tp, H, Hkv, d, ldqkv, window;
   float scale_log2;  // log2(e) / sqrt(Dh)
   unsigned* amax_o;   // forward: if set, max |stored o| (float bits)
   unsigned* amax_dv;  // dV pass: if set, max |stored dv| (float bits)
   float scale;       // 1 / sqrt(Dh)
 };
 int attn_fwd(int dtype, int Dh, const AttnArgs& a, hipStream_t st);
-// part 0: dV, part 1: dK (one work-group per 128-key tile); part 2: dQ (per 128-query tile).
+// part 0: dV, part 1: dK (one work-group per 128-key tile of a key/value
+// head, summing over its query heads); part 2: dQ (per 128-query tile).
 int attn_bwd(int dtype, int Dh, const AttnArgs& a, int part, hipStream_t st);
 
 }  // namespace gk

@@ -38,6 +38,7 @@ inline size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a;
 
 struct Shape {
   int L, d, H, Dh, F, V, T, B, BT, Tp, dtype, es;
+  int Hkv, dkv, Nqkv;   // key/value heads, their width Hkv*Dh, and the fused QKV width d + 2*dkv
   bool fp8;   // linear layers (QKV, O, W1, W2) in fp8; everything else as bf16
   float eps, base;
   std::vector<int> win;   // keys visible per layer

@@ -29,8 +29,12 @@ def _windows(s):
 
 
 def scaling_params(s) -> int:
+    """Matrix parameters except the token embedding: per layer Wq, Wo [d, d],
+    Wk, Wv [Hkv*Dh, d] (d x d without grouped-query attention), W1, W2; plus
+    the lm_head."""
     d, f, v, L = s.d_model, s.mlp_hidden, s.vocab, s.depth
-    return L * (4 * d * d + 2 * d * f) + v * d
+    dkv = getattr(s, "kv_heads", s.n_head) * s.head_dim
+    return L * (2 * d * d + 2 * dkv * d + 2 * d * f) + v * d
 
 
 def flops_per_token(s) -> int:

@@ -13,7 +13,8 @@
  *   - "supa beginna nanochat" (discussions/677), troubleshooting: mean
  *     cross-entropy over rows of T+1 tokens split into inputs and targets.
  * Per layer: a = N(h); q,k,v = a Wq^T, a Wk^T, a Wv^T; q^ = N_h(RoPE(q)),
- * k^ = N_h(RoPE(k)); o = softmax(q^ k^T / sqrt(Dh) | window mask) v;
+ * k^ = N_h(RoPE(k)); o = softmax(q^ k^T / sqrt(Dh) | window mask) v, head by
+ * head (with n_kv_head < n_head, groups of query heads share k and v);
  * h += o Wo^T; h += relu(N(h) W1^T)^2 W2^T.  Then loss = mean CE(N(h) U^T, y).
  * N is parameter-free RMSNorm with eps = norm_eps; RoPE rotates the pairs
  * (x[i], x[i+Dh/2]) by t * base^(-2i/Dh); a layer of window W lets query i
@@ -66,6 +67,11 @@ typedef struct gpt_config {
   void* workspace;      /* device, caller-owned, >= gpt_workspace_bytes()     */
   size_t workspace_bytes;
   void* stream;         /* hipStream_t on which all work is enqueued (NULL = default) */
+  int32_t n_kv_head;    /* Hkv, key/value heads (grouped-query attention): a
+                           divisor of n_head; 0 means n_head (plain multi-head
+                           attention).  Query head h uses key/value head
+                           h / (n_head / Hkv) (nanochat User Guide, section 10,
+                           base model paragraph: Group-Query Attention). */
 } gpt_config;
 /* Precision policy.  GPT_FP32: weights, activations and every product in
  * fp32 (fp32 MFMA).  GPT_BF16: bf16 weights and activations, fp32
@@ -80,10 +86,11 @@ typedef struct gpt_config {
  * prior art; the format split and scaling rule are this library's. */
 
 /* Parameter layout.  One contiguous buffer, tensors in this order:
- *   E [V, d]; for l in 0..L-1: Wq, Wk, Wv [d, d], Wo [d, d], W1 [F, d],
- *   W2 [d, F]; U [V, d].
+ *   E [V, d]; for l in 0..L-1: Wq [d, d], Wk, Wv [Hkv*Dh, d], Wo [d, d],
+ *   W1 [F, d], W2 [d, F]; U [V, d].
  * Shapes are [out, in].  Each tensor starts at an element offset that is a
- * multiple of 128; Wq, Wk, Wv of a layer are adjacent (one [3d, d] block).
+ * multiple of 128; Wq, Wk, Wv of a layer are adjacent (one
+ * [d + 2*Hkv*Dh, d] block; [3d, d] without grouping).
  * The weight buffer holds elements of the parameter type (fp32 for GPT_FP32,
  * bf16 otherwise); the gradient buffer uses the same element offsets with
  * fp32 elements. */

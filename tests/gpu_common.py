@@ -49,6 +49,17 @@ SMALL = {
                            vocab=1000, seq_len=224, batch=2, window=64, window_pattern="SL",
                            precision="fp8", token_dist="zipf"),
     "d24_fp8_short": gi.preset("d24-fp8", seq_len=384, batch=1, window=128),
+    # grouped-query attention: query heads sharing key/value heads
+    "gqa_fp32": gi.GPTShape("gqa_fp32", depth=2, d_model=128, n_head=4, head_dim=32, mlp_hidden=256,
+                            vocab=520, seq_len=150, batch=2, window=40, window_pattern="SL",
+                            precision="fp32", token_dist="uniform", n_kv_head=2),
+    "gqa_bf16": gi.GPTShape("gqa_bf16", depth=2, d_model=512, n_head=4, head_dim=128, mlp_hidden=1024,
+                            vocab=1000, seq_len=200, batch=2, window=64, window_pattern="SL",
+                            precision="bf16", token_dist="zipf", n_kv_head=1),
+    "d24_gqa_short": gi.preset("d24", seq_len=384, batch=1, window=128, n_kv_head=4),
+    "gqa_fp8": gi.GPTShape("gqa_fp8", depth=2, d_model=256, n_head=2, head_dim=128, mlp_hidden=1024,
+                           vocab=1000, seq_len=224, batch=2, window=64, window_pattern="SL",
+                           precision="fp8", token_dist="zipf", n_kv_head=1),
 }
 
 

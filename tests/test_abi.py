@@ -85,6 +85,8 @@ BAD = [
     dict(depth=0),
     dict(precision="fp8", seq_len=100, batch=1),  # fp8 needs B*T % 64 == 0
     dict(precision="fp8", head_dim=32, d_model=64, n_head=2),  # fp8 attention is bf16: Dh 64/128
+    dict(n_head=4, d_model=128, n_kv_head=3),    # key/value heads must divide the query heads
+    dict(n_kv_head=4),                           # more key/value heads than query heads
     dict(norm_eps=0.0),                          # the norms need eps > 0
     dict(norm_eps=-1e-6),
     dict(rope_base=0.0),
@@ -205,3 +207,19 @@ def test_noalloc_rejects_partials_beyond_its_scratch(M):
         M.gpt_gemm_noalloc(1, 0, 64, 64, 64, 256, 256, 256, splits=2)   # KK layout is not split
     with pytest.raises(M.GPTError):
         M.gpt_gemm_noalloc(1, 2, 64, 64, 64, 0, 256, 256, splits=2)     # NULL operand
+
+
+@pytest.mark.parametrize("kv", [1, 2, 4])
+def test_grouped_query_layout(M, kv):
+    """Wk and Wv are [Hkv*Dh, d] and the fused QKV block stays contiguous."""
+    s = gi.preset("d24").replace(n_kv_head=kv)
+    layout, total = M.gpt_param_layout(M.make_config(s))
+    assert [(n, (r, c)) for n, _, r, c in layout] == gi.param_shapes(s)
+    offs = {n: o for n, o, _, _ in layout}
+    d, dkv = s.d_model, kv * s.head_dim
+    for l in range(s.depth):
+        assert offs[f"L{l}.Wk"] == offs[f"L{l}.Wq"] + d * d
+        assert offs[f"L{l}.Wv"] == offs[f"L{l}.Wq"] + d * d + dkv * d
+    assert M.gpt_kv_cache_bytes(M.make_config(s)) == 2 * s.depth * s.batch * kv * s.seq_len * s.head_dim * 2
+    # fewer key/value heads need less workspace
+    assert M.gpt_workspace_bytes(M.make_config(s)) < M.gpt_workspace_bytes(M.make_config(gi.preset("d24")))

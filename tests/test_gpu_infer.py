@@ -29,6 +29,10 @@ INFER = {
     "dh64": gi.GPTShape("dh64", depth=3, d_model=192, n_head=3, head_dim=64, mlp_hidden=768, vocab=520,
                         seq_len=320, batch=5, window=100, window_pattern="SSL", precision="bf16",
                         token_dist="uniform"),
+    # grouped-query attention: 4 query heads share 2 key/value heads
+    "gqa_dh64": gi.GPTShape("gqa_dh64", depth=2, d_model=256, n_head=4, head_dim=64, mlp_hidden=512, vocab=520,
+                            seq_len=300, batch=3, window=90, window_pattern="SL", precision="bf16",
+                            token_dist="uniform", n_kv_head=2),
 }
 
 

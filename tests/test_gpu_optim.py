@@ -82,7 +82,7 @@ def _compare(name, d_gpu, d_ref, is_matrix, lr):
     return 1.0
 
 
-@pytest.mark.parametrize("name", ["tiny", "bf16_mid"])
+@pytest.mark.parametrize("name", ["tiny", "bf16_mid", "gqa_bf16"])
 def test_optimizer_steps_match_oracle(name):
     import decoder_only_transformer_fwd_amd as G
     from oracle import optim_oracle as OO
