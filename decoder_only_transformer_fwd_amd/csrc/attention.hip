@@ -94,9 +94,12 @@ __device__ __forceinline__ typename Mfma<T>::frag acc_frag(const floatx16 (&p)[N
 
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
-__device__ __forceinline__ bool visible(int i, int j, int W, int Tn) {
-  return j <= i && i - j < W && i < Tn;
-}
+// Visibility from the offset i - j alone: 0 <= i - j < W, one unsigned
+// compare.  Positions past T need no test: their query, key, value, dO and
+// D entries are zero (padded copies, zero-filled tile loads), so they add
+// nothing to any stored result, and a valid query never sees a padded key
+// (j <= i < T).
+__device__ __forceinline__ bool visible_off(int i_minus_j, int W) { return (unsigned)i_minus_j < (unsigned)W; }
 
 // ------------------------------------------------------------------ forward
 // Work-group: 4 waves x 32 queries; key tiles of 64 (K rows and V^T columns)
@@ -190,14 +193,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < KS; ++k) sc[jb] = MF::mma(row_frag<T, KROW>(ks, jb * 32 + l32, k, g), qf[k], sc[jb]);
       }
-      const bool need_mask = (j0 + BKV - 1 > iw0) || (iw0 + 31 - j0 >= W) || (j0 + BKV > Tn) || (iw0 + 31 >= Tn);
+      const bool need_mask = (j0 + BKV - 1 > iw0) || (iw0 + 31 - j0 >= W);
       if (need_mask) {
+        const int dij = i - j0;   // i - j of key row jb * 32 + acc_row(r, g)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float x = __builtin_fmaf(sc[jb][r], c, -M);
-            sc[jb][r] = visible(i, j0 + jb * 32 + acc_row(r, g), W, Tn) ? x : -INFINITY;
+            sc[jb][r] = visible_off(dij - jb * 32 - acc_row(r, g), W) ? x : -INFINITY;
           }
       } else {
 #pragma unroll
@@ -265,11 +269,16 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
   constexpr int KS = DH / MF::KM;
   constexpr int PS = BQ / MF::KM;
   constexpr int DB = DH / 32;
-  // stage layout: Q rows | dO rows (dK) | Q^T (dK) | dO^T (dV)
+  // stage layout: Q rows | dO rows (dK) | Q^T (dK) | dO^T (dV) | lse | D (dK);
+  // lse and D of the tile's BQ queries arrive with the tile (one 64-lane
+  // copy each, 1 KB of LDS of which the first BQ * 4 bytes are used)
   constexpr int OFF_DO = BQ * RROW;
   constexpr int OFF_QT = OFF_DO + (DO_DK ? BQ * RROW : 0);
   constexpr int OFF_DOT = OFF_QT + (DO_DK ? DH * TROW : 0);
-  constexpr int STAGE = OFF_DOT + (DO_DV ? DH * TROW : 0);
+  constexpr int OFF_LSE = OFF_DOT + (DO_DV ? DH * TROW : 0);
+  constexpr int OFF_D = OFF_LSE + 1024;
+  constexpr int STAGE = OFF_D + (DO_DK ? 1024 : 0);
+  static_assert(BQ / 4 <= 64, "one 64-lane copy holds the tile's lse / D");
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
@@ -303,10 +312,24 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
   const int iend = min(Tn, j0 + BKV - 1 + W);
   const int nq = iend > ib ? (iend - ib + BQ - 1) / BQ : 0;
 
+  // The G query heads that share this key/value head are walked one after
+  // another, as one sequence of G * nq query tiles.  Each operand's buffer
+  // covers the whole group (its first head's columns / rows onwards), and a
+  // head's offset within it goes into the scalar offset of the copies.
+  const int hq0 = hk * G;                  // first query head of the group
+  const long hoff0 = (long)b * a.H + hq0;
   RowDma<BQ, RROW, 4> lq, ldo;
   RowDma<DH, TROW, 4> lqt, ldot;
-  const float* lseb;
-  const float* Db;
+  lq.init(qkv + (((long)b * Tn) * row3 + hq0 * DH) * ES, (int)(row3 * ES),
+          (long)(Tn - 1) * row3 * ES + (long)G * RROW, wave, lane);
+  if constexpr (DO_DK) {
+    ldo.init((const char*)a.dO + (((long)b * Tn) * d + hq0 * DH) * ES, d * ES,
+             (long)(Tn - 1) * d * ES + (long)G * RROW, wave, lane);
+    lqt.init((const char*)a.qT + hoff0 * DH * Tp * ES, Tp * ES, (long)G * DH * Tp * ES, wave, lane);
+  }
+  if constexpr (DO_DV) ldot.init((const char*)a.dOT + hoff0 * DH * Tp * ES, Tp * ES, (long)G * DH * Tp * ES, wave, lane);
+  const __amdgpu_buffer_rsrc_t rs_lse = uniform_rsrc(a.lse2 + hoff0 * Tp, G * Tp * 4);
+  const __amdgpu_buffer_rsrc_t rs_D = uniform_rsrc(a.Dv + hoff0 * Tp, G * Tp * 4);
 
   floatx16 dk[DO_DK ? DB : 1], dv[DO_DV ? DB : 1];
 #pragma unroll
@@ -317,50 +340,44 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
       if constexpr (DO_DV) dv[x][r] = 0.f;
     }
 
-  auto issue = [&](int i0, int stage) {
+  // tile itx of the sequence: query head hq0 + gq, queries from i0
+  auto issue = [&](int itx, int stage) {
+    const int gq = itx / nq, i0 = ib + (itx - gq * nq) * BQ;
     char* st = smem + stage * STAGE;
-    lq.issue(st, i0 * (int)(row3 * ES), wave);
+    lq.issue(st, i0 * (int)(row3 * ES) + gq * RROW, wave);
     if constexpr (DO_DK) {
-      ldo.issue(st + OFF_DO, i0 * d * ES, wave);
-      lqt.issue(st + OFF_QT, i0 * ES, wave);
+      ldo.issue(st + OFF_DO, i0 * d * ES + gq * RROW, wave);
+      lqt.issue(st + OFF_QT, (gq * DH * Tp + i0) * ES, wave);
     }
-    if constexpr (DO_DV) ldot.issue(st + OFF_DOT, i0 * ES, wave);
+    if constexpr (DO_DV) ldot.issue(st + OFF_DOT, (gq * DH * Tp + i0) * ES, wave);
+    if (wave == 0) {
+      const int off = lane < BQ / 4 ? (gq * Tp + i0 + 4 * lane) * 4 : (int)0x80000000;
+      dma16(rs_lse, st + OFF_LSE, off);
+      if constexpr (DO_DK) dma16(rs_D, st + OFF_D, off);
+    }
   };
 
-  // the query heads that share this key/value head, one after another
-  for (int gq = 0; gq < G; ++gq) {
-  const int hq = hk * G + gq;
-  const long hoff = ((long)b * a.H + hq);
-  lq.init(qkv + (((long)b * Tn) * row3 + hq * DH) * ES, (int)(row3 * ES), (long)(Tn - 1) * row3 * ES + RROW, wave,
-          lane);
-  if constexpr (DO_DK) {
-    ldo.init((const char*)a.dO + (((long)b * Tn) * d + hq * DH) * ES, d * ES, (long)(Tn - 1) * d * ES + RROW, wave,
-             lane);
-    lqt.init((const char*)a.qT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
-  }
-  if constexpr (DO_DV) ldot.init((const char*)a.dOT + hoff * DH * Tp * ES, Tp * ES, (long)DH * Tp * ES, wave, lane);
-  // lse / D of the queries this lane's accumulator rows cover: i0 + 32qb + 8q + 4g + e
-  lseb = a.lse2 + hoff * Tp + 4 * g;
-  Db = a.Dv + hoff * Tp + 4 * g;
-  if (gq > 0) __syncthreads();   // every wave is done with the previous head's stages
-  if (nq > 0) issue(ib, 0);
-  for (int it = 0; it < nq; ++it) {
-    const int i0 = ib + it * BQ;
+  const int ntot = G * nq;
+  if (ntot > 0) issue(0, 0);
+  for (int it = 0; it < ntot; ++it) {
+    const int gq = it / nq;
+    const int i0 = ib + (it - gq * nq) * BQ;
     const int s = it & 1;
     __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
-    floatx4 lse_c[QB][4], D_c[DO_DK ? QB : 1][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        lse_c[qb][q] = *(const floatx4*)(lseb + i0 + 32 * qb + 8 * q);
-        if constexpr (DO_DK) D_c[qb][q] = *(const floatx4*)(Db + i0 + 32 * qb + 8 * q);
-      }
-    if (it + 1 < nq) issue(i0 + BQ, s ^ 1);
+    if (it + 1 < ntot) issue(it + 1, s ^ 1);
     const char* qs = smem + s * STAGE;
     const bool skip = i0 + BQ - 1 < jw0 || i0 - (jw0 + 31) >= W || jw0 >= Tn || i0 >= Tn;
     if (!skip) {
+      // lse / D of the queries this lane's accumulator rows cover: i0 + 32qb + 8q + 4g + e
+      floatx4 lse_c[QB][4], D_c[DO_DK ? QB : 1][4];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          lse_c[qb][q] = *(const floatx4*)(qs + OFF_LSE + (32 * qb + 8 * q + 4 * g) * 4);
+          if constexpr (DO_DK) D_c[qb][q] = *(const floatx4*)(qs + OFF_D + (32 * qb + 8 * q + 4 * g) * 4);
+        }
       floatx16 sc[QB], dp[DO_DK ? QB : 1];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -377,17 +394,18 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
           sc[qb] = MF::mma(row_frag<T, RROW>(qs, qb * 32 + l32, k, g), kf[k], sc[qb]);
           if constexpr (DO_DK) dp[qb] = MF::mma(row_frag<T, RROW>(qs + OFF_DO, qb * 32 + l32, k, g), vf[k], dp[qb]);
         }
-      const bool need_mask = (i0 < jw0 + 31) || (i0 + BQ - 1 - jw0 >= W) || (i0 + BQ > Tn) || (jw0 + 31 >= Tn);
+      const bool need_mask = (i0 < jw0 + 31) || (i0 + BQ - 1 - jw0 >= W);
       // invisible pairs get a -inf exponent (exp2 -> 0); the exponentials
       // themselves are unconditional so the loop stays branch-free
       if (need_mask) {
+        const int dij = i0 - j;   // i - j of accumulator row il is dij + il
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int il = qb * 32 + acc_row(r, g);
             const float x = __builtin_fmaf(sc[qb][r], c, -lse_c[qb][r >> 2][r & 3]);
-            sc[qb][r] = visible(i0 + il, j, W, Tn) ? x : -INFINITY;
+            sc[qb][r] = visible_off(dij + il, W) ? x : -INFINITY;
           }
       } else {
 #pragma unroll
@@ -415,7 +433,6 @@ __global__ __launch_bounds__(256, MODE == 1 ? 3 : 2) void attn_bwd_dkdv_kernel(A
       }
     }
   }
-  }   // query heads of the group
 
   float vm = 0.f;
   if (j < Tn) {
@@ -534,13 +551,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a) {
         sc[0] = MF::mma(row_frag<T, RROW>(ks, l32, k, g), qf[k], sc[0]);
         dp[0] = MF::mma(row_frag<T, RROW>(vs, l32, k, g), df[k], dp[0]);
       }
-      const bool need_mask = (j0 + BKV - 1 > iw0) || (iw0 + 31 - j0 >= W) || (j0 + BKV > Tn) || (iw0 + 31 >= Tn);
+      const bool need_mask = (j0 + BKV - 1 > iw0) || (iw0 + 31 - j0 >= W);
       // invisible pairs get a -inf exponent (exp2 -> 0), branch-free
       if (need_mask) {
+        const int dij = i - j0;   // i - j of accumulator row r is dij - acc_row(r, g)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = __builtin_fmaf(sc[0][r], c, -lse_i);
-          sc[0][r] = visible(i, j0 + acc_row(r, g), W, Tn) ? x : -INFINITY;
+          sc[0][r] = visible_off(dij - acc_row(r, g), W) ? x : -INFINITY;
         }
       } else {
 #pragma unroll
