@@ -310,7 +310,9 @@ int build_layout(gpt_model& m) {
     L.lse2 = take((size_t)s.B * s.H * s.Tp * 4);
     L.n2 = take(BT * s.d * A);
     L.rstd2 = take(BT * 4);
-    L.u = take(BT * s.F * A);
+    // fp8: u is kept in fp32, so that du = dg * 2 relu(u) is computed from the
+    // value the forward encoded
+    L.u = take(BT * s.F * (s.fp8 ? 4 : A));
     L.g = take(BT * s.F * A);
   }
   m.h = take(BT * s.d * 4);
@@ -332,7 +334,7 @@ int build_layout(gpt_model& m) {
   m.dtok = take((size_t)s.B * 4);
   m.dsplit = take((size_t)DEC_KSPLIT * s.B * std::max(s.d, s.F) * 4);
   m.dpos = take(64);
-  m.dz = take(BT * s.V * A);
+  m.dz = take(BT * std::min(s.V, VOCAB_CHUNK) * A);   // one vocabulary chunk of the logit gradient
   m.dm = take(BT * s.d * 4);
   m.dh = take(BT * s.d * 4);
   m.dhA = take(BT * s.d * A);
@@ -349,8 +351,10 @@ int build_layout(gpt_model& m) {
     const TailPlan tp = plan_tail(s.dtype, layout, EPI_STORE_F32, M, N, K);
     if (tp.n1 > 0) need = std::max(need, (size_t)tp.splits * M * (N - tp.n1 * 256));
   };
-  consider(LAYOUT_KN, s.BT, s.d, s.V);
-  consider(LAYOUT_MN, s.V, s.d, s.BT);
+  // the lm_head's products run one vocabulary chunk at a time
+  const int vc = std::min(s.V, VOCAB_CHUNK);
+  consider(LAYOUT_KN, s.BT, s.d, vc);
+  consider(LAYOUT_MN, vc, s.d, s.BT);
   consider(LAYOUT_KN, s.BT, s.F, s.d);
   consider(LAYOUT_MN, s.d, s.F, s.BT);
   consider(LAYOUT_KN, s.BT, s.d, s.F);
@@ -387,6 +391,7 @@ int build_layout(gpt_model& m) {
       }
     }
     m.q8row = take(BT * wide);
+    m.f32w = take(BT * s.F * 4);
     m.q8T = take(BT * wide);
     m.n_slots = 12 * s.L;
     m.amax = take((size_t)m.n_slots * AMAX_SLOT * 4);
@@ -472,6 +477,10 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   if (epi != EPI_STORE_F32 && !(wgrad && epi == EPI_ACCUM_F32)) g.splits = 1, g.k_split = K;
   if (g.splits > 1 && ldc != N) g.splits = 1, g.k_split = K;
   if (g.splits > 1) {
+    // the partial sums must fit the workspace's split-K region (sized by
+    // build_layout from the same plans); refuse rather than write past it
+    if ((size_t)g.splits * M * N > m.splitk_floats)
+      return fail(GPT_EINVAL, std::string(site) + ": split-K partials exceed the planned workspace region");
     a.part = at<float>(m, m.splitk);
     a.k_split = g.k_split;
     char label[128];
@@ -505,6 +514,8 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
     int ks = (K + tp.splits - 1) / tp.splits;
     ks = (ks + 63) / 64 * 64;
     const int sp = (K + ks - 1) / ks;
+    if ((size_t)sp * M * N2 > m.splitk_floats)
+      return fail(GPT_EINVAL, std::string(site) + ": split-K partials exceed the planned workspace region");
     t.k_split = ks;
     t.part = at<float>(m, m.splitk);
     gemm_kernel_label(dty, layout, EPI_PARTIAL, g.tile, label, sizeof label);
@@ -574,13 +585,17 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   // Weights get their own amax pass; every activation and gradient operand's
   // amax is folded in by the kernel that produces it (the slot's pointer is
   // passed to that kernel), so its quantisation reads it once.
+  // x32: the operand is fp32 (times rowscale[r], a norm's rstd, when given):
+  // activations and gradients are encoded from the fp32 values their
+  // producers computed, not from a bf16-rounded copy
   auto quant = [&](const char* site, int fmt, const void* x, int R, int C, int sl, void* q, void* qT,
-                   bool amax_done = true) {
-    prof_begin(m, site, (double)R * C * (qT ? 4.0 : 3.0), 1,
-               std::string(amax_done ? "" : "amax_kernel + ") + "quant_kernel<" + (fmt == FP8_E4M3 ? "0" : "1") + ">");
+                   bool amax_done = true, bool x32 = false, const float* rowscale = nullptr, bool relu2 = false) {
+    prof_begin(m, site, (double)R * C * ((x32 ? 4.0 : 2.0) + (qT ? 2.0 : 1.0)), 1,
+               std::string(amax_done ? "" : "amax_kernel + ") + "quant_kernel<" + (fmt == FP8_E4M3 ? "0" : "1") +
+                   (x32 ? ", float" : ", bf16") + (relu2 ? ", relu2>" : ">"));
     unsigned* am = amax8 + (size_t)sl * AMAX_SLOT;
     if (!amax_done) fp8_amax(x, (long)R * C, am, st);
-    fp8_quantize(fmt, x, R, C, am, sc8 + sl, q, qT, st);
+    fp8_quantize(fmt, x, R, C, am, sc8 + sl, q, qT, st, x32 ? 1 : 0, rowscale, relu2 ? 1 : 0);
     prof_end(m);
   };
   auto amx = [&](int l, int k) { return f8 && l >= 0 ? amax8 + (size_t)slot(l, k) * AMAX_SLOT : (unsigned*)nullptr; };
@@ -627,7 +642,8 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     rmsnorm_fwd(dt, h, m.ws + Ly.n1, at<float>(m, Ly.rstd1), BT, d, s.eps, st, amx(l, SL_N1));
     prof_end(m);
     if (f8) {
-      quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.n1, BT, d, slot(l, SL_N1), q8row, m.ws + Ly.n1T);
+      quant("fp8_quant_act", FP8_E4M3, h, BT, d, slot(l, SL_N1), q8row, m.ws + Ly.n1T, true, true,
+            at<float>(m, Ly.rstd1));
       rc = gemm8("gemm_qkv", DT_FP8_A4B4, EPI_STORE, BT, Nqkv, d, q8row, m.ws + Ly.wq[0], m.ws + Ly.qkv, Nqkv,
                  slot(l, SL_N1), slot(l, SL_WQKV));
     } else {
@@ -664,14 +680,16 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     rmsnorm_fwd(dt, h, m.ws + Ly.n2, at<float>(m, Ly.rstd2), BT, d, s.eps, st, amx(l, SL_N2));
     prof_end(m);
     GemmArgs ex{};
-    ex.C2 = m.ws + Ly.g;
+    ex.C2 = f8 ? nullptr : m.ws + Ly.g;   // fp8: relu(u)^2 is recomputed from u by its quantiser
     ex.amax = amx(l, SL_G);
     if (f8) {
-      quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.n2, BT, d, slot(l, SL_N2), q8row, m.ws + Ly.n2T);
-      if ((rc = gemm8("gemm_w1_relu2", DT_FP8_A4B4, EPI_RELU2, BT, F, d, q8row, m.ws + Ly.wq[2], m.ws + Ly.u, F,
+      quant("fp8_quant_act", FP8_E4M3, h, BT, d, slot(l, SL_N2), q8row, m.ws + Ly.n2T, true, true,
+            at<float>(m, Ly.rstd2));
+      if ((rc = gemm8("gemm_w1_relu2", DT_FP8_A4B4, EPI_RELU2_F32, BT, F, d, q8row, m.ws + Ly.wq[2], m.ws + Ly.u, F,
                       slot(l, SL_N2), slot(l, SL_W1), ex)))
         return rc;
-      quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.g, BT, F, slot(l, SL_G), q8row, m.ws + Ly.gT);
+      quant("fp8_quant_act", FP8_E4M3, m.ws + Ly.u, BT, F, slot(l, SL_G), q8row, m.ws + Ly.gT, true, true, nullptr,
+            true);
       rc = gemm8("gemm_w2", DT_FP8_A4B4, EPI_ACCUM_F32, BT, d, F, q8row, m.ws + Ly.wq[3], h, d, slot(l, SL_G),
                  slot(l, SL_W2));
     } else {
@@ -704,32 +722,46 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   prof_end(m);
 
   // ---------------------------------------------------------------- backward
-  {
-    GemmArgs ex{};
-    ex.aux = targets;
-    ex.auxf = at<float>(m, m.lse);
-    ex.beta = grad_scale / (float)BT;
-    if ((rc = gemm(m, "gemm_lm_head_xent_bwd", LAYOUT_KK, EPI_XENT_BWD, BT, V, d, m.ws + m.nL, d, wp(P.U), d, m.ws + m.dz, V, ex))) return rc;
-  }
   // The input gradients of the products that feed a norm backward (lm_head,
   // W1, Wqkv) are stored bf16 in the bf16 configuration, as the other
   // activation gradients are; the residual gradient dh stays fp32.
   void* dm = m.ws + m.dm;
   const bool dn_act = dt == DT_BF16 && !f8 && norm_chunks(d) != 0;
   const int epi_dn = dn_act ? EPI_STORE : EPI_STORE_F32;
-  const double dn_b = dn_act ? 2.0 : 4.0;   // bytes per dy element read by the norm backward
-  auto norm_bwd = [&](const void* y, const float* rstd, int accumulate, unsigned* amax) {
-    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (dn_b + 4.0 + 4.0 * accumulate + 2.0 * es_d), 1,
+  auto norm_bwd = [&](const void* y, const float* rstd, int accumulate, unsigned* amax, bool dy_act) {
+    const double dy_b = dy_act ? 2.0 : 4.0;   // bytes per dy element read
+    prof_begin(m, "rmsnorm_bwd", (double)BT * d * (dy_b + 4.0 + 4.0 * accumulate + 2.0 * es_d), 1,
                norm_label("rmsnorm_bwd"));
-    const int r = rmsnorm_bwd(dt, dm, dn_act, y, rstd, at<float>(m, m.dh), m.ws + m.dhA, BT, d, accumulate, st, amax);
+    const int r = rmsnorm_bwd(dt, dm, dy_act, y, rstd, at<float>(m, m.dh), m.ws + m.dhA, BT, d, accumulate, st, amax);
     prof_end(m);
     return r ? fail(GPT_EINVAL, "rmsnorm_bwd variant not built") : GPT_OK;
   };
   float* dh = at<float>(m, m.dh);
   void* dhA = m.ws + m.dhA;
-  if ((rc = gemm(m, "dgrad_lm_head", LAYOUT_KN, epi_dn, BT, d, V, m.ws + m.dz, V, wp(P.U), d, dm, d))) return rc;
-  if ((rc = wgrad("wgrad_lm_head", V, d, BT, m.ws + m.dz, V, m.ws + m.nL, d, grads + P.U, d))) return rc;
-  if ((rc = norm_bwd(m.ws + m.nL, at<float>(m, m.rstdL), 0, amx(s.L - 1, SL_DH2)))) return rc;
+  // Cross-entropy + lm_head backward, one vocabulary chunk of VOCAB_CHUNK
+  // columns at a time: the chunk's logits are recomputed and its logit
+  // gradient dz = (softmax - onehot) * grad_scale / BT formed in the
+  // product's epilogue; the input gradient of the lm_head accumulates the
+  // chunk's share (dn += dz U_c, fp32), and the chunk's rows of dU are
+  // written.  Neither the logits nor their gradient exist for the whole
+  // vocabulary at once.
+  const bool vchunked = V > VOCAB_CHUNK;
+  for (int v0 = 0; v0 < V; v0 += VOCAB_CHUNK) {
+    const int vn = std::min(VOCAB_CHUNK, V - v0);
+    GemmArgs ex{};
+    ex.aux = targets;
+    ex.auxf = at<float>(m, m.lse);
+    ex.beta = grad_scale / (float)BT;
+    ex.col0 = v0;
+    const long uoff = P.U + (long)v0 * d;
+    if ((rc = gemm(m, "gemm_lm_head_xent_bwd", LAYOUT_KK, EPI_XENT_BWD, BT, vn, d, m.ws + m.nL, d, wp(uoff), d,
+                   m.ws + m.dz, vn, ex)))
+      return rc;
+    const int epi = !vchunked ? epi_dn : v0 == 0 ? EPI_STORE_F32 : EPI_ACCUM_F32;
+    if ((rc = gemm(m, "dgrad_lm_head", LAYOUT_KN, epi, BT, d, vn, m.ws + m.dz, vn, wp(uoff), d, dm, d))) return rc;
+    if ((rc = wgrad("wgrad_lm_head", vn, d, BT, m.ws + m.dz, vn, m.ws + m.nL, d, grads + uoff, d))) return rc;
+  }
+  if ((rc = norm_bwd(m.ws + m.nL, at<float>(m, m.rstdL), 0, amx(s.L - 1, SL_DH2), dn_act && !vchunked))) return rc;
   for (int l = s.L - 1; l >= 0; --l) {
     auto& Ly = m.lay[l];
     GemmArgs ex{};
@@ -737,14 +769,14 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     ex.amax = amx(l, SL_DU);
     const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
     if (f8) {
-      quant("fp8_quant_grad", FP8_E5M2, dhA, BT, d, slot(l, SL_DH2), q8row, q8T);
-      if ((rc = gemm8("dgrad_w2_drelu2", DT_FP8_A5B4, EPI_DRELU2, BT, F, d, q8row, m.ws + Ly.wqT[3], m.ws + m.du, F,
-                      slot(l, SL_DH2), slot(l, SL_W2), ex)))
+      quant("fp8_quant_grad", FP8_E5M2, dh, BT, d, slot(l, SL_DH2), q8row, q8T, true, true);
+      if ((rc = gemm8("dgrad_w2_drelu2", DT_FP8_A5B4, EPI_DRELU2_F32, BT, F, d, q8row, m.ws + Ly.wqT[3],
+                      m.ws + m.f32w, F, slot(l, SL_DH2), slot(l, SL_W2), ex)))
         return rc;
       if ((rc = wgrad8("wgrad_w2", d, F, BT, q8T, m.ws + Ly.gT, grads + P.W2[l], F, slot(l, SL_DH2),
                        slot(l, SL_G))))
         return rc;
-      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.du, BT, F, slot(l, SL_DU), q8row, q8T);
+      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.f32w, BT, F, slot(l, SL_DU), q8row, q8T, true, true);
       if ((rc = gemm8("dgrad_w1", DT_FP8_A5B4, EPI_STORE_F32, BT, d, F, q8row, m.ws + Ly.wqT[2], dm, d,
                       slot(l, SL_DU), slot(l, SL_W1))))
         return rc;
@@ -762,9 +794,9 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
       if ((rc = wgrad("wgrad_w1", F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d, grads + P.W1[l], d)))
         return rc;
     }
-    if ((rc = norm_bwd(m.ws + Ly.n2, at<float>(m, Ly.rstd2), 1, amx(l, SL_DH1)))) return rc;
+    if ((rc = norm_bwd(m.ws + Ly.n2, at<float>(m, Ly.rstd2), 1, amx(l, SL_DH1), dn_act))) return rc;
     if (f8) {
-      quant("fp8_quant_grad", FP8_E5M2, dhA, BT, d, slot(l, SL_DH1), q8row, q8T);
+      quant("fp8_quant_grad", FP8_E5M2, dh, BT, d, slot(l, SL_DH1), q8row, q8T, true, true);
       if ((rc = gemm8("dgrad_o", DT_FP8_A5B4, EPI_STORE, BT, d, d, q8row, m.ws + Ly.wqT[1], m.ws + m.dO, d,
                       slot(l, SL_DH1), slot(l, SL_WO))))
         return rc;
@@ -821,7 +853,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
       if ((rc = wgrad("wgrad_qkv", Nqkv, d, BT, m.ws + m.dqkv, Nqkv, m.ws + Ly.n1, d, grads + P.Wqkv[l], d)))
         return rc;
     }
-    if ((rc = norm_bwd(m.ws + Ly.n1, at<float>(m, Ly.rstd1), 1, amx(l - 1, SL_DH2)))) return rc;
+    if ((rc = norm_bwd(m.ws + Ly.n1, at<float>(m, Ly.rstd1), 1, amx(l - 1, SL_DH2), dn_act))) return rc;
   }
   prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * (accumulate ? 8.0 : 4.0) + BT * 8.0, 1,
              "sort_keys_kernel + embed_bwd_runs_kernel");
@@ -1041,7 +1073,7 @@ int gpt_debug_tensor(gpt_model* m, int which, int layer, void** ptr, int64_t* ro
     case 2: *ptr = m->ws + m->lay[layer].o; *cols = s.d; break;
     case 3: *ptr = m->ws + m->rowloss; *cols = 1; *elem_bytes = 4; break;
     case 4: *ptr = m->ws + m->lse; *cols = 1; *elem_bytes = 4; break;
-    case 5: *ptr = m->ws + m->lay[layer].u; *cols = s.F; break;
+    case 5: *ptr = m->ws + m->lay[layer].u; *cols = s.F; if (s.fp8) *elem_bytes = 4; break;
     default: return fail(GPT_EINVAL, "unknown tensor id");
   }
   return GPT_OK;

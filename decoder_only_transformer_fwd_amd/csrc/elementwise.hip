@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float* __restric
     for (int c = lane * 4; c < d; c += 256) {
       const floatx4 v = load4(xr + c) * r;
       store4(y + (long)row * d + c, v);
-      if (amax) m = fmaxf(m, abs_max4<T>(v));
+      if (amax) m = fmaxf(m, abs_max4<float>(v));
     }
     if (lane == 0) rstd[row] = r;
   }
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_reg_kernel(const float* __res
       if (c < d) {
         const floatx4 lo = v[k][0] * r, hi = v[k][1] * r;
         store8(y + (long)row * d + c, lo, hi);
-        if (amax) m = fmaxf(m, fmaxf(abs_max4<T>(lo), abs_max4<T>(hi)));
+        if (amax) m = fmaxf(m, fmaxf(abs_max4<float>(lo), abs_max4<float>(hi)));
       }
     }
     if (lane == 0) rstd[row] = r;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_reg_kernel(const void* __rest
         }
         store8(dx + base + c, g[0], g[1]);
         store8(dxa + base + c, g[0], g[1]);
-        if (amax) m = fmaxf(m, fmaxf(abs_max4<T>(g[0]), abs_max4<T>(g[1])));
+        if (amax) m = fmaxf(m, fmaxf(abs_max4<float>(g[0]), abs_max4<float>(g[1])));
       }
     }
   }
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
       if (accumulate) g += load4(dx + base + c);
       store4(dx + base + c, g);
       store4(dxa + base + c, g);
-      if (amax) m = fmaxf(m, abs_max4<T>(g));
+      if (amax) m = fmaxf(m, abs_max4<float>(g));
     }
   }
   if (amax) block_amax<4>(amax, m, red);

@@ -45,13 +45,44 @@ __global__ __launch_bounds__(256) void amax_kernel(const bf16* __restrict__ x, l
     atomicMax(amax + (blockIdx.x & (AMAX_WAYS - 1)), __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
+// Sixteen consecutive values of row r as fp32: bf16 (widened exactly) or
+// fp32, times rowscale[r] when given, or max(x, 0)^2 with RELU2.
+template <bool RELU2>
+__device__ __forceinline__ void load16(const bf16* src, const float*, int, float* f) {
+  const bf16x8 v0 = *(const bf16x8*)src;
+  const bf16x8 v1 = *(const bf16x8*)(src + 8);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    f[e] = (float)v0[e];
+    f[8 + e] = (float)v1[e];
+  }
+}
+template <bool RELU2>
+__device__ __forceinline__ void load16(const float* src, const float* rowscale, int r, float* f) {
+  const float rs = rowscale ? rowscale[r] : 1.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const floatx4 v = *(const floatx4*)(src + 4 * k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (RELU2) {
+        const float x = fmaxf(v[e], 0.f);
+        f[4 * k + e] = x * x;
+      } else {
+        f[4 * k + e] = rowscale ? v[e] * rs : v[e];
+      }
+    }
+  }
+}
+
 // Grid (C/64, ceil(R/64)), 256 threads: a 64x64 tile; thread t converts 16
 // consecutive elements of row t/4.  Codes go to q[r][c] and (if qT) to
 // qT[c][r] through an LDS transpose.  scale_out (if set) receives s.
-template <int FMT>
-__global__ __launch_bounds__(256) void quant_kernel(const bf16* __restrict__ x, int R, int C,
-                                                    const unsigned* __restrict__ amax, float* scale_out,
-                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ qT) {
+template <int FMT, typename TI, bool RELU2>
+__global__ __launch_bounds__(256) void quant_kernel(const TI* __restrict__ x, const float* __restrict__ rowscale,
+                                                    int R, int C, const unsigned* __restrict__ amax,
+                                                    float* scale_out, uint8_t* __restrict__ q,
+                                                    uint8_t* __restrict__ qT) {
   __shared__ uint8_t tile[64][64 + 4];
   __shared__ float amax_s;
   const float fmax = fp8_max(FMT);
@@ -69,15 +100,10 @@ __global__ __launch_bounds__(256) void quant_kernel(const bf16* __restrict__ x, 
   const int r = r0 + rl;
   uint32_t w[4] = {0u, 0u, 0u, 0u};
   if (r < R) {
-    const bf16* src = x + (long)r * C + c0 + cl;
-    const bf16x8 v0 = *(const bf16x8*)src;
-    const bf16x8 v1 = *(const bf16x8*)(src + 8);
     float f[16];
+    load16<RELU2>(x + (long)r * C + c0 + cl, rowscale, r, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      f[e] = fminf(fmaxf((float)v0[e] * s, -fmax), fmax);
-      f[8 + e] = fminf(fmaxf((float)v1[e] * s, -fmax), fmax);
-    }
+    for (int e = 0; e < 16; ++e) f[e] = fminf(fmaxf(f[e] * s, -fmax), fmax);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       w[k] = (cvt2(FMT, f[4 * k], f[4 * k + 1]) & 0xFFFFu) | (cvt2(FMT, f[4 * k + 2], f[4 * k + 3]) << 16);
@@ -119,15 +145,23 @@ void fp8_amax(const void* x, long n, unsigned* amax, hipStream_t st) {
   hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const bf16*)x, n, amax);
 }
 
-void fp8_quantize(int fmt, const void* x, int R, int C, const unsigned* amax, float* scale_out, void* q, void* qT,
-                  hipStream_t st) {
+template <typename TI, bool RELU2>
+static void quantize_t(int fmt, const TI* x, const float* rowscale, int R, int C, const unsigned* amax,
+                       float* scale_out, void* q, void* qT, hipStream_t st) {
   dim3 g(C / 64, (R + 63) / 64);
   if (fmt == FP8_E4M3)
-    hipLaunchKernelGGL(quant_kernel<FP8_E4M3>, g, dim3(256), 0, st, (const bf16*)x, R, C, amax, scale_out,
-                       (uint8_t*)q, (uint8_t*)qT);
+    hipLaunchKernelGGL((quant_kernel<FP8_E4M3, TI, RELU2>), g, dim3(256), 0, st, x, rowscale, R, C, amax,
+                       scale_out, (uint8_t*)q, (uint8_t*)qT);
   else
-    hipLaunchKernelGGL(quant_kernel<FP8_E5M2>, g, dim3(256), 0, st, (const bf16*)x, R, C, amax, scale_out,
-                       (uint8_t*)q, (uint8_t*)qT);
+    hipLaunchKernelGGL((quant_kernel<FP8_E5M2, TI, RELU2>), g, dim3(256), 0, st, x, rowscale, R, C, amax,
+                       scale_out, (uint8_t*)q, (uint8_t*)qT);
+}
+
+void fp8_quantize(int fmt, const void* x, int R, int C, const unsigned* amax, float* scale_out, void* q, void* qT,
+                  hipStream_t st, int x_f32, const float* rowscale, int relu2) {
+  if (x_f32 && relu2) quantize_t<float, true>(fmt, (const float*)x, nullptr, R, C, amax, scale_out, q, qT, st);
+  else if (x_f32) quantize_t<float, false>(fmt, (const float*)x, rowscale, R, C, amax, scale_out, q, qT, st);
+  else quantize_t<bf16, false>(fmt, (const bf16*)x, nullptr, R, C, amax, scale_out, q, qT, st);
 }
 
 }  // namespace gk

@@ -558,7 +558,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
               const float x = fmaxf(v[e], 0.f);
               rr[e] = x * x;
             }
-            store4((TC*)p.C2 + off, rr);
+            if (p.C2) store4((TC*)p.C2 + off, rr);   // without C2 only the amax of relu(u)^2 is taken
             if (p.amax) amax_acc = fmaxf(amax_acc, abs_max4<TC>(rr));
           } else if constexpr (E == EPI_DRELU2) {
             const floatx4 u = pre[st];
@@ -573,7 +573,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
             const int y = ((const int*)p.aux)[m];
             floatx4 rr;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rr[e] = (fast_exp2((v[e] - lse) * L2E) - (n + e == y ? 1.f : 0.f)) * p.beta;
+            for (int e = 0; e < 4; ++e)
+              rr[e] = (fast_exp2((v[e] - lse) * L2E) - (p.col0 + n + e == y ? 1.f : 0.f)) * p.beta;
             store4((TC*)p.C + off, rr);
           } else if constexpr (E == EPI_PARTIAL) {
             store4(p.part + (long)blockIdx.z * p.M * p.N + (long)m * p.N + n, v);
@@ -718,6 +719,7 @@ static int launch_epi(const GemmArgs& a, int layout, int epi, int tile, int spli
   // input gradients: grad [M][K] x weight [K][N]
   GK_CASE(LAYOUT_KN, true, false, EPI_STORE)
   GK_CASE(LAYOUT_KN, true, false, EPI_STORE_F32)
+  GK_CASE(LAYOUT_KN, true, false, EPI_ACCUM_F32)   // the lm_head's input gradient over vocabulary chunks
   GK_CASE(LAYOUT_KN, true, false, EPI_DRELU2)
   GK_CASE(LAYOUT_KN, true, false, EPI_PARTIAL)
   // weight gradients: grad [K][M] x activation [K][N]
@@ -734,6 +736,16 @@ static int launch_epi(const GemmArgs& a, int layout, int epi, int tile, int spli
 template <typename MF>
 static int launch_fp8(const GemmArgs& a, int layout, int epi, int tile, int splits, hipStream_t st) {
   if (layout != LAYOUT_KK) return -1;
+  // ReLU^2 / dReLU^2 with fp32 outputs (and fp32 aux): the values the next
+  // quantiser encodes
+  if (epi == EPI_RELU2_F32) {
+    launch_cfg<uint8_t, MF, TILE_128x128, true, true, EPI_RELU2, float>(a, splits, st);
+    return 0;
+  }
+  if (epi == EPI_DRELU2_F32) {
+    launch_cfg<uint8_t, MF, TILE_128x128, true, true, EPI_DRELU2, float>(a, splits, st);
+    return 0;
+  }
 #define GK_F8(E)                                                                    \
   if (epi == E) {                                                                   \
     launch_cfg<uint8_t, MF, TILE_128x128, true, true, E, bf16>(a, splits, st);      \

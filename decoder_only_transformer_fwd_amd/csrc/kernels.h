@@ -36,6 +36,11 @@ enum Epi {
   // each stored also transposed (batched launches only)
   EPI_STORE_SYM = 9,
   EPI_AXPBY_SYM = 10,
+  // fp8 products only: EPI_RELU2 / EPI_DRELU2 with fp32 outputs (and, for
+  // EPI_DRELU2, an fp32 aux), so that the next quantiser encodes the fp32
+  // values the epilogue computed
+  EPI_RELU2_F32 = 11,
+  EPI_DRELU2_F32 = 12,
 };
 
 // Work-group tiles (M x N); _W8 variants use 8 waves (2 x 4) instead of 4 (2 x 2).
@@ -64,7 +69,7 @@ struct GemmArgs {
   long lda, ldb;   // leading dimensions, in elements
   void* C;
   long ldc;
-  void* C2;        // EPI_RELU2: g
+  void* C2;        // EPI_RELU2: g (may be NULL: only u is stored, and the amax of g taken)
   const void* aux; // EPI_DRELU2: u; EPI_XENT_*: int32 targets
   const float* auxf; // EPI_XENT_BWD: per-row logsumexp
   float* part;     // EPI_XENT_FWD: [M][nblk][2]; EPI_PARTIAL: [splits][M][N]
@@ -75,6 +80,7 @@ struct GemmArgs {
   float beta;      // EPI_XENT_BWD: 1 / rows
   int k_split;     // K elements handled per blockIdx.z
   int nblk;        // EPI_XENT_FWD: number of column blocks of width BN/2
+  int col0;        // EPI_XENT_BWD: vocabulary index of column 0 (a chunk of the vocabulary)
   unsigned* amax;  // EPI_RELU2 / EPI_DRELU2: if set, max |stored g / du| is folded in (float bits)
   // Batched products (grid y = batch index): element strides between the
   // batch's A, B and C (aux shares C's); zero for a single product.
@@ -98,7 +104,9 @@ void splitk_reduce_strided(const float* part, int splits, int M, int N, void* ou
 // Also checks that every token and target id is in [0, vocab) (sets *flag).
 void embed_fwd(int dtype, const int32_t* tokens, const int32_t* targets, const void* E, float* h, int rows, int d,
                int vocab, int* flag, hipStream_t st);
-// amax (optional): max |stored value| folded in as float bits (for fp8 scaling)
+// amax (optional): max |value| of the output, taken from the fp32 value before
+// it is rounded to the stored type, folded in as float bits (fp8 scaling: the
+// quantiser encodes the same fp32 values)
 // Chunks of 8 elements per lane for the register-resident norm kernels (0:
 // the row does not fit, the looping kernels run instead).
 inline int norm_chunks(int d) {
@@ -193,9 +201,14 @@ void zero_u32(unsigned* p, int n, hipStream_t st);
 // the tensor is produced; fp8_amax folds in max |x| over n bf16 values.
 constexpr int AMAX_SLOT = 64;
 void fp8_amax(const void* x, long n, unsigned* amax, hipStream_t st);
-// x [R][C] bf16 (C a multiple of 64) -> codes q [R][C] and, if qT, [C][R].
+// x [R][C] bf16, or fp32 when x_f32 (C a multiple of 64) -> codes q [R][C]
+// and, if qT, [C][R].  fp32 x only: with rowscale the encoded value of
+// x[r][c] is x[r][c] * rowscale[r] (a norm's output recomputed from its fp32
+// input and rstd, exactly as the norm computes it); with relu2 it is
+// max(x[r][c], 0)^2 (the MLP activation recomputed from u, as the W1
+// epilogue computes it).
 void fp8_quantize(int fmt, const void* x, int R, int C, const unsigned* amax, float* scale_out, void* q, void* qT,
-                  hipStream_t st);
+                  hipStream_t st, int x_f32 = 0, const float* rowscale = nullptr, int relu2 = 0);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

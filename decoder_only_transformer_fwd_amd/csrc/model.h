@@ -34,6 +34,11 @@ constexpr int DEC_KSPLIT = 8;
 static_assert(DEC_KSPLIT <= 8, "the decoder's add + norm kernel adds at most 8 partials");
 // micro-batches per gpt_step_micro call
 constexpr int MAX_MICRO = 1024;
+// The cross-entropy backward works on the vocabulary in chunks of at most
+// this many columns: the logit gradient of one chunk is formed, consumed by
+// the lm_head's input- and weight-gradient products, and overwritten by the
+// next chunk's.
+constexpr int VOCAB_CHUNK = 8192;
 inline size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 
 struct Shape {
@@ -103,6 +108,7 @@ struct gpt_model {
       cosb, sinb, keys, total;
   size_t splitk_floats;
   size_t q8row, q8T, amax, scales;   // fp8: transient codes, per-tensor amax / scale slots
+  size_t f32w;   // fp8: transient fp32 [BT][F], du in the backward
   int n_slots;
   int xent_tile, xent_nblk;
   // optional per-launch-site timing with HIP events on the step's stream

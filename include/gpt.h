@@ -265,8 +265,9 @@ void gpt_destroy(gpt_model* model);
  * workspace).  which: 0 residual h after the forward [B*T, d] fp32,
  * 1 normalised q/k + raw v of `layer` [B*T, 3d], 2 attention output of
  * `layer` [B*T, d], 3 per-row loss [B*T] fp32, 4 per-row logsumexp [B*T] fp32,
- * 5 u (MLP pre-activation) of `layer` [B*T, F].  Activation-typed buffers
- * hold the parameter type.  *elem_bytes receives the element size. */
+ * 5 u (MLP pre-activation) of `layer` [B*T, F] (fp32 in GPT_FP8 models).
+ * Activation-typed buffers hold the parameter type.  *elem_bytes receives the
+ * element size. */
 int gpt_debug_tensor(gpt_model* model, int which, int layer, void** ptr, int64_t* rows, int64_t* cols,
                      int* elem_bytes);
 

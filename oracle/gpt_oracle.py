@@ -182,15 +182,20 @@ def logsumexp_rows(z: np.ndarray) -> np.ndarray:
 
 
 class LinearOperands:
-    """Exact operands: the linear layers multiply the values themselves."""
+    """Exact operands: the linear layers multiply the values themselves.
+
+    ``what`` names the operand: activations "n1" (attention input norm),
+    "o" (attention output), "n2" (MLP input norm), "g" (relu(u)^2);
+    gradients "dh2" (residual gradient into W2), "du" (into W1), "dh1"
+    (into Wo); ``grad_fused`` is the fused QKV output gradient."""
 
     def weights(self, s: gi.GPTShape, W: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
         return W
 
-    def act(self, x: np.ndarray) -> np.ndarray:
+    def act(self, x: np.ndarray, what: str = "") -> np.ndarray:
         return x
 
-    def grad(self, g: np.ndarray) -> np.ndarray:
+    def grad(self, g: np.ndarray, what: str = "") -> np.ndarray:
         return g
 
     def grad_fused(self, *parts: np.ndarray) -> Tuple[np.ndarray, ...]:
@@ -219,10 +224,10 @@ class Fp8Operands(LinearOperands):
                 out[f"L{l}.{w}"] = fp8_value(W[f"L{l}.{w}"], "e4m3")
         return out
 
-    def act(self, x):
+    def act(self, x, what=""):
         return fp8_value(x, "e4m3")
 
-    def grad(self, g):
+    def grad(self, g, what=""):
         return fp8_value(g, "e5m2")
 
     def grad_fused(self, *parts):
@@ -246,7 +251,7 @@ class _Layer:
         Hkv = s.kv_heads
         self.h_in = h
         self.a, self.r1 = rmsnorm(h, eps)                          # [BT, d]
-        self.aq = enc.act(self.a)
+        self.aq = enc.act(self.a, "n1")
         q = (self.aq @ W[f"L{l}.Wq"].T).reshape(B, T, H, Dh)
         k = (self.aq @ W[f"L{l}.Wk"].T).reshape(B, T, Hkv, Dh)
         self.v = (self.aq @ W[f"L{l}.Wv"].T).reshape(B, T, Hkv, Dh)
@@ -260,13 +265,13 @@ class _Layer:
             vb = expand_kv(self.v[b].transpose(1, 0, 2), H)
             o[b] = attention_fwd(qb, kb, vb, window).transpose(1, 0, 2)
         self.o = o.reshape(B * T, H * Dh)
-        self.oq = enc.act(self.o)
+        self.oq = enc.act(self.o, "o")
         self.h_mid = h + self.oq @ W[f"L{l}.Wo"].T
         self.m, self.r2 = rmsnorm(self.h_mid, eps)
-        self.mq = enc.act(self.m)
+        self.mq = enc.act(self.m, "n2")
         self.u = self.mq @ W[f"L{l}.W1"].T
         self.g = np.maximum(self.u, 0.0) ** 2
-        self.gq = enc.act(self.g)
+        self.gq = enc.act(self.g, "g")
         self.h_out = self.h_mid + self.gq @ W[f"L{l}.W2"].T
 
 
@@ -375,16 +380,16 @@ def forward_backward(s: gi.GPTShape, W: Dict[str, np.ndarray], X: np.ndarray,
         L = _Layer(s, Wl, l, h_ins[l], cos, sin, wins[l], enc)
         h_ins[l] = None
         # MLP: h_out = h_mid + g W2^T, g = relu(u)^2, u = m W1^T, m = N(h_mid)
-        dhq = enc.grad(dh)
+        dhq = enc.grad(dh, "dh2")
         grads[f"L{l}.W2"] = dhq.T @ L.gq
         dg = dhq @ Wl[f"L{l}.W2"]
         du = dg * 2.0 * np.maximum(L.u, 0.0)
-        duq = enc.grad(du)
+        duq = enc.grad(du, "du")
         grads[f"L{l}.W1"] = duq.T @ L.mq
         dm = duq @ Wl[f"L{l}.W1"]
         dh = dh + rmsnorm_bwd(dm, L.m, L.r2)
         # attention: h_mid = h_in + o Wo^T
-        dhq = enc.grad(dh)
+        dhq = enc.grad(dh, "dh1")
         grads[f"L{l}.Wo"] = dhq.T @ L.oq
         do = (dhq @ Wl[f"L{l}.Wo"]).reshape(B, T, H, Dh)
         Hkv = s.kv_heads

@@ -1,18 +1,35 @@
-"""How well-conditioned the FP8 configuration's step is, measured on the oracle alone.
+"""How reproducible the FP8 configuration's gradients are, measured on the oracle alone.
 
-Two fp64 evaluations of the same fp8 recipe are compared: the oracle's own
-(operands encoded from their exact values) and one whose operands are first
-rounded to bf16 (RNE) and then encoded, as an implementation that keeps its
-activations and gradients in bf16 does.  Both are faithful evaluations of the
-recipe; where they disagree, the encoding has amplified a bf16-level
-difference (a value that lands on the other side of an fp8 rounding
-boundary moves by a whole fp8 step).  The per-tensor gradient cosine between
-the two is stored, and the GPU parity tests derive the fp8 gradient bar for
-each tensor from it.  Only ``oracle/``, ``gpt_inputs`` and the test-suite's
-workload table are used.
+The fp8 recipe rounds every linear-layer operand to an 8-bit code.  A value
+that moves by any amount across a rounding boundary changes its code by a
+whole fp8 step, and through the depth of the network such changes cascade.
+Two faithful evaluations of the recipe that differ only in how their
+operands were rounded before encoding can therefore disagree by much more
+than that rounding.
 
-Usage:  python tests/golden/make_fp8_sensitivity.py fp8_mid d24_fp8_short d24-fp8
-(d24-fp8 reuses the stored oracle_d24-fp8.npz and compares sampled values.)
+This script measures it.  For each workload it evaluates the recipe exactly
+(the oracle: operands encoded from their fp64 values) and again with the fp8
+operands first rounded (round to nearest even), under three policies:
+  "7"     every operand rounded to 7 mantissa bits (bf16);
+  "23"    every operand rounded to 23 bits (fp32: an implementation that
+          computes every operand in fp32 and encodes that);
+  "attn7" every operand at 23 bits except the two that come out of the
+          attention, its output o and the fused QKV output gradient, at 7
+          bits: the recipe keeps attention in bf16 (in the FP8 workload only
+          the four linear layers are fp8; attention, norms, lm_head and loss
+          stay bf16/fp32), so an implementation of the recipe carries at
+          least that rounding there.
+It stores the per-tensor gradient cosine between each evaluation and the
+exact one (for the full-size workload, over the stored gradient samples).
+The GPU parity tests use the "attn7" table only to name the tensors whose
+fp8 gradient the recipe, with its bf16 attention, cannot reproduce to 0.99;
+their bar is not lowered: they are reported in an expected-failure test.
+Only ``oracle/``, ``gpt_inputs`` and the test-suite's workload table are
+used.
+
+Usage:  python tests/golden/make_fp8_sensitivity.py fp8_mid d24_fp8_short gqa_fp8 d24-fp8
+        (d24-fp8 compares the stored full-size oracle samples; about an
+        hour of CPU per policy; the table is written after every policy)
 """
 import json
 import os
@@ -30,18 +47,31 @@ from oracle import gpt_oracle as O  # noqa: E402
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "fp8_sensitivity.json")
 
 
-class Fp8OperandsFromBf16(O.Fp8Operands):
-    """The fp8 encoding applied to operands rounded to bf16 first."""
+def round_bits(x: np.ndarray, bits: int) -> np.ndarray:
+    """x rounded to `bits` explicit mantissa bits, ties to even (fp64)."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    sc = float(2 ** (bits + 1))
+    return np.ldexp(np.round(m * sc) / sc, e)   # np.round: half to even
 
-    @staticmethod
-    def _bf16(x):
-        return gi.bf16_bits_to_f64(gi.bf16_bits_from_f32(np.asarray(x, dtype=np.float32))).reshape(x.shape)
 
-    def act(self, x):
-        return super().act(self._bf16(x))
+class Fp8OperandsRounded(O.Fp8Operands):
+    """The fp8 encoding applied to operands first rounded to `bits` bits, the
+    attention's outputs (o, the fused QKV gradient) to `attn_bits`."""
 
-    def grad(self, g):
-        return super().grad(self._bf16(g))
+    def __init__(self, bits: int, attn_bits: int):
+        self.bits, self.attn_bits = bits, attn_bits
+
+    def act(self, x, what=""):
+        return super().act(round_bits(x, self.attn_bits if what == "o" else self.bits))
+
+    def grad(self, g, what=""):
+        return super().grad(round_bits(g, self.bits))
+
+    def grad_fused(self, *parts):
+        return super().grad_fused(*(round_bits(p, self.attn_bits) for p in parts))
+
+
+POLICIES = {"7": (7, 7), "23": (23, 23), "attn7": (23, 7)}
 
 
 def _cos(a, b):
@@ -50,32 +80,48 @@ def _cos(a, b):
     return 1.0 if na == nb == 0 else float(a @ b / (na * nb))
 
 
-def run(name: str) -> dict:
+def run(name: str, data: dict) -> None:
     from tests.gpu_common import SMALL
-    t0 = time.time()
     full = name in gi.PRESETS and name not in SMALL
     s = gi.preset(name) if full else SMALL[name]
     W = gi.weights_f64(s, gi.make_weights(s))
     X, Y = gi.make_tokens(s)
-    loss_b, Gb = O.forward_backward(s, W, X, Y, enc=Fp8OperandsFromBf16())
     if full:
         ref = np.load(os.path.join(os.path.dirname(OUT), f"oracle_{name}.npz"), allow_pickle=False)
         idx = gi.grad_sample_indices(s, int(ref["n_samples"]))
-        cos = {str(n): _cos(Gb[str(n)].reshape(-1)[idx[str(n)]], ref["samples"][k])
-               for k, n in enumerate(ref["names"])}
         loss = float(ref["loss"])
+        G = None
+        order = ("attn7", "23", "7")
     else:
         loss, G = O.forward_backward(s, W, X, Y)
-        cos = {n: _cos(Gb[n], G[n]) for n in G if np.any(G[n])}
-    worst = min(cos.items(), key=lambda kv: kv[1])
-    print(f"{name}: loss {loss:.9f} vs {loss_b:.9f}; worst cosine {worst[1]:.5f} ({worst[0]}); "
-          f"{time.time() - t0:.0f}s", flush=True)
-    return {"loss": loss, "loss_bf16_operands": loss_b, "cosine": cos}
+        order = ("attn7", "23", "7")
+    out = data.setdefault(name, {})
+    out["loss"] = loss
+    out.setdefault("bits", {})
+    for pol in order:
+        t0 = time.time()
+        loss_b, Gb = O.forward_backward(s, W, X, Y, enc=Fp8OperandsRounded(*POLICIES[pol]))
+        if full:
+            cos = {str(n): _cos(Gb[str(n)].reshape(-1)[idx[str(n)]], ref["samples"][k])
+                   for k, n in enumerate(ref["names"])}
+        else:
+            cos = {n: _cos(Gb[n], G[n]) for n in G if np.any(G[n])}
+        worst = min(cos.items(), key=lambda kv: kv[1])
+        below = sorted(n for n, c in cos.items() if c < 0.99)
+        print(f"{name} {pol}: loss {loss:.9f} vs {loss_b:.9f}; worst cosine {worst[1]:.5f} ({worst[0]}); "
+              f"{len(below)} of {len(cos)} below 0.99; {time.time() - t0:.0f}s", flush=True)
+        out["bits"][pol] = {"loss": loss_b, "cosine": cos}
+        with open(OUT, "w") as f:
+            json.dump(data, f, indent=1, sort_keys=True)
+
+
+def below_099(table: dict, workload: str, policy: str = "attn7") -> set:
+    """Tensors whose recipe gradient moves below cosine 0.99 under `policy`."""
+    ent = table.get(workload, {}).get("bits", {}).get(policy, {}).get("cosine", {})
+    return {n for n, c in ent.items() if c < 0.99}
 
 
 if __name__ == "__main__":
     data = json.load(open(OUT)) if os.path.exists(OUT) else {}
     for n in sys.argv[1:]:
-        data[n] = run(n)
-        with open(OUT, "w") as f:
-            json.dump(data, f, indent=1, sort_keys=True)
+        run(n, data)
