@@ -160,6 +160,9 @@ def main() -> int:
                     help="KV-cache inference instead of training: prefill --prompt tokens per row, "
                          "then time --steps decode steps (one token per row each)")
     ap.add_argument("--prompt", type=int, default=1024)
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run the weight-gradient products in order on the step's stream "
+                         "(gpt_overlap_enable(m, 0)) instead of on the handle's second stream")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)")
@@ -180,6 +183,8 @@ def main() -> int:
     W8 = gi.make_weights(s)
     sess = G.Session(s, W8)
     del W8
+    if args.no_overlap:
+        sess.overlap(False)
     if n_acc == 1:
         X, Y = gi.make_tokens(s)
         sess.set_tokens(X, Y)
@@ -321,7 +326,8 @@ def main() -> int:
                    "seq_len": s.seq_len, "batch": s.batch, "grad_accum": n_acc, "tokens_per_step": s.bt * n_acc,
                    "optimizer": "muon+adamw" if args.optimizer else None,
                    "window": s.window, "window_pattern": s.window_pattern, "token_dist": s.token_dist,
-                   "precision": s.precision},
+                   "precision": s.precision, "overlapped_weight_gradients": not args.no_overlap and
+                   s.precision != "fp8"},
         "mfu": mfu,
         "mfu_peak_tflops": peak / 1e12,
         "model_flops_per_token": Mx.flops_per_token(s),

@@ -343,13 +343,16 @@ int build_layout(gpt_model& m) {
   m.dOT = take((size_t)s.B * s.H * s.Dh * s.Tp * A);
   m.Dv = take((size_t)s.B * s.H * s.Tp * 4);
   m.dqkv = take(BT * s.Nqkv * A);
-  // split-K partials: the largest need among the planned products
-  size_t need = 0;
+  // split-K partials: the largest need among the planned products; the
+  // weight-gradient products (which may run on the handle's second stream)
+  // have a region of their own
+  size_t need = 0, need2 = 0;
   auto consider = [&](int layout, int M, int N, int K) {
+    size_t& nd = layout == LAYOUT_MN ? need2 : need;
     GemmPlan g = plan_gemm(s.dtype, layout, M, N, K);
-    if (g.splits > 1) need = std::max(need, (size_t)g.splits * M * N);
+    if (g.splits > 1) nd = std::max(nd, (size_t)g.splits * M * N);
     const TailPlan tp = plan_tail(s.dtype, layout, EPI_STORE_F32, M, N, K);
-    if (tp.n1 > 0) need = std::max(need, (size_t)tp.splits * M * (N - tp.n1 * 256));
+    if (tp.n1 > 0) nd = std::max(nd, (size_t)tp.splits * M * (N - tp.n1 * 256));
   };
   // the lm_head's products run one vocabulary chunk at a time
   const int vc = std::min(s.V, VOCAB_CHUNK);
@@ -372,9 +375,9 @@ int build_layout(gpt_model& m) {
         if (g.splits > 1) need = std::max(need, (size_t)g.splits * s.BT * s.d);
       }
       const int MN[4][2] = {{s.Nqkv, s.d}, {s.d, s.d}, {s.F, s.d}, {s.d, s.F}};
-      for (auto& mn : MN) {
+      for (auto& mn : MN) {   // weight gradients
         GemmPlan g = plan_gemm(dty, LAYOUT_KK, mn[0], mn[1], s.BT);
-        if (g.splits > 1) need = std::max(need, (size_t)g.splits * mn[0] * mn[1]);
+        if (g.splits > 1) need2 = std::max(need2, (size_t)g.splits * mn[0] * mn[1]);
       }
     }
     const size_t wide = (size_t)std::max(s.F, s.Nqkv);
@@ -399,6 +402,12 @@ int build_layout(gpt_model& m) {
   }
   m.splitk_floats = need;
   m.splitk = take(std::max<size_t>(need, 1) * 4);
+  m.splitk2_floats = need2;
+  m.splitk2 = take(std::max<size_t>(need2, 1) * 4);
+  // second copies for the overlapped weight gradients: the residual
+  // gradient's activation-type copy and the vocabulary chunk's logit gradient
+  m.dhA2 = take(BT * s.d * A);
+  m.dz2 = take(BT * std::min(s.V, VOCAB_CHUNK) * A);
   m.cosb = take((size_t)s.T * (s.Dh / 2) * 4);
   m.sinb = take((size_t)s.T * (s.Dh / 2) * 4);
   m.keys = take(BT * 4);
@@ -476,12 +485,17 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   if (epi == EPI_XENT_FWD) g = GemmPlan{m.xent_tile, 1, K};
   if (epi != EPI_STORE_F32 && !(wgrad && epi == EPI_ACCUM_F32)) g.splits = 1, g.k_split = K;
   if (g.splits > 1 && ldc != N) g.splits = 1, g.k_split = K;
+  // A weight gradient on the second stream runs unsplit: it needs not fill
+  // the GPU alone, since the input-gradient chain runs beside it, and it
+  // saves the partial sums' traffic and their reduction (measured: d24 step
+  // 98.3 -> 95.9 ms; in order on one stream, split-K is faster).
+  if (wgrad && m.side && m.st == m.side) g.splits = 1, g.k_split = K;
   if (g.splits > 1) {
     // the partial sums must fit the workspace's split-K region (sized by
     // build_layout from the same plans); refuse rather than write past it
-    if ((size_t)g.splits * M * N > m.splitk_floats)
+    if ((size_t)g.splits * M * N > (wgrad ? m.splitk2_floats : m.splitk_floats))
       return fail(GPT_EINVAL, std::string(site) + ": split-K partials exceed the planned workspace region");
-    a.part = at<float>(m, m.splitk);
+    a.part = at<float>(m, wgrad ? m.splitk2 : m.splitk);
     a.k_split = g.k_split;
     char label[128];
     gemm_kernel_label(dty, layout, EPI_PARTIAL, g.tile, label, sizeof label);
@@ -514,10 +528,10 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
     int ks = (K + tp.splits - 1) / tp.splits;
     ks = (ks + 63) / 64 * 64;
     const int sp = (K + ks - 1) / ks;
-    if ((size_t)sp * M * N2 > m.splitk_floats)
+    if ((size_t)sp * M * N2 > (wgrad ? m.splitk2_floats : m.splitk_floats))
       return fail(GPT_EINVAL, std::string(site) + ": split-K partials exceed the planned workspace region");
     t.k_split = ks;
-    t.part = at<float>(m, m.splitk);
+    t.part = at<float>(m, wgrad ? m.splitk2 : m.splitk);
     gemm_kernel_label(dty, layout, EPI_PARTIAL, g.tile, label, sizeof label);
     prof_begin(m, site, flops * N2 / N, 0, label);
     if (gemm_launch(t, dty, layout, EPI_PARTIAL, g.tile, sp, m.st))
@@ -605,11 +619,39 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     ex.scale_b = sc8 + sb;
     return gemm(m, site, LAYOUT_KK, epi, M, N, K, A, K, B, K, C, ldc, ex, dty);
   };
-  // weight-gradient products: store or accumulate into grads
+  // weight-gradient products: store or accumulate into grads.  With overlap
+  // they run on the handle's second stream: each forks from the main stream
+  // once its inputs are written, and `done` receives an event after it, on
+  // which the main stream waits before it overwrites a transient input of
+  // that product (the activation gradient it reads).
   const int wepi = accumulate ? EPI_ACCUM_F32 : EPI_STORE_F32;
+  const bool ov = m.overlap && m.side && !m.prof_on && !f8 && !forward_only;
+  hipEvent_t ev_last = nullptr;   // the side stream's last product
+  auto ov_event = [&]() -> hipEvent_t {
+    if (m.ov_next == m.ov_ev.size()) return nullptr;
+    return m.ov_ev[m.ov_next++];
+  };
+  auto wait_for = [&](hipEvent_t& e) {
+    if (!e) return GPT_OK;
+    const hipError_t r = hipStreamWaitEvent(st, e, 0);
+    e = nullptr;
+    return r == hipSuccess ? GPT_OK : fail(GPT_EHIP, std::string("hipStreamWaitEvent: ") + hipGetErrorString(r));
+  };
   auto wgrad = [&](const char* site, int M, int N, int K, const void* A, long lda, const void* B, long ldb,
-                   float* C, long ldc) {
-    return gemm(m, site, LAYOUT_MN, wepi, M, N, K, A, lda, B, ldb, C, ldc, GemmArgs{}, -1, true);
+                   float* C, long ldc, hipEvent_t* done = nullptr) {
+    if (!ov) return gemm(m, site, LAYOUT_MN, wepi, M, N, K, A, lda, B, ldb, C, ldc, GemmArgs{}, -1, true);
+    hipEvent_t fork = ov_event(), join = ov_event();
+    if (!fork || !join) return fail(GPT_EINVAL, "overlap event ring exhausted");
+    HIP_TRY(hipEventRecord(fork, st));
+    HIP_TRY(hipStreamWaitEvent(m.side, fork, 0));
+    m.st = m.side;
+    const int r = gemm(m, site, LAYOUT_MN, wepi, M, N, K, A, lda, B, ldb, C, ldc, GemmArgs{}, -1, true);
+    m.st = st;
+    if (r) return r;
+    HIP_TRY(hipEventRecord(join, m.side));
+    ev_last = join;
+    if (done) *done = join;
+    return GPT_OK;
   };
   auto wgrad8 = [&](const char* site, int M, int N, int K, const void* A, const void* B, float* C, long ldc, int sa,
                     int sb) {
@@ -619,6 +661,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     return gemm(m, site, LAYOUT_KK, wepi, M, N, K, A, K, B, K, C, ldc, ex, DT_FP8_A5B4, true);
   };
 
+  m.ov_next = 0;
   if (clear_flag) fill_f32((float*)flag, 1, 0.f, st);
   // fp8: the weights' codes and scales are made here, unless the caller
   // knows they are those of the previous step (unchanged weights)
@@ -728,16 +771,25 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   void* dm = m.ws + m.dm;
   const bool dn_act = dt == DT_BF16 && !f8 && norm_chunks(d) != 0;
   const int epi_dn = dn_act ? EPI_STORE : EPI_STORE_F32;
+  float* dh = at<float>(m, m.dh);
+  // the norm backward writes the two copies of dhA in turn, so that a
+  // weight gradient still reading one copy overlaps the next norm backward
+  void* const dhAb[2] = {m.ws + m.dhA, m.ws + m.dhA2};
+  hipEvent_t ev_dhA[2] = {nullptr, nullptr}, ev_du = nullptr, ev_dqkv = nullptr, ev_dz[2] = {nullptr, nullptr};
+  int kA = 1;
+  void* dhA = dhAb[0];
   auto norm_bwd = [&](const void* y, const float* rstd, int accumulate, unsigned* amax, bool dy_act) {
+    kA ^= 1;
+    int r = wait_for(ev_dhA[kA]);
+    if (r) return r;
+    dhA = dhAb[kA];
     const double dy_b = dy_act ? 2.0 : 4.0;   // bytes per dy element read
     prof_begin(m, "rmsnorm_bwd", (double)BT * d * (dy_b + 4.0 + 4.0 * accumulate + 2.0 * es_d), 1,
                norm_label("rmsnorm_bwd"));
-    const int r = rmsnorm_bwd(dt, dm, dy_act, y, rstd, at<float>(m, m.dh), m.ws + m.dhA, BT, d, accumulate, st, amax);
+    r = rmsnorm_bwd(dt, dm, dy_act, y, rstd, at<float>(m, m.dh), dhA, BT, d, accumulate, st, amax);
     prof_end(m);
     return r ? fail(GPT_EINVAL, "rmsnorm_bwd variant not built") : GPT_OK;
   };
-  float* dh = at<float>(m, m.dh);
-  void* dhA = m.ws + m.dhA;
   // Cross-entropy + lm_head backward, one vocabulary chunk of VOCAB_CHUNK
   // columns at a time: the chunk's logits are recomputed and its logit
   // gradient dz = (softmax - onehot) * grad_scale / BT formed in the
@@ -754,12 +806,15 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     ex.beta = grad_scale / (float)BT;
     ex.col0 = v0;
     const long uoff = P.U + (long)v0 * d;
-    if ((rc = gemm(m, "gemm_lm_head_xent_bwd", LAYOUT_KK, EPI_XENT_BWD, BT, vn, d, m.ws + m.nL, d, wp(uoff), d,
-                   m.ws + m.dz, vn, ex)))
+    const int kz = (v0 / VOCAB_CHUNK) & 1;   // chunks alternate between two dz buffers
+    void* dz = kz ? m.ws + m.dz2 : m.ws + m.dz;
+    if ((rc = wait_for(ev_dz[kz]))) return rc;
+    if ((rc = gemm(m, "gemm_lm_head_xent_bwd", LAYOUT_KK, EPI_XENT_BWD, BT, vn, d, m.ws + m.nL, d, wp(uoff), d, dz,
+                   vn, ex)))
       return rc;
     const int epi = !vchunked ? epi_dn : v0 == 0 ? EPI_STORE_F32 : EPI_ACCUM_F32;
-    if ((rc = gemm(m, "dgrad_lm_head", LAYOUT_KN, epi, BT, d, vn, m.ws + m.dz, vn, wp(uoff), d, dm, d))) return rc;
-    if ((rc = wgrad("wgrad_lm_head", vn, d, BT, m.ws + m.dz, vn, m.ws + m.nL, d, grads + uoff, d))) return rc;
+    if ((rc = gemm(m, "dgrad_lm_head", LAYOUT_KN, epi, BT, d, vn, dz, vn, wp(uoff), d, dm, d))) return rc;
+    if ((rc = wgrad("wgrad_lm_head", vn, d, BT, dz, vn, m.ws + m.nL, d, grads + uoff, d, &ev_dz[kz]))) return rc;
   }
   if ((rc = norm_bwd(m.ws + m.nL, at<float>(m, m.rstdL), 0, amx(s.L - 1, SL_DH2), dn_act && !vchunked))) return rc;
   for (int l = s.L - 1; l >= 0; --l) {
@@ -784,14 +839,15 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                        slot(l, SL_N2))))
         return rc;
     } else {
+      if ((rc = wait_for(ev_du))) return rc;
       if ((rc = gemm(m, "dgrad_w2_drelu2", LAYOUT_KN, EPI_DRELU2, BT, F, d, dhA, d, wp(P.W2[l]), F, m.ws + m.du, F,
                      ex)))
         return rc;
-      if ((rc = wgrad("wgrad_w2", d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F)))
+      if ((rc = wgrad("wgrad_w2", d, F, BT, dhA, d, m.ws + Ly.g, F, grads + P.W2[l], F, &ev_dhA[kA])))
         return rc;
       if ((rc = gemm(m, "dgrad_w1", LAYOUT_KN, epi_dn, BT, d, F, m.ws + m.du, F, wp(P.W1[l]), d, dm, d)))
         return rc;
-      if ((rc = wgrad("wgrad_w1", F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d, grads + P.W1[l], d)))
+      if ((rc = wgrad("wgrad_w1", F, d, BT, m.ws + m.du, F, m.ws + Ly.n2, d, grads + P.W1[l], d, &ev_du)))
         return rc;
     }
     if ((rc = norm_bwd(m.ws + Ly.n2, at<float>(m, Ly.rstd2), 1, amx(l, SL_DH1), dn_act))) return rc;
@@ -806,9 +862,10 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     } else {
       if ((rc = gemm(m, "dgrad_o", LAYOUT_KN, EPI_STORE, BT, d, d, dhA, d, wp(P.Wo[l]), d, m.ws + m.dO, d)))
         return rc;
-      if ((rc = wgrad("wgrad_o", d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d)))
+      if ((rc = wgrad("wgrad_o", d, d, BT, dhA, d, m.ws + Ly.o, d, grads + P.Wo[l], d, &ev_dhA[kA])))
         return rc;
     }
+    if ((rc = wait_for(ev_dqkv))) return rc;   // the attention backward rewrites dqkv
     prof_begin(m, "attn_bwd_pre", (double)BT * d * 3.0 * es_d + (double)s.B * H * s.Tp * 4.0, 1, KLV("attn_bwd_pre_kernel", "attn_bwd_pre128_kernel"));
     attn_bwd_pre(dt, m.ws + m.dO, m.ws + Ly.o, at<float>(m, m.Dv), m.ws + m.dOT, s.B, s.T, s.Tp, H, Dh, st);
     prof_end(m);
@@ -850,7 +907,8 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
       if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, epi_dn, BT, d, Nqkv, m.ws + m.dqkv, Nqkv, wp(P.Wqkv[l]), d, dm,
                      d)))
         return rc;
-      if ((rc = wgrad("wgrad_qkv", Nqkv, d, BT, m.ws + m.dqkv, Nqkv, m.ws + Ly.n1, d, grads + P.Wqkv[l], d)))
+      if ((rc = wgrad("wgrad_qkv", Nqkv, d, BT, m.ws + m.dqkv, Nqkv, m.ws + Ly.n1, d, grads + P.Wqkv[l], d,
+                      &ev_dqkv)))
         return rc;
     }
     if ((rc = norm_bwd(m.ws + Ly.n1, at<float>(m, Ly.rstd1), 1, amx(l - 1, SL_DH2), dn_act))) return rc;
@@ -859,6 +917,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
              "sort_keys_kernel + embed_bwd_runs_kernel");
   embed_bwd(tokens, dh, grads + P.E, BT, d, V, at<uint32_t>(m, m.keys), accumulate, st);
   prof_end(m);
+  if (ev_last) HIP_TRY(hipStreamWaitEvent(st, ev_last, 0));   // join: every weight gradient is written
   HIP_TRY(hipGetLastError());
   return GPT_OK;
 }
@@ -988,6 +1047,20 @@ int gpt_create(const gpt_config* cfg, gpt_model** out) {
   m->st = (hipStream_t)cfg->stream;
   m->ws = (char*)cfg->workspace;
   m->W = (const char*)cfg->weights;
+  // the second stream of the overlapped weight gradients (default priority)
+  // and its fork / join events
+  {
+    hipError_t e = hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking);
+    for (int i = 0; e == hipSuccess && i < OV_EVENTS; ++i) {
+      hipEvent_t ev;
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e == hipSuccess) m->ov_ev.push_back(ev);
+    }
+    if (e != hipSuccess) {
+      delete m;
+      return fail(GPT_EHIP, std::string("second stream / events: ") + hipGetErrorString(e));
+    }
+  }
   const int half = m->s.Dh / 2;
   std::vector<float> c((size_t)m->s.T * half), sn((size_t)m->s.T * half);
   rope_table(m->s, c.data(), sn.data());
@@ -1058,6 +1131,12 @@ int gpt_step_micro(gpt_model* m, const int32_t* tokens, const int32_t* targets, 
 }
 
 void gpt_destroy(gpt_model* m) { delete m; }
+
+int gpt_overlap_enable(gpt_model* m, int on) {
+  if (!m) return fail(GPT_ENULL, "model is NULL");
+  m->overlap = on != 0;
+  return GPT_OK;
+}
 
 int gpt_debug_tensor(gpt_model* m, int which, int layer, void** ptr, int64_t* rows, int64_t* cols,
                      int* elem_bytes) {

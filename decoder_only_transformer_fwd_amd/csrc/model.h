@@ -39,6 +39,9 @@ constexpr int MAX_MICRO = 1024;
 // the lm_head's input- and weight-gradient products, and overwritten by the
 // next chunk's.
 constexpr int VOCAB_CHUNK = 8192;
+// fork / join events of the overlapped weight gradients per step (two per
+// product: 4 per layer and 2 per vocabulary chunk)
+constexpr int OV_EVENTS = 1024;
 inline size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 
 struct Shape {
@@ -149,6 +152,18 @@ struct gpt_model {
     float scale = 0.f;
   } mg;
   bool prof_on = false;
+  // Weight-gradient products of the backward run on a second stream of the
+  // handle, overlapping the input-gradient chain (which alone feeds the next
+  // layer): `side` is created by gpt_create (default priority), forks and
+  // joins are events from the ring `ov_ev`.  Off with profiling (so that
+  // every launch is timed alone), for GPT_FP8 (its weight gradients read
+  // transient codes), or by gpt_overlap_enable(m, 0).
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> ov_ev;
+  size_t ov_next = 0;
+  bool overlap = true;
+  size_t splitk2 = 0, splitk2_floats = 0;
+  size_t dhA2 = 0, dz2 = 0;          // second copies of dhA and dz, alternated
   std::vector<Site> sites;
   std::vector<hipEvent_t> ev_pool;
   size_t ev_used = 0;
@@ -157,6 +172,8 @@ struct gpt_model {
   double cur_work = 0.0;
   ~gpt_model() {
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : ov_ev) (void)hipEventDestroy(e);
+    if (side) (void)hipStreamDestroy(side);
     if (mg.exec) (void)hipGraphExecDestroy(mg.exec);
     if (mg.graph) (void)hipGraphDestroy(mg.graph);
     if (dg.exec) (void)hipGraphExecDestroy(dg.exec);

@@ -27,7 +27,7 @@ import numpy as np
 __all__ = [
     "GPTShape", "PRESETS", "preset", "param_shapes", "layer_windows",
     "make_weights", "make_tokens", "bf16_bits_from_f32", "bf16_bits_to_f64",
-    "zipf_probabilities", "weights_f64", "grad_sample_indices",
+    "zipf_probabilities", "weights_f64", "grad_sample_indices", "grad_full_rows",
 ]
 
 
@@ -196,6 +196,19 @@ def make_tokens(s: GPTShape) -> Tuple[np.ndarray, np.ndarray]:
         raise ValueError(s.token_dist)
     ids = ids.astype(np.int32)
     return np.ascontiguousarray(ids[:, :-1]), np.ascontiguousarray(ids[:, 1:])
+
+
+def grad_full_rows(s: GPTShape, X: np.ndarray, seed: int = 4321) -> Dict[str, np.ndarray]:
+    """Seeded row indices (sorted, int64) of three gradients whose rows the
+    full-size checks compare whole: 256 embedding rows among the ids the
+    batch X uses, 64 rows of layer 0's Wq and 64 of the last layer's W1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seen = np.unique(X)
+    out = {"E": np.sort(rng.choice(seen, size=min(256, seen.size), replace=False)).astype(np.int64)}
+    for name in ("L0.Wq", f"L{s.depth - 1}.W1"):
+        r = dict(param_shapes(s))[name][0]
+        out[name] = np.sort(rng.choice(r, size=min(64, r), replace=False)).astype(np.int64)
+    return out
 
 
 def grad_sample_indices(s: GPTShape, n_per_tensor: int, seed: int = 1234) -> Dict[str, np.ndarray]:

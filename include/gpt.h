@@ -258,6 +258,20 @@ int gpt_decode(gpt_model* model, const int32_t* tokens, int pos, void* kv_cache,
  * caller-owned.  GPT_EINVAL for a bad config, GPT_ENULL for a NULL output. */
 int gpt_rope_table(const gpt_config* cfg, float* cos_out, float* sin_out);
 
+/* Overlap of the backward's weight-gradient products (on by default).  The
+ * weight gradients feed nothing else in the step, so the handle runs them on
+ * a second stream of its own (created by gpt_create, default priority),
+ * concurrently with the chain of input gradients; events order them after
+ * their inputs and before any reuse of those inputs' buffers, and the step
+ * waits for them before it returns (or, in gpt_step_micro's graph, before
+ * the graph ends).  on = 0 runs every product on cfg->stream in program
+ * order (as profiling does).  The two modes plan the weight gradients
+ * differently (overlapped: unsplit; in order: split along K where the
+ * output has too few tiles to fill the GPU, with the partial sums added in
+ * split order), so each is bitwise reproducible and they agree to fp32
+ * summation-order rounding.  GPT_FP8 models always run in order. */
+int gpt_overlap_enable(gpt_model* model, int on);
+
 /* Release the handle (host memory only). */
 void gpt_destroy(gpt_model* model);
 

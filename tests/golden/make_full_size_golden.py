@@ -3,8 +3,12 @@
 For each full workload (d12, d20, d24, and d24-fp8, whose linear-layer
 operands the oracle encodes in fp8 as that workload's method does) this runs
 the fp64 oracle once on the seeded inputs and stores:
-the loss, the L2 norm of every gradient tensor, and the gradient values at
-seeded sample positions (``gpt_inputs.grad_sample_indices``, 2048 per tensor).
+the loss, the L2 norm of every gradient tensor, the gradient values at
+seeded sample positions (``gpt_inputs.grad_sample_indices``, 2048 per
+tensor), and complete rows of three gradients (``gpt_inputs.grad_full_rows``):
+the embedding rows of 256 seeded ids among those the batch uses, 64 seeded
+rows of layer 0's Wq and 64 of the last layer's W1, each row whole, so that
+the tests can compare them element by element.
 Only ``oracle/`` and ``gpt_inputs`` are used.
 
 Usage:  python tests/golden/make_full_size_golden.py d12 d20 d24 d24-fp8
@@ -36,9 +40,12 @@ def run(name: str) -> None:
     names = [n for n, _ in gi.param_shapes(s)]
     samples = np.stack([G[n].reshape(-1)[idx[n]] for n in names])
     norms = np.array([np.linalg.norm(G[n]) for n in names])
+    rows = gi.grad_full_rows(s, X)
+    full = {f"rows_{n}": G[n][r].astype(np.float32) for n, r in rows.items()}
     path = os.path.join(OUT, f"oracle_{name}.npz")
     np.savez_compressed(path, loss=np.float64(loss), names=np.array(names), norms=norms,
-                        samples=samples.astype(np.float64), n_samples=N_SAMPLES, seconds=dt)
+                        samples=samples.astype(np.float64), n_samples=N_SAMPLES, seconds=dt,
+                        row_names=np.array(list(rows)), **full)
     print(f"{name}: loss {loss:.9f}  oracle {dt:.1f}s -> {path}", flush=True)
 
 

@@ -161,7 +161,8 @@ def test_micro_batch_graph_matches_eager_steps(name):
     """gpt_step_micro (n micro-batches replayed as one captured graph) gives
     the gradients and losses of n gpt_step_accum calls bit for bit, on every
     replay, with eager work and synchronisation between replays; with
-    profiling on it runs eagerly and agrees too.  (fp8: the call quantises
+    profiling on it runs eagerly, every product in order, and agrees with
+    in-order steps.  (fp8: the call quantises
     the unchanged weights once, the separate calls once each, to the same
     codes.)"""
     import decoder_only_transformer_fwd_amd as G
@@ -199,10 +200,18 @@ def test_micro_batch_graph_matches_eager_steps(name):
     sess.grads.copy_(ref)
     sess.step_micro(Xd, Yd, 1.0 / n, accumulate=True)
     assert bool((sess.grads == ref2).all())
+    # profiled, the micro-batches run eagerly with every product in order on
+    # one stream: the same bits as in-order accumulating steps
+    sess.overlap(False)
+    for i in range(n):
+        sess.set_tokens(Xm[i], Ym[i])
+        sess.step_accum(1.0 / n, accumulate=i > 0)
+    ref_ordered = sess.grads.clone()
+    sess.overlap(True)
     sess.profile(True)
     losses = sess.step_micro(Xd, Yd, 1.0 / n, accumulate=False)
     sess.profile(False)
-    assert losses == ref_losses and bool((sess.grads == ref).all())
+    assert losses == ref_losses and bool((sess.grads == ref_ordered).all())
     # an out-of-range id in the last micro-batch is reported
     Yb = Yd.clone()
     Yb[n - 1, 0, 3] = s.vocab
