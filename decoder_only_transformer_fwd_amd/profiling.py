@@ -11,7 +11,10 @@
     python -m decoder_only_transformer_fwd_amd.profiling traffic --fetch F.csv --write W.csv
             --copy-fetch CF.csv --copy-write CW.csv --copy-mib 1024 --command C
         per-kernel HBM bytes per dispatch from two --pmc passes, each scaled by
-        the same counter's reading for the plain copy.
+        the same counter's reading for the plain copy;
+
+    python -m decoder_only_transformer_fwd_amd.profiling report B1.json B2.json ... --command C
+        one table row per bench.py JSON line.
 
 The kernel names in rocprofv3's CSV output are the mangled template names;
 GEMM instantiations are decoded into their tile parameters.
@@ -139,8 +142,8 @@ def traffic_md(fetch: str, write: str, copy_fetch: str, copy_write: str, copy_mi
            "| kernel | dispatches | read MB / dispatch | written MB / dispatch | HBM GB/s |",
            "|---|---:|---:|---:|---:|"]
     if stats:
-        out[-3:-3] = ["", "HBM GB/s: the measured bytes per dispatch over the kernel's average duration in a "
-                          "kernel trace of the same command (`--kernel-trace --stats`, its own run)."]
+        out[-3:-3] = ["", "HBM GB/s: the measured bytes per dispatch over the kernel's average duration in the "
+                          "workload's kernel trace (`--kernel-trace --stats`, its own run)."]
     labels = _decode_all(list(agg))
     dur = _avg_ns(stats)
     for name, (n, rd, wr) in sorted(agg.items(), key=lambda kv: -(kv[1][1] + kv[1][2]))[:top]:
@@ -183,6 +186,38 @@ def mfma_md(pmc: str, stats: str, command: str, note: str = "", top: int = 30) -
         c = cyc / n
         du = f"{dur[name] / 1e3:.1f}" if name in dur else "-"
         out.append(f"| {labels[name]} | {n} | {du} | {c:.3g} | {100 * b / n / N_SIMD / c:.0f} % |")
+    return "\n".join(out) + "\n"
+
+
+def report_md(paths, command: str, note: str = "") -> str:
+    """One row per bench JSON line (a file each): throughput, MFU, the
+    dominant kernel's roofline and the oracle's CPU rate."""
+    import json
+    out = ["# Training step per workload: throughput, MFU, roofline, CPU oracle", "",
+           "Command (from the repository root, on one MI355X), once per workload W:", "", "```", command, "```", ""]
+    if note:
+        out += [note, ""]
+    out += ["| workload | precision | tokens / step | ms / step | tokens/s | MFU | dominant kernel (sites) | "
+            "bound | achieved | peak | frac | HBM traffic MB / launch | share of step | CPU oracle tokens/s (cores) |",
+            "|---|---|---:|---:|---:|---:|---|---|---:|---:|---:|---:|---:|---:|"]
+    for p in paths:
+        r = json.loads(open(p).read().strip().splitlines()[-1])
+        c, f = r["config"], r["roofline"]
+        cb = r.get("cpu_baseline")
+        cpu = f"{cb['value']:.1f} ({cb['cores']})" if cb else "-"
+        tr = f"{f['traffic'] / 1e6:.1f}" if f.get("traffic") else "-"
+        sites = ", ".join(f.get("sites", []))
+        out.append(f"| {c['workload']} | {c['precision']} | {c['tokens_per_step']} | {r['ms_per_step']:.2f} | "
+                   f"{r['value']:.0f} | {100 * r['mfu']:.1f} % | {f['kernel']} ({sites}) | {f['bound']} | "
+                   f"{f['achieved']:.1f} {f['unit']} | {f['peak']:.1f} | {f['frac']:.3f} | {tr} | "
+                   f"{100 * f.get('share_of_step', 0):.1f} % | {cpu} |")
+    samples = []
+    for p in paths:
+        r = json.loads(open(p).read().strip().splitlines()[-1])
+        if r.get("cpu_baseline"):
+            samples.append(f"{r['config']['workload']}: {r['cpu_baseline']['sample']}")
+    if samples:
+        out += ["", "CPU oracle samples:", ""] + [f"- {x}" for x in samples]
     return "\n".join(out) + "\n"
 
 
@@ -255,11 +290,17 @@ def main(argv=None) -> int:
     for k in ("pmc", "stats", "command"):
         u.add_argument("--" + k, required=True)
     u.add_argument("--note", default="")
+    r = sub.add_parser("report")
+    r.add_argument("json", nargs="+")
+    r.add_argument("--command", required=True)
+    r.add_argument("--note", default="")
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         _copy(a.mib)
     elif a.cmd == "stats":
         sys.stdout.write(stats_md(a.csv, a.title, a.command, a.note))
+    elif a.cmd == "report":
+        sys.stdout.write(report_md(a.json, a.command, a.note))
     elif a.cmd == "mfma":
         sys.stdout.write(mfma_md(a.pmc, a.stats, a.command, a.note))
     else:
