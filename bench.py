@@ -163,6 +163,9 @@ def main() -> int:
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the weight-gradient products in order on the step's stream "
                          "(gpt_overlap_enable(m, 0)) instead of on the handle's second stream")
+    ap.add_argument("--no-rope-epilogue", action="store_true",
+                    help="run the rotary step and QK norm as a separate pass after the QKV product "
+                         "(gpt_rope_epilogue_enable(m, 0)) instead of in its epilogue")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)")
@@ -185,6 +188,8 @@ def main() -> int:
     del W8
     if args.no_overlap:
         sess.overlap(False)
+    if args.no_rope_epilogue:
+        sess.rope_epilogue(False)
     if n_acc == 1:
         X, Y = gi.make_tokens(s)
         sess.set_tokens(X, Y)
@@ -327,7 +332,9 @@ def main() -> int:
                    "optimizer": "muon+adamw" if args.optimizer else None,
                    "window": s.window, "window_pattern": s.window_pattern, "token_dist": s.token_dist,
                    "precision": s.precision, "overlapped_weight_gradients": not args.no_overlap and
-                   s.precision != "fp8"},
+                   s.precision != "fp8",
+                   "rope_in_qkv_epilogue": not args.no_rope_epilogue and s.precision == "bf16" and
+                   s.head_dim == 128 and s.seq_len % 64 == 0},
         "mfu": mfu,
         "mfu_peak_tflops": peak / 1e12,
         "model_flops_per_token": Mx.flops_per_token(s),

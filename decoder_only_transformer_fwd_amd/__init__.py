@@ -21,7 +21,8 @@ GPT_FP32, GPT_BF16, GPT_FP8 = 0, 1, 2
 
 EXPORTED = ["gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_step_micro",
             "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
-            "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_rope_table", "gpt_overlap_enable", "gpt_destroy",
+            "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_rope_table", "gpt_overlap_enable",
+            "gpt_rope_epilogue_enable", "gpt_destroy",
             "gpt_debug_tensor", "gpt_gemm", "gpt_gemm_noalloc", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
             "gpt_profile_sites", "gpt_profile_get", "gpt_strerror", "gpt_last_error"]
 
@@ -88,6 +89,7 @@ def _load():
     lib.gpt_decode.argtypes = [P, P, I, P, P]
     lib.gpt_rope_table.argtypes = [ctypes.POINTER(gpt_config), P, P]
     lib.gpt_overlap_enable.argtypes = [P, I]
+    lib.gpt_rope_epilogue_enable.argtypes = [P, I]
     lib.gpt_destroy.argtypes = [P]
     lib.gpt_destroy.restype = None
     lib.gpt_debug_tensor.argtypes = [P, I, I, ctypes.POINTER(P), ctypes.POINTER(I64), ctypes.POINTER(I64),
@@ -108,7 +110,7 @@ def _load():
     for name in ("gpt_param_layout", "gpt_workspace_bytes", "gpt_create", "gpt_step", "gpt_step_accum", "gpt_step_micro",
                  "gpt_optim_state_bytes", "gpt_optim_init", "gpt_optim_step", "gpt_optim_master",
                  "gpt_kv_cache_bytes", "gpt_prefill", "gpt_decode", "gpt_rope_table", "gpt_overlap_enable",
-                 "gpt_debug_tensor", "gpt_gemm", "gpt_gemm_noalloc", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
+                 "gpt_rope_epilogue_enable", "gpt_debug_tensor", "gpt_gemm", "gpt_gemm_noalloc", "gpt_fp8_quantize", "gpt_gemm_fp8", "gpt_profile_enable",
                  "gpt_profile_sites", "gpt_profile_get"):
         getattr(lib, name).restype = I
     return lib
@@ -255,6 +257,10 @@ def gpt_rope_table(cfg: gpt_config) -> Tuple[np.ndarray, np.ndarray]:
 
 def gpt_overlap_enable(model: int, on: bool) -> None:
     _check(_lib.gpt_overlap_enable(model, 1 if on else 0), "gpt_overlap_enable")
+
+
+def gpt_rope_epilogue_enable(model: int, on: bool) -> None:
+    _check(_lib.gpt_rope_epilogue_enable(model, 1 if on else 0), "gpt_rope_epilogue_enable")
 
 
 def gpt_destroy(model: int) -> None:
@@ -476,6 +482,9 @@ class Session:
 
     def overlap(self, on: bool = True) -> None:
         gpt_overlap_enable(self.handle, on)
+
+    def rope_epilogue(self, on: bool = True) -> None:
+        gpt_rope_epilogue_enable(self.handle, on)
 
     def profile_sites(self) -> List[dict]:
         return [gpt_profile_get(self.handle, i) for i in range(gpt_profile_sites(self.handle))]

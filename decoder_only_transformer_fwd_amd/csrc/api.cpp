@@ -483,13 +483,24 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   if (a.alpha == 0.f) a.alpha = 1.f;
   GemmPlan g = plan_gemm(dty, layout, M, N, K);
   if (epi == EPI_XENT_FWD) g = GemmPlan{m.xent_tile, 1, K};
+  // the rotary epilogue runs the planned tile with one head of columns per wave
+  if (epi == EPI_ROPE_QKN) g = GemmPlan{g.tile == TILE_256x256_PP4 ? TILE_256x256_PP4_H : TILE_128x128_H, 1, K};
   if (epi != EPI_STORE_F32 && !(wgrad && epi == EPI_ACCUM_F32)) g.splits = 1, g.k_split = K;
   if (g.splits > 1 && ldc != N) g.splits = 1, g.k_split = K;
-  // A weight gradient on the second stream runs unsplit: it needs not fill
-  // the GPU alone, since the input-gradient chain runs beside it, and it
-  // saves the partial sums' traffic and their reduction (measured: d24 step
-  // 98.3 -> 95.9 ms; in order on one stream, split-K is faster).
-  if (wgrad && m.side && m.st == m.side) g.splits = 1, g.k_split = K;
+  // A weight gradient on the second stream needs not fill the GPU alone,
+  // since the input-gradient chain runs beside it: it takes the fewest K
+  // splits (at most the planned ones) that give SIDE_WG_TARGET work-groups.
+  // That saves most partial sums and their reduction while a product of a
+  // few tiles does not run alone for its whole K.  Measured (ms per step):
+  // unsplit d12 29.3 / d24 96.2 / d20 138.4; 64 work-groups 22.3 / 95.1 /
+  // 136.6; 128 21.7 / 95.2 / 139.3; the planned splits 22.0 / 98.9 / 140.7.
+  if (wgrad && m.side && m.st == m.side) {
+    const long tiles = (long)((M + tile_bm(g.tile) - 1) / tile_bm(g.tile)) * ((N + tile_bn(g.tile) - 1) / tile_bn(g.tile));
+    int sp = 1;
+    while (sp < g.splits && tiles * sp < SIDE_WG_TARGET) ++sp;
+    if (sp == 1) g.splits = 1, g.k_split = K;
+    else if (sp < g.splits) g.splits = gemm_real_splits(dty, K, sp, &g.k_split);
+  }
   if (g.splits > 1) {
     // the partial sums must fit the workspace's split-K region (sized by
     // build_layout from the same plans); refuse rather than write past it
@@ -678,6 +689,9 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   prof_begin(m, "embed_fwd", (double)BT * d * (es_d + 4.0) + BT * 8.0, 1, KL("embed_fwd_kernel"));
   embed_fwd(dt, tokens, targets, wp(P.E), h, BT, d, V, flag, st);
   prof_end(m);
+  // bf16 heads of 128 over whole 64-token blocks: the rotary step and QK norm
+  // run in the QKV product's epilogue
+  const bool rope_fused = dt == DT_BF16 && Dh == 128 && s.T % 64 == 0 && m.rope_epilogue;
   for (int l = 0; l < s.L; ++l) {
     auto& Ly = m.lay[l];
     const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
@@ -689,16 +703,28 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
             at<float>(m, Ly.rstd1));
       rc = gemm8("gemm_qkv", DT_FP8_A4B4, EPI_STORE, BT, Nqkv, d, q8row, m.ws + Ly.wq[0], m.ws + Ly.qkv, Nqkv,
                  slot(l, SL_N1), slot(l, SL_WQKV));
+    } else if (rope_fused) {
+      // the product's epilogue rotates and normalises q and k and writes the
+      // transposed copies
+      GemmArgs ex{};
+      ex.rope_cos = cosb; ex.rope_sin = sinb; ex.rqk = at<float>(m, Ly.rqk);
+      ex.qT = m.ws + Ly.qT; ex.kT = m.ws + Ly.kT; ex.vT = m.ws + Ly.vT;
+      ex.seqT = s.T; ex.nH = H; ex.nHkv = Hkv; ex.eps = s.eps;
+      rc = gemm(m, "gemm_qkv_rope", LAYOUT_KK, EPI_ROPE_QKN, BT, Nqkv, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d,
+                m.ws + Ly.qkv, Nqkv, ex);
     } else {
       rc = gemm(m, "gemm_qkv", LAYOUT_KK, EPI_STORE, BT, Nqkv, d, m.ws + Ly.n1, d, wp(P.Wqkv[l]), d, m.ws + Ly.qkv,
                 Nqkv);
     }
     if (rc) return rc;
-    // reads q, k, v; writes q^, k^ in place and the transposed q^, k^, v
-    prof_begin(m, "rope_qknorm_fwd", (double)BT * (3.0 * d + 5.0 * s.dkv) * es_d + BT * (double)(H + Hkv) * 4.0, 1,
-               KLV("rope_qknorm_fwd_kernel", "rope_qknorm_fwd128_kernel"));
-    rope_qknorm_fwd(dt, m.ws + Ly.qkv, at<float>(m, Ly.rqk), m.ws + Ly.qT, m.ws + Ly.kT, m.ws + Ly.vT, cosb, sinb,
-                    s.B, s.T, s.Tp, H, Hkv, Dh, s.eps, st);
+    if (!rope_fused || f8) {
+      // reads q, k, v; writes q^, k^ in place and the transposed q^, k^, v
+      prof_begin(m, "rope_qknorm_fwd", (double)BT * (3.0 * d + 5.0 * s.dkv) * es_d + BT * (double)(H + Hkv) * 4.0, 1,
+                 KLV("rope_qknorm_fwd_kernel", "rope_qknorm_fwd128_kernel"));
+      rope_qknorm_fwd(dt, m.ws + Ly.qkv, at<float>(m, Ly.rqk), m.ws + Ly.qT, m.ws + Ly.kT, m.ws + Ly.vT, cosb, sinb,
+                      s.B, s.T, s.Tp, H, Hkv, Dh, s.eps, st);
+      prof_end(m);
+    }
     AttnArgs aa{};
     aa.qkv = m.ws + Ly.qkv; aa.qT = m.ws + Ly.qT; aa.kT = m.ws + Ly.kT; aa.vT = m.ws + Ly.vT;
     aa.o = m.ws + Ly.o; aa.lse2 = at<float>(m, Ly.lse2);
@@ -706,7 +732,6 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     aa.scale = 1.0f / std::sqrt((float)Dh);
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Dh));
     aa.amax_o = amx(l, SL_O);
-    prof_end(m);
     prof_begin(m, s.win[l] < s.T ? "attn_fwd_window" : "attn_fwd_causal", 4.0 * Dh * pairs, 0,
                KLD("attn_fwd_kernel"));
     if (attn_fwd(dt, Dh, aa, st)) return fail(GPT_EINVAL, "attention variant not instantiated");
@@ -1135,6 +1160,12 @@ void gpt_destroy(gpt_model* m) { delete m; }
 int gpt_overlap_enable(gpt_model* m, int on) {
   if (!m) return fail(GPT_ENULL, "model is NULL");
   m->overlap = on != 0;
+  return GPT_OK;
+}
+
+int gpt_rope_epilogue_enable(gpt_model* m, int on) {
+  if (!m) return fail(GPT_ENULL, "model is NULL");
+  m->rope_epilogue = on != 0;
   return GPT_OK;
 }
 

@@ -213,6 +213,89 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
   tn = in_group / gsize;
 }
 
+// Rotary embedding + QK RMS norm of one 32-row block of the fused QKV
+// product (EPI_ROPE_QKN), in the accumulators of a wave that owns one whole
+// head of 128 columns: lane (l32, g) holds row l32 of the block and columns
+// j*32 + 8q + 4g + e (j < 4), so the rotation pair (x[i], x[i+64]) of each of
+// its values is in the same lane (j and j+2), and the other half of the
+// head's squares sits in lane l32 ^ 32.  q and k heads: rotate each pair by
+// the token's angle, scale by rstd = 1/sqrt(mean square + eps) (written by
+// the g = 0 lanes); v heads pass through.  Then the wave writes its 32
+// tokens x 128 dimensions transposed into its own LDS region `wr` and from
+// there 16-byte runs of 8 tokens into the transposed copy.  The accumulators
+// leave holding the results (alpha applied); the caller stores them
+// row-major through the same region.  No work-group barrier.
+__device__ __forceinline__ void rope_qkn_block(const GemmArgs& p, floatx16 (&acc)[4], char* wr, int lane,
+                                               int mrow0, int hcol, float alpha) {
+  const int g = lane >> 5, l32 = lane & 31;
+  if (hcol >= p.N) return;                    // wave-uniform
+  const int H = p.nH, Hkv = p.nHkv;
+  const int slot = hcol >> 7;                 // head slot in the row
+  const int part = slot < H ? 0 : slot < H + Hkv ? 1 : 2;
+  const int m = mrow0 + l32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] *= alpha;
+  if (part < 2) {
+    const int tok = m % p.seqT;
+    floatx4 c[2][4], sn[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[j][q] = *(const floatx4*)(p.rope_cos + (long)tok * 64 + j * 32 + 8 * q + 4 * g);
+        sn[j][q] = *(const floatx4*)(p.rope_sin + (long)tok * 64 + j * 32 + 8 * q + 4 * g);
+      }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x1 = acc[j][4 * q + e], x2 = acc[j + 2][4 * q + e];
+          const float r1 = x1 * c[j][q][e] - x2 * sn[j][q][e];
+          const float r2 = x1 * sn[j][q][e] + x2 * c[j][q][e];
+          ss += r1 * r1 + r2 * r2;
+          acc[j][4 * q + e] = r1;
+          acc[j + 2][4 * q + e] = r2;
+        }
+    ss += __shfl_xor(ss, 32, 64);
+    const float r = 1.0f / sqrtf(ss / 128.f + p.eps);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] *= r;
+    if (g == 0 && m < p.M) p.rqk[(long)m * (H + Hkv) + slot] = r;
+  }
+  constexpr int LDT = 40;   // bf16 per transposed row: 32 tokens + padding (80 bytes, 16-byte aligned)
+  bf16* tb = (bf16*)wr;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tb[(j * 32 + 8 * q + 4 * g + e) * LDT + l32] = (bf16)acc[j][4 * q + e];
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  const int hh = part == 0 ? slot : part == 1 ? slot - H : slot - H - Hkv;
+  const int nh = part == 0 ? H : Hkv;
+  bf16* dst = (bf16*)(part == 0 ? p.qT : part == 1 ? p.kT : p.vT);
+#pragma unroll
+  for (int ps = 0; ps < 8; ++ps) {
+    const int dim = ps * 16 + (lane >> 2), tq = (lane & 3) * 8;
+    const int mf = mrow0 + tq;               // 8 tokens of one sequence (seqT % 64 == 0)
+    if (mf < p.M) {
+      const int b = mf / p.seqT, t = mf % p.seqT;
+      const u32x4 v = *(const u32x4*)(tb + dim * LDT + tq);
+      *(u32x4*)(dst + (((long)b * nh + hh) * 128 + dim) * p.seqT + t) = v;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // transposed reads done before the region is rewritten
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <typename TA, typename MF, int BM, int BN, int WGM, int WGN, int RB, int NS, bool A_KC, bool B_KC, int EPI,
           typename TC, bool PP, bool BATCHED>
 // Two waves per SIMD except for the 4-wave tiles whose accumulators need the
@@ -453,6 +536,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
   // ------------------------------------------------------------ epilogue
   float alpha = p.alpha;
   if constexpr (ES == 1) alpha = alpha / p.scale_a[0] / p.scale_b[0];
+  static_assert(E != EPI_ROPE_QKN || (WN == 128 && ES == 2), "rotary epilogue: one head of 128 per wave");
   if constexpr (EPI == EPI_XENT_FWD) {
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
@@ -504,8 +588,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
     // compiler cannot move a load above an earlier store that may alias it.
     constexpr bool PRELOAD = E == EPI_ACCUM_F32 || E == EPI_DRELU2 || E == EPI_AXPBY;
     float amax_acc = 0.f;   // RELU2 / DRELU2: largest |stored activation|
+    const float alpha_in = alpha;
+    if constexpr (E == EPI_ROPE_QKN) alpha = 1.f;   // applied by the rotary step
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
+      if constexpr (E == EPI_ROPE_QKN) rope_qkn_block(p, acc[i], region, lane, m0 + wm * WM + i * 32, n0 + wn * WN,
+                                                      alpha_in);
       floatx4 pre[PRELOAD ? 32 / RPS : 1];
       if constexpr (PRELOAD) {
         asm volatile("" ::: "memory");   // keep the next block's loads from being hoisted here
@@ -540,7 +628,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (WGM * WGN == 4 && BM * BN >= 256 *
         const int n = n0 + wn * WN + c4 * 4;
         if (m < p.M && n < p.N) {
           const long off = (long)m * p.ldc + n;
-          if constexpr (E == EPI_STORE) {
+          if constexpr (E == EPI_STORE || E == EPI_ROPE_QKN) {
             store4((TC*)p.C + off, v);
             if constexpr (SYM)
               if (tm != tn)
@@ -656,6 +744,8 @@ static constexpr TileCfg TILES[] = {
     {256, 256, 2, 4, 64, 4, true},   // TILE_256x256_PP4
     {256, 256, 2, 4, 64, 5, true},   // TILE_256x256_PP5
     {256, 128, 4, 2, 128, 3, true},  // TILE_256x128_PP3
+    {256, 256, 4, 2, 64, 4, true},   // TILE_256x256_PP4_H
+    {128, 128, 4, 1, 128, 2},        // TILE_128x128_H
 };
 int tile_bm(int tile) { return TILES[tile].bm; }
 int tile_bn(int tile) { return TILES[tile].bn; }
@@ -722,6 +812,16 @@ static int launch_epi(const GemmArgs& a, int layout, int epi, int tile, int spli
   GK_CASE(LAYOUT_KN, true, false, EPI_ACCUM_F32)   // the lm_head's input gradient over vocabulary chunks
   GK_CASE(LAYOUT_KN, true, false, EPI_DRELU2)
   GK_CASE(LAYOUT_KN, true, false, EPI_PARTIAL)
+  // the fused QKV product with its rotary epilogue: the two tiles whose
+  // waves own 128 columns
+  if constexpr (sizeof(TA) == 2) {
+    if (layout == LAYOUT_KK && epi == EPI_ROPE_QKN) {
+      if (tile == TILE_256x256_PP4_H) launch_cfg<TA, MF, TILE_256x256_PP4_H, true, true, EPI_ROPE_QKN, TC>(a, splits, st);
+      else if (tile == TILE_128x128_H) launch_cfg<TA, MF, TILE_128x128_H, true, true, EPI_ROPE_QKN, TC>(a, splits, st);
+      else return -1;
+      return 0;
+    }
+  }
   // weight gradients: grad [K][M] x activation [K][N]
   GK_CASE(LAYOUT_MN, false, false, EPI_STORE_F32)
   GK_CASE(LAYOUT_MN, false, false, EPI_ACCUM_F32)

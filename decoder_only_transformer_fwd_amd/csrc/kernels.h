@@ -41,6 +41,10 @@ enum Epi {
   // values the epilogue computed
   EPI_RELU2_F32 = 11,
   EPI_DRELU2_F32 = 12,
+  // the fused QKV product (bf16, heads of 128, one wave per head): rotate the
+  // q and k heads, RMS-normalise them, store q^, k^, v row-major (C), their
+  // rstd, and the transposed copies q^T, k^T, v^T
+  EPI_ROPE_QKN = 13,
 };
 
 // Work-group tiles (M x N); _W8 variants use 8 waves (2 x 4) instead of 4 (2 x 2).
@@ -53,6 +57,9 @@ enum Tile {
   // 8 waves in two ping-pong groups: 4 / 5 stages of 64-byte rows, 3 of 128
   TILE_256x256_PP4 = 10, TILE_256x256_PP5 = 11, TILE_256x128_PP3 = 12,
   TILE_COUNT = 13,
+  // the rotary epilogue's tiles (EPI_ROPE_QKN only): PP4 and 128x128 with the
+  // waves laid out so that each owns 128 whole columns, one head
+  TILE_256x256_PP4_H = 13, TILE_128x128_H = 14,
 };
 bool tile_needs_kc(int tile);   // usable only when both operands are K-contiguous
 // Readable template signature of the kernel a product launches (as profilers
@@ -85,6 +92,18 @@ struct GemmArgs {
   // Batched products (grid y = batch index): element strides between the
   // batch's A, B and C (aux shares C's); zero for a single product.
   long bsA, bsB, bsC;
+  // EPI_ROPE_QKN: the rotary table [seqT][64] (cos, sin); rstd out
+  // [M][nH + nHkv]; the transposed copies [B][heads][128][seqT] (seqT a
+  // multiple of 64, so that no padding columns exist); the C row holds nH q
+  // heads, then nHkv k heads, then nHkv v heads.
+  const float* rope_cos;
+  const float* rope_sin;
+  float* rqk;
+  void* qT;
+  void* kT;
+  void* vT;
+  int seqT, nH, nHkv;
+  float eps;
 };
 
 int gemm_launch(const GemmArgs& a, int dtype, int layout, int epi, int tile, int splits,

@@ -41,6 +41,8 @@ constexpr int MAX_MICRO = 1024;
 constexpr int VOCAB_CHUNK = 8192;
 // fork / join events of the overlapped weight gradients per step (two per
 // product: 4 per layer and 2 per vocabulary chunk)
+// work-groups a weight-gradient product on the second stream aims for
+constexpr long SIDE_WG_TARGET = 64;
 constexpr int OV_EVENTS = 1024;
 inline size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 
@@ -162,6 +164,7 @@ struct gpt_model {
   std::vector<hipEvent_t> ov_ev;
   size_t ov_next = 0;
   bool overlap = true;
+  bool rope_epilogue = true;   // the fused rotary epilogue where it applies (gpt_rope_epilogue_enable)
   size_t splitk2 = 0, splitk2_floats = 0;
   size_t dhA2 = 0, dz2 = 0;          // second copies of dhA and dz, alternated
   std::vector<Site> sites;

@@ -266,11 +266,24 @@ int gpt_rope_table(const gpt_config* cfg, float* cos_out, float* sin_out);
  * waits for them before it returns (or, in gpt_step_micro's graph, before
  * the graph ends).  on = 0 runs every product on cfg->stream in program
  * order (as profiling does).  The two modes plan the weight gradients
- * differently (overlapped: unsplit; in order: split along K where the
- * output has too few tiles to fill the GPU, with the partial sums added in
- * split order), so each is bitwise reproducible and they agree to fp32
- * summation-order rounding.  GPT_FP8 models always run in order. */
+ * differently (in order: split along K where the output has too few tiles
+ * to fill the GPU, with the partial sums added in split order; overlapped:
+ * the fewest of those splits that give 64 work-groups, since the product
+ * shares the GPU with the other stream), so each is bitwise reproducible
+ * and they agree to fp32 summation-order rounding.  GPT_FP8 models always
+ * run in order. */
 int gpt_overlap_enable(gpt_model* model, int on);
+
+/* The rotary step and QK norm in the QKV product's epilogue (on by
+ * default).  It applies to GPT_BF16 models with head_dim 128 and seq_len a
+ * multiple of 64; there the product rotates the fp32 accumulators of each q
+ * and k head (the pair (x[i], x[i+64]) by t * theta_i, "How It Works" in
+ * the nanochat User Guide), RMS-normalises the head and stores q^, k^, v
+ * with their transposed copies, instead of storing bf16 q, k, v for a
+ * separate pass to read back.  on = 0 runs that separate pass (which
+ * rotates the bf16-rounded product), as every other configuration does.
+ * The two agree to bf16 rounding. */
+int gpt_rope_epilogue_enable(gpt_model* model, int on);
 
 /* Release the handle (host memory only). */
 void gpt_destroy(gpt_model* model);

@@ -57,6 +57,15 @@ SMALL = {
                             vocab=1000, seq_len=200, batch=2, window=64, window_pattern="SL",
                             precision="bf16", token_dist="zipf", n_kv_head=1),
     "d24_gqa_short": gi.preset("d24", seq_len=384, batch=1, window=128, n_kv_head=4),
+    # sequences of 192 tokens, three rows: the 256- and 128-row tiles of the
+    # QKV product (with the rotary epilogue) straddle sequence boundaries and
+    # end past the last row
+    "bf16_t192": gi.GPTShape("bf16_t192", depth=2, d_model=1536, n_head=12, head_dim=128, mlp_hidden=2048,
+                             vocab=1000, seq_len=192, batch=3, window=64, window_pattern="SL",
+                             precision="bf16", token_dist="zipf"),
+    "gqa_t192": gi.GPTShape("gqa_t192", depth=2, d_model=512, n_head=4, head_dim=128, mlp_hidden=1024,
+                            vocab=1000, seq_len=192, batch=3, window=64, window_pattern="SL",
+                            precision="bf16", token_dist="zipf", n_kv_head=2),
     "gqa_fp8": gi.GPTShape("gqa_fp8", depth=2, d_model=256, n_head=2, head_dim=128, mlp_hidden=1024,
                            vocab=1000, seq_len=224, batch=2, window=64, window_pattern="SL",
                            precision="fp8", token_dist="zipf", n_kv_head=1),
