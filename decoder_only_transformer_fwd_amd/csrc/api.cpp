@@ -112,13 +112,13 @@ struct GemmPlan {
 
 
 // Tile and split-K choice, set from measurements of this kernel on MI355X at
-// the step's shapes: 8-wave 256x256 tiles for wide products, the 256x256
-// ping-pong tile for narrow input gradients with a long K, 128x128 (two
-// work-groups per CU) for narrow short products, and the ping-pong tile for
-// bf16 weight gradients (K = B*T, few
-// output tiles), which are split along K by a cost model: waves of
-// work-groups (512 resident at two per CU, 256 at one) times K steps per
-// split, plus the fp32 partial-sum reduction at ~5 TB/s.
+// the step's shapes: the 256x256 ping-pong tile for every bf16 product
+// (forward, input and weight gradients), 128x128 for fp8 and for fp32 (64x64
+// for small fp32 outputs).  Weight gradients (K = B*T, few output tiles) are
+// split along K by a cost model, over the ping-pong tile and, for bf16
+// outputs small enough to need many splits, 128x128 (two work-groups per
+// CU): waves of work-groups (512 resident at two per CU, 256 at one) times K
+// steps per split, plus the fp32 partial-sum reduction at ~5 TB/s.
 GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   GemmPlan g{TILE_64x64, 1, K};
   const bool f8 = dtype == DT_FP8_A4B4 || dtype == DT_FP8_A5B4;
@@ -128,9 +128,11 @@ GemmPlan plan_gemm(int dtype, int layout, int M, int N, int K) {
   } else if (dtype == DT_F32) {
     g.tile = (long)M * N >= 256L * 128 * 128 ? TILE_128x128 : TILE_64x64;
   } else if (layout == LAYOUT_KK) {
-    // ping-pong 256x256 unless both N and K are short (measured at the
-    // step's shapes: 16384 x {1536, 4608, 6144, 32768} x {1536, 6144})
-    g.tile = N >= 4096 || K >= 4096 ? TILE_256x256_PP4 : TILE_128x128;
+    // forward products: the ping-pong 256x256 tile at every step shape
+    // (measured against 128x128, 256x128 and 8-wave tiles at 16384 x
+    // {768 .. 4608} x {768 .. 6144}; in the d20 step the QKV product went
+    // 8.96 -> 7.58 ms and d12's W2 1.39 -> 1.25 ms per step)
+    g.tile = TILE_256x256_PP4;
   } else if (layout == LAYOUT_KN) {
     // input gradients: the ping-pong 256x256 tile measured best at every
     // step shape, narrow and wide
@@ -410,7 +412,13 @@ int build_layout(gpt_model& m) {
   m.dz2 = take(BT * std::min(s.V, VOCAB_CHUNK) * A);
   m.cosb = take((size_t)s.T * (s.Dh / 2) * 4);
   m.sinb = take((size_t)s.T * (s.Dh / 2) * 4);
+  // the embedding gradient's counting sort: sorted positions, ranks, per-chunk
+  // counts (chunks of 1024 positions), per-id totals and starts
   m.keys = take(BT * 4);
+  m.emb_rank = take(BT * 4);
+  m.emb_cnt = take((BT + 1023) / 1024 * (size_t)s.V * 4);
+  m.emb_tot = take((size_t)s.V * 4);
+  m.emb_start = take((size_t)s.V * 4);
   m.total = off;
   return GPT_OK;
 }
@@ -939,8 +947,9 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     if ((rc = norm_bwd(m.ws + Ly.n1, at<float>(m, Ly.rstd1), 1, amx(l - 1, SL_DH2), dn_act))) return rc;
   }
   prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * (accumulate ? 8.0 : 4.0) + BT * 8.0, 1,
-             "sort_keys_kernel + embed_bwd_runs_kernel");
-  embed_bwd(tokens, dh, grads + P.E, BT, d, V, at<uint32_t>(m, m.keys), accumulate, st);
+             "emb_rank_kernel + emb_prefix_kernel + emb_scan_kernel + emb_scatter_kernel + emb_runs_kernel");
+  embed_bwd(tokens, dh, grads + P.E, BT, d, V, at<int>(m, m.keys), at<int>(m, m.emb_rank), at<int>(m, m.emb_cnt),
+            at<int>(m, m.emb_tot), at<int>(m, m.emb_start), accumulate, st);
   prof_end(m);
   if (ev_last) HIP_TRY(hipStreamWaitEvent(st, ev_last, 0));   // join: every weight gradient is written
   HIP_TRY(hipGetLastError());

@@ -602,89 +602,125 @@ __global__ __launch_bounds__(1024) void mean_reduce_kernel(const float* __restri
 }
 
 // ------------------------------------------------------------------ embedding gradient
-// Sort keys (id << PB | position) in one work-group (bitonic, in LDS), so
-// that equal ids form runs in position order.  Then one work-group per run
-// head and 256-column slice sums the run's rows in order: deterministic.
-// Ids outside [0, vocab) get the key 0xFFFFFFFF and are skipped by the sum
-// (vocab <= 65536 and rows <= 32768 keep every valid key below 2^31).
-__global__ __launch_bounds__(1024) void sort_keys_kernel(const int32_t* __restrict__ tok, int rows, int pbits,
-                                                         int n2, int vocab, uint32_t* __restrict__ keys_out) {
-  extern __shared__ uint32_t sk[];
-  for (int i = threadIdx.x; i < n2; i += 1024) {
-    uint32_t k = 0xFFFFFFFFu;
-    if (i < rows) {
-      const int id = tok[i];
-      if (id >= 0 && id < vocab) k = (((uint32_t)id) << pbits) | (uint32_t)i;
-    }
-    sk[i] = k;
-  }
+// dE[id] = sum of the dh rows whose token is id, each id's rows added in
+// position order (deterministic, no atomics on values).  A stable counting
+// sort by id, over chunks of EMB_CHUNK positions, gives each id's positions
+// in order:
+//   1. per chunk: each position's rank among the chunk's earlier positions
+//      with the same id, and (from its last occurrence) the id's count in the
+//      chunk, cnt[c][id] (zeroed beforehand);
+//   2. per id: cnt[c][id] becomes the id's count in the chunks before c, and
+//      tot[id] its count in all of them;
+//   3. start[id] = exclusive prefix sum of tot over ids (one work-group);
+//   4. position p goes to sorted[start[id] + cnt[c][id] + rank[p]].
+// Then one work-group per (id with rows, 256-column slice) sums the id's rows
+// in sorted order.  Ids outside [0, vocab) take no part (the step reports
+// them through its token check).
+constexpr int EMB_CHUNK = 1024;
+
+__global__ __launch_bounds__(1024) void emb_rank_kernel(const int32_t* __restrict__ tok, int rows, int vocab,
+                                                        int* __restrict__ rank, int* __restrict__ cnt) {
+  __shared__ int ids[EMB_CHUNK];
+  const int c = blockIdx.x, t = threadIdx.x, p = c * EMB_CHUNK + t;
+  int id = p < rows ? tok[p] : -1;
+  if (id < 0 || id >= vocab) id = -1;
+  ids[t] = id;
   __syncthreads();
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n2; i += 1024) {
-        const int p = i ^ j;
-        if (p > i) {
-          const uint32_t a = sk[i], b = sk[p];
-          const bool up = (i & k) == 0;
-          if ((a > b) == up) {
-            sk[i] = b;
-            sk[p] = a;
-          }
-        }
-      }
-      __syncthreads();
+  if (id < 0) return;
+  int r = 0;
+  for (int k = 0; k < t; ++k) r += ids[k] == id;
+  bool last = true;
+  for (int k = t + 1; k < EMB_CHUNK; ++k)
+    if (ids[k] == id) {
+      last = false;
+      break;
     }
-  }
-  for (int i = threadIdx.x; i < rows; i += 1024) keys_out[i] = sk[i];
+  rank[p] = r;
+  if (last) cnt[(long)c * vocab + id] = r + 1;
 }
 
-// One work-group per (run head, 256-column slice): the run's end is found by
-// binary search over the sorted keys, then wave w sums rows w, w+4, w+8, ...
-// of the run (four loads in flight per lane) and the four partial sums are
-// added in wave order, so the result does not depend on timing.
-__global__ __launch_bounds__(256) void embed_bwd_runs_kernel(const uint32_t* __restrict__ keys,
-                                                             const float* __restrict__ dh, float* __restrict__ dE,
-                                                             int rows, int d, int pbits, int vocab,
-                                                             int accumulate) {
-  __shared__ floatx4 part[3][64];
+__global__ __launch_bounds__(256) void emb_prefix_kernel(int* __restrict__ cnt, int chunks, int vocab,
+                                                         int* __restrict__ tot) {
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id >= vocab) return;
+  int run = 0;
+  for (int c = 0; c < chunks; ++c) {
+    const int v = cnt[(long)c * vocab + id];
+    cnt[(long)c * vocab + id] = run;
+    run += v;
+  }
+  tot[id] = run;
+}
+
+// Exclusive prefix sum of tot[0 .. n) into start, one work-group of 1024:
+// thread t sums a contiguous block of ids, the block sums are scanned
+// through LDS, then each thread writes its block's prefixes.
+__global__ __launch_bounds__(1024) void emb_scan_kernel(const int* __restrict__ tot, int n, int* __restrict__ start) {
+  __shared__ int sums[1024];
+  const int t = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int b0 = min(n, t * per), b1 = min(n, b0 + per);
+  int s = 0;
+  for (int i = b0; i < b1; ++i) s += tot[i];
+  sums[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {   // inclusive Hillis-Steele scan
+    const int v = t >= off ? sums[t - off] : 0;
+    __syncthreads();
+    sums[t] += v;
+    __syncthreads();
+  }
+  int run = t > 0 ? sums[t - 1] : 0;
+  for (int i = b0; i < b1; ++i) {
+    start[i] = run;
+    run += tot[i];
+  }
+}
+
+__global__ __launch_bounds__(256) void emb_scatter_kernel(const int32_t* __restrict__ tok, int rows, int vocab,
+                                                          const int* __restrict__ rank, const int* __restrict__ cnt,
+                                                          const int* __restrict__ start, int* __restrict__ sorted) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= rows) return;
+  const int id = tok[p];
+  if (id < 0 || id >= vocab) return;
+  sorted[start[id] + cnt[(long)(p / EMB_CHUNK) * vocab + id] + rank[p]] = p;
+}
+
+// One work-group of 8 waves per (sorted index, 256-column slice) that starts
+// an id's rows: wave w adds rows w, w+8, w+16, ... of the id (eight loads in
+// flight per lane), and the eight partial sums are added in wave order, so
+// the result does not depend on timing.
+__global__ __launch_bounds__(512) void emb_runs_kernel(const int* __restrict__ sorted, const int32_t* __restrict__ tok,
+                                                       const int* __restrict__ start, const int* __restrict__ tot,
+                                                       const float* __restrict__ dh, float* __restrict__ dE,
+                                                       int vocab, int d, int accumulate) {
+  __shared__ floatx4 part[7][64];
   const int i = blockIdx.x;
-  const uint32_t id = keys[i] >> pbits;
-  if (id >= (uint32_t)vocab) return;                     // invalid id (uniform over the work-group)
-  if (i > 0 && (keys[i - 1] >> pbits) == id) return;   // not a run head
+  if (i >= start[vocab - 1] + tot[vocab - 1]) return;   // past the positions with a valid id
+  const int id = tok[sorted[i]];
+  if (start[id] != i) return;                          // not the first row of its id (uniform)
+  const int end = i + tot[id];
   const int c = blockIdx.y * 256 + (threadIdx.x & 63) * 4;
   const int w = threadIdx.x >> 6;
-  // end of the run: first index whose key belongs to a larger id
-  const uint32_t bound = (id + 1u) << pbits;
-  int lo = i + 1, hi = rows;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (keys[mid] < bound) lo = mid + 1;
-    else hi = mid;
-  }
-  const int end = lo;
-  const uint32_t pmask = (1u << pbits) - 1u;
   floatx4 s = {0.f, 0.f, 0.f, 0.f};
   if (c < d) {
     int j = i + w;
-    for (; j + 12 < end; j += 16) {
-      const floatx4 a0 = load4(dh + (long)(keys[j] & pmask) * d + c);
-      const floatx4 a1 = load4(dh + (long)(keys[j + 4] & pmask) * d + c);
-      const floatx4 a2 = load4(dh + (long)(keys[j + 8] & pmask) * d + c);
-      const floatx4 a3 = load4(dh + (long)(keys[j + 12] & pmask) * d + c);
-      s += a0;
-      s += a1;
-      s += a2;
-      s += a3;
+    for (; j + 56 < end; j += 64) {
+      floatx4 a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = load4(dh + (long)sorted[j + 8 * u] * d + c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += a[u];
     }
-    for (; j < end; j += 4) s += load4(dh + (long)(keys[j] & pmask) * d + c);
+    for (; j < end; j += 8) s += load4(dh + (long)sorted[j] * d + c);
   }
   if (w > 0) part[w - 1][threadIdx.x & 63] = s;
   __syncthreads();
   if (w == 0 && c < d) {
-    s += part[0][threadIdx.x];
-    s += part[1][threadIdx.x];
-    s += part[2][threadIdx.x];
-    // one work-group owns each id's row: the read-modify-write is race-free
+#pragma unroll
+    for (int u = 0; u < 7; ++u) s += part[u][threadIdx.x];
+    // one work-group owns each id's row slice: the read-modify-write is race-free
     if (accumulate) s += load4(dE + (long)id * d + c);
     store4(dE + (long)id * d + c, s);
   }
@@ -840,26 +876,18 @@ void mean_reduce(const float* x, int n, float* out, hipStream_t st) {
   hipLaunchKernelGGL(mean_reduce_kernel, dim3(1), dim3(1024), 0, st, x, n, out);
 }
 
-void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab, uint32_t* keys,
-               int accumulate, hipStream_t st) {
-  int pbits = 0;
-  while ((1 << pbits) < rows) ++pbits;
-  int n2 = 1;
-  while (n2 < rows) n2 <<= 1;
+void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab, int* sorted, int* rank,
+               int* cnt, int* tot, int* start, int accumulate, hipStream_t st) {
+  const int chunks = (rows + EMB_CHUNK - 1) / EMB_CHUNK;
   if (!accumulate) fill_f32(dE, (long)vocab * d, 0.f, st);
-  // the sort holds up to 32768 keys in LDS: raise the kernel's dynamic LDS
-  // limit once per device (a function attribute is per device)
-  static bool attr_set[64] = {};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    (void)hipFuncSetAttribute((const void*)sort_keys_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
-    if (dev >= 0 && dev < 64) attr_set[dev] = true;
-  }
-  hipLaunchKernelGGL(sort_keys_kernel, dim3(1), dim3(1024), n2 * sizeof(uint32_t), st, tokens, rows, pbits, n2,
-                     vocab, keys);
-  hipLaunchKernelGGL(embed_bwd_runs_kernel, dim3(rows, (d + 255) / 256), dim3(256), 0, st, keys, dh, dE, rows, d,
-                     pbits, vocab, accumulate);
+  fill_f32((float*)cnt, (long)chunks * vocab, 0.f, st);   // all-zero bits: integer zeros
+  hipLaunchKernelGGL(emb_rank_kernel, dim3(chunks), dim3(EMB_CHUNK), 0, st, tokens, rows, vocab, rank, cnt);
+  hipLaunchKernelGGL(emb_prefix_kernel, dim3((vocab + 255) / 256), dim3(256), 0, st, cnt, chunks, vocab, tot);
+  hipLaunchKernelGGL(emb_scan_kernel, dim3(1), dim3(1024), 0, st, tot, vocab, start);
+  hipLaunchKernelGGL(emb_scatter_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, tokens, rows, vocab, rank, cnt,
+                     start, sorted);
+  hipLaunchKernelGGL(emb_runs_kernel, dim3(rows, (d + 255) / 256), dim3(512), 0, st, sorted, tokens, start, tot, dh,
+                     dE, vocab, d, accumulate);
 }
 
 void fill_f32(float* p, long n, float v, hipStream_t st) {
