@@ -413,12 +413,16 @@ int build_layout(gpt_model& m) {
   m.cosb = take((size_t)s.T * (s.Dh / 2) * 4);
   m.sinb = take((size_t)s.T * (s.Dh / 2) * 4);
   // the embedding gradient's counting sort: sorted positions, ranks, per-chunk
-  // counts (chunks of 1024 positions), per-id totals and starts
+  // counts (chunks of 1024 positions), per-id totals and block-local starts,
+  // block sums and offsets, the list of ids with rows
   m.keys = take(BT * 4);
   m.emb_rank = take(BT * 4);
   m.emb_cnt = take((BT + 1023) / 1024 * (size_t)s.V * 4);
   m.emb_tot = take((size_t)s.V * 4);
   m.emb_start = take((size_t)s.V * 4);
+  m.emb_bsum = take((2 * (((size_t)s.V + 255) / 256) + 1) * 4);
+  m.emb_heads = take(((size_t)s.V + 2) * 4);
+  m.emb_part = take((size_t)emb_part_rows(s.BT) * s.d * 4);
   m.total = off;
   return GPT_OK;
 }
@@ -947,9 +951,10 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     if ((rc = norm_bwd(m.ws + Ly.n1, at<float>(m, Ly.rstd1), 1, amx(l - 1, SL_DH2), dn_act))) return rc;
   }
   prof_begin(m, "embed_bwd", (double)BT * d * 4.0 + (double)V * d * (accumulate ? 8.0 : 4.0) + BT * 8.0, 1,
-             "emb_rank_kernel + emb_prefix_kernel + emb_scan_kernel + emb_scatter_kernel + emb_runs_kernel");
+             "emb_rank_kernel + emb_prefix_kernel + emb_scan_kernel + emb_scatter_kernel + emb_short_kernel + emb_long_kernel + emb_long_sum_kernel");
   embed_bwd(tokens, dh, grads + P.E, BT, d, V, at<int>(m, m.keys), at<int>(m, m.emb_rank), at<int>(m, m.emb_cnt),
-            at<int>(m, m.emb_tot), at<int>(m, m.emb_start), accumulate, st);
+            at<int>(m, m.emb_tot), at<int>(m, m.emb_start), at<int>(m, m.emb_bsum), at<int>(m, m.emb_heads),
+            at<float>(m, m.emb_part), accumulate, st);
   prof_end(m);
   if (ev_last) HIP_TRY(hipStreamWaitEvent(st, ev_last, 0));   // join: every weight gradient is written
   HIP_TRY(hipGetLastError());

@@ -606,123 +606,282 @@ __global__ __launch_bounds__(1024) void mean_reduce_kernel(const float* __restri
 // position order (deterministic, no atomics on values).  A stable counting
 // sort by id, over chunks of EMB_CHUNK positions, gives each id's positions
 // in order:
-//   1. per chunk: each position's rank among the chunk's earlier positions
-//      with the same id, and (from its last occurrence) the id's count in the
-//      chunk, cnt[c][id] (zeroed beforehand);
+//   1. per chunk: the chunk's keys (id, position) sorted in LDS; a position's
+//      rank among the chunk's earlier positions with the same id is its
+//      distance from the start of its id's run there, and the run's last
+//      entry records the id's count in the chunk, cnt[c][id] (zeroed
+//      beforehand);
 //   2. per id: cnt[c][id] becomes the id's count in the chunks before c, and
-//      tot[id] its count in all of them;
-//   3. start[id] = exclusive prefix sum of tot over ids (one work-group);
-//   4. position p goes to sorted[start[id] + cnt[c][id] + rank[p]].
-// Then one work-group per (id with rows, 256-column slice) sums the id's rows
-// in sorted order.  Ids outside [0, vocab) take no part (the step reports
-// them through its token check).
+//      tot[id] its count in all of them; per block of 256 ids, the exclusive
+//      prefix sum of tot (lstart) and the block's total (bsum);
+//   3. one work-group scans the block totals (boff; boff[nb] = all valid
+//      positions), so that an id's first sorted index is
+//      start(id) = boff[id / 256] + lstart[id];
+//   4. position p goes to sorted[start(id) + cnt[c][id] + rank[p]]; the
+//      position that lands at start(id) appends id to the list of ids with
+//      few rows or to the list of ids with many (the lists' order varies, the
+//      sums do not).
+// Then each id's rows are added in sorted order: by one wave over the whole
+// row for ids with few rows, by eight waves per 256-column slice (partial sums
+// added in wave order) for ids with many.  Ids outside [0, vocab) take no part
+// (the step reports them through its token check).
 constexpr int EMB_CHUNK = 1024;
+
+__device__ __forceinline__ int emb_start(const int* lstart, const int* boff, int id) {
+  return boff[id >> 8] + lstart[id];
+}
 
 __global__ __launch_bounds__(1024) void emb_rank_kernel(const int32_t* __restrict__ tok, int rows, int vocab,
                                                         int* __restrict__ rank, int* __restrict__ cnt) {
-  __shared__ int ids[EMB_CHUNK];
+  __shared__ uint32_t sk[EMB_CHUNK];
   const int c = blockIdx.x, t = threadIdx.x, p = c * EMB_CHUNK + t;
-  int id = p < rows ? tok[p] : -1;
-  if (id < 0 || id >= vocab) id = -1;
-  ids[t] = id;
+  const int id = p < rows ? tok[p] : -1;
+  // key: id above the position in the chunk (ids < 65536, 10 position bits)
+  sk[t] = (id >= 0 && id < vocab) ? ((uint32_t)id << 10) | (uint32_t)t : 0xFFFFFFFFu;
   __syncthreads();
-  if (id < 0) return;
-  int r = 0;
-  for (int k = 0; k < t; ++k) r += ids[k] == id;
-  bool last = true;
-  for (int k = t + 1; k < EMB_CHUNK; ++k)
-    if (ids[k] == id) {
-      last = false;
-      break;
+  // bitonic sort, ascending: each thread keeps the smaller or the larger
+  // key of its pair (t, t ^ jj), as the pair's direction asks
+  for (int k = 2; k <= EMB_CHUNK; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      const uint32_t a = sk[t], b = sk[t ^ jj];
+      const bool lower = (t & jj) == 0, up = (t & k) == 0;
+      const uint32_t keep = (lower == up) ? min(a, b) : max(a, b);
+      __syncthreads();
+      sk[t] = keep;
+      __syncthreads();
     }
-  rank[p] = r;
-  if (last) cnt[(long)c * vocab + id] = r + 1;
+  const uint32_t key = sk[t];
+  if (key == 0xFFFFFFFFu) return;
+  const uint32_t kid = key >> 10;
+  // first entry of this id's run: lower bound of (kid << 10)
+  int lo = 0, hi = t;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((sk[mid] >> 10) < kid) lo = mid + 1;
+    else hi = mid;
+  }
+  rank[c * EMB_CHUNK + (int)(key & 1023u)] = t - lo;
+  if (t + 1 == EMB_CHUNK || sk[t + 1] == 0xFFFFFFFFu || (sk[t + 1] >> 10) != kid)
+    cnt[(long)c * vocab + kid] = t - lo + 1;
 }
 
 __global__ __launch_bounds__(256) void emb_prefix_kernel(int* __restrict__ cnt, int chunks, int vocab,
-                                                         int* __restrict__ tot) {
+                                                         int* __restrict__ tot, int* __restrict__ lstart,
+                                                         int* __restrict__ bsum) {
+  __shared__ int ws[4];
   const int id = blockIdx.x * 256 + threadIdx.x;
-  if (id >= vocab) return;
   int run = 0;
-  for (int c = 0; c < chunks; ++c) {
-    const int v = cnt[(long)c * vocab + id];
-    cnt[(long)c * vocab + id] = run;
-    run += v;
+  if (id < vocab)
+    for (int c = 0; c < chunks; ++c) {
+      const int v = cnt[(long)c * vocab + id];
+      cnt[(long)c * vocab + id] = run;
+      run += v;
+    }
+  // exclusive scan of the block's totals: wave scans, then the wave offsets
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
   }
-  tot[id] = run;
+  if (lane == 63) ws[w] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int u = 0; u < w; ++u) off += ws[u];
+  if (id < vocab) {
+    tot[id] = run;
+    lstart[id] = off + incl - run;
+  }
+  if (threadIdx.x == 255) bsum[blockIdx.x] = off + incl;
 }
 
-// Exclusive prefix sum of tot[0 .. n) into start, one work-group of 1024:
-// thread t sums a contiguous block of ids, the block sums are scanned
-// through LDS, then each thread writes its block's prefixes.
-__global__ __launch_bounds__(1024) void emb_scan_kernel(const int* __restrict__ tot, int n, int* __restrict__ start) {
-  __shared__ int sums[1024];
-  const int t = threadIdx.x;
-  const int per = (n + 1023) / 1024;
-  const int b0 = min(n, t * per), b1 = min(n, b0 + per);
-  int s = 0;
-  for (int i = b0; i < b1; ++i) s += tot[i];
-  sums[t] = s;
+// boff[b] = sum of bsum[0 .. b), for b = 0 .. nb (nb <= 256), one work-group
+__global__ __launch_bounds__(256) void emb_scan_kernel(const int* __restrict__ bsum, int nb, int* __restrict__ boff) {
+  __shared__ int ws[4];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int v0 = t < nb ? bsum[t] : 0;
+  int incl = v0;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) ws[w] = incl;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {   // inclusive Hillis-Steele scan
-    const int v = t >= off ? sums[t - off] : 0;
-    __syncthreads();
-    sums[t] += v;
-    __syncthreads();
-  }
-  int run = t > 0 ? sums[t - 1] : 0;
-  for (int i = b0; i < b1; ++i) {
-    start[i] = run;
-    run += tot[i];
-  }
+  int off = 0;
+  for (int u = 0; u < w; ++u) off += ws[u];
+  if (t < nb) boff[t] = off + incl - v0;
+  if (t == nb - 1) boff[nb] = off + incl;
 }
+
+// Ids with at most EMB_LONG rows go to the short list, the others to the
+// long list: heads[0] and heads[1] count them; the short list fills heads
+// from index 2 upwards and the long list from the top (index 1 + vocab)
+// downwards.
+constexpr int EMB_LONG = 256;
 
 __global__ __launch_bounds__(256) void emb_scatter_kernel(const int32_t* __restrict__ tok, int rows, int vocab,
                                                           const int* __restrict__ rank, const int* __restrict__ cnt,
-                                                          const int* __restrict__ start, int* __restrict__ sorted) {
+                                                          const int* __restrict__ lstart, const int* __restrict__ boff,
+                                                          const int* __restrict__ tot, int* __restrict__ sorted,
+                                                          int* __restrict__ heads) {
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= rows) return;
   const int id = tok[p];
   if (id < 0 || id >= vocab) return;
-  sorted[start[id] + cnt[(long)(p / EMB_CHUNK) * vocab + id] + rank[p]] = p;
+  const int within = cnt[(long)(p / EMB_CHUNK) * vocab + id] + rank[p];
+  sorted[emb_start(lstart, boff, id) + within] = p;
+  if (within == 0) {
+    if (tot[id] <= EMB_LONG) heads[2 + atomicAdd(heads, 1)] = id;
+    else heads[1 + vocab - atomicAdd(heads + 1, 1)] = id;
+  }
 }
 
-// One work-group of 8 waves per (sorted index, 256-column slice) that starts
-// an id's rows: wave w adds rows w, w+8, w+16, ... of the id (eight loads in
-// flight per lane), and the eight partial sums are added in wave order, so
-// the result does not depend on timing.
-__global__ __launch_bounds__(512) void emb_runs_kernel(const int* __restrict__ sorted, const int32_t* __restrict__ tok,
-                                                       const int* __restrict__ start, const int* __restrict__ tot,
-                                                       const float* __restrict__ dh, float* __restrict__ dE,
-                                                       int vocab, int d, int accumulate) {
-  __shared__ floatx4 part[7][64];
-  const int i = blockIdx.x;
-  if (i >= start[vocab - 1] + tot[vocab - 1]) return;   // past the positions with a valid id
-  const int id = tok[sorted[i]];
-  if (start[id] != i) return;                          // not the first row of its id (uniform)
-  const int end = i + tot[id];
+// Short runs: one wave per id, over the whole row in blocks of 2048 columns
+// (lane l holds columns 256 g + 4 l .. +3 of group g); the id's rows are
+// added one after another in sorted order, two rows' loads in flight.  Loads
+// past the row's end read a clamped in-row address and are not added, so no
+// load sits behind a branch.
+__global__ __launch_bounds__(256) void emb_short_kernel(const int* __restrict__ sorted, const int* __restrict__ heads,
+                                                        const int* __restrict__ lstart, const int* __restrict__ boff,
+                                                        const int* __restrict__ tot, const float* __restrict__ dh,
+                                                        float* __restrict__ dE, int d, int accumulate) {
+  const int nh = heads[0];
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6), nw = gridDim.x * 4;
+  for (int h = gw; h < nh; h += nw) {
+    const int id = heads[2 + h];
+    const int i0 = emb_start(lstart, boff, id), n = tot[id];
+    for (int cb = 0; cb < d; cb += 2048) {
+      int col[8];
+      bool ok[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        ok[g] = cb + g * 256 + lane * 4 < d;
+        col[g] = ok[g] ? cb + g * 256 + lane * 4 : d - 4;
+      }
+      floatx4 s[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) s[g] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      int r = 0;
+      for (; r + 1 < n; r += 2) {
+        const float* x0 = dh + (long)sorted[i0 + r] * d;
+        const float* x1 = dh + (long)sorted[i0 + r + 1] * d;
+        floatx4 a[8], b[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          a[g] = load4(x0 + col[g]);
+          b[g] = load4(x1 + col[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          s[g] += ok[g] ? a[g] : z;
+          s[g] += ok[g] ? b[g] : z;
+        }
+      }
+      if (r < n) {
+        const float* x0 = dh + (long)sorted[i0 + r] * d;
+        floatx4 a[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) a[g] = load4(x0 + col[g]);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) s[g] += ok[g] ? a[g] : z;
+      }
+      floatx4 o[8];
+      if (accumulate) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) o[g] = load4(dE + (long)id * d + col[g]);
+      }
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        if (ok[g]) store4(dE + (long)id * d + col[g], accumulate ? o[g] + s[g] : s[g]);
+    }
+  }
+}
+
+// Long runs are cut into segments of EMB_SEG rows.  Segment work: work-group
+// b takes the segments b, b + gridDim.x, ... of the flattened (long id,
+// segment) sequence, for its 256-column slice; wave w adds rows w, w+8, ... of
+// the segment (sixteen loads in flight per lane) and the eight wave sums are
+// added in wave order into part[segment] (the long ids' segments are numbered
+// in the order of the long list).  Then emb_long_sum_kernel adds each long
+// id's segment sums in segment order.  Both orders are fixed, so the result
+// does not depend on timing.
+constexpr int EMB_SEG = 128;
+constexpr int EMB_MAXLONG = 256;   // long ids hold > EMB_LONG rows each: at most rows / EMB_LONG of them
+
+__device__ __forceinline__ void emb_long_table(const int* heads, const int* tot, int vocab, int nl, int* lid,
+                                               int* lseg) {
+  // lid[k]: k-th long id; lseg[k]: its first segment (lseg[nl]: all)
+  for (int k = threadIdx.x; k < nl; k += blockDim.x) {
+    const int id = heads[1 + vocab - k];
+    lid[k] = id;
+    lseg[k + 1] = (tot[id] + EMB_SEG - 1) / EMB_SEG;   // segment counts, summed below
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    lseg[0] = 0;
+    for (int k = 0; k < nl; ++k) lseg[k + 1] += lseg[k];
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(512) void emb_long_kernel(const int* __restrict__ sorted, const int* __restrict__ heads,
+                                                       const int* __restrict__ lstart, const int* __restrict__ boff,
+                                                       const int* __restrict__ tot, const float* __restrict__ dh,
+                                                       float* __restrict__ part, int vocab, int d) {
+  __shared__ floatx4 wsum[7][64];
+  __shared__ int lid[EMB_MAXLONG], lseg[EMB_MAXLONG + 1];
+  const int nl = min(heads[1], EMB_MAXLONG);
+  emb_long_table(heads, tot, vocab, nl, lid, lseg);
+  const int nseg = lseg[nl];
   const int c = blockIdx.y * 256 + (threadIdx.x & 63) * 4;
   const int w = threadIdx.x >> 6;
-  floatx4 s = {0.f, 0.f, 0.f, 0.f};
-  if (c < d) {
-    int j = i + w;
-    for (; j + 56 < end; j += 64) {
-      floatx4 a[8];
+  for (int sg = blockIdx.x; sg < nseg; sg += gridDim.x) {
+    int k = 0;
+    while (lseg[k + 1] <= sg) ++k;                 // the long id owning segment sg
+    const int id = lid[k];
+    const int i0 = emb_start(lstart, boff, id) + (sg - lseg[k]) * EMB_SEG;
+    const int m = min(EMB_SEG, tot[id] - (sg - lseg[k]) * EMB_SEG);
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+    if (c < d) {
+      int j = w;
+      for (; j + 120 < m; j += 128) {
+        floatx4 a[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] = load4(dh + (long)sorted[j + 8 * u] * d + c);
+        for (int u = 0; u < 16; ++u) a[u] = load4(dh + (long)sorted[i0 + j + 8 * u] * d + c);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += a[u];
+        for (int u = 0; u < 16; ++u) s += a[u];
+      }
+      for (; j < m; j += 8) s += load4(dh + (long)sorted[i0 + j] * d + c);
     }
-    for (; j < end; j += 8) s += load4(dh + (long)sorted[j] * d + c);
-  }
-  if (w > 0) part[w - 1][threadIdx.x & 63] = s;
-  __syncthreads();
-  if (w == 0 && c < d) {
+    if (w > 0) wsum[w - 1][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (w == 0 && c < d) {
 #pragma unroll
-    for (int u = 0; u < 7; ++u) s += part[u][threadIdx.x];
-    // one work-group owns each id's row slice: the read-modify-write is race-free
-    if (accumulate) s += load4(dE + (long)id * d + c);
-    store4(dE + (long)id * d + c, s);
+      for (int u = 0; u < 7; ++u) s += wsum[u][threadIdx.x];
+      store4(part + (long)sg * d + c, s);
+    }
+    __syncthreads();   // wsum is rewritten by the next segment
+  }
+}
+
+__global__ __launch_bounds__(256) void emb_long_sum_kernel(const int* __restrict__ heads, const int* __restrict__ tot,
+                                                           const float* __restrict__ part, float* __restrict__ dE,
+                                                           int vocab, int d, int accumulate) {
+  __shared__ int lid[EMB_MAXLONG], lseg[EMB_MAXLONG + 1];
+  const int nl = min(heads[1], EMB_MAXLONG);
+  emb_long_table(heads, tot, vocab, nl, lid, lseg);
+  const int c = blockIdx.y * 1024 + threadIdx.x * 4;
+  if (c >= d) return;
+  for (int k = blockIdx.x; k < nl; k += gridDim.x) {
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int sg = lseg[k]; sg < lseg[k + 1]; ++sg) s += load4(part + (long)sg * d + c);
+    const long o = (long)lid[k] * d + c;
+    if (accumulate) s += load4(dE + o);
+    store4(dE + o, s);
   }
 }
 
@@ -877,17 +1036,24 @@ void mean_reduce(const float* x, int n, float* out, hipStream_t st) {
 }
 
 void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab, int* sorted, int* rank,
-               int* cnt, int* tot, int* start, int accumulate, hipStream_t st) {
+               int* cnt, int* tot, int* lstart, int* bsum, int* heads, float* part, int accumulate, hipStream_t st) {
   const int chunks = (rows + EMB_CHUNK - 1) / EMB_CHUNK;
+  const int nb = (vocab + 255) / 256;   // <= 256 (vocab <= 65536)
+  int* boff = bsum + nb;
   if (!accumulate) fill_f32(dE, (long)vocab * d, 0.f, st);
   fill_f32((float*)cnt, (long)chunks * vocab, 0.f, st);   // all-zero bits: integer zeros
+  fill_f32((float*)heads, 2, 0.f, st);
   hipLaunchKernelGGL(emb_rank_kernel, dim3(chunks), dim3(EMB_CHUNK), 0, st, tokens, rows, vocab, rank, cnt);
-  hipLaunchKernelGGL(emb_prefix_kernel, dim3((vocab + 255) / 256), dim3(256), 0, st, cnt, chunks, vocab, tot);
-  hipLaunchKernelGGL(emb_scan_kernel, dim3(1), dim3(1024), 0, st, tot, vocab, start);
+  hipLaunchKernelGGL(emb_prefix_kernel, dim3(nb), dim3(256), 0, st, cnt, chunks, vocab, tot, lstart, bsum);
+  hipLaunchKernelGGL(emb_scan_kernel, dim3(1), dim3(256), 0, st, bsum, nb, boff);
   hipLaunchKernelGGL(emb_scatter_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, tokens, rows, vocab, rank, cnt,
-                     start, sorted);
-  hipLaunchKernelGGL(emb_runs_kernel, dim3(rows, (d + 255) / 256), dim3(512), 0, st, sorted, tokens, start, tot, dh,
-                     dE, vocab, d, accumulate);
+                     lstart, boff, tot, sorted, heads);
+  hipLaunchKernelGGL(emb_short_kernel, dim3(1024), dim3(256), 0, st, sorted, heads, lstart, boff, tot, dh, dE, d,
+                     accumulate);
+  hipLaunchKernelGGL(emb_long_kernel, dim3(256, (d + 255) / 256), dim3(512), 0, st, sorted, heads, lstart, boff, tot,
+                     dh, part, vocab, d);
+  hipLaunchKernelGGL(emb_long_sum_kernel, dim3(64, (d + 1023) / 1024), dim3(256), 0, st, heads, tot, part, dE, vocab,
+                     d, accumulate);
 }
 
 void fill_f32(float* p, long n, float v, hipStream_t st) {

@@ -154,10 +154,13 @@ void xent_reduce(const float* part, const float* tgt, int rows, int nblk, float*
                  hipStream_t st);
 void mean_reduce(const float* x, int n, float* out, hipStream_t st);
 // dE[id] = (accumulate ? dE[id] : 0) + sum of dh rows whose token is id, in
-// position order.  Scratch: sorted and rank [rows], cnt [ceil(rows / 1024)]
-// [vocab], tot and start [vocab] (int32).
+// position order (vocab <= 65536).  Scratch (int32): sorted and rank [rows],
+// cnt [ceil(rows / 1024)][vocab], tot and lstart [vocab], bsum
+// [2 * ceil(vocab / 256) + 1], heads [2 + vocab]; fp32 part [emb_part_rows(rows)][d].
 void embed_bwd(const int32_t* tokens, const float* dh, float* dE, int rows, int d, int vocab, int* sorted, int* rank,
-               int* cnt, int* tot, int* start, int accumulate, hipStream_t st);
+               int* cnt, int* tot, int* lstart, int* bsum, int* heads, float* part, int accumulate, hipStream_t st);
+// segment sums of the ids with many rows (> 256 each, 128-row segments)
+inline long emb_part_rows(long rows) { return rows / 128 + rows / 256 + 1; }
 void fill_f32(float* p, long n, float v, hipStream_t st);
 
 // ---------------------------------------------------------------- optimizer

@@ -110,7 +110,7 @@ struct gpt_model {
   };
   std::vector<Layer> lay;
   size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, mloss, dpart, dtok, dpos, dsplit, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
-      cosb, sinb, keys, emb_rank, emb_cnt, emb_tot, emb_start, total;
+      cosb, sinb, keys, emb_rank, emb_cnt, emb_tot, emb_start, emb_bsum, emb_heads, emb_part, total;
   size_t splitk_floats;
   size_t q8row, q8T, amax, scales;   // fp8: transient codes, per-tensor amax / scale slots
   size_t f32w;   // fp8: transient fp32 [BT][F], du in the backward
