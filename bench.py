@@ -331,8 +331,7 @@ def main() -> int:
                    "seq_len": s.seq_len, "batch": s.batch, "grad_accum": n_acc, "tokens_per_step": s.bt * n_acc,
                    "optimizer": "muon+adamw" if args.optimizer else None,
                    "window": s.window, "window_pattern": s.window_pattern, "token_dist": s.token_dist,
-                   "precision": s.precision, "overlapped_weight_gradients": not args.no_overlap and
-                   s.precision != "fp8",
+                   "precision": s.precision, "overlapped_weight_gradients": not args.no_overlap,
                    "rope_in_qkv_epilogue": not args.no_rope_epilogue and s.precision == "bf16" and
                    s.head_dim == 128 and s.seq_len % 64 == 0},
         "mfu": mfu,

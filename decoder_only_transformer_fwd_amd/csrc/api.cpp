@@ -398,6 +398,7 @@ int build_layout(gpt_model& m) {
     m.q8row = take(BT * wide);
     m.f32w = take(BT * s.F * 4);
     m.q8T = take(BT * wide);
+    m.q8T2 = take(BT * wide);   // the overlapped weight gradients alternate the transposed gradient codes
     m.n_slots = 12 * s.L;
     m.amax = take((size_t)m.n_slots * AMAX_SLOT * 4);
     m.scales = take((size_t)m.n_slots * 4);
@@ -648,7 +649,7 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
   // which the main stream waits before it overwrites a transient input of
   // that product (the activation gradient it reads).
   const int wepi = accumulate ? EPI_ACCUM_F32 : EPI_STORE_F32;
-  const bool ov = m.overlap && m.side && !m.prof_on && !f8 && !forward_only;
+  const bool ov = m.overlap && m.side && !m.prof_on && !forward_only;
   hipEvent_t ev_last = nullptr;   // the side stream's last product
   auto ov_event = [&]() -> hipEvent_t {
     if (m.ov_next == m.ov_ev.size()) return nullptr;
@@ -676,12 +677,35 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     if (done) *done = join;
     return GPT_OK;
   };
+  // fp8 weight gradients: the transposed gradient codes (A) are transient,
+  // so with overlap the quantiser alternates two buffers (next_q8T), and
+  // `done` receives the event after which the buffer this product read may
+  // be rewritten
   auto wgrad8 = [&](const char* site, int M, int N, int K, const void* A, const void* B, float* C, long ldc, int sa,
-                    int sb) {
+                    int sb, hipEvent_t* done) {
     GemmArgs ex{};
     ex.scale_a = sc8 + sa;
     ex.scale_b = sc8 + sb;
-    return gemm(m, site, LAYOUT_KK, wepi, M, N, K, A, K, B, K, C, ldc, ex, DT_FP8_A5B4, true);
+    if (!ov) return gemm(m, site, LAYOUT_KK, wepi, M, N, K, A, K, B, K, C, ldc, ex, DT_FP8_A5B4, true);
+    hipEvent_t fork = ov_event(), join = ov_event();
+    if (!fork || !join) return fail(GPT_EINVAL, "overlap event ring exhausted");
+    HIP_TRY(hipEventRecord(fork, st));
+    HIP_TRY(hipStreamWaitEvent(m.side, fork, 0));
+    m.st = m.side;
+    const int r = gemm(m, site, LAYOUT_KK, wepi, M, N, K, A, K, B, K, C, ldc, ex, DT_FP8_A5B4, true);
+    m.st = st;
+    if (r) return r;
+    HIP_TRY(hipEventRecord(join, m.side));
+    ev_last = join;
+    *done = join;
+    return GPT_OK;
+  };
+  int kq = 0;
+  hipEvent_t ev_q8T[2] = {nullptr, nullptr};
+  auto next_q8T = [&](void*& qt) {
+    if (ov) kq ^= 1;
+    qt = kq ? m.ws + m.q8T2 : q8T;
+    return wait_for(ev_q8T[kq]);   // the product that read this buffer last is done
   };
 
   m.ov_next = 0;
@@ -861,19 +885,22 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     ex.amax = amx(l, SL_DU);
     const double pairs = (double)s.B * H * visible_pairs(s.T, s.win[l]);
     if (f8) {
-      quant("fp8_quant_grad", FP8_E5M2, dh, BT, d, slot(l, SL_DH2), q8row, q8T, true, true);
+      void* qt = nullptr;
+      if ((rc = next_q8T(qt))) return rc;
+      quant("fp8_quant_grad", FP8_E5M2, dh, BT, d, slot(l, SL_DH2), q8row, qt, true, true);
       if ((rc = gemm8("dgrad_w2_drelu2", DT_FP8_A5B4, EPI_DRELU2_F32, BT, F, d, q8row, m.ws + Ly.wqT[3],
                       m.ws + m.f32w, F, slot(l, SL_DH2), slot(l, SL_W2), ex)))
         return rc;
-      if ((rc = wgrad8("wgrad_w2", d, F, BT, q8T, m.ws + Ly.gT, grads + P.W2[l], F, slot(l, SL_DH2),
-                       slot(l, SL_G))))
+      if ((rc = wgrad8("wgrad_w2", d, F, BT, qt, m.ws + Ly.gT, grads + P.W2[l], F, slot(l, SL_DH2),
+                       slot(l, SL_G), &ev_q8T[kq])))
         return rc;
-      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.f32w, BT, F, slot(l, SL_DU), q8row, q8T, true, true);
+      if ((rc = next_q8T(qt))) return rc;
+      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.f32w, BT, F, slot(l, SL_DU), q8row, qt, true, true);
       if ((rc = gemm8("dgrad_w1", DT_FP8_A5B4, EPI_STORE_F32, BT, d, F, q8row, m.ws + Ly.wqT[2], dm, d,
                       slot(l, SL_DU), slot(l, SL_W1))))
         return rc;
-      if ((rc = wgrad8("wgrad_w1", F, d, BT, q8T, m.ws + Ly.n2T, grads + P.W1[l], d, slot(l, SL_DU),
-                       slot(l, SL_N2))))
+      if ((rc = wgrad8("wgrad_w1", F, d, BT, qt, m.ws + Ly.n2T, grads + P.W1[l], d, slot(l, SL_DU),
+                       slot(l, SL_N2), &ev_q8T[kq])))
         return rc;
     } else {
       if ((rc = wait_for(ev_du))) return rc;
@@ -889,12 +916,14 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
     }
     if ((rc = norm_bwd(m.ws + Ly.n2, at<float>(m, Ly.rstd2), 1, amx(l, SL_DH1), dn_act))) return rc;
     if (f8) {
-      quant("fp8_quant_grad", FP8_E5M2, dh, BT, d, slot(l, SL_DH1), q8row, q8T, true, true);
+      void* qt = nullptr;
+      if ((rc = next_q8T(qt))) return rc;
+      quant("fp8_quant_grad", FP8_E5M2, dh, BT, d, slot(l, SL_DH1), q8row, qt, true, true);
       if ((rc = gemm8("dgrad_o", DT_FP8_A5B4, EPI_STORE, BT, d, d, q8row, m.ws + Ly.wqT[1], m.ws + m.dO, d,
                       slot(l, SL_DH1), slot(l, SL_WO))))
         return rc;
-      if ((rc = wgrad8("wgrad_o", d, d, BT, q8T, m.ws + Ly.oT, grads + P.Wo[l], d, slot(l, SL_DH1),
-                       slot(l, SL_O))))
+      if ((rc = wgrad8("wgrad_o", d, d, BT, qt, m.ws + Ly.oT, grads + P.Wo[l], d, slot(l, SL_DH1),
+                       slot(l, SL_O), &ev_q8T[kq])))
         return rc;
     } else {
       if ((rc = gemm(m, "dgrad_o", LAYOUT_KN, EPI_STORE, BT, d, d, dhA, d, wp(P.Wo[l]), d, m.ws + m.dO, d)))
@@ -933,12 +962,14 @@ int run_step(gpt_model& m, const int32_t* tokens, const int32_t* targets, float*
                     amx(l, SL_DQKV));
     prof_end(m);
     if (f8) {
-      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.dqkv, BT, Nqkv, slot(l, SL_DQKV), q8row, q8T);
+      void* qt = nullptr;
+      if ((rc = next_q8T(qt))) return rc;
+      quant("fp8_quant_grad", FP8_E5M2, m.ws + m.dqkv, BT, Nqkv, slot(l, SL_DQKV), q8row, qt);
       if ((rc = gemm8("dgrad_qkv", DT_FP8_A5B4, EPI_STORE_F32, BT, d, Nqkv, q8row, m.ws + Ly.wqT[0], dm, d,
                       slot(l, SL_DQKV), slot(l, SL_WQKV))))
         return rc;
-      if ((rc = wgrad8("wgrad_qkv", Nqkv, d, BT, q8T, m.ws + Ly.n1T, grads + P.Wqkv[l], d, slot(l, SL_DQKV),
-                       slot(l, SL_N1))))
+      if ((rc = wgrad8("wgrad_qkv", Nqkv, d, BT, qt, m.ws + Ly.n1T, grads + P.Wqkv[l], d, slot(l, SL_DQKV),
+                       slot(l, SL_N1), &ev_q8T[kq])))
         return rc;
     } else {
       if ((rc = gemm(m, "dgrad_qkv", LAYOUT_KN, epi_dn, BT, d, Nqkv, m.ws + m.dqkv, Nqkv, wp(P.Wqkv[l]), d, dm,

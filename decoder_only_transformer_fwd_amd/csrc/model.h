@@ -112,7 +112,7 @@ struct gpt_model {
   size_t h, nL, rstdL, part, tgt, lse, rowloss, lossdev, flag, mloss, dpart, dtok, dpos, dsplit, dz, dm, dh, dhA, du, dO, dOT, Dv, dqkv, splitk,
       cosb, sinb, keys, emb_rank, emb_cnt, emb_tot, emb_start, emb_bsum, emb_heads, emb_part, total;
   size_t splitk_floats;
-  size_t q8row, q8T, amax, scales;   // fp8: transient codes, per-tensor amax / scale slots
+  size_t q8row, q8T, q8T2, amax, scales;   // fp8: transient codes, per-tensor amax / scale slots
   size_t f32w;   // fp8: transient fp32 [BT][F], du in the backward
   int n_slots;
   int xent_tile, xent_nblk;
@@ -158,8 +158,7 @@ struct gpt_model {
   // handle, overlapping the input-gradient chain (which alone feeds the next
   // layer): `side` is created by gpt_create (default priority), forks and
   // joins are events from the ring `ov_ev`.  Off with profiling (so that
-  // every launch is timed alone), for GPT_FP8 (its weight gradients read
-  // transient codes), or by gpt_overlap_enable(m, 0).
+  // every launch is timed alone) or by gpt_overlap_enable(m, 0).
   hipStream_t side = nullptr;
   std::vector<hipEvent_t> ov_ev;
   size_t ov_next = 0;

@@ -270,8 +270,9 @@ int gpt_rope_table(const gpt_config* cfg, float* cos_out, float* sin_out);
  * to fill the GPU, with the partial sums added in split order; overlapped:
  * the fewest of those splits that give 64 work-groups, since the product
  * shares the GPU with the other stream), so each is bitwise reproducible
- * and they agree to fp32 summation-order rounding.  GPT_FP8 models always
- * run in order. */
+ * and they agree to fp32 summation-order rounding.  In GPT_FP8 models the
+ * product reads the transposed gradient codes, which alternate between two
+ * workspace buffers while the overlap is on. */
 int gpt_overlap_enable(gpt_model* model, int on);
 
 /* The rotary step and QK norm in the QKV product's epilogue (on by

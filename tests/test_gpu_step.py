@@ -142,7 +142,7 @@ def test_step_is_bitwise_deterministic():
     sess.close()
 
 
-@pytest.mark.parametrize("name", ["d24_short", "gqa_bf16", "fp32_win"])
+@pytest.mark.parametrize("name", ["d24_short", "gqa_bf16", "fp32_win", "fp8_mid", "d24_fp8_short"])
 def test_overlapped_weight_gradients_match_in_order_step(name):
     """The weight-gradient products on the handle's second stream (unsplit)
     against the in-order step (split along K where planned): the same loss,
