@@ -535,7 +535,12 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   }
   a.k_split = K;
   char label[128];
-  const TailPlan tp = plan_tail(dty, layout, epi, M, N, K);
+  // An input gradient's partly filled last round of tiles is left as it is
+  // when the weight gradients overlap the chain: their products fill the
+  // idle CUs, and the K split of that round and its reduction are saved
+  // (measured: d24 94.2 -> 93.7 ms, d20 133.6 -> 132.8 ms per step).
+  const bool keep_tail = layout == LAYOUT_KN && m.overlap && m.side && !m.prof_on;
+  const TailPlan tp = keep_tail ? TailPlan{0, 1} : plan_tail(dty, layout, epi, M, N, K);
   if (tp.n1 > 0) {
     // whole rounds: the first n1 tile columns
     const int N1 = tp.n1 * 256, N2 = N - N1;
