@@ -31,7 +31,7 @@ _GARBLED = re.compile(r"gemm_kernel<[^>]*?>?, (\d+), (\d+), (\d+), (\d+), (\d+),
 # tiles with the ping-pong schedule, by (BM, BN, waves M, waves N, row bytes,
 # stages); the library's bf16 plan launches the 8-wave, 64-byte, 4-stage tile
 # only with the ping-pong schedule
-_PP = {(256, 256, 2, 4, 64, 4), (256, 256, 2, 4, 64, 5), (256, 128, 4, 2, 128, 3)}
+_PP = {(256, 256, 2, 4, 64, 4), (256, 256, 2, 4, 64, 5), (256, 128, 4, 2, 128, 3), (256, 256, 4, 2, 64, 4)}
 
 
 def _demangle(names):
