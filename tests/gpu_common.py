@@ -66,6 +66,12 @@ SMALL = {
     "gqa_t192": gi.GPTShape("gqa_t192", depth=2, d_model=512, n_head=4, head_dim=128, mlp_hidden=1024,
                             vocab=1000, seq_len=192, batch=3, window=64, window_pattern="SL",
                             precision="bf16", token_dist="zipf", n_kv_head=2),
+    # skewed ids over many positions: the embedding gradient's long runs
+    # (ids with more than 256 rows, summed in 128-row segments) at a size the
+    # oracle compares whole
+    "zipf_long_runs": gi.GPTShape("zipf_long_runs", depth=1, d_model=256, n_head=2, head_dim=128, mlp_hidden=512,
+                                  vocab=1000, seq_len=2048, batch=2, window=0, window_pattern="L",
+                                  precision="bf16", token_dist="zipf"),
     "gqa_fp8": gi.GPTShape("gqa_fp8", depth=2, d_model=256, n_head=2, head_dim=128, mlp_hidden=1024,
                            vocab=1000, seq_len=224, batch=2, window=64, window_pattern="SL",
                            precision="fp8", token_dist="zipf", n_kv_head=1),
