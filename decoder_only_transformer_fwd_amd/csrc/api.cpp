@@ -506,7 +506,9 @@ int gemm(gpt_model& m, const char* site, int layout, int epi, int M, int N, int 
   // That saves most partial sums and their reduction while a product of a
   // few tiles does not run alone for its whole K.  Measured (ms per step):
   // unsplit d12 29.3 / d24 96.2 / d20 138.4; 64 work-groups 22.3 / 95.1 /
-  // 136.6; 128 21.7 / 95.2 / 139.3; the planned splits 22.0 / 98.9 / 140.7.
+  // 136.6; the planned splits 22.0 / 98.9 / 140.7.  With the later plan
+  // (input gradients keeping their last round), on one box: 64 work-groups
+  // 22.1 / 96.5 / 137.2, 96 21.5 / 96.5 / 136.0, 128 21.4 / 97.3 / 136.8.
   if (wgrad && m.side && m.st == m.side) {
     const long tiles = (long)((M + tile_bm(g.tile) - 1) / tile_bm(g.tile)) * ((N + tile_bn(g.tile) - 1) / tile_bn(g.tile));
     int sp = 1;

@@ -42,7 +42,7 @@ constexpr int VOCAB_CHUNK = 8192;
 // fork / join events of the overlapped weight gradients per step (two per
 // product: 4 per layer and 2 per vocabulary chunk)
 // work-groups a weight-gradient product on the second stream aims for
-constexpr long SIDE_WG_TARGET = 64;
+constexpr long SIDE_WG_TARGET = 96;
 constexpr int OV_EVENTS = 1024;
 inline size_t align_up(size_t x, size_t a = ALIGN) { return (x + a - 1) / a * a; }
 

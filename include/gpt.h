@@ -268,7 +268,7 @@ int gpt_rope_table(const gpt_config* cfg, float* cos_out, float* sin_out);
  * order (as profiling does).  The two modes plan the weight gradients
  * differently (in order: split along K where the output has too few tiles
  * to fill the GPU, with the partial sums added in split order; overlapped:
- * the fewest of those splits that give 64 work-groups, since the product
+ * the fewest of those splits that give 96 work-groups, since the product
  * shares the GPU with the other stream), so each is bitwise reproducible
  * and they agree to fp32 summation-order rounding.  In GPT_FP8 models the
  * product reads the transposed gradient codes, which alternate between two
